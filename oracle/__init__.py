@@ -1,0 +1,303 @@
+"""Plain fp64 CPU oracle of the ZGCM-1 hybrid attention core (gated SWA + global causal).
+
+TEST INFRASTRUCTURE ONLY: only tests/, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It shares no code with the HIP path
+(``global_attention_gated_amd``) and never imports it; the only module both sides use is ``synth``,
+the seeded input generator, which holds none of the method's arithmetic.
+
+The arithmetic lives in ``zg_oracle.c`` (plain loops in float64, compiled with gcc); this module
+decodes bf16 inputs, orders the steps and keeps the oracle's own KV cache.
+
+Steps and where the pages define them (ZGCM-1 paper summaries on onedev.kr, "How it works", and
+jaehun.me, "New Approach" and "How Gated SWA Behaves"):
+  1. RMSNorm of each (token, head) row of q and k with a per-layer weight vector     -- QK-norm
+  2. partial RoPE on the leading R dims (fraction 0.33 -> R = 42 of 128)               -- Partial RoPE
+  3. visible keys: causal; gated-SWA layers also require q_pos - k_pos < W (W = 128)  -- window
+  4. softmax(q.k / sqrt(D)) . v                                                        -- A_SWA / global
+  5. gated-SWA layers multiply the output element-wise by sigmoid(g)                   -- gate
+  6. the KV cache holds the post-norm, post-RoPE key and the raw value; SWA layers keep only the last
+     W positions (slot = position mod W), global layers keep every position          -- KV cache
+Layer schedule: 32 layers, global at 6, 12, 18, 24, 30 (1-indexed), the other 27 gated SWA.
+
+Readings where the pages are silent are listed in the design doc of this repository.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "zg_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+
+
+def build(force: bool = False) -> str:
+    """Compile zg_oracle.c into liboracle.so with gcc (OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        lib.zo_rmsnorm.argtypes = [_dp, ctypes.c_int64, ctypes.c_int32, _dp, ctypes.c_double, _dp]
+        lib.zo_rope.argtypes = [_dp, ctypes.c_int64, ctypes.c_int32, _i64p, ctypes.c_int32, ctypes.c_double]
+        lib.zo_attend.argtypes = [ctypes.c_int64, ctypes.c_int32, _dp, _i64p, ctypes.c_int64, _dp, _dp, _i64p,
+                                  ctypes.c_int64, _dp, _dp]
+        lib.zo_decode_bf16.argtypes = [_u16p, ctypes.c_int64, _dp]
+        lib.zo_round_bf16.argtypes = [_dp, ctypes.c_int64, _u16p]
+        lib.zo_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(a, t):
+    return a.ctypes.data_as(t)
+
+
+def num_threads() -> int:
+    return int(_load().zo_num_threads())
+
+
+# ---------------------------------------------------------------------------- formats
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact decode of bf16 bit patterns (uint16) to float64."""
+    b = _c(bits, np.uint16)
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().zo_decode_bf16(_ptr(b, _u16p), b.size, _ptr(out, _dp))
+    return out
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
+    a = _c(x, np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().zo_round_bf16(_ptr(a, _dp), a.size, _ptr(out, _u16p))
+    return out
+
+
+def _as_f64(x) -> np.ndarray:
+    x = np.asarray(x)
+    return bf16_to_f64(x) if x.dtype == np.uint16 else _c(x, np.float64)
+
+
+# ---------------------------------------------------------------------------- steps 1-2
+def rmsnorm(x, w, eps: float) -> np.ndarray:
+    """Step 1: y = x * w / sqrt(mean(x^2) + eps) over the last axis (D)."""
+    x = _as_f64(x)
+    w = _as_f64(w)
+    D = x.shape[-1]
+    xf = _c(x.reshape(-1, D), np.float64)
+    y = np.empty_like(xf)
+    _load().zo_rmsnorm(_ptr(xf, _dp), xf.shape[0], D, _ptr(_c(w, np.float64), _dp), float(eps), _ptr(y, _dp))
+    return y.reshape(x.shape)
+
+
+def rope(x, pos, rotary_dims: int, base: float) -> np.ndarray:
+    """Step 2: rotate pairs (2i, 2i+1), 2i+1 < rotary_dims, of each row by pos * base^(-2i/R).
+
+    ``x`` has shape [..., D]; ``pos`` broadcasts against x.shape[:-1].
+    """
+    x = _as_f64(x)
+    D = x.shape[-1]
+    p = np.broadcast_to(np.asarray(pos, dtype=np.int64), x.shape[:-1])
+    xf = _c(x.reshape(-1, D), np.float64).copy()
+    pf = _c(p.reshape(-1), np.int64)
+    _load().zo_rope(_ptr(xf, _dp), xf.shape[0], D, _ptr(pf, _i64p), int(rotary_dims), float(base))
+    return xf.reshape(x.shape)
+
+
+def qk_prologue(x, pos, w, eps: float, rotary_dims: int, base: float) -> np.ndarray:
+    """Steps 1 then 2 on raw q or k rows (bf16 bits or float); returns float64."""
+    return rope(rmsnorm(x, w, eps), pos, rotary_dims, base)
+
+
+# ---------------------------------------------------------------------------- steps 3-5
+def attend(qhat, qpos, khat, v, kpos, window: int | None, gate=None) -> np.ndarray:
+    """Steps 3-5 for query rows qhat [nq, D] at positions qpos over keys khat/v [nk, D] at kpos.
+
+    window None (or <= 0) = global causal; otherwise the sliding window W.  ``gate`` = logits [nq, D]
+    (bf16 bits or float) for gated-SWA layers, None for global layers.
+    """
+    q = _c(_as_f64(qhat), np.float64)
+    k = _c(_as_f64(khat), np.float64)
+    vv = _c(_as_f64(v), np.float64)
+    nq, D = q.shape
+    nk = k.shape[0]
+    qp = _c(np.broadcast_to(np.asarray(qpos, dtype=np.int64), (nq,)), np.int64)
+    kp = _c(np.broadcast_to(np.asarray(kpos, dtype=np.int64), (nk,)), np.int64)
+    g = None if gate is None else _c(_as_f64(gate).reshape(nq, D), np.float64)
+    out = np.empty((nq, D), dtype=np.float64)
+    _load().zo_attend(nq, D, _ptr(q, _dp), _ptr(qp, _i64p), nk, _ptr(k, _dp), _ptr(vv, _dp), _ptr(kp, _i64p),
+                      0 if window is None else int(window), None if g is None else _ptr(g, _dp), _ptr(out, _dp))
+    return out
+
+
+# ---------------------------------------------------------------------------- schedule + footprint
+def is_global_layer(layer_1based: int, n_layers: int = 32) -> bool:
+    """5:1 hybrid: five blocks of (5 gated-SWA layers + 1 global layer), then 2 gated-SWA layers."""
+    if not 1 <= layer_1based <= n_layers:
+        raise ValueError("layer out of range")
+    return layer_1based % 6 == 0 and layer_1based <= 30
+
+
+def global_layers(n_layers: int = 32) -> list[int]:
+    return [l for l in range(1, n_layers + 1) if is_global_layer(l, n_layers)]
+
+
+def kv_footprint_bytes(tokens: int, *, n_layers: int = 32, global_layer_ids=None, batch: int = 1,
+                       n_kv_heads: int = 8, head_dim: int = 128, window: int = 128, elem_bytes: int = 2) -> int:
+    """KV-cache bytes for ``tokens`` positions per sequence: K and V per KV head per layer; global
+    layers store every position, SWA layers at most ``window`` positions."""
+    g = set(global_layers(n_layers) if global_layer_ids is None else global_layer_ids)
+    per_pos = 2 * n_kv_heads * head_dim * elem_bytes
+    total = 0
+    for l in range(1, n_layers + 1):
+        total += per_pos * (tokens if l in g else min(tokens, window))
+    return total * batch
+
+
+# ---------------------------------------------------------------------------- the oracle's KV cache
+class OracleCache:
+    """The oracle's KV cache: float64 history of (k_hat, v) per layer, sequence and KV head.
+
+    It keeps every position (the visible set is decided by position in ``attend``); ``ring_image`` and
+    ``global_image`` give the stored bf16 layout the method defines (SWA: slot = position mod W holding the
+    last W positions; global: index = position)."""
+
+    def __init__(self, n_layers: int, global_layer_ids, batch: int, n_kv_heads: int, head_dim: int, window: int):
+        self.L, self.B, self.Hkv, self.D, self.W = n_layers, batch, n_kv_heads, head_dim, window
+        self.glob = set(global_layer_ids)
+        self.k = {l: [[np.zeros((0, head_dim)) for _ in range(n_kv_heads)] for _ in range(batch)]
+                  for l in range(1, n_layers + 1)}
+        self.v = {l: [[np.zeros((0, head_dim)) for _ in range(n_kv_heads)] for _ in range(batch)]
+                  for l in range(1, n_layers + 1)}
+
+    def length(self, layer: int, b: int) -> int:
+        return self.k[layer][b][0].shape[0]
+
+    def append(self, layer: int, b: int, khat, v):
+        """Append positions length..length+n-1: khat, v of shape [n, Hkv, D]."""
+        khat = _as_f64(khat)
+        v = _as_f64(v)
+        for h in range(self.Hkv):
+            self.k[layer][b][h] = np.concatenate([self.k[layer][b][h], khat[:, h, :]], axis=0)
+            self.v[layer][b][h] = np.concatenate([self.v[layer][b][h], v[:, h, :]], axis=0)
+
+    def keys(self, layer: int, b: int, h: int):
+        n = self.length(layer, b)
+        return self.k[layer][b][h], self.v[layer][b][h], np.arange(n, dtype=np.int64)
+
+    def ring_image(self, layer: int):
+        """(K bits, V bits, slot positions) of an SWA layer's ring: [B][Hkv][W][D] bf16, [B][W] int64
+        (position held by each slot, -1 if none)."""
+        K = np.zeros((self.B, self.Hkv, self.W, self.D), dtype=np.uint16)
+        V = np.zeros_like(K)
+        P = np.full((self.B, self.W), -1, dtype=np.int64)
+        for b in range(self.B):
+            n = self.length(layer, b)
+            for p in range(max(0, n - self.W), n):
+                s = p % self.W
+                P[b, s] = p
+                for h in range(self.Hkv):
+                    K[b, h, s] = round_bf16(self.k[layer][b][h][p])
+                    V[b, h, s] = round_bf16(self.v[layer][b][h][p])
+        return K, V, P
+
+    def global_image(self, layer: int):
+        """(K bits, V bits) of a global layer: [B][Hkv][T][D] bf16 with T = the cache length."""
+        n = self.length(layer, 0)
+        K = np.zeros((self.B, self.Hkv, n, self.D), dtype=np.uint16)
+        V = np.zeros_like(K)
+        for b in range(self.B):
+            for h in range(self.Hkv):
+                K[b, h] = round_bf16(self.k[layer][b][h])
+                V[b, h] = round_bf16(self.v[layer][b][h])
+        return K, V
+
+
+# ---------------------------------------------------------------------------- whole-layer helpers
+def prefill_layer(q, k, v, gate, wq, wk, *, window: int | None, rotary_dims: int, base: float, eps: float,
+                  pos0: int = 0, cache: OracleCache | None = None, layer: int | None = None) -> np.ndarray:
+    """One attention layer over a chunk of S new tokens at absolute positions pos0..pos0+S-1.
+
+    q [B,S,Hq,D], k/v [B,S,Hkv,D], gate [B,S,Hq,D] (None for a global layer), wq/wk [D].
+    Keys are the cache's earlier positions (if a cache is given) followed by the chunk's own keys; the
+    chunk's k_hat and v are appended to the cache.  Query head h reads KV head h // (Hq / Hkv).
+    Returns float64 [B,S,Hq,D]."""
+    q = np.asarray(q)
+    B, S, Hq, D = q.shape
+    Hkv = np.asarray(k).shape[2]
+    G = Hq // Hkv
+    if cache is None and pos0 != 0:
+        raise ValueError("pos0 > 0 needs a cache holding positions 0..pos0-1")
+    pos = pos0 + np.arange(S, dtype=np.int64)
+    khat = qk_prologue(k, pos[None, :, None], wk, eps, rotary_dims, base)      # [B,S,Hkv,D]
+    qhat = qk_prologue(q, pos[None, :, None], wq, eps, rotary_dims, base)      # [B,S,Hq,D]
+    vf = _as_f64(v)
+    gf = None if gate is None else _as_f64(gate)
+    out = np.empty((B, S, Hq, D), dtype=np.float64)
+    for b in range(B):
+        if cache is not None:
+            if cache.length(layer, b) != pos0:
+                raise ValueError("cache length differs from pos0")
+            cache.append(layer, b, khat[b], vf[b])
+        for kh in range(Hkv):
+            if cache is not None:
+                kk, vv, kp = cache.keys(layer, b, kh)
+            else:
+                kk, vv, kp = khat[b, :, kh], vf[b, :, kh], pos
+            heads = list(range(kh * G, (kh + 1) * G))
+            qrows = qhat[b][:, heads, :].transpose(1, 0, 2).reshape(-1, D)       # [G*S, D]
+            qp = np.tile(pos, G)
+            grows = None if gf is None else gf[b][:, heads, :].transpose(1, 0, 2).reshape(-1, D)
+            o = attend(qrows, qp, kk, vv, kp, window, grows)
+            out[b][:, heads, :] = o.reshape(G, S, D).transpose(1, 0, 2)
+    return out
+
+
+def decode_step(q, k, v, gate, wq, wk, positions, cache: OracleCache, *, rotary_dims: int, base: float,
+                eps: float) -> np.ndarray:
+    """One new token per sequence in every layer: q/gate [L,B,Hq,D], k/v [L,B,Hkv,D], wq/wk [L,D],
+    positions [B] (absolute position of the new token; the cache must hold positions 0..p-1).
+    The new key and value are appended first, then the token attends over the cache (itself included).
+    Layer l (1-indexed) is global iff it is in the cache's global set; others use the window and gate.
+    Returns float64 [L,B,Hq,D]."""
+    q = np.asarray(q)
+    L, B, Hq, D = q.shape
+    Hkv = np.asarray(k).shape[2]
+    G = Hq // Hkv
+    positions = np.asarray(positions, dtype=np.int64)
+    out = np.empty((L, B, Hq, D), dtype=np.float64)
+    for li in range(L):
+        layer = li + 1
+        glob = layer in cache.glob
+        for b in range(B):
+            p = int(positions[b])
+            if cache.length(layer, b) != p:
+                raise ValueError("cache length differs from the new token's position")
+            khat = qk_prologue(np.asarray(k)[li, b][None], p, wk[li], eps, rotary_dims, base)
+            cache.append(layer, b, khat, _as_f64(np.asarray(v)[li, b])[None])
+            qhat = qk_prologue(np.asarray(q)[li, b], p, wq[li], eps, rotary_dims, base)   # [Hq, D]
+            for kh in range(Hkv):
+                kk, vv, kp = cache.keys(layer, b, kh)
+                heads = slice(kh * G, (kh + 1) * G)
+                g = None if glob else np.asarray(gate)[li, b, heads]
+                out[li, b, heads] = attend(qhat[heads], p, kk, vv, kp, None if glob else cache.W, g)
+    return out

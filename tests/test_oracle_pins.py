@@ -1,0 +1,276 @@
+"""Pins of the fp64 CPU oracle against what the pages and the mathematics fix (CPU only).
+
+Each test ties one step of the oracle to something other than the oracle itself: a library routine
+(torch's rms_norm and scaled_dot_product_attention in float64), the textbook complex form of RoPE, a
+closed form, a special case, an invariant, or a value the pages print (tests/golden/*.json).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+RNG = np.random.default_rng(12345)
+
+
+def _sdpa(q, k, v, mask):
+    """torch's softmax attention in float64 on the CPU: q [H,Sq,D], k/v [H,Sk,D], mask [Sq,Sk] bool."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=torch.from_numpy(mask)[None, None]).numpy()[0]
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+def test_rmsnorm_matches_torch_rms_norm():
+    x = RNG.standard_normal((37, 128)) * 3.0
+    w = 1.0 + 0.1 * RNG.standard_normal(128)
+    for eps in (1e-6, 0.5):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(w), eps).numpy()
+        np.testing.assert_allclose(oracle.rmsnorm(x, w, eps), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_rmsnorm_constant_vector_closed_form():
+    c, eps = -2.5, 1e-6
+    w = 1.0 + 0.1 * RNG.standard_normal(128)
+    y = oracle.rmsnorm(np.full((1, 128), c), w, eps)[0]
+    np.testing.assert_allclose(y, w * c / math.sqrt(c * c + eps), rtol=1e-14)
+
+
+def test_rmsnorm_scale_invariant_without_eps():
+    x = RNG.standard_normal((5, 64))
+    w = RNG.standard_normal(64)
+    np.testing.assert_allclose(oracle.rmsnorm(7.0 * x, w, 0.0), oracle.rmsnorm(x, w, 0.0), rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- partial RoPE
+def _rope_complex(x, pos, R, base):
+    """RoFormer's rotary embedding in complex form: pair (x_2i, x_2i+1) as x_2i + i x_2i+1, multiplied by
+    exp(i * pos * theta_i), theta_i = base^(-2i/R), for the leading R dims."""
+    y = x.copy()
+    i = np.arange(R // 2)
+    theta = base ** (-2.0 * i / R)
+    z = x[..., 0:R:2] + 1j * x[..., 1:R:2]
+    z = z * np.exp(1j * np.asarray(pos)[..., None] * theta)
+    y[..., 0:R:2] = z.real
+    y[..., 1:R:2] = z.imag
+    return y
+
+
+@pytest.mark.parametrize("R,base", [(42, 1e4), (42, 1e7), (128, 1e4), (6, 10.0)])
+def test_rope_matches_complex_form(R, base):
+    x = RNG.standard_normal((9, 128))
+    pos = np.array([0, 1, 2, 127, 128, 4095, 16383, 262143, 262144])
+    np.testing.assert_allclose(oracle.rope(x, pos, R, base), _rope_complex(x, pos, R, base), rtol=0, atol=1e-9)
+
+
+def test_rope_leaves_trailing_dims_and_position_zero_alone():
+    x = RNG.standard_normal((3, 128))
+    y = oracle.rope(x, np.array([5, 77, 262144]), 42, 1e4)
+    np.testing.assert_array_equal(y[:, 42:], x[:, 42:])
+    np.testing.assert_array_equal(oracle.rope(x, 0, 42, 1e4), x)
+
+
+def test_rope_preserves_norm_and_is_relative():
+    q = RNG.standard_normal(128)
+    k = RNG.standard_normal(128)
+    for R in (42, 128):
+        a = oracle.rope(q[None], 1000, R, 1e4)[0]
+        assert abs(np.linalg.norm(a) - np.linalg.norm(q)) < 1e-12
+        d1 = oracle.rope(q[None], 1000, R, 1e4)[0] @ oracle.rope(k[None], 990, R, 1e4)[0]
+        d2 = oracle.rope(q[None], 5010, R, 1e4)[0] @ oracle.rope(k[None], 5000, R, 1e4)[0]
+        assert abs(d1 - d2) < 1e-9
+
+
+def test_rope_rotation_direction_at_position_one():
+    # e_0 rotated by +theta_0 = +1 rad lands at (cos 1, sin 1) in dims (0, 1): counter-clockwise.
+    e0 = np.zeros((1, 128))
+    e0[0, 0] = 1.0
+    y = oracle.rope(e0, 1, 42, 1e4)[0]
+    assert abs(y[0] - math.cos(1.0)) < 1e-15 and abs(y[1] - math.sin(1.0)) < 1e-15
+
+
+# ----------------------------------------------------------------------------- attention
+def _band(Sq, Sk, qpos, kpos, window):
+    m = (kpos[None, :] <= qpos[:, None]) & (kpos[None, :] >= 0)
+    if window:
+        m &= (qpos[:, None] - kpos[None, :]) < window
+    return m
+
+
+@pytest.mark.parametrize("window", [None, 1, 4, 128])
+def test_attend_matches_torch_sdpa(window):
+    S, D = 300, 128
+    q = RNG.standard_normal((S, D))
+    k = RNG.standard_normal((S, D))
+    v = RNG.standard_normal((S, D))
+    pos = np.arange(S)
+    out = oracle.attend(q, pos, k, v, pos, window)
+    ref = _sdpa(q[None], k[None], v[None], _band(S, S, pos, pos, window))[0]
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_attend_gqa_matches_sdpa_with_repeated_kv():
+    B, S, Hq, Hkv, D = 1, 200, 8, 2, 32
+    G = Hq // Hkv
+    q = RNG.standard_normal((B, S, Hq, D))
+    k = RNG.standard_normal((B, S, Hkv, D))
+    v = RNG.standard_normal((B, S, Hkv, D))
+    w = np.ones(D)
+    o = oracle.prefill_layer(q, k, v, None, w, w, window=None, rotary_dims=0, base=1e4, eps=0.0)
+    qh = oracle.rmsnorm(q, w, 0.0)[0].transpose(1, 0, 2)
+    kh = np.repeat(oracle.rmsnorm(k, w, 0.0)[0].transpose(1, 0, 2), G, axis=0)
+    vh = np.repeat(v[0].transpose(1, 0, 2), G, axis=0)
+    pos = np.arange(S)
+    ref = _sdpa(qh, kh, vh, _band(S, S, pos, pos, None)).transpose(1, 0, 2)
+    np.testing.assert_allclose(o[0], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_zero_query_gives_mean_of_visible_values_page_window_example(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "window_example.json")))
+    W, S, D = ex["window"], 7, 16
+    v = RNG.standard_normal((S, D))
+    k = RNG.standard_normal((S, D))
+    pos = np.arange(S)
+    out = oracle.attend(np.zeros((S, D)), pos, k, v, pos, W)
+    i = ex["query_index"]
+    np.testing.assert_allclose(out[i], v[ex["visible_key_indices"]].mean(axis=0), rtol=1e-14)
+    for i in range(S):
+        lo = max(0, i - W + 1)
+        np.testing.assert_allclose(out[i], v[lo:i + 1].mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_identical_keys_give_uniform_weights():
+    S, D = 50, 32
+    k = np.tile(RNG.standard_normal(D), (S, 1))
+    v = RNG.standard_normal((S, D))
+    q = RNG.standard_normal((S, D))
+    pos = np.arange(S)
+    out = oracle.attend(q, pos, k, v, pos, None)
+    for i in range(S):
+        np.testing.assert_allclose(out[i], v[:i + 1].mean(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_window_one_is_gated_value():
+    S, D = 20, 16
+    q, k, v, g = (RNG.standard_normal((S, D)) for _ in range(4))
+    pos = np.arange(S)
+    out = oracle.attend(q, pos, k, v, pos, 1, g)
+    np.testing.assert_allclose(out, v / (1.0 + np.exp(-g)), rtol=1e-14)
+
+
+def test_window_at_least_sequence_equals_global():
+    S, D = 64, 32
+    q, k, v = (RNG.standard_normal((S, D)) for _ in range(3))
+    pos = np.arange(S)
+    np.testing.assert_array_equal(oracle.attend(q, pos, k, v, pos, S), oracle.attend(q, pos, k, v, pos, None))
+    np.testing.assert_array_equal(oracle.attend(q, pos, k, v, pos, 10 * S), oracle.attend(q, pos, k, v, pos, None))
+
+
+def test_gate_plus_infinity_is_ungated_minus_infinity_is_zero():
+    S, D = 40, 16
+    q, k, v = (RNG.standard_normal((S, D)) for _ in range(3))
+    pos = np.arange(S)
+    un = oracle.attend(q, pos, k, v, pos, 8)
+    np.testing.assert_array_equal(oracle.attend(q, pos, k, v, pos, 8, np.full((S, D), np.inf)), un)
+    assert np.all(oracle.attend(q, pos, k, v, pos, 8, np.full((S, D), -np.inf)) == 0.0)
+
+
+def test_gate_matches_page_worked_example(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "gate_example.json")))
+    a = np.array(ex["attention_output"])
+    s = np.array(ex["sigmoid_of_gate"])
+    g = np.log(s / (1.0 - s))                       # logits whose sigmoid is the page's gate
+    # window 1: the output is the query's own value, gated -- so v = the page's attention output
+    out = oracle.attend(np.zeros((1, 3)), [0], np.zeros((1, 3)), a[None], [0], 1, g[None])[0]
+    np.testing.assert_allclose(out, ex["gated_output"], rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- cache, decode, chunks
+def _small_problem(seed, L, B, S, Hq, Hkv, D):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((L, B, S, Hq, D)), r.standard_normal((L, B, S, Hkv, D)),
+            r.standard_normal((L, B, S, Hkv, D)), r.standard_normal((L, B, S, Hq, D)),
+            1 + 0.1 * r.standard_normal((L, D)), 1 + 0.1 * r.standard_normal((L, D)))
+
+
+def test_decode_equals_prefill_at_every_position():
+    L, B, S, Hq, Hkv, D, W, R = 3, 2, 140, 4, 2, 16, 8, 6
+    glob = [2]
+    q, k, v, g, wq, wk = _small_problem(7, L, B, S, Hq, Hkv, D)
+    kw = dict(rotary_dims=R, base=1e4, eps=1e-6)
+    ref = [oracle.prefill_layer(q[l], k[l], v[l], None if (l + 1) in glob else g[l], wq[l], wk[l],
+                                window=None if (l + 1) in glob else W, **kw) for l in range(L)]
+    cache = oracle.OracleCache(L, glob, B, Hkv, D, W)
+    for t in range(S):
+        o = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t], wq, wk, [t] * B, cache, **kw)
+        for l in range(L):
+            np.testing.assert_allclose(o[l], ref[l][:, t], rtol=0, atol=1e-12)
+
+
+def test_chunked_prefill_equals_one_shot():
+    L, B, S, Hq, Hkv, D, W, R = 2, 1, 300, 4, 1, 16, 32, 6
+    glob = [2]
+    q, k, v, g, wq, wk = _small_problem(9, L, B, S, Hq, Hkv, D)
+    kw = dict(rotary_dims=R, base=1e7, eps=1e-6)
+    cache = oracle.OracleCache(L, glob, B, Hkv, D, W)
+    for l in range(L):
+        gl = (l + 1) in glob
+        one = oracle.prefill_layer(q[l], k[l], v[l], None if gl else g[l], wq[l], wk[l], window=None if gl else W, **kw)
+        parts = []
+        for c0, c1 in ((0, 100), (100, 131), (131, 300)):
+            parts.append(oracle.prefill_layer(q[l][:, c0:c1], k[l][:, c0:c1], v[l][:, c0:c1],
+                                              None if gl else g[l][:, c0:c1], wq[l], wk[l], window=None if gl else W,
+                                              pos0=c0, cache=cache, layer=l + 1, **kw))
+        np.testing.assert_allclose(np.concatenate(parts, axis=1), one, rtol=0, atol=1e-12)
+
+
+def test_ring_image_holds_last_window_positions_by_slot():
+    L, B, S, Hq, Hkv, D, W = 1, 2, 300, 2, 1, 8, 128
+    q, k, v, g, wq, wk = _small_problem(3, L, B, S, Hq, Hkv, D)
+    cache = oracle.OracleCache(L, [], B, Hkv, D, W)
+    oracle.prefill_layer(q[0], k[0], v[0], g[0], wq[0], wk[0], window=W, rotary_dims=4, base=1e4, eps=1e-6,
+                         cache=cache, layer=1)
+    K, V, P = cache.ring_image(1)
+    for s in range(W):
+        p = P[0, s]
+        assert p % W == s and S - W <= p < S
+        np.testing.assert_array_equal(V[0, 0, s], oracle.round_bf16(v[0, 0, p, 0]))
+
+
+# ----------------------------------------------------------------------------- pages' closed forms
+def test_kv_footprint_matches_page(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "kv_footprint.json")))
+    L = ex["n_layers"]
+    kw = dict(n_layers=L, n_kv_heads=ex["n_kv_heads"], head_dim=ex["head_dim"], window=ex["window"],
+              elem_bytes=ex["bytes_per_elem"])
+    all_global = list(range(1, L + 1))
+    T = ex["tokens_256k"]
+    full = oracle.kv_footprint_bytes(T, global_layer_ids=all_global, **kw)
+    hyb = oracle.kv_footprint_bytes(T, **kw)
+    assert full // T == ex["full_attention_bytes_per_token"]
+    # per-token growth once every SWA ring is full
+    assert oracle.kv_footprint_bytes(T + 1, **kw) - hyb == ex["hybrid_bytes_per_token"]
+    assert round(full / 2**30, 1) == ex["full_attention_gib_256k"]
+    assert round(hyb / 2**30, 1) == ex["hybrid_gib_256k"]
+    assert round(round(full / 2**30, 1) / round(hyb / 2**30, 1), 1) == ex["reduction"]
+
+
+def test_layer_schedule_matches_page(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "layer_schedule.json")))
+    assert oracle.global_layers(ex["n_layers"]) == ex["global_layers_1based"]
+    n_glob = sum(oracle.is_global_layer(l) for l in range(1, ex["n_layers"] + 1))
+    assert (ex["n_layers"] - n_glob, n_glob) == (ex["n_swa"], ex["n_global"])
+
+
+def test_bf16_rounding_ties_to_even_and_matches_torch():
+    cases = {1.0: 0x3F80, 1.0 + 2**-8: 0x3F80, 1.0 + 3 * 2**-8: 0x3F82, -2.0: 0xC000, 0.0: 0, 3.0 + 2**-7: 0x4040}
+    for x, bits in cases.items():
+        assert int(oracle.round_bf16(np.array([x]))[0]) == bits, x
+    x = RNG.standard_normal(10000).astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.round_bf16(x), ref)
+    np.testing.assert_array_equal(oracle.bf16_to_f64(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
