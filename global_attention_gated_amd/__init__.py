@@ -1,0 +1,242 @@
+"""Python binding of libzgattn.so: the MI355X (gfx950) attention core of the ZGCM-1 hybrid backbone.
+
+Argument marshalling only: every step runs in the library's HIP kernels.  Tensors are torch CUDA
+(ROCm) tensors of dtype bfloat16, contiguous; work is enqueued on torch's current stream.  The library
+must have been built (``python -m global_attention_gated_amd.build``); importing this module raises if
+it is missing.
+
+Entry points (C ABI in include/zgattn.h):
+  swa_prefill        gated sliding-window layer prefill   (A_SWA(q,k,v) (.) sigmoid(gate))
+  global_prefill     ungated global causal layer prefill
+  hybrid_decode_step one new token per sequence through every layer of a KVCache
+  KVCache            kv_cache_alloc / kv_cache_free / footprint / layer views / lengths
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzgattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m global_attention_gated_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+ZG_OK, ZG_EINVAL, ZG_EUNSUPPORTED, ZG_ERANGE, ZG_ENOMEM, ZG_EHIP = range(6)
+_STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "ERANGE", 4: "ENOMEM", 5: "EHIP"}
+
+_vp, _i32, _i64, _u64, _f32, _f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_double
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("n_layers", _i32), ("global_layers", ctypes.POINTER(_i32)), ("n_global", _i32),
+                ("batch", _i32), ("n_kv_heads", _i32), ("head_dim", _i32), ("window", _i32),
+                ("max_tokens", _i64)]
+
+
+_lib.kv_cache_alloc.argtypes = [ctypes.POINTER(CacheDesc), ctypes.POINTER(_vp), ctypes.POINTER(_u64)]
+_lib.kv_cache_free.argtypes = [_vp]
+_lib.kv_cache_footprint_bytes.argtypes = [ctypes.POINTER(CacheDesc), _i64]
+_lib.kv_cache_footprint_bytes.restype = _u64
+_lib.kv_cache_layer_view.argtypes = [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i64)]
+_lib.kv_cache_length.argtypes = [_vp, _i32, _i32, ctypes.POINTER(_i64)]
+_lib.kv_cache_set_length.argtypes = [_vp, _i32, _i32, _i64]
+_lib.prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+_lib.prefill_workspace_bytes.restype = _u64
+_lib.swa_prefill.argtypes = [_vp] * 7 + [_i32] * 7 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
+_lib.global_prefill.argtypes = [_vp] * 6 + [_i32] * 6 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
+_lib.hybrid_decode_step.argtypes = [_vp] * 7 + [ctypes.POINTER(_i64), _i32, _i32, _f64, _f32, _vp, _vp]
+_lib.zg_last_error.restype = ctypes.c_char_p
+_lib.zg_kernel_timer_enable.argtypes = [_i32]
+_lib.zg_kernel_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_f64), ctypes.POINTER(_i64)]
+
+EXPORTED = ["kv_cache_alloc", "kv_cache_free", "kv_cache_footprint_bytes", "kv_cache_layer_view", "kv_cache_length",
+            "kv_cache_set_length", "prefill_workspace_bytes", "swa_prefill", "global_prefill", "hybrid_decode_step",
+            "zg_last_error", "zg_kernel_timer_enable", "zg_kernel_timer_read"]
+
+
+class ZgError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(rc: int):
+    if rc != ZG_OK:
+        raise ZgError(rc, _lib.zg_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _bf16(t, name):
+    if t is None:
+        return None
+    if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()):
+        raise TypeError(f"{name} must be a contiguous bfloat16 CUDA tensor")
+    return t
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ------------------------------------------------------------------------------------------- cache
+def _desc(n_layers, global_layers, batch, n_kv_heads, head_dim, window, max_tokens):
+    gl = (_i32 * max(1, len(global_layers)))(*global_layers)
+    d = CacheDesc(n_layers, gl, len(global_layers), batch, n_kv_heads, head_dim, window, max_tokens)
+    d._keep = gl
+    return d
+
+
+def footprint_bytes(tokens, *, n_layers=32, global_layers=(6, 12, 18, 24, 30), batch=1, n_kv_heads=8, head_dim=128,
+                    window=128) -> int:
+    """kv_cache_footprint_bytes: the cache bytes ``tokens`` positions of every sequence take."""
+    d = _desc(n_layers, list(global_layers), batch, n_kv_heads, head_dim, window, max(1, tokens))
+    return int(_lib.kv_cache_footprint_bytes(ctypes.byref(d), tokens))
+
+
+class KVCache:
+    """Library-owned KV cache (kv_cache_alloc / kv_cache_free)."""
+
+    def __init__(self, *, n_layers=32, global_layers=(6, 12, 18, 24, 30), batch=1, n_kv_heads=8, head_dim=128,
+                 window=128, max_tokens):
+        self.n_layers, self.global_layers = n_layers, list(global_layers)
+        self.batch, self.n_kv_heads, self.head_dim, self.window, self.max_tokens = batch, n_kv_heads, head_dim, window, max_tokens
+        self._desc = _desc(n_layers, self.global_layers, batch, n_kv_heads, head_dim, window, max_tokens)
+        h = _vp()
+        nbytes = _u64()
+        _check(_lib.kv_cache_alloc(ctypes.byref(self._desc), ctypes.byref(h), ctypes.byref(nbytes)))
+        self.handle = h.value
+        self.device_bytes = int(nbytes.value)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _check(_lib.kv_cache_free(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def layer_view(self, layer: int):
+        """(k device pointer, v device pointer, slots) of a 1-based layer."""
+        k, v, s = _vp(), _vp(), _i64()
+        _check(_lib.kv_cache_layer_view(self.handle, layer, ctypes.byref(k), ctypes.byref(v), ctypes.byref(s)))
+        return k.value, v.value, int(s.value)
+
+    def length(self, layer: int, b: int) -> int:
+        n = _i64()
+        _check(_lib.kv_cache_length(self.handle, layer, b, ctypes.byref(n)))
+        return int(n.value)
+
+    def set_length(self, layer: int, b: int, n: int):
+        _check(_lib.kv_cache_set_length(self.handle, layer, b, n))
+
+    def read_layer(self, layer: int):
+        """Copy a layer's K and V arrays to the host: two torch uint16-as-int16 CPU tensors
+        [B][Hkv][slots][D] (bf16 bits)."""
+        k, v, slots = self.layer_view(layer)
+        shape = (self.batch, self.n_kv_heads, slots, self.head_dim)
+        out = []
+        for p in (k, v):
+            t = torch.empty(shape, dtype=torch.int16)
+            _hip_memcpy_d2h(t.data_ptr(), p, t.numel() * 2)
+            out.append(t)
+        return out
+
+
+_hip = None
+
+
+def _hip_memcpy_d2h(dst, src, n):
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpy.argtypes = [_vp, _vp, ctypes.c_size_t, ctypes.c_int]
+    torch.cuda.synchronize()
+    rc = _hip.hipMemcpy(dst, src, n, 2)
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed with {rc}")
+
+
+# ------------------------------------------------------------------------------------------- prefill
+def workspace_bytes(B, S, Hkv, D=128) -> int:
+    return int(_lib.prefill_workspace_bytes(B, S, Hkv, D))
+
+
+def _prefill(gated, q, k, v, gate, q_norm_w, k_norm_w, out, window, rotary_dims, rope_base, eps, pos0, cache, layer,
+             workspace):
+    _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _bf16(gate, "gate"), _bf16(q_norm_w, "q_norm_w"), _bf16(k_norm_w, "k_norm_w")
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _bf16(out, "out")
+    need_ws = gated or cache is None
+    if workspace is None and need_ws:
+        workspace = torch.empty(max(16, workspace_bytes(B, S, Hkv, D)), dtype=torch.uint8, device=q.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ch = None if cache is None else cache.handle
+    if gated:
+        rc = _lib.swa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out),
+                              B, S, Hq, Hkv, D, window, rotary_dims, rope_base, eps, pos0, ch, layer, ws_ptr, ws_n,
+                              _stream())
+    else:
+        rc = _lib.global_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out),
+                                 B, S, Hq, Hkv, D, rotary_dims, rope_base, eps, pos0, ch, layer, ws_ptr, ws_n,
+                                 _stream())
+    _check(rc)
+    return out
+
+
+def swa_prefill(q, k, v, gate, q_norm_w, k_norm_w, out=None, *, window=128, rotary_dims=42, rope_base=1e4, eps=1e-6,
+                pos0=0, cache: KVCache | None = None, layer=0, workspace=None):
+    """Gated sliding-window layer: q/gate [B,S,Hq,D], k/v [B,S,Hkv,D], weights [D] (bf16); returns out."""
+    return _prefill(True, q, k, v, gate, q_norm_w, k_norm_w, out, window, rotary_dims, rope_base, eps, pos0, cache,
+                    layer, workspace)
+
+
+def global_prefill(q, k, v, q_norm_w, k_norm_w, out=None, *, rotary_dims=42, rope_base=1e4, eps=1e-6, pos0=0,
+                   cache: KVCache | None = None, layer=0, workspace=None):
+    """Ungated global causal layer: q [B,S,Hq,D], k/v [B,S,Hkv,D], weights [D] (bf16); returns out."""
+    return _prefill(False, q, k, v, None, q_norm_w, k_norm_w, out, 0, rotary_dims, rope_base, eps, pos0, cache,
+                    layer, workspace)
+
+
+# ------------------------------------------------------------------------------------------- decode
+def hybrid_decode_step(q, k, v, gate, q_norm_w, k_norm_w, positions, cache: KVCache, out=None, *, rotary_dims=42,
+                       rope_base=1e7, eps=1e-6):
+    """q/gate [L,B,Hq,D], k/v [L,B,Hkv,D], weights [L,D] (bf16), positions: B ints; returns out [L,B,Hq,D]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        _bf16(t, n)
+    L, B, Hq, D = q.shape
+    if (L, B, D) != (cache.n_layers, cache.batch, cache.head_dim) or tuple(k.shape) != (L, B, cache.n_kv_heads, D):
+        raise ValueError("tensor shapes do not match the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    _bf16(out, "out")
+    pos = (_i64 * B)(*[int(p) for p in positions])
+    _check(_lib.hybrid_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out),
+                                   pos, Hq, rotary_dims, rope_base, eps, cache.handle, _stream()))
+    return out
+
+
+# ------------------------------------------------------------------------------------------- timer
+def kernel_timer_enable(on: bool = True):
+    _check(_lib.zg_kernel_timer_enable(1 if on else 0))
+
+
+def kernel_timer_read(name: str):
+    """(total ms, launches) of a kernel family since the timer was enabled."""
+    ms, n = _f64(), _i64()
+    _check(_lib.zg_kernel_timer_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)

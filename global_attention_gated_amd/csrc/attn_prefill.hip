@@ -1,0 +1,365 @@
+// Prefill kernels of the ZGCM-1 attention core for gfx950 (CDNA4, wave64, MFMA).
+//
+//   kv_prologue_kernel  k_hat = RoPE(RMSNorm(k) * w_k) of a chunk, computed once and rounded to bf16 (the
+//                       KV-cache format); written as bf16 to the KV cache or, converted exactly, as fp16
+//                       to the workspace; v copied alongside when needed.
+//   attn_prefill_kernel flash-style attention of 128 query rows (one KV group) per work-group against
+//                       64-key tiles staged in LDS.  The Q prologue (RMSNorm * w_q, partial RoPE, softmax
+//                       scale) is fused into the Q load; QK^T and PV run on v_mfma_f32_32x32x16_f16 with
+//                       fp32 accumulation and fp32 online softmax.  GATED=true is the gated sliding-window
+//                       layer (band of W keys, tiles outside skipped, sigmoid(gate) in the epilogue),
+//                       GATED=false the global causal layer.
+//   ring_write_kernel   after an SWA chunk, its last min(S, W) keys/values go to ring slot pos mod W.
+//
+// Method (ZGCM-1 paper summaries: onedev.kr "How it works"; jaehun.me "How Gated SWA Behaves"):
+// per (token, head) q_hat = RoPE(RMSNorm(q) w_q), k_hat likewise; SWA output
+// softmax_{i-W < j <= i}(q_hat k_hat_j / sqrt(D)) v_j (.) sigmoid(g); global output has j <= i, no gate.
+//
+// Precision: I/O and the KV cache are bf16.  Inside the MFMAs q_hat, k_hat, P and v are fp16 (11
+// significant bits against bf16's 8): k_hat and v are bf16 values, which fp16 holds exactly in their
+// range, and q_hat and P are rounded once to fp16.  This keeps the attention error well below the bf16
+// rounding of the output.
+#include "common.h"
+#include "launch.h"
+
+namespace zg {
+namespace {
+
+constexpr int kBN = 64;         // keys per LDS tile
+constexpr int kKsStride = 136;  // halfs per K row in LDS: 128 + 8 pad (272 B keeps 16-B lane reads conflict-free)
+constexpr int kVtStride = 72;   // halfs per V^T row in LDS: 64 keys + 8 pad
+
+// ---------------------------------------------------------------------------------------------
+// k_hat prologue: one 16-lane group per (b, s, kv head) row, 8 dims per lane.
+__global__ void __launch_bounds__(256) kv_prologue_kernel(KvPrologueArgs a) {
+  const int c = threadIdx.x & 15;
+  const int64_t n_rows = (int64_t)a.B * a.S * a.Hkv;
+  const int64_t row_raw = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool valid = row_raw < n_rows;
+  const int64_t row = valid ? row_raw : n_rows - 1;
+  const int h = (int)(row % a.Hkv);
+  const int64_t s = (row / a.Hkv) % a.S;
+  const int64_t b = row / ((int64_t)a.Hkv * a.S);
+
+  float f[8];
+  unpack8(*reinterpret_cast<const uint4*>(a.k + row * kHeadDim + 8 * c), f);
+  norm_rope8_g16(f, a.kw, c, a.pos0 + s, a.eps, a.rot_pairs, a.inv_freq_rev);
+  if (valid) {
+    const int64_t off = b * a.d_sb + h * a.d_sh + s * a.d_st + 8 * c;
+    const uint4 kb = pack8(f);   // the KV-cache value of k_hat (bf16, nearest-even)
+    *reinterpret_cast<uint4*>(a.kdst + off) = a.dst_f16 ? bf16x8_to_f16x8(kb) : kb;
+    if (a.v) {
+      const uint4 vb = *reinterpret_cast<const uint4*>(a.v + row * kHeadDim + 8 * c);
+      *reinterpret_cast<uint4*>(a.vdst + off) = a.dst_f16 ? bf16x8_to_f16x8(vb) : vb;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) ring_write_kernel(RingWriteArgs a) {
+  const int c = threadIdx.x & 15;
+  const int64_t n_rows = (int64_t)a.B * a.Hkv * a.n;
+  const int64_t row_raw = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool valid = row_raw < n_rows;
+  const int64_t row = valid ? row_raw : n_rows - 1;
+  const int j = (int)(row % a.n);
+  const int h = (int)((row / a.n) % a.Hkv);
+  const int64_t b = row / ((int64_t)a.n * a.Hkv);
+  const int64_t s = a.S - a.n + j;
+  const int64_t src = ((b * a.S + s) * a.Hkv + h) * kHeadDim + 8 * c;
+  float f[8];
+  unpack8(*reinterpret_cast<const uint4*>(a.k + src), f);
+  norm_rope8_g16(f, a.kw, c, a.pos0 + s, a.eps, a.rot_pairs, a.inv_freq_rev);
+  if (valid) {
+    const int64_t slot = (a.pos0 + s) % a.W;
+    const int64_t dst = ((b * a.Hkv + h) * a.W + slot) * kHeadDim + 8 * c;
+    *reinterpret_cast<uint4*>(a.kring + dst) = pack8(f);
+    *reinterpret_cast<uint4*>(a.vring + dst) = *reinterpret_cast<const uint4*>(a.v + src);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t half_of(const uint4& w, int e) {
+  const uint32_t d = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
+  return (e & 1) ? (d >> 16) : (d & 0xffffu);
+}
+
+// Work-group: 256 threads = 4 waves; 128 query rows = G heads x P positions of one KV head; wave w
+// owns rows 32w..32w+31 (row r -> head r / P, position i0 + r % P).  The S^T = K Q^T formulation puts
+// one query per lane column, so the softmax statistics of a query live in lanes l and l+32 only.
+template <bool GATED, bool KA_BF16, bool VA_BF16>
+__global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * kKsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kHeadDim * kVtStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // Block order: consecutive block ids walk the (b, kv head) units first, so with B*Hkv a multiple of 8
+  // every block of one unit lands on the same XCD (blocks go round-robin over the 8 XCDs) and its K/V
+  // stay in that XCD's L2.  Global layers take the longest query tiles first.
+  const int unit = blockIdx.x % a.n_units;
+  const int qt_rank = blockIdx.x / a.n_units;
+  const int qt = GATED ? qt_rank : (a.n_qtiles - 1 - qt_rank);
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int i0 = qt * a.P;
+
+  const int r = wave * 32 + l32;
+  const int hq = kvh * a.G + r / a.P;
+  const int i = i0 + r % a.P;
+  const bool qvalid = i < a.S;
+  const int ic = qvalid ? i : a.S - 1;
+  const int64_t qpos = a.pos0 + ic;
+
+  // wave-uniform position range of this wave's rows (clamped to the chunk)
+  int pl_lo, pl_hi;
+  if (a.P >= 32) { pl_lo = (wave * 32) % a.P; pl_hi = pl_lo + 31; } else { pl_lo = 0; pl_hi = a.P - 1; }
+  const int64_t wlo = a.pos0 + min(i0 + pl_lo, a.S - 1);
+  const int64_t whi = a.pos0 + min(i0 + pl_hi, a.S - 1);
+
+  // key range of the work-group (absolute positions, end exclusive)
+  const int64_t khi = a.pos0 + min(i0 + a.P, a.S);
+  int64_t klo = 0;
+  if (GATED) { klo = a.pos0 + i0 - a.window + 1; if (klo < 0) klo = 0; }
+  const int t0 = (int)(klo / kBN), t1 = (int)((khi + kBN - 1) / kBN);
+
+  // ---- Q prologue: load, RMSNorm * w_q, partial RoPE, scale by log2(e)/sqrt(D), round to fp16.
+  // MFMA B operand (Q^T, K = d): lane holds q_hat[query l32][16t + 8hi .. +8] for k-step t.
+  half8 qf[8];
+  {
+    const uint16_t* qrow = a.q + (((int64_t)b * a.S + ic) * a.Hq + hq) * kHeadDim;
+    float f[8][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      unpack8(*reinterpret_cast<const uint4*>(qrow + 16 * t + 8 * hi), f[t]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) ss += f[t][e] * f[t][e];
+    }
+    ss += __shfl_xor(ss, 32);
+    const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps);
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      float w[8];
+      unpack8(*reinterpret_cast<const uint4*>(a.qw + 16 * t + 8 * hi), w);
+#pragma unroll
+      for (int e = 0; e < 8; e++) f[t][e] = f[t][e] * inv * w[e];
+      rope8(f[t], 16 * t + 8 * hi, qpos, a.rot_pairs, a.inv_freq_rev);
+#pragma unroll
+      for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)(f[t][e] * a.q_scale);
+    }
+  }
+
+  floatx16 acc_o[4];
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) acc_o[db][j] = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
+
+  // ---- tile loading roles
+  const int kc = tid & 15, kr = tid >> 4;   // K: 16-byte chunk kc of rows kr + 16 rr
+  const int vq = tid & 15, vd = tid >> 4;   // V: keys 4vq..4vq+3, dims 8vd..8vd+7
+  uint4 kreg[4], vreg[4];
+
+  auto load_tile = [&](int t) {
+    const int64_t kt = (int64_t)t * kBN;
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) {
+      const int64_t pos = kt + kr + 16 * rr;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (pos < khi) {
+        if (pos < a.a_pos0) {   // SWA ring (bf16)
+          w = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.kR + b * a.R_sb + kvh * a.R_sh +
+                                                               (pos % a.window) * kHeadDim + 8 * kc));
+        } else {
+          w = *reinterpret_cast<const uint4*>(a.kA + b * a.kA_sb + kvh * a.kA_sh + (pos - a.a_pos0) * a.kA_st + 8 * kc);
+          if (KA_BF16) w = bf16x8_to_f16x8(w);
+        }
+      }
+      kreg[rr] = w;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) {
+      const int64_t pos = kt + 4 * vq + rr;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (pos < khi) {
+        if (pos < a.a_pos0) {
+          w = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.vR + b * a.R_sb + kvh * a.R_sh +
+                                                               (pos % a.window) * kHeadDim + 8 * vd));
+        } else {
+          w = *reinterpret_cast<const uint4*>(a.vA + b * a.vA_sb + kvh * a.vA_sh + (pos - a.a_pos0) * a.vA_st + 8 * vd);
+          if (VA_BF16) w = bf16x8_to_f16x8(w);
+        }
+      }
+      vreg[rr] = w;
+    }
+  };
+  // V^T column of key k within a tile: 16-key groups, inside a group the quads 1 and 2 swap places so
+  // that the 8 keys an MFMA lane needs for one PV k-step are contiguous.
+  const int vq_in = vq & 3;
+  const int vcol = 16 * (vq >> 2) + 4 * (vq_in == 1 ? 2 : vq_in == 2 ? 1 : vq_in);
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) *reinterpret_cast<uint4*>(&Ks[buf][(kr + 16 * rr) * kKsStride + 8 * kc]) = kreg[rr];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      uint2 w;
+      w.x = half_of(vreg[0], e) | (half_of(vreg[1], e) << 16);
+      w.y = half_of(vreg[2], e) | (half_of(vreg[3], e) << 16);
+      *reinterpret_cast<uint2*>(&Vt[buf][(8 * vd + e) * kVtStride + vcol]) = w;
+    }
+  };
+
+  const half2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  auto compute = [&](int buf, int t) {
+    const int64_t kt = (int64_t)t * kBN;
+    if (kt > whi) return;                                             // beyond every query of the wave
+    if (GATED && kt + kBN - 1 < wlo - a.window + 1) return;           // before every window of the wave
+    floatx16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+      for (int j = 0; j < 16; j++) sacc[kb][j] = 0.f;
+#pragma unroll
+      for (int t8 = 0; t8 < 8; t8++) {
+        const half8 ka = *reinterpret_cast<const half8*>(&Ks[buf][(kb * 32 + l32) * kKsStride + 16 * t8 + 8 * hi]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[t8], sacc[kb], 0, 0, 0);
+      }
+    }
+    const bool full = (kt + kBN - 1 <= wlo) && (!GATED || kt >= whi - a.window + 1);
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int64_t key = kt + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+          bool vis = key <= qpos;
+          if (GATED) vis = vis && (qpos - key < a.window);
+          if (!vis) sacc[kb][j] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) mx = fmaxf(mx, sacc[kb][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    // Rescale only when the running max grows by more than 2^8: exact (the max used is carried along)
+    // and keeps every p <= 256.
+    const bool need = m_new > m_run + 8.0f;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = need ? m_new : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) acc_o[db][j] *= alpha;
+    }
+    // P = exp2(s - m) rounded to fp16; the row sum adds the same rounded values (v_dot2 with ones), so
+    // numerator and denominator use identical weights.
+    half8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; h2++) {
+        uint4 w;
+        uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int j = 8 * h2 + 2 * e;
+          wp[e] = pack_f16(__builtin_amdgcn_exp2f(sacc[kb][j] - m_run), __builtin_amdgcn_exp2f(sacc[kb][j + 1] - m_run));
+          l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2, wp[e]), ones, l_run, false);
+        }
+        pf[kb][h2] = __builtin_bit_cast(half8, w);
+      }
+#pragma unroll
+    for (int db = 0; db < 4; db++)
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+          const half8 va = *reinterpret_cast<const half8*>(&Vt[buf][(db * 32 + l32) * kVtStride + kb * 32 + 16 * h2 + 8 * hi]);
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[kb][h2], acc_o[db], 0, 0, 0);
+        }
+  };
+
+  if (t0 < t1) {
+    load_tile(t0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    const bool more = t + 1 < t1;
+    if (more) load_tile(t + 1);
+    compute(buf, t);
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O^T lane layout: acc_o[db][j] is d = 32db + 8(j/4) + 4hi + j%4 of query l32.
+  l_run += __shfl_xor(l_run, 32);
+  const float inv_l = 1.0f / l_run;
+  if (qvalid) {
+    const int64_t rowoff = (((int64_t)b * a.S + i) * a.Hq + hq) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; db++)
+#pragma unroll
+      for (int jq = 0; jq < 4; jq++) {
+        const int d = db * 32 + 8 * jq + 4 * hi;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = acc_o[db][4 * jq + e] * inv_l;
+        if (GATED) {
+          const uint2 g = *reinterpret_cast<const uint2*>(a.gate + rowoff + d);
+          o[0] *= 1.0f / (1.0f + __expf(-bf16lo(g.x)));
+          o[1] *= 1.0f / (1.0f + __expf(-bf16hi(g.x)));
+          o[2] *= 1.0f / (1.0f + __expf(-bf16lo(g.y)));
+          o[3] *= 1.0f / (1.0f + __expf(-bf16hi(g.y)));
+        }
+        uint2 w;
+        w.x = pack_bf16(o[0], o[1]);
+        w.y = pack_bf16(o[2], o[3]);
+        *reinterpret_cast<uint2*>(a.out + rowoff + d) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_prologue(const KvPrologueArgs& a, hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * a.S * a.Hkv;
+  const int64_t blocks = (rows + 15) / 16;
+  hipLaunchKernelGGL(kv_prologue_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_write(const RingWriteArgs& a, hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.n;
+  const int64_t blocks = (rows + 15) / 16;
+  hipLaunchKernelGGL(ring_write_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
+  const int64_t blocks = (int64_t)a.n_units * a.n_qtiles;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (a.gate) {
+    // gated SWA: chunk keys come from the fp16 workspace, values from the bf16 input
+    if (a.ka_bf16 || !a.va_bf16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_prefill_kernel<true, false, true>), grid, block, 0, st, a);
+  } else if (a.ka_bf16 && a.va_bf16) {
+    hipLaunchKernelGGL((attn_prefill_kernel<false, true, true>), grid, block, 0, st, a);    // from the KV cache
+  } else if (!a.ka_bf16 && !a.va_bf16) {
+    hipLaunchKernelGGL((attn_prefill_kernel<false, false, false>), grid, block, 0, st, a);  // from the workspace
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace zg

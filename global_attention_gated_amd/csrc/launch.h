@@ -1,0 +1,114 @@
+// Internal launch interface between the C-ABI host code (zgattn_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zg {
+
+constexpr int kMaxLayers = 64;
+constexpr int kMaxDecodeBatch = 128;
+constexpr int kDecodeChunk = 8192;   // keys per split-K work-group of a global decode layer
+
+// k_hat = RoPE(RMSNorm(k) * w) for a chunk of S tokens, rounded to bf16 (the KV-cache format) and
+// written to a destination with strides, either as those bf16 bits (KV cache) or converted exactly to
+// fp16 (workspace read by the fp16 MFMAs); v optionally copied alongside (bf16, or converted to fp16).
+// Rows are (b, s, h) of k [B][S][Hkv][D].
+struct KvPrologueArgs {
+  const uint16_t* k;
+  const uint16_t* v;         // nullable: copy v rows to vdst when set
+  const uint16_t* kw;        // [D]
+  uint16_t* kdst;
+  uint16_t* vdst;
+  int64_t d_sb, d_sh, d_st;  // destination element strides for (b, h, s), same for kdst and vdst
+  int32_t dst_f16;           // 1: write fp16 (workspace), 0: write bf16 (KV cache)
+  int32_t B, S, Hkv;
+  int64_t pos0;
+  int32_t rot_pairs;
+  float eps;
+  double inv_freq_rev[64];
+};
+
+// After an SWA chunk: k_hat (recomputed from k, bit-identical to the prologue's) and raw v of the chunk's
+// last n rows go to ring slot (position mod W).
+struct RingWriteArgs {
+  const uint16_t* k;         // input k [B][S][Hkv][D]
+  const uint16_t* v;         // input v [B][S][Hkv][D]
+  const uint16_t* kw;        // [D]
+  uint16_t* kring;           // [B][Hkv][W][D]
+  uint16_t* vring;
+  int32_t B, S, Hkv, W, n;   // rows S-n .. S-1 of the chunk
+  int64_t pos0;
+  int32_t rot_pairs;
+  float eps;
+  double inv_freq_rev[64];
+};
+
+struct PrefillArgs {
+  const uint16_t* q;     // [B][S][Hq][D]
+  const uint16_t* gate;  // [B][S][Hq][D], null for global layers
+  const uint16_t* qw;    // [D]
+  uint16_t* out;         // [B][S][Hq][D]
+  // key/value source A holds positions >= a_pos0: row(b,h,pos) = base + b*sb + h*sh + (pos-a_pos0)*st
+  const uint16_t* kA;        // fp16 bits (workspace) unless ka_bf16
+  const uint16_t* vA;        // fp16 bits (workspace) unless va_bf16
+  int32_t ka_bf16, va_bf16;  // source A element format; ring rows are always bf16
+  int64_t kA_sb, kA_sh, kA_st;
+  int64_t vA_sb, vA_sh, vA_st;
+  int64_t a_pos0;
+  // ring source for positions < a_pos0 (SWA chunked prefill): row = base + b*R_sb + h*R_sh + (pos mod W)*D
+  const uint16_t* kR;
+  const uint16_t* vR;
+  int64_t R_sb, R_sh;
+  int32_t B, S, Hq, Hkv, G, P;  // G = Hq/Hkv, P = 128/G query positions per work-group
+  int64_t pos0;
+  int32_t window;               // 0 for a global layer
+  int32_t rot_pairs;
+  float eps;
+  float q_scale;                // log2(e) / sqrt(D)
+  int32_t n_units;              // B * Hkv
+  int32_t n_qtiles;             // ceil(S / P)
+  double inv_freq_rev[64];
+};
+
+// One entry per layer of a KV cache, in device memory.
+struct LayerDesc {
+  uint16_t* k;
+  uint16_t* v;
+  int64_t slots;     // rows per (b, h): max_tokens (global) or W (SWA)
+  int32_t is_global;
+  int32_t index;     // global: index among global layers (for the partials); SWA: index among SWA layers
+};
+
+struct DecodeArgs {
+  const uint16_t* q;       // [L][B][Hq][D]
+  const uint16_t* k;       // [L][B][Hkv][D]
+  const uint16_t* v;
+  const uint16_t* gate;    // [L][B][Hq][D]
+  const uint16_t* qw;      // [L][D]
+  const uint16_t* kw;
+  uint16_t* out;           // [L][B][Hq][D]
+  const LayerDesc* layers; // device [L]
+  const int32_t* glob_ids; // device [n_global]: 0-based layer numbers of the global layers
+  const int32_t* swa_ids;  // device [n_swa]
+  float* part_m;           // [n_global][B][Hkv][max_chunks][G]
+  float* part_l;
+  float* part_acc;         // [n_global][B][Hkv][max_chunks][G][D]
+  int32_t L, B, Hq, Hkv, G, W;
+  int32_t n_global, n_swa, max_chunks;
+  int32_t rot_pairs;
+  float eps;
+  float q_scale;
+  double inv_freq_rev[64];
+  int64_t pos[kMaxDecodeBatch];
+};
+
+hipError_t launch_kv_prologue(const KvPrologueArgs& a, hipStream_t st);
+hipError_t launch_ring_write(const RingWriteArgs& a, hipStream_t st);
+hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_global(const DecodeArgs& a, int32_t chunks_needed, hipStream_t st);
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace zg

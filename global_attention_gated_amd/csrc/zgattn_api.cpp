@@ -1,0 +1,574 @@
+// zgattn C ABI: argument validation, KV-cache ownership, launch planning.  All device work is
+// enqueued on the caller's stream by the kernels in attn_prefill.hip and decode.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/zgattn.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace zg;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ZG_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// base^(-2i/R) / (2 pi) in double for the pairs i < R/2 (the rotary angle in revolutions per position).
+void fill_inv_freq(double* out, int rot_pairs, int rotary_dims, double base) {
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < 64; i++)
+    out[i] = i < rot_pairs ? std::pow(base, -2.0 * (double)i / (double)rotary_dims) / two_pi : 0.0;
+}
+
+// ---------------------------------------------------------------------------------- kernel timer
+struct TimerEntry {
+  hipEvent_t start, stop;
+  std::string name;
+};
+std::mutex g_timer_mu;
+bool g_timer_on = false;
+std::vector<TimerEntry> g_timer_log;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_timer_pool;
+
+struct ScopedTimer {
+  bool on = false;
+  TimerEntry ent;
+  hipStream_t st;
+  ScopedTimer(const char* name, hipStream_t s) : st(s) {
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    if (!g_timer_on) return;
+    if (g_timer_pool.empty()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      g_timer_pool.push_back({a, b});
+    }
+    ent.start = g_timer_pool.back().first;
+    ent.stop = g_timer_pool.back().second;
+    g_timer_pool.pop_back();
+    ent.name = name;
+    on = hipEventRecord(ent.start, st) == hipSuccess;
+  }
+  ~ScopedTimer() {
+    if (!on) return;
+    (void)hipEventRecord(ent.stop, st);
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    g_timer_log.push_back(ent);
+  }
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------- KV cache
+struct zg_kv_cache {
+  zg_cache_desc desc;
+  std::vector<int32_t> is_global;   // [L]
+  std::vector<int32_t> glob_ids, swa_ids;
+  std::vector<LayerDesc> layers;    // host copy
+  std::vector<int64_t> length;      // [L][B]
+  int device = 0;
+  void* arena = nullptr;
+  uint64_t arena_bytes = 0;
+  LayerDesc* d_layers = nullptr;
+  int32_t* d_glob = nullptr;
+  int32_t* d_swa = nullptr;
+  float* part_m = nullptr;
+  float* part_l = nullptr;
+  float* part_acc = nullptr;
+  int32_t max_chunks = 0;
+};
+
+namespace {
+
+int check_desc(const zg_cache_desc* d) {
+  if (!d) return fail(ZG_EINVAL, "null cache descriptor");
+  if (d->n_layers < 1 || d->n_layers > kMaxLayers) return fail(ZG_EINVAL, "n_layers must be in 1..%d", kMaxLayers);
+  if (d->n_global < 0 || d->n_global > d->n_layers) return fail(ZG_EINVAL, "n_global out of range");
+  if (d->n_global > 0 && !d->global_layers) return fail(ZG_EINVAL, "global_layers is null");
+  if (d->batch < 1 || d->n_kv_heads < 1) return fail(ZG_EINVAL, "batch and n_kv_heads must be >= 1");
+  if (d->window < 1) return fail(ZG_EINVAL, "window must be >= 1");
+  if (d->max_tokens < 1) return fail(ZG_EINVAL, "max_tokens must be >= 1");
+  std::vector<int> seen(d->n_layers + 1, 0);
+  for (int i = 0; i < d->n_global; i++) {
+    const int l = d->global_layers[i];
+    if (l < 1 || l > d->n_layers) return fail(ZG_EINVAL, "global layer %d outside 1..%d", l, d->n_layers);
+    if (seen[l]++) return fail(ZG_EINVAL, "global layer %d listed twice", l);
+  }
+  if (d->head_dim != kHeadDim) return fail(ZG_EUNSUPPORTED, "head_dim %d: only 128 is implemented", d->head_dim);
+  return ZG_OK;
+}
+
+int check_layer(const zg_kv_cache* c, int32_t layer) {
+  if (!c) return fail(ZG_EINVAL, "null cache");
+  if (layer < 1 || layer > c->desc.n_layers) return fail(ZG_EINVAL, "layer %d outside 1..%d", layer, c->desc.n_layers);
+  return ZG_OK;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) (void)hipSetDevice(dev);
+    else prev = -1;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+extern "C" uint64_t kv_cache_footprint_bytes(const zg_cache_desc* d, int64_t tokens) {
+  if (check_desc(d) != ZG_OK || tokens < 0) return 0;
+  std::vector<int> glob(d->n_layers + 1, 0);
+  for (int i = 0; i < d->n_global; i++) glob[d->global_layers[i]] = 1;
+  const uint64_t per_pos = 2ull * d->n_kv_heads * d->head_dim * 2ull;
+  uint64_t total = 0;
+  for (int l = 1; l <= d->n_layers; l++) {
+    const int64_t n = glob[l] ? tokens : (tokens < d->window ? tokens : d->window);
+    total += per_pos * (uint64_t)n;
+  }
+  return total * (uint64_t)d->batch;
+}
+
+extern "C" int kv_cache_alloc(const zg_cache_desc* d, zg_kv_cache** out, uint64_t* bytes_out) {
+  if (!out) return fail(ZG_EINVAL, "null output handle");
+  *out = nullptr;
+  int rc = check_desc(d);
+  if (rc) return rc;
+  zg_kv_cache* c = new (std::nothrow) zg_kv_cache();
+  if (!c) return fail(ZG_ENOMEM, "host allocation failed");
+  c->desc = *d;
+  c->desc.global_layers = nullptr;   // not retained
+  c->is_global.assign(d->n_layers, 0);
+  for (int i = 0; i < d->n_global; i++) c->is_global[d->global_layers[i] - 1] = 1;
+  for (int l = 0; l < d->n_layers; l++) (c->is_global[l] ? c->glob_ids : c->swa_ids).push_back(l);
+  c->length.assign((size_t)d->n_layers * d->batch, 0);
+  if (hipGetDevice(&c->device) != hipSuccess) { delete c; return fail(ZG_EHIP, "hipGetDevice failed"); }
+
+  // arena layout: per layer K then V, each [B][Hkv][slots][D] bf16, 256-byte aligned
+  const uint64_t row = (uint64_t)kHeadDim * 2;
+  uint64_t off = 0;
+  std::vector<uint64_t> koff(d->n_layers), voff(d->n_layers);
+  c->layers.resize(d->n_layers);
+  for (int l = 0; l < d->n_layers; l++) {
+    const int64_t slots = c->is_global[l] ? d->max_tokens : d->window;
+    const uint64_t bytes = (uint64_t)d->batch * d->n_kv_heads * (uint64_t)slots * row;
+    koff[l] = off; off += (bytes + 255) & ~255ull;
+    voff[l] = off; off += (bytes + 255) & ~255ull;
+    c->layers[l].slots = slots;
+    c->layers[l].is_global = c->is_global[l];
+  }
+  int gi = 0, si = 0;
+  for (int l = 0; l < d->n_layers; l++) c->layers[l].index = c->is_global[l] ? gi++ : si++;
+  c->max_chunks = (int32_t)((d->max_tokens + kDecodeChunk - 1) / kDecodeChunk);
+  const int G_max = 8;   // partial buffers sized for the largest supported group
+  const uint64_t n_part = (uint64_t)c->glob_ids.size() * d->batch * d->n_kv_heads * c->max_chunks * G_max;
+  const uint64_t part_off = off;
+  off += ((n_part * 4 + 255) & ~255ull) * 2 + ((n_part * kHeadDim * 4 + 255) & ~255ull);
+  const uint64_t meta_off = off;
+  off += (sizeof(LayerDesc) * d->n_layers + 255) & ~255ull;
+  off += 2 * ((sizeof(int32_t) * d->n_layers + 255) & ~255ull);
+
+  hipError_t e = hipMalloc(&c->arena, off);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    delete c;
+    return fail(ZG_ENOMEM, "hipMalloc of %llu bytes failed: %s", (unsigned long long)off, hipGetErrorString(e));
+  }
+  c->arena_bytes = off;
+  char* base = static_cast<char*>(c->arena);
+  for (int l = 0; l < d->n_layers; l++) {
+    c->layers[l].k = reinterpret_cast<uint16_t*>(base + koff[l]);
+    c->layers[l].v = reinterpret_cast<uint16_t*>(base + voff[l]);
+  }
+  c->part_m = reinterpret_cast<float*>(base + part_off);
+  c->part_l = reinterpret_cast<float*>(base + part_off + ((n_part * 4 + 255) & ~255ull));
+  c->part_acc = reinterpret_cast<float*>(base + part_off + 2 * ((n_part * 4 + 255) & ~255ull));
+  c->d_layers = reinterpret_cast<LayerDesc*>(base + meta_off);
+  c->d_glob = reinterpret_cast<int32_t*>(base + meta_off + ((sizeof(LayerDesc) * d->n_layers + 255) & ~255ull));
+  c->d_swa = c->d_glob + (((sizeof(int32_t) * d->n_layers + 255) & ~255ull) / sizeof(int32_t));
+
+  e = hipMemset(c->arena, 0, meta_off);
+  if (e == hipSuccess) e = hipMemcpy(c->d_layers, c->layers.data(), sizeof(LayerDesc) * d->n_layers, hipMemcpyHostToDevice);
+  if (e == hipSuccess && !c->glob_ids.empty())
+    e = hipMemcpy(c->d_glob, c->glob_ids.data(), sizeof(int32_t) * c->glob_ids.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess && !c->swa_ids.empty())
+    e = hipMemcpy(c->d_swa, c->swa_ids.data(), sizeof(int32_t) * c->swa_ids.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(c->arena);
+    delete c;
+    return hip_fail(e, "initialising the KV cache");
+  }
+  *out = c;
+  if (bytes_out) *bytes_out = off;
+  return ZG_OK;
+}
+
+extern "C" int kv_cache_free(zg_kv_cache* c) {
+  if (!c) return ZG_OK;
+  DeviceGuard g(c->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (c->arena) {
+    hipError_t e2 = hipFree(c->arena);
+    if (e == hipSuccess) e = e2;
+  }
+  delete c;
+  return e == hipSuccess ? ZG_OK : hip_fail(e, "kv_cache_free");
+}
+
+extern "C" int kv_cache_layer_view(const zg_kv_cache* c, int32_t layer, void** k, void** v, int64_t* slots) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  const LayerDesc& ld = c->layers[layer - 1];
+  if (k) *k = ld.k;
+  if (v) *v = ld.v;
+  if (slots) *slots = ld.slots;
+  return ZG_OK;
+}
+
+extern "C" int kv_cache_length(const zg_kv_cache* c, int32_t layer, int32_t b, int64_t* len) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (b < 0 || b >= c->desc.batch) return fail(ZG_EINVAL, "sequence %d outside 0..%d", b, c->desc.batch - 1);
+  if (!len) return fail(ZG_EINVAL, "null output");
+  *len = c->length[(size_t)(layer - 1) * c->desc.batch + b];
+  return ZG_OK;
+}
+
+extern "C" int kv_cache_set_length(zg_kv_cache* c, int32_t layer, int32_t b, int64_t len) {
+  int rc = check_layer(c, layer);
+  if (rc) return rc;
+  if (b < 0 || b >= c->desc.batch) return fail(ZG_EINVAL, "sequence %d outside 0..%d", b, c->desc.batch - 1);
+  if (len < 0 || (c->is_global[layer - 1] && len > c->desc.max_tokens))
+    return fail(ZG_ERANGE, "length %lld out of range", (long long)len);
+  c->length[(size_t)(layer - 1) * c->desc.batch + b] = len;
+  return ZG_OK;
+}
+
+extern "C" uint64_t prefill_workspace_bytes(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
+  if (B < 0 || S < 0 || Hkv < 0 || D < 0) return 0;
+  return 2ull * (uint64_t)B * (uint64_t)S * (uint64_t)Hkv * (uint64_t)D * 2ull;
+}
+
+// ---------------------------------------------------------------------------------- prefill
+namespace {
+
+int prefill_common(bool gated, const void* q, const void* k, const void* v, const void* gate, const void* qw,
+                   const void* kw, void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                   int32_t window, int32_t R, double base, float eps, int64_t pos0, zg_kv_cache* cache,
+                   int32_t layer, void* ws, uint64_t ws_bytes, void* stream) {
+  const char* fn = gated ? "swa_prefill" : "global_prefill";
+  if (B < 0 || S < 0) return fail(ZG_EINVAL, "%s: negative B or S", fn);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(ZG_EINVAL, "%s: Hq (%d) must be a positive multiple of Hkv (%d)", fn, Hq, Hkv);
+  if (D != kHeadDim) return fail(ZG_EUNSUPPORTED, "%s: head dim %d, only 128 is implemented", fn, D);
+  const int G = Hq / Hkv;
+  if (128 % G) return fail(ZG_EUNSUPPORTED, "%s: GQA group %d must divide 128", fn, G);
+  if (gated && window < 1) return fail(ZG_EINVAL, "%s: window must be >= 1", fn);
+  if (R < 0 || R > D || (R & 1)) return fail(ZG_EINVAL, "%s: rotary_dims %d must be even and in 0..%d", fn, R, D);
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(ZG_EINVAL, "%s: rope_base must be positive and finite", fn);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(ZG_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (pos0 < 0) return fail(ZG_EINVAL, "%s: pos0 must be >= 0", fn);
+  if (!cache && pos0 != 0) return fail(ZG_EINVAL, "%s: pos0 > 0 needs a cache holding the earlier positions", fn);
+  if ((int64_t)B * S * Hq >= (1ll << 40)) return fail(ZG_ERANGE, "%s: problem too large", fn);
+  if (cache) {
+    int rc = check_layer(cache, layer);
+    if (rc) return rc;
+    if (cache->desc.batch != B) return fail(ZG_EINVAL, "%s: cache batch %d != B %d", fn, cache->desc.batch, B);
+    if (cache->desc.n_kv_heads != Hkv) return fail(ZG_EINVAL, "%s: cache has %d KV heads, not %d", fn, cache->desc.n_kv_heads, Hkv);
+    const bool lg = cache->is_global[layer - 1] != 0;
+    if (lg == gated) return fail(ZG_EINVAL, "%s: layer %d of the cache is a %s layer", fn, layer, lg ? "global" : "gated-SWA");
+    if (gated && cache->desc.window != window) return fail(ZG_EINVAL, "%s: window %d != cache window %d", fn, window, cache->desc.window);
+    for (int b = 0; b < B; b++)
+      if (cache->length[(size_t)(layer - 1) * B + b] != pos0)
+        return fail(ZG_ERANGE, "%s: cache length of sequence %d is %lld, pos0 is %lld", fn, b,
+                    (long long)cache->length[(size_t)(layer - 1) * B + b], (long long)pos0);
+    if (!gated && pos0 + S > cache->desc.max_tokens)
+      return fail(ZG_ERANGE, "%s: positions up to %lld exceed the cache capacity %lld", fn, (long long)(pos0 + S),
+                  (long long)cache->desc.max_tokens);
+  }
+  if (B == 0 || S == 0) return ZG_OK;
+  if (!q || !k || !v || !qw || !kw || !out || (gated && !gate)) return fail(ZG_EINVAL, "%s: null tensor pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(qw) || !aligned16(kw) || !aligned16(out) ||
+      (gated && !aligned16(gate)))
+    return fail(ZG_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+  const bool need_ws = gated || !cache;
+  if (need_ws) {
+    if (!ws) return fail(ZG_EINVAL, "%s: workspace required", fn);
+    if (!aligned16(ws)) return fail(ZG_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+    if (ws_bytes < prefill_workspace_bytes(B, S, Hkv, D))
+      return fail(ZG_ERANGE, "%s: workspace of %llu bytes < %llu needed", fn, (unsigned long long)ws_bytes,
+                  (unsigned long long)prefill_workspace_bytes(B, S, Hkv, D));
+  }
+  if (cache) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != cache->device)
+      return fail(ZG_EINVAL, "%s: the cache lives on device %d, the current device is %d", fn, cache->device, cur);
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int rot_pairs = R / 2;
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  const int64_t D64 = kHeadDim;
+  const LayerDesc* ld = cache ? &cache->layers[layer - 1] : nullptr;
+
+  // 1. k_hat of the chunk, rounded to the bf16 cache format: into the cache (global layer with a cache,
+  //    with v) or, as exact fp16, into the workspace [B][Hkv][S][D] (a global layer without a cache also
+  //    puts v there, as fp16, right after the keys)
+  uint16_t* ws16 = static_cast<uint16_t*>(ws);
+  const int64_t ws_half = (int64_t)B * Hkv * S * D64;
+  KvPrologueArgs pa{};
+  pa.k = k16;
+  pa.kw = static_cast<const uint16_t*>(kw);
+  pa.B = B; pa.S = S; pa.Hkv = Hkv; pa.pos0 = pos0; pa.rot_pairs = rot_pairs; pa.eps = eps;
+  fill_inv_freq(pa.inv_freq_rev, rot_pairs, R, base);
+  if (!gated && cache) {
+    pa.v = v16;
+    pa.kdst = ld->k + pos0 * D64;
+    pa.vdst = ld->v + pos0 * D64;
+    pa.d_sb = (int64_t)Hkv * ld->slots * D64; pa.d_sh = ld->slots * D64; pa.d_st = D64;
+    pa.dst_f16 = 0;
+  } else {
+    pa.v = gated ? nullptr : v16;
+    pa.kdst = ws16;
+    pa.vdst = gated ? nullptr : ws16 + ws_half;
+    pa.d_sb = (int64_t)Hkv * S * D64; pa.d_sh = (int64_t)S * D64; pa.d_st = D64;
+    pa.dst_f16 = 1;
+  }
+  {
+    ScopedTimer tm("kv_prologue", st);
+    hipError_t e = launch_kv_prologue(pa, st);
+    if (e != hipSuccess) return hip_fail(e, "kv_prologue launch");
+  }
+
+  // 2. attention
+  PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.gate = gated ? static_cast<const uint16_t*>(gate) : nullptr;
+  a.qw = static_cast<const uint16_t*>(qw);
+  a.out = static_cast<uint16_t*>(out);
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.P = 128 / G;
+  a.pos0 = pos0;
+  a.window = gated ? window : 0;
+  a.rot_pairs = rot_pairs;
+  a.eps = eps;
+  a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
+  a.n_units = B * Hkv;
+  a.n_qtiles = (S + a.P - 1) / a.P;
+  std::memcpy(a.inv_freq_rev, pa.inv_freq_rev, sizeof a.inv_freq_rev);
+  if (!gated && cache) {          // every key from the cache (bf16), absolute positions
+    a.kA = ld->k; a.vA = ld->v;
+    a.ka_bf16 = a.va_bf16 = 1;
+    a.kA_sb = a.vA_sb = (int64_t)Hkv * ld->slots * D64;
+    a.kA_sh = a.vA_sh = ld->slots * D64;
+    a.kA_st = a.vA_st = D64;
+    a.a_pos0 = 0;
+  } else if (!gated) {            // keys and values from the workspace (fp16)
+    a.kA = ws16; a.vA = ws16 + ws_half;
+    a.ka_bf16 = a.va_bf16 = 0;
+    a.kA_sb = a.vA_sb = (int64_t)Hkv * S * D64;
+    a.kA_sh = a.vA_sh = (int64_t)S * D64;
+    a.kA_st = a.vA_st = D64;
+    a.a_pos0 = 0;
+  } else {                        // SWA: chunk keys from the workspace, values from the input, older from the ring
+    a.kA = ws16;
+    a.ka_bf16 = 0;
+    a.kA_sb = (int64_t)Hkv * S * D64; a.kA_sh = (int64_t)S * D64; a.kA_st = D64;
+    a.vA = v16;
+    a.va_bf16 = 1;
+    a.vA_sb = (int64_t)S * Hkv * D64; a.vA_sh = D64; a.vA_st = (int64_t)Hkv * D64;
+    a.a_pos0 = pos0;
+    if (cache) {
+      a.kR = ld->k; a.vR = ld->v;
+      a.R_sb = (int64_t)Hkv * window * D64; a.R_sh = (int64_t)window * D64;
+    }
+  }
+  {
+    ScopedTimer tm(gated ? "attn_swa" : "attn_global", st);
+    hipError_t e = launch_attn_prefill(a, st);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+  }
+
+  // 3. SWA with a cache: the chunk's last min(S, W) positions go to the ring (after the attention has
+  //    read the ring's previous contents)
+  if (gated && cache) {
+    RingWriteArgs ra{};
+    ra.k = k16;
+    ra.v = v16;
+    ra.kw = static_cast<const uint16_t*>(kw);
+    ra.kring = ld->k; ra.vring = ld->v;
+    ra.B = B; ra.S = S; ra.Hkv = Hkv; ra.W = window; ra.n = S < window ? S : window; ra.pos0 = pos0;
+    ra.rot_pairs = rot_pairs; ra.eps = eps;
+    std::memcpy(ra.inv_freq_rev, pa.inv_freq_rev, sizeof ra.inv_freq_rev);
+    hipError_t e = launch_ring_write(ra, st);
+    if (e != hipSuccess) return hip_fail(e, "ring write launch");
+  }
+  if (cache)
+    for (int b = 0; b < B; b++) cache->length[(size_t)(layer - 1) * B + b] = pos0 + S;
+  return ZG_OK;
+}
+
+}  // namespace
+
+extern "C" int swa_prefill(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
+                           const void* k_norm_w, void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                           int32_t window, int32_t rotary_dims, double rope_base, float eps, int64_t pos0,
+                           zg_kv_cache* cache, int32_t layer, void* workspace, uint64_t workspace_bytes,
+                           void* stream) {
+  return prefill_common(true, q, k, v, gate, q_norm_w, k_norm_w, out, B, S, Hq, Hkv, D, window, rotary_dims,
+                        rope_base, eps, pos0, cache, layer, workspace, workspace_bytes, stream);
+}
+
+extern "C" int global_prefill(const void* q, const void* k, const void* v, const void* q_norm_w, const void* k_norm_w,
+                              void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t rotary_dims, double rope_base, float eps, int64_t pos0, zg_kv_cache* cache,
+                              int32_t layer, void* workspace, uint64_t workspace_bytes, void* stream) {
+  return prefill_common(false, q, k, v, nullptr, q_norm_w, k_norm_w, out, B, S, Hq, Hkv, D, 0, rotary_dims, rope_base,
+                        eps, pos0, cache, layer, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------------- decode
+extern "C" int hybrid_decode_step(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
+                                  const void* k_norm_w, void* out, const int64_t* positions, int32_t Hq,
+                                  int32_t R, double base, float eps, zg_kv_cache* cache, void* stream) {
+  const char* fn = "hybrid_decode_step";
+  if (!cache) return fail(ZG_EINVAL, "%s: null cache", fn);
+  const zg_cache_desc& d = cache->desc;
+  const int B = d.batch, Hkv = d.n_kv_heads, L = d.n_layers;
+  if (Hq < 1 || Hq % Hkv) return fail(ZG_EINVAL, "%s: Hq (%d) must be a positive multiple of Hkv (%d)", fn, Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(ZG_EUNSUPPORTED, "%s: GQA group %d (1, 2, 4 or 8 implemented)", fn, G);
+  if (B > kMaxDecodeBatch) return fail(ZG_EUNSUPPORTED, "%s: batch %d > %d", fn, B, kMaxDecodeBatch);
+  if (R < 0 || R > kHeadDim || (R & 1)) return fail(ZG_EINVAL, "%s: rotary_dims %d must be even and in 0..128", fn, R);
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(ZG_EINVAL, "%s: rope_base must be positive and finite", fn);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(ZG_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (!positions) return fail(ZG_EINVAL, "%s: null positions", fn);
+  if (!q || !k || !v || !gate || !q_norm_w || !k_norm_w || !out) return fail(ZG_EINVAL, "%s: null tensor pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w) || !aligned16(out))
+    return fail(ZG_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+  int64_t pmax = 0;
+  for (int b = 0; b < B; b++) {
+    const int64_t p = positions[b];
+    if (p < 0) return fail(ZG_ERANGE, "%s: negative position for sequence %d", fn, b);
+    if (p >= d.max_tokens) return fail(ZG_ERANGE, "%s: position %lld of sequence %d reaches the capacity %lld", fn,
+                                       (long long)p, b, (long long)d.max_tokens);
+    for (int l = 0; l < L; l++)
+      if (cache->length[(size_t)l * B + b] != p)
+        return fail(ZG_ERANGE, "%s: layer %d of sequence %d holds %lld positions, the new token is at %lld", fn, l + 1,
+                    b, (long long)cache->length[(size_t)l * B + b], (long long)p);
+    if (p > pmax) pmax = p;
+  }
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != cache->device)
+    return fail(ZG_EINVAL, "%s: the cache lives on device %d, the current device is %d", fn, cache->device, cur);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.qw = static_cast<const uint16_t*>(q_norm_w);
+  a.kw = static_cast<const uint16_t*>(k_norm_w);
+  a.out = static_cast<uint16_t*>(out);
+  a.layers = cache->d_layers;
+  a.glob_ids = cache->d_glob;
+  a.swa_ids = cache->d_swa;
+  a.part_m = cache->part_m;
+  a.part_l = cache->part_l;
+  a.part_acc = cache->part_acc;
+  a.L = L; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.W = d.window;
+  a.n_global = (int32_t)cache->glob_ids.size();
+  a.n_swa = (int32_t)cache->swa_ids.size();
+  a.max_chunks = cache->max_chunks;
+  a.rot_pairs = R / 2;
+  a.eps = eps;
+  a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+  fill_inv_freq(a.inv_freq_rev, R / 2, R, base);
+  for (int b = 0; b < B; b++) a.pos[b] = positions[b];
+  const int32_t chunks = (int32_t)((pmax + 1 + kDecodeChunk - 1) / kDecodeChunk);
+
+  hipError_t e;
+  {
+    ScopedTimer tm("decode_append", st);
+    e = launch_decode_append(a, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode append launch");
+  {
+    ScopedTimer tm("decode_swa", st);
+    e = launch_decode_swa(a, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "decode SWA launch");
+  if (a.n_global) {
+    {
+      ScopedTimer tm("decode_global", st);
+      e = launch_decode_global(a, chunks, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "decode global launch");
+    {
+      ScopedTimer tm("decode_merge", st);
+      e = launch_decode_merge(a, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+  }
+  for (int l = 0; l < L; l++)
+    for (int b = 0; b < B; b++) cache->length[(size_t)l * B + b] = positions[b] + 1;
+  return ZG_OK;
+}
+
+extern "C" const char* zg_last_error(void) { return g_err.c_str(); }
+
+extern "C" int zg_kernel_timer_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  for (auto& t : g_timer_log) g_timer_pool.push_back({t.start, t.stop});
+  g_timer_log.clear();
+  g_timer_on = on != 0;
+  return ZG_OK;
+}
+
+extern "C" int zg_kernel_timer_read(const char* name, double* total_ms, int64_t* launches) {
+  if (!name || !total_ms || !launches) return fail(ZG_EINVAL, "zg_kernel_timer_read: null argument");
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  double sum = 0.0;
+  int64_t n = 0;
+  for (auto& t : g_timer_log) {
+    if (t.name != name) continue;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e != hipSuccess) return hip_fail(e, "zg_kernel_timer_read");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess) return hip_fail(e, "zg_kernel_timer_read");
+    sum += ms;
+    n++;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return ZG_OK;
+}

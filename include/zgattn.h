@@ -1,0 +1,160 @@
+/*
+ * zgattn.h -- C ABI of the MI355X (gfx950) attention core of the ZGCM-1 hybrid backbone:
+ * gated sliding-window attention (SWA) layers interleaved 5:1 with ungated global causal layers,
+ * GQA heads, QK-RMSNorm and partial RoPE, prefill and single-token decode against a KV cache.
+ *
+ * The operation (ZGCM-1 paper summaries: onedev.kr "How it works"; jaehun.me "New Approach" and
+ * "How Gated SWA Behaves"):
+ *   q_hat = RoPE_R(RMSNorm(q) * w_q),  k_hat = RoPE_R(RMSNorm(k) * w_k)     per (token, head), over D
+ *   gated SWA layer:  out = softmax_{j in (i-W, i]}(q_hat . k_hat_j / sqrt(D)) v_j  (.)  sigmoid(gate)
+ *   global layer:     out = softmax_{j <= i}(q_hat . k_hat_j / sqrt(D)) v_j           (no gate)
+ *   query head h reads KV head h / (Hq / Hkv).  RMSNorm: x * w / sqrt(mean(x^2) + eps).
+ *   RoPE_R rotates pairs (2i, 2i+1), 2i+1 < R, of a row at absolute position p by p * base^(-2i/R);
+ *   dims >= R are unchanged.  The window W counts the query itself.
+ * The projections around this core (q/k/v/g_proj before, o_proj after) are not part of this library:
+ * the gate argument is the precomputed g_proj(h) logits.
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as pointers to 16-bit bf16 bit patterns in DEVICE memory, contiguous,
+ *     16-byte aligned, in the stated layout (row-major, last index fastest).  Host pointers are marked.
+ *   - Only D == 128 is implemented (ZG_EUNSUPPORTED otherwise); Hq must be a multiple of Hkv and
+ *     128 must be a multiple of Hq / Hkv; rotary_dims must be even and <= D.
+ *   - Every call validates its arguments on the host first; on a non-zero status nothing has been
+ *     enqueued and zg_last_error() (thread-local) describes the failure.  On ZG_OK the work is only
+ *     enqueued on `stream` (a hipStream_t passed as void*; NULL = the default stream): outputs are
+ *     ready after the stream reaches that point, and kernel faults surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this ABI.
+ *   - The caller owns every q/k/v/gate/weight/out/workspace buffer; the library never frees them and
+ *     keeps no reference to them after the enqueued work completes.  The KV cache is library-owned.
+ *   - Calls that share a KV cache or a workspace must be ordered on one stream (or synchronised by
+ *     the caller); the library does not lock.
+ */
+#ifndef ZGATTN_H
+#define ZGATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum zg_status {
+  ZG_OK = 0,
+  ZG_EINVAL = 1,       /* malformed argument: null pointer, bad size, misalignment, inconsistent shape */
+  ZG_EUNSUPPORTED = 2, /* well-formed but not implemented (D != 128, GQA group not dividing 128, ...) */
+  ZG_ERANGE = 3,       /* position / capacity / workspace size out of range */
+  ZG_ENOMEM = 4,       /* device allocation failed */
+  ZG_EHIP = 5          /* a HIP runtime call failed (launch error, ...) */
+};
+
+/* Opaque, library-owned KV cache. */
+typedef struct zg_kv_cache zg_kv_cache;
+
+/* Shape of a KV cache.  Layers are numbered 1..n_layers; the global ones are listed in global_layers
+ * (HOST array of n_global distinct 1-based layer numbers, e.g. {6,12,18,24,30} for the 32-layer 5:1
+ * schedule of the pages).  Every other layer is a gated-SWA layer that keeps a `window`-slot ring. */
+typedef struct {
+  int32_t n_layers;
+  const int32_t* global_layers; /* HOST, may be NULL when n_global == 0 */
+  int32_t n_global;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;  /* must be 128 */
+  int32_t window;    /* SWA window W (the pages: 128) */
+  int64_t max_tokens; /* capacity of each global layer: positions 0 .. max_tokens-1 */
+} zg_cache_desc;
+
+/* Device layout of the cache (all bf16, K and V in separate arrays per layer):
+ *   global layer: K[b][kv_head][max_tokens][D], V the same; row p holds position p.
+ *   SWA layer:    K[b][kv_head][window][D],     V the same; slot p mod W holds position p
+ *                 (the last W positions; slots whose position would be negative are unused).
+ * K rows hold k_hat (after RMSNorm and RoPE, rounded to nearest-even bf16); V rows hold v unchanged.
+ * The cache also keeps, on the host, the current length (next position) of every (layer, sequence).
+ *
+ * KV-cache footprint as the pages count it (onedev.kr "How it works"; jaehun.me "Why the KV Cache
+ * Shrinks by 6.4x"): 2 (K,V) x Hkv x D x 2 bytes per position per layer, every position in a global
+ * layer and at most W positions in an SWA layer. */
+
+/* Allocate and zero a cache (one device allocation, on the current HIP device; all lengths 0).
+ * *out receives the handle; *bytes_out (nullable) the device bytes allocated.
+ * Errors: EINVAL (bad descriptor), EUNSUPPORTED (head_dim != 128), ENOMEM. */
+int kv_cache_alloc(const zg_cache_desc* desc, zg_kv_cache** out, uint64_t* bytes_out);
+
+/* Release a cache (synchronises the device first).  NULL is accepted. */
+int kv_cache_free(zg_kv_cache* cache);
+
+/* Host-only closed form: cache bytes for `tokens` positions of every sequence in desc->batch,
+ * sum over layers of 2*Hkv*D*2*batch*(global ? tokens : min(tokens, window)).  0 on a bad descriptor. */
+uint64_t kv_cache_footprint_bytes(const zg_cache_desc* desc, int64_t tokens);
+
+/* Device pointers to layer `layer`'s K and V arrays (layout above) and their slot count per (b, head)
+ * (max_tokens or window).  For filling a cache with precomputed contents, and for tests. */
+int kv_cache_layer_view(const zg_kv_cache* cache, int32_t layer, void** k, void** v, int64_t* slots);
+
+/* Current length (number of positions written) of sequence b in layer `layer`. */
+int kv_cache_length(const zg_kv_cache* cache, int32_t layer, int32_t b, int64_t* len);
+
+/* Set that length (after filling the arrays through kv_cache_layer_view).  ERANGE if len < 0 or,
+ * for a global layer, len > max_tokens. */
+int kv_cache_set_length(zg_kv_cache* cache, int32_t layer, int32_t b, int64_t len);
+
+/* Device workspace bytes that swa_prefill / global_prefill need for a chunk of S tokens:
+ * 2 * B*Hkv*S*D 16-bit elements (the chunk's normalised, rotated keys and, for a global layer without a
+ * cache, its values, staged as fp16 for the MFMAs). */
+uint64_t prefill_workspace_bytes(int32_t B, int32_t S, int32_t Hkv, int32_t D);
+
+/* Gated sliding-window attention layer, prefill of S new tokens per sequence at absolute positions
+ * pos0 .. pos0+S-1 (onedev.kr "How it works": GatedSWA(h) = o_proj(A_SWA(q,k,v) (.) sigmoid(g_proj(h))),
+ * 128-token window; jaehun.me "How Gated SWA Behaves").
+ *   q, gate, out: [B][S][Hq][D]; k, v: [B][S][Hkv][D]; q_norm_w, k_norm_w: [D]   (device bf16)
+ *   window: W >= 1; rotary_dims: R; rope_base: RoPE base; eps: RMSNorm epsilon.
+ *   cache (nullable): with a cache, keys at positions pos0-W+1 .. pos0-1 are read from layer `layer`'s
+ *     ring, whose length must equal pos0, and the chunk's last min(S, W) positions are written into
+ *     the ring (length becomes pos0+S).  Without a cache pos0 must be 0.
+ *   workspace: device buffer of at least prefill_workspace_bytes(B, S, Hkv, D) bytes, 16-byte aligned.
+ * S == 0 or B == 0 is a no-op.  Errors: EINVAL, EUNSUPPORTED, ERANGE, EHIP. */
+int swa_prefill(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
+                const void* k_norm_w, void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                int32_t window, int32_t rotary_dims, double rope_base, float eps, int64_t pos0,
+                zg_kv_cache* cache, int32_t layer, void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Ungated global causal attention layer, prefill (onedev.kr "How it works": the global layers see the
+ * whole context without the gate).  Arguments as swa_prefill without gate and window.
+ *   cache (nullable): with a cache, layer `layer` must be a global layer of the cache whose length
+ *     equals pos0 (positions 0..pos0-1 are read from it: chunked prefill), pos0+S <= max_tokens, and the
+ *     chunk's k_hat and v are written at rows pos0 .. pos0+S-1 first.  Without a cache pos0 must be 0.
+ *   workspace: as swa_prefill (unused, may be NULL, when a cache is given). */
+int global_prefill(const void* q, const void* k, const void* v, const void* q_norm_w, const void* k_norm_w,
+                   void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t rotary_dims,
+                   double rope_base, float eps, int64_t pos0, zg_kv_cache* cache, int32_t layer,
+                   void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* One decode step of every layer of the cache: each sequence b adds one token at absolute position
+ * positions[b] (HOST array [B]; must equal the cache length of every layer for that sequence).
+ *   q, gate, out: [L][B][Hq][D]; k, v: [L][B][Hkv][D]; q_norm_w, k_norm_w: [L][D]   (device bf16)
+ *   with L = the cache's n_layers, B = its batch.  gate rows of global layers are ignored.
+ * Per layer the new k_hat and v are appended first (SWA: ring slot p mod W; global: row p), then the
+ * token attends over the cache (itself included): SWA layers over positions p-W+1..p with the gate,
+ * global layers over 0..p without it.  The layers' inputs are all given, so the layers are computed
+ * concurrently.  Every length advances by one.  Errors: EINVAL, EUNSUPPORTED, ERANGE (a position that
+ * differs from the cache length or reaches max_tokens), EHIP. */
+int hybrid_decode_step(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
+                       const void* k_norm_w, void* out, const int64_t* positions, int32_t Hq,
+                       int32_t rotary_dims, double rope_base, float eps, zg_kv_cache* cache, void* stream);
+
+/* Thread-local description of the last non-OK status returned on this thread ("" if none). */
+const char* zg_last_error(void);
+
+/* Kernel timer: while enabled, every launch of the main attention kernels records a pair of HIP
+ * events on the launch stream.  zg_kernel_timer_read synchronises on the recorded events and returns,
+ * for the kernel family `name` ("attn_swa", "attn_global", "decode_global", "decode_swa",
+ * "kv_prologue", "decode_merge", "decode_append"), the summed device time in ms and the launch count
+ * since the last reset.  Enabling resets the counters. */
+int zg_kernel_timer_enable(int32_t on);
+int zg_kernel_timer_read(const char* name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZGATTN_H */

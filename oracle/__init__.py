@@ -15,8 +15,11 @@ jaehun.me, "New Approach" and "How Gated SWA Behaves"):
   3. visible keys: causal; gated-SWA layers also require q_pos - k_pos < W (W = 128)  -- window
   4. softmax(q.k / sqrt(D)) . v                                                        -- A_SWA / global
   5. gated-SWA layers multiply the output element-wise by sigmoid(g)                   -- gate
-  6. the KV cache holds the post-norm, post-RoPE key and the raw value; SWA layers keep only the last
-     W positions (slot = position mod W), global layers keep every position          -- KV cache
+  6. the KV cache holds the post-norm, post-RoPE key and the raw value, in bf16 (jaehun.me, "Why the KV
+     Cache Shrinks by 6.4x": 2 bytes per element since it is bf16); SWA layers keep only the last W
+     positions (slot = position mod W), global layers keep every position             -- KV cache
+     Keys enter attention in that stored form, k_hat rounded once to bf16 (nearest-even), in prefill as
+     in decode; q_hat, the scores, the softmax and the output stay in float64.
 Layer schedule: 32 layers, global at 6, 12, 18, 24, 30 (1-indexed), the other 27 gated SWA.
 
 Readings where the pages are silent are listed in the design doc of this repository.
@@ -126,6 +129,11 @@ def rope(x, pos, rotary_dims: int, base: float) -> np.ndarray:
 def qk_prologue(x, pos, w, eps: float, rotary_dims: int, base: float) -> np.ndarray:
     """Steps 1 then 2 on raw q or k rows (bf16 bits or float); returns float64."""
     return rope(rmsnorm(x, w, eps), pos, rotary_dims, base)
+
+
+def cache_key(khat) -> np.ndarray:
+    """Step 6: the stored (bf16, nearest-even) form of k_hat, as float64: what attention reads."""
+    return bf16_to_f64(round_bf16(khat))
 
 
 # ---------------------------------------------------------------------------- steps 3-5
@@ -248,7 +256,7 @@ def prefill_layer(q, k, v, gate, wq, wk, *, window: int | None, rotary_dims: int
     if cache is None and pos0 != 0:
         raise ValueError("pos0 > 0 needs a cache holding positions 0..pos0-1")
     pos = pos0 + np.arange(S, dtype=np.int64)
-    khat = qk_prologue(k, pos[None, :, None], wk, eps, rotary_dims, base)      # [B,S,Hkv,D]
+    khat = cache_key(qk_prologue(k, pos[None, :, None], wk, eps, rotary_dims, base))   # [B,S,Hkv,D]
     qhat = qk_prologue(q, pos[None, :, None], wq, eps, rotary_dims, base)      # [B,S,Hq,D]
     vf = _as_f64(v)
     gf = None if gate is None else _as_f64(gate)
@@ -292,7 +300,7 @@ def decode_step(q, k, v, gate, wq, wk, positions, cache: OracleCache, *, rotary_
             p = int(positions[b])
             if cache.length(layer, b) != p:
                 raise ValueError("cache length differs from the new token's position")
-            khat = qk_prologue(np.asarray(k)[li, b][None], p, wk[li], eps, rotary_dims, base)
+            khat = cache_key(qk_prologue(np.asarray(k)[li, b][None], p, wk[li], eps, rotary_dims, base))
             cache.append(layer, b, khat, _as_f64(np.asarray(v)[li, b])[None])
             qhat = qk_prologue(np.asarray(q)[li, b], p, wq[li], eps, rotary_dims, base)   # [Hq, D]
             for kh in range(Hkv):

@@ -1,0 +1,87 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point, and rejects malformed
+arguments with a status code before touching the GPU (no device is needed for these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def zg():
+    lib = os.path.join(ROOT, "global_attention_gated_amd", "libzgattn.so")
+    if not os.path.exists(lib):
+        import __graft_entry__
+        __graft_entry__.build()
+    import global_attention_gated_amd as m
+    return m
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "zgattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_entry_points_are_exported(zg):
+    names = _declared()
+    assert {"swa_prefill", "global_prefill", "hybrid_decode_step", "kv_cache_alloc"} <= set(names)
+    lib = ctypes.CDLL(zg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(zg.EXPORTED) == set(names)
+
+
+def test_footprint_closed_form_matches_oracle_and_page(zg):
+    for T in (0, 1, 127, 128, 129, 4096, 262144):
+        assert zg.footprint_bytes(T) == oracle.kv_footprint_bytes(T)
+        assert zg.footprint_bytes(T, global_layers=range(1, 33)) == oracle.kv_footprint_bytes(T, global_layer_ids=range(1, 33))
+    assert zg.footprint_bytes(262144, global_layers=range(1, 33)) == 32 * 2**30
+    assert round(zg.footprint_bytes(262144) / 2**30, 1) == 5.0
+    assert zg.footprint_bytes(1001) - zg.footprint_bytes(1000) == 20480
+    assert zg.footprint_bytes(10, batch=3) == 3 * zg.footprint_bytes(10)
+
+
+def test_workspace_bytes(zg):
+    assert zg.workspace_bytes(1, 16384, 8) == 2 * 16384 * 8 * 128 * 2
+
+
+def _swa(zg, **over):
+    a = dict(q=16, k=16, v=16, gate=16, qw=16, kw=16, out=16, B=1, S=4, Hq=4, Hkv=1, D=128, window=128, R=42,
+             base=1e4, eps=1e-6, pos0=0, cache=None, layer=0, ws=16, ws_bytes=1 << 20, stream=None)
+    a.update(over)
+    return zg._lib.swa_prefill(a["q"], a["k"], a["v"], a["gate"], a["qw"], a["kw"], a["out"], a["B"], a["S"], a["Hq"],
+                               a["Hkv"], a["D"], a["window"], a["R"], a["base"], a["eps"], a["pos0"], a["cache"],
+                               a["layer"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(D=64), 2), (dict(Hq=6, Hkv=4), 1), (dict(Hq=12, Hkv=1), 2), (dict(window=0), 1), (dict(R=41), 1),
+    (dict(R=130), 1), (dict(base=0.0), 1), (dict(eps=-1.0), 1), (dict(pos0=3), 1), (dict(q=None), 1),
+    (dict(gate=None), 1), (dict(out=24), 1), (dict(ws=None), 1), (dict(ws_bytes=100), 3), (dict(B=-1), 1),
+])
+def test_swa_prefill_rejects_bad_arguments(zg, over, status):
+    assert _swa(zg, **over) == status
+    assert zg._lib.zg_last_error()
+
+
+def test_noop_sizes_return_ok(zg):
+    assert _swa(zg, S=0) == 0
+    assert _swa(zg, B=0) == 0
+
+
+def test_decode_and_cache_reject_bad_arguments(zg):
+    lib = zg._lib
+    assert lib.hybrid_decode_step(16, 16, 16, 16, 16, 16, 16, None, 32, 42, 1e7, 1e-6, None, None) == 1
+    bad = zg._desc(32, [6, 12], 1, 8, 64, 128, 1024)
+    h = ctypes.c_void_p()
+    assert lib.kv_cache_alloc(ctypes.byref(bad), ctypes.byref(h), None) == 2
+    bad = zg._desc(32, [6, 6], 1, 8, 128, 128, 1024)
+    assert lib.kv_cache_alloc(ctypes.byref(bad), ctypes.byref(h), None) == 1
+    bad = zg._desc(32, [33], 1, 8, 128, 128, 1024)
+    assert lib.kv_cache_alloc(ctypes.byref(bad), ctypes.byref(h), None) == 1
+    assert lib.kv_cache_free(None) == 0

@@ -1,0 +1,206 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the same seeded inputs.
+
+Bar: |gpu_bf16 - oracle_fp64| <= 1e-2 per element and <= 1e-3 on average; KV-cache layout and indexing
+bit-exact (V bytes equal; K within one bf16 ulp of the oracle's rounding of k_hat).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _inputs import Layer, compare, to_dev, to_host_bits, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def zg():
+    import torch
+    assert torch.cuda.is_available()
+    import global_attention_gated_amd as m
+    return m
+
+
+def gpu_prefill(zg, L, gated, window, R, base, eps, **kw):
+    if gated:
+        return zg.swa_prefill(L.dq, L.dk, L.dv, L.dgate, L.dwq, L.dwk, window=window, rotary_dims=R, rope_base=base,
+                              eps=eps, **kw)
+    return zg.global_prefill(L.dq, L.dk, L.dv, L.dwq, L.dwk, rotary_dims=R, rope_base=base, eps=eps, **kw)
+
+
+def oracle_prefill(L, gated, window, R, base, eps, **kw):
+    return oracle.prefill_layer(L.q, L.k, L.v, L.gate if gated else None, L.wq, L.wk,
+                                window=window if gated else None, rotary_dims=R, base=base, eps=eps, **kw)
+
+
+# ------------------------------------------------------------------------------------------ generator
+def test_gpu_generator_is_bit_equal_to_cpu(zg):
+    import torch
+    for shape, off in (((1000,), 0), ((3, 77), 5), ((2, 4096, 8, 128), 123456789)):
+        d = synth.normal_bf16_device(1004, 7, synth.TENSOR_CACHE_K, shape, index_offset=off)
+        np.testing.assert_array_equal(to_host_bits(d), synth.normal_bf16(1004, 7, synth.TENSOR_CACHE_K, shape, off))
+    # strided fill: 5 rows of 40 elements into a buffer of row stride 64, indices 1000 + 100*o + i
+    buf = torch.zeros(5 * 64, dtype=torch.bfloat16, device="cuda")
+    synth.fill_device(buf.data_ptr(), 1, 2, 3, 5, 40, 64, 1000, 100)
+    got = to_host_bits(buf).reshape(5, 64)
+    for o in range(5):
+        np.testing.assert_array_equal(got[o, :40], synth.normal_bf16_at(1, 2, 3, 1000 + 100 * o + np.arange(40)))
+        assert np.all(got[o, 40:] == 0)
+
+
+# ------------------------------------------------------------------------------------------ prefill
+def test_single_gated_swa_layer_1x512_4q1kv(zg):
+    """One gated-SWA layer: batch 1, seq 512, 4 query / 1 KV head, window 128, weights 1, eps 1e-6, RoPE on
+    42 dims with base 10,000, seed 1001 -- compared in full."""
+    L = Layer(1001, 0, 1, 512, 4, 1, w_spread=0.0)
+    got = to_host_f64(gpu_prefill(zg, L, True, 128, 42, 1e4, 1e-6))
+    compare(got, oracle_prefill(L, True, 128, 42, 1e4, 1e-6), "swa 1x512")
+
+
+SHAPES = [
+    # gated, B, S, Hq, Hkv, window, rotary dims
+    (True, 2, 300, 8, 2, 128, 42),
+    (True, 1, 200, 4, 4, 16, 42),
+    (True, 1, 257, 16, 2, 128, 42),
+    (True, 1, 130, 2, 1, 1, 42),
+    (True, 1, 100, 4, 1, 4, 128),
+    (True, 1, 97, 4, 1, 1000, 0),
+    (True, 3, 33, 32, 8, 128, 42),
+    (False, 2, 300, 8, 2, None, 42),
+    (False, 1, 700, 4, 1, None, 42),
+    (False, 1, 257, 16, 2, None, 42),
+    (False, 1, 1, 4, 1, None, 42),
+    (False, 1, 65, 4, 4, None, 42),
+    (False, 1, 129, 32, 8, None, 128),
+]
+
+
+@pytest.mark.parametrize("gated,B,S,Hq,Hkv,W,R", SHAPES)
+def test_prefill_shapes(zg, gated, B, S, Hq, Hkv, W, R):
+    L = Layer(2000 + S, 3, B, S, Hq, Hkv, gated=gated)
+    got = to_host_f64(gpu_prefill(zg, L, gated, W, R, 1e4, 1e-6))
+    compare(got, oracle_prefill(L, gated, W, R, 1e4, 1e-6), f"{'swa' if gated else 'global'} B{B} S{S} {Hq}/{Hkv} W{W} R{R}")
+
+
+def test_gate_infinities(zg):
+    import torch
+    L = Layer(77, 1, 1, 300, 8, 2)
+    plus = torch.full_like(L.dgate, float("inf"))
+    minus = torch.full_like(L.dgate, float("-inf"))
+    o_plus = zg.swa_prefill(L.dq, L.dk, L.dv, plus, L.dwq, L.dwk, window=1 << 20, rotary_dims=42, rope_base=1e4, eps=1e-6)
+    o_glob = zg.global_prefill(L.dq, L.dk, L.dv, L.dwq, L.dwk, rotary_dims=42, rope_base=1e4, eps=1e-6)
+    o_minus = zg.swa_prefill(L.dq, L.dk, L.dv, minus, L.dwq, L.dwk, window=128, rotary_dims=42, rope_base=1e4, eps=1e-6)
+    np.testing.assert_array_equal(to_host_bits(o_plus), to_host_bits(o_glob))
+    assert np.all(to_host_f64(o_minus) == 0.0)
+
+
+def test_empty_inputs_are_noops(zg):
+    import torch
+    L = Layer(5, 0, 1, 8, 4, 1)
+    e = torch.empty((1, 0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    ek = torch.empty((1, 0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    out = zg.swa_prefill(e, ek, ek, e, L.dwq, L.dwk, window=128)
+    assert out.numel() == 0
+    out = zg.global_prefill(e, ek, ek, L.dwq, L.dwk)
+    assert out.numel() == 0
+
+
+# ------------------------------------------------------------------------------------------ cache
+def _cache_check(zg, cache, ocache, layer, glob):
+    K, V = cache.read_layer(layer)
+    K = K.numpy().view(np.uint16)
+    V = V.numpy().view(np.uint16)
+    if glob:
+        OK, OV = ocache.global_image(layer)
+        n = OK.shape[2]
+        K, V = K[:, :, :n], V[:, :, :n]
+    else:
+        OK, OV, P = ocache.ring_image(layer)
+        valid = P >= 0
+        K = np.where(valid[:, None, :, None], K, 0)
+        V = np.where(valid[:, None, :, None], V, 0)
+    np.testing.assert_array_equal(V, OV)
+    kd = np.abs(K.astype(np.int32) - OK.astype(np.int32))     # same sign: bit distance = ulp distance
+    assert kd.max() <= 1, f"layer {layer}: k_hat differs by {kd.max()} ulp"
+    return float(np.mean(kd != 0))
+
+
+def test_chunked_prefill_with_cache_matches_oracle(zg):
+    """A 2-layer cache (layer 1 gated SWA with window 128, layer 2 global), 2 sequences of 400 tokens in
+    chunks of 150, 40 and 210: every chunk's output against the oracle, then the cache images."""
+    B, Hq, Hkv, R, base, eps, W = 2, 8, 2, 42, 1e7, 1e-6, 128
+    cache = zg.KVCache(n_layers=2, global_layers=[2], batch=B, n_kv_heads=Hkv, window=W, max_tokens=512)
+    ocache = oracle.OracleCache(2, [2], B, Hkv, 128, W)
+    S_total = 400
+    mism = []
+    for layer, gated in ((1, True), (2, False)):
+        pos0 = 0
+        for S in (150, 40, 210):
+            L = Layer(31, layer, B, S, Hq, Hkv, gated=gated, pos0=pos0, S_total=S_total)
+            got = to_host_f64(gpu_prefill(zg, L, gated, W, R, base, eps, pos0=pos0, cache=cache, layer=layer))
+            ref = oracle_prefill(L, gated, W, R, base, eps, pos0=pos0, cache=ocache, layer=layer)
+            compare(got, ref, f"layer {layer} chunk at {pos0}")
+            pos0 += S
+        assert cache.length(layer, 0) == S_total and cache.length(layer, 1) == S_total
+        mism.append(_cache_check(zg, cache, ocache, layer, not gated))
+    assert max(mism) < 0.01
+    cache.close()
+
+
+# ------------------------------------------------------------------------------------------ decode
+def _decode_inputs(seed, L, B, Hq, Hkv, step):
+    def gen(tensor, H, layer_base=0):
+        return synth.normal_bf16(seed, 1000 + step, tensor, (L, B, H, 128))
+    q, k, v, g = gen(synth.TENSOR_Q, Hq), gen(synth.TENSOR_K, Hkv), gen(synth.TENSOR_V, Hkv), gen(synth.TENSOR_GATE, Hq)
+    return q, k, v, g
+
+
+def test_decode_after_prefill_matches_oracle(zg):
+    """3 layers (global = layer 2), window 16, 3 sequences: prefill 37 tokens into the cache, then 24
+    decode steps (ring wrap-around included); every step against the oracle's decode."""
+    Lh, B, Hq, Hkv, W, R, base, eps = 3, 3, 8, 2, 16, 42, 1e7, 1e-6
+    glob = [2]
+    cache = zg.KVCache(n_layers=Lh, global_layers=glob, batch=B, n_kv_heads=Hkv, window=W, max_tokens=100)
+    ocache = oracle.OracleCache(Lh, glob, B, Hkv, 128, W)
+    wq = np.stack([synth.norm_weight_bf16(9, l, synth.TENSOR_WQ, 128) for l in range(Lh)])
+    wk = np.stack([synth.norm_weight_bf16(9, l, synth.TENSOR_WK, 128) for l in range(Lh)])
+    S0 = 37
+    for li in range(Lh):
+        gated = (li + 1) not in glob
+        L = Layer(9, li, B, S0, Hq, Hkv, gated=gated)
+        L.wq, L.wk, L.dwq, L.dwk = wq[li], wk[li], to_dev(wq[li]), to_dev(wk[li])
+        gpu_prefill(zg, L, gated, W, R, base, eps, cache=cache, layer=li + 1)
+        oracle_prefill(L, gated, W, R, base, eps, cache=ocache, layer=li + 1)
+    dwq, dwk = to_dev(wq), to_dev(wk)
+    for step in range(24):
+        p = S0 + step
+        q, k, v, g = _decode_inputs(9, Lh, B, Hq, Hkv, step)
+        got = to_host_f64(zg.hybrid_decode_step(to_dev(q), to_dev(k), to_dev(v), to_dev(g), dwq, dwk, [p] * B, cache,
+                                                rotary_dims=R, rope_base=base, eps=eps))
+        ref = oracle.decode_step(q, k, v, g, wq, wk, [p] * B, ocache, rotary_dims=R, base=base, eps=eps)
+        compare(got, ref, f"decode step at {p}")
+    for li in range(Lh):
+        _cache_check(zg, cache, ocache, li + 1, (li + 1) in glob)
+    cache.close()
+
+
+def test_decode_from_empty_cache_equals_prefill(zg):
+    """Token-by-token decode from position 0 reproduces the oracle's prefill of the same inputs."""
+    Lh, B, Hq, Hkv, W, R, base, eps, S = 2, 2, 4, 1, 8, 42, 1e4, 1e-6, 40
+    glob = [2]
+    cache = zg.KVCache(n_layers=Lh, global_layers=glob, batch=B, n_kv_heads=Hkv, window=W, max_tokens=64)
+    layers = [Layer(11, li, B, S, Hq, Hkv, gated=(li + 1) not in glob, device=None) for li in range(Lh)]
+    wq = np.stack([l.wq for l in layers])
+    wk = np.stack([l.wk for l in layers])
+    refs = [oracle_prefill(l, (li + 1) not in glob, W, R, base, eps) for li, l in enumerate(layers)]
+    dwq, dwk = to_dev(wq), to_dev(wk)
+    for t in range(S):
+        q = np.stack([l.q[:, t] for l in layers])
+        k = np.stack([l.k[:, t] for l in layers])
+        v = np.stack([l.v[:, t] for l in layers])
+        g = np.stack([l.gate[:, t] if l.gate is not None else np.zeros_like(l.q[:, t]) for l in layers])
+        got = to_host_f64(zg.hybrid_decode_step(to_dev(q), to_dev(k), to_dev(v), to_dev(g), dwq, dwk, [t] * B, cache,
+                                                rotary_dims=R, rope_base=base, eps=eps))
+        for li in range(Lh):
+            compare(got[li], refs[li][:, t], f"decode t={t} layer {li + 1}")
+    cache.close()

@@ -122,7 +122,9 @@ def test_attend_gqa_matches_sdpa_with_repeated_kv():
     w = np.ones(D)
     o = oracle.prefill_layer(q, k, v, None, w, w, window=None, rotary_dims=0, base=1e4, eps=0.0)
     qh = oracle.rmsnorm(q, w, 0.0)[0].transpose(1, 0, 2)
-    kh = np.repeat(oracle.rmsnorm(k, w, 0.0)[0].transpose(1, 0, 2), G, axis=0)
+    # keys enter attention in the bf16 cache format
+    kb = oracle.bf16_to_f64(oracle.round_bf16(oracle.rmsnorm(k, w, 0.0)))
+    kh = np.repeat(kb[0].transpose(1, 0, 2), G, axis=0)
     vh = np.repeat(v[0].transpose(1, 0, 2), G, axis=0)
     pos = np.arange(S)
     ref = _sdpa(qh, kh, vh, _band(S, S, pos, pos, None)).transpose(1, 0, 2)
@@ -226,6 +228,23 @@ def test_chunked_prefill_equals_one_shot():
                                               None if gl else g[l][:, c0:c1], wq[l], wk[l], window=None if gl else W,
                                               pos0=c0, cache=cache, layer=l + 1, **kw))
         np.testing.assert_allclose(np.concatenate(parts, axis=1), one, rtol=0, atol=1e-12)
+
+
+def test_prefill_keys_are_read_in_bf16_cache_form():
+    """Attention over keys reads k_hat as stored in the bf16 cache: rounding k_hat first changes nothing,
+    perturbing it by less than half a bf16 ulp changes nothing either."""
+    B, S, Hq, Hkv, D = 1, 50, 2, 1, 16
+    r = np.random.default_rng(5)
+    q, k, v = r.standard_normal((B, S, Hq, D)), r.standard_normal((B, S, Hkv, D)), r.standard_normal((B, S, Hkv, D))
+    w = np.ones(D)
+    kw = dict(window=None, rotary_dims=4, base=1e4, eps=1e-6)
+    o = oracle.prefill_layer(q, k, v, None, w, w, **kw)
+    pos = np.arange(S)
+    qh = oracle.qk_prologue(q, pos[None, :, None], w, 1e-6, 4, 1e4)[0]
+    kh = oracle.qk_prologue(k, pos[None, :, None], w, 1e-6, 4, 1e4)[0, :, 0]
+    kb = oracle.bf16_to_f64(oracle.round_bf16(kh))
+    for h in range(Hq):
+        np.testing.assert_allclose(o[0, :, h], oracle.attend(qh[:, h], pos, kb, v[0, :, 0], pos, None), rtol=1e-12, atol=1e-13)
 
 
 def test_ring_image_holds_last_window_positions_by_slot():
