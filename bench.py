@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of the ZGCM-1 attention core on one MI355X.
+
+Headline workload: the full 32-layer attention schedule (27 gated-SWA layers, global causal layers at
+6, 12, 18, 24, 30) prefilling one 16,384-token sequence, 32 query / 8 KV heads of dim 128, window 128,
+RoPE on 42 dims with base 10,000, seeded N(0,1) bf16 q/k/v/gate per layer.  One step = the 32 layer
+calls.  Metric: attention tokens/s (16,384 / step time) and the global-layer kernel against the MFMA
+roofline.
+
+Second workload ("decode"): one hybrid decode step of 32 sequences, each at position 262,144, through all
+32 layers: the 5 global layers read full bf16 KV caches (262,144 cached positions x 8 KV heads x 128) and
+the 27 SWA layers their 128-slot rings; cache contents and new q/k/v/gate ~N(0,1), RoPE base 1e7.
+Metric: tokens/s (32 / step time), and the split-K decode kernel against the HBM roofline.
+
+Inputs are generated on the GPU before the timed region.  The CPU baseline times the fp64 oracle on a
+bounded sample of the prefill workload (see cpu_baseline.sample in the output).
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-decode] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, TFLOP/s
+GLOBAL_LAYERS = (6, 12, 18, 24, 30)
+N_LAYERS, HQ, HKV, D, W, R = 32, 32, 8, 128, 128, 42
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------------------------ prefill
+def setup_prefill(seed=1003, S=16384, B=1):
+    import torch
+    import synth
+    layers = []
+    for l in range(1, N_LAYERS + 1):
+        glob = l in GLOBAL_LAYERS
+        t = {}
+        for name, tid, H in (("q", synth.TENSOR_Q, HQ), ("k", synth.TENSOR_K, HKV), ("v", synth.TENSOR_V, HKV)) + \
+                (() if glob else (("gate", synth.TENSOR_GATE, HQ),)):
+            t[name] = synth.normal_bf16_device(seed, l, tid, (B, S, H, D))
+        for name, tid in (("wq", synth.TENSOR_WQ), ("wk", synth.TENSOR_WK)):
+            bits = synth.norm_weight_bf16(seed, l, tid, D)
+            t[name] = torch.from_numpy(bits.view("int16")).cuda().view(torch.bfloat16)
+        t["out"] = torch.empty((B, S, HQ, D), dtype=torch.bfloat16, device="cuda")
+        t["glob"] = glob
+        layers.append(t)
+    import global_attention_gated_amd as zg
+    ws = torch.empty(zg.workspace_bytes(B, S, HKV, D), dtype=torch.uint8, device="cuda")
+    sync()
+    return layers, ws
+
+
+def prefill_step(zg, layers, ws):
+    for t in layers:
+        if t["glob"]:
+            zg.global_prefill(t["q"], t["k"], t["v"], t["wq"], t["wk"], t["out"], rotary_dims=R, rope_base=1e4,
+                              eps=1e-6, workspace=ws)
+        else:
+            zg.swa_prefill(t["q"], t["k"], t["v"], t["gate"], t["wq"], t["wk"], t["out"], window=W, rotary_dims=R,
+                           rope_base=1e4, eps=1e-6, workspace=ws)
+
+
+def run_prefill(zg, steps, warmup, S=16384, B=1):
+    layers, ws = setup_prefill(S=S, B=B)
+    for _ in range(warmup):
+        prefill_step(zg, layers, ws)
+    sync()
+    zg.kernel_timer_enable(True)
+    sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        prefill_step(zg, layers, ws)
+    sync()
+    t1 = time.perf_counter()
+    kt = {n: zg.kernel_timer_read(n) for n in ("attn_global", "attn_swa", "kv_prologue")}
+    zg.kernel_timer_enable(False)
+    ms = (t1 - t0) * 1e3 / steps
+    pairs_global = S * (S + 1) // 2
+    flop_global = 4 * D * HQ * B * pairs_global                       # per launch (one global layer)
+    pairs_swa = sum(min(i + 1, W) for i in range(S))
+    flop_swa = 4 * D * HQ * B * pairs_swa
+    bytes_swa = B * S * (3 * HQ * D * 2 + 2 * HKV * D * 2)             # q, gate, out + k, v (bf16)
+    total_flop = 5 * flop_global + 27 * flop_swa
+    g_ms, g_n = kt["attn_global"]
+    s_ms, s_n = kt["attn_swa"]
+    p_ms, p_n = kt["kv_prologue"]
+    g_avg = g_ms / max(g_n, 1)
+    s_avg = s_ms / max(s_n, 1)
+    res = {
+        "ms_per_step": ms,
+        "tokens_per_s": B * S / (ms / 1e3),
+        "schedule_tflops": total_flop / (ms / 1e3) / 1e12,
+        "schedule_mfma_frac": total_flop / (ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS,
+        "kernels": {
+            "attn_global": {"avg_ms": g_avg, "launches": g_n, "algorithmic_tflop_per_launch": flop_global / 1e12,
+                            "tflops": flop_global / (g_avg / 1e3) / 1e12},
+            "attn_swa": {"avg_ms": s_avg, "launches": s_n, "algorithmic_bytes_per_launch": bytes_swa,
+                         "gbs": bytes_swa / (s_avg / 1e3) / 1e9,
+                         "hbm_frac": bytes_swa / (s_avg / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "tflops": flop_swa / (s_avg / 1e3) / 1e12},
+            "kv_prologue": {"avg_ms": p_ms / max(p_n, 1), "launches": p_n},
+        },
+        "roofline": {"bound": "mfma", "achieved": flop_global / (g_avg / 1e3) / 1e12, "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flop_global / (g_avg / 1e3) / 1e12 / MFMA_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "attn_prefill_kernel<global> (one global layer per launch)"},
+    }
+    del layers, ws
+    import torch
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------------------------------ decode
+def fill_cache(zg, cache, seed, P):
+    """Cache contents ~N(0,1) in the cache layout, as if positions 0..P-1 had been written: global row p
+    and ring slot p mod W hold position p; element value = stream (seed, layer, cacheK/V) at the flat index
+    ((b*Hkv + h)*P + p)*D + d."""
+    import synth
+    B = cache.batch
+    for l in range(1, cache.n_layers + 1):
+        kp, vp, slots = cache.layer_view(l)
+        for ptr, tid in ((kp, synth.TENSOR_CACHE_K), (vp, synth.TENSOR_CACHE_V)):
+            if l in cache.global_layers:
+                synth.fill_device(ptr, seed, l, tid, B * HKV, P * D, slots * D, 0, P * D)
+            else:
+                # positions max(0, P-W)..P-1 live in slots p mod W: fill contiguous runs of slots
+                p = max(0, P - W)
+                while p < P:
+                    s = p % W
+                    run = min(P - p, W - s)
+                    synth.fill_device(ptr + s * D * 2, seed, l, tid, B * HKV, run * D, slots * D, p * D, P * D)
+                    p += run
+        for b in range(B):
+            cache.set_length(l, b, P)
+
+
+def run_decode(zg, steps, warmup, B=32, P=262144, seed=1004):
+    import torch
+    import synth
+    cache = zg.KVCache(n_layers=N_LAYERS, global_layers=GLOBAL_LAYERS, batch=B, n_kv_heads=HKV, head_dim=D, window=W,
+                       max_tokens=P + 1)
+    fill_cache(zg, cache, seed, P)
+    q = synth.normal_bf16_device(seed, 1000, synth.TENSOR_Q, (N_LAYERS, B, HQ, D))
+    k = synth.normal_bf16_device(seed, 1000, synth.TENSOR_K, (N_LAYERS, B, HKV, D))
+    v = synth.normal_bf16_device(seed, 1000, synth.TENSOR_V, (N_LAYERS, B, HKV, D))
+    g = synth.normal_bf16_device(seed, 1000, synth.TENSOR_GATE, (N_LAYERS, B, HQ, D))
+    import numpy as np
+    wq = np.stack([synth.norm_weight_bf16(seed, l, synth.TENSOR_WQ, D) for l in range(1, N_LAYERS + 1)])
+    wk = np.stack([synth.norm_weight_bf16(seed, l, synth.TENSOR_WK, D) for l in range(1, N_LAYERS + 1)])
+    wq = torch.from_numpy(wq.view(np.int16)).cuda().view(torch.bfloat16)
+    wk = torch.from_numpy(wk.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty_like(q)
+    positions = [P] * B
+    sync()
+
+    def step():
+        zg.hybrid_decode_step(q, k, v, g, wq, wk, positions, cache, out, rotary_dims=R, rope_base=1e7, eps=1e-6)
+        for l in range(1, N_LAYERS + 1):       # host-side: back to P cached positions (rewriting row P is idempotent)
+            for b in range(B):
+                cache.set_length(l, b, P)
+
+    for _ in range(warmup):
+        step()
+    sync()
+    zg.kernel_timer_enable(True)
+    sync()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    sync()
+    t1 = time.perf_counter()
+    kt = {n: zg.kernel_timer_read(n) for n in ("decode_global", "decode_swa", "decode_append", "decode_merge")}
+    zg.kernel_timer_enable(False)
+    ms = (t1 - t0) * 1e3 / steps
+    keys = P + 1
+    glob_bytes = 5 * B * HKV * keys * D * 2 * 2                        # K and V rows read per launch
+    swa_bytes = 27 * B * HKV * W * D * 2 * 2
+    io_bytes = N_LAYERS * B * (3 * HQ * D * 2 + 2 * HKV * D * 2)        # q, gate, out, k, v of the new token
+    step_bytes = glob_bytes + swa_bytes + io_bytes
+    g_ms, g_n = kt["decode_global"]
+    g_avg = g_ms / max(g_n, 1)
+    res = {
+        "ms_per_step": ms,
+        "tokens_per_s": B / (ms / 1e3),
+        "step_bytes": step_bytes,
+        "step_gbs": step_bytes / (ms / 1e3) / 1e9,
+        "step_hbm_frac": step_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "kv_cache_device_bytes": cache.device_bytes,
+        "kernels": {n: {"avg_ms": t / max(c, 1), "launches": c} for n, (t, c) in kt.items()},
+        "roofline": {"bound": "hbm", "achieved": glob_bytes / (g_avg / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": glob_bytes / (g_avg / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode_attn_kernel<global split-K> (5 global layers per launch)",
+                     "algorithmic_bytes_per_launch": glob_bytes},
+        "config": {"workload": "hybrid decode step, 32 seqs at position 262144, 32 layers (27 SWA ring + 5 global)",
+                   "batch": B, "position": P, "layers": N_LAYERS, "global_layers": list(GLOBAL_LAYERS), "q_heads": HQ,
+                   "kv_heads": HKV, "head_dim": D, "window": W, "rotary_dims": R, "rope_base": 1e7, "seed": seed},
+    }
+    cache.close()
+    del q, k, v, g, out
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------------------------------ CPU baseline
+def cpu_baseline(S=16384, n_rows=1024, seed=1003):
+    """The fp64 oracle on a sample of the prefill workload: n_rows random positions, all 32 query heads, in
+    one gated-SWA layer (layer 1) and one global layer (layer 6).  Per-token time = 27 x (SWA row time +
+    SWA key-prologue time / S) + 5 x (global row time + global key-prologue time / S).  Input generation
+    is not timed."""
+    import numpy as np
+    import oracle
+    import synth
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(S, size=n_rows, replace=False))
+    per_layer = {}
+    for layer, glob in ((1, False), (6, True)):
+        k = synth.normal_bf16(seed, layer, synth.TENSOR_K, (1, S, HKV, D))[0]
+        v = synth.normal_bf16(seed, layer, synth.TENSOR_V, (1, S, HKV, D))[0]
+        wq = synth.norm_weight_bf16(seed, layer, synth.TENSOR_WQ, D)
+        wk = synth.norm_weight_bf16(seed, layer, synth.TENSOR_WK, D)
+        qidx = (rows[:, None, None] * HQ * D + np.arange(HQ)[None, :, None] * D + np.arange(D)[None, None, :])
+        q = synth.normal_bf16_at(seed, layer, synth.TENSOR_Q, qidx)              # [n_rows, HQ, D]
+        gate = None if glob else synth.normal_bf16_at(seed, layer, synth.TENSOR_GATE, qidx)
+        pos = np.arange(S)
+        t0 = time.perf_counter()
+        khat = oracle.cache_key(oracle.qk_prologue(k, pos[:, None], wk, 1e-6, R, 1e4))     # [S, HKV, D]
+        t1 = time.perf_counter()
+        qhat = oracle.qk_prologue(q, rows[:, None], wq, 1e-6, R, 1e4)
+        vf = oracle.bf16_to_f64(v)
+        for h in range(HQ):
+            kh = h // (HQ // HKV)
+            if glob:
+                lo = 0
+            else:
+                lo = max(0, int(rows.min()) - W + 1)
+            hi = int(rows.max()) + 1
+            oracle.attend(qhat[:, h], rows, khat[lo:hi, kh], vf[lo:hi, kh], pos[lo:hi], None if glob else W,
+                          None if gate is None else gate[:, h])
+        t2 = time.perf_counter()
+        per_layer["global" if glob else "swa"] = ((t2 - t1) / n_rows, (t1 - t0) / S)
+    per_tok = 27 * sum(per_layer["swa"]) + 5 * sum(per_layer["global"])
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_rows} random positions x 32 heads of layer 1 (gated SWA) and layer 6 (global) of the "
+                      f"1x16384 schedule, plus each layer's key prologue over all {S} positions; scaled to one "
+                      f"token through 27 SWA + 5 global layers",
+            "seconds": None}
+
+
+# ------------------------------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention core here runs on a single MI355X "
+              "(no sharding or collectives); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import global_attention_gated_amd as zg
+    torch.cuda.set_device(0)
+    log("prefill: setting up 32 layers of 1x16384 inputs")
+    pre = run_prefill(zg, args.steps, args.warmup)
+    log(f"prefill: {pre['ms_per_step']:.3f} ms/step, {pre['tokens_per_s']:.0f} tokens/s, "
+        f"global kernel {pre['kernels']['attn_global']['tflops']:.0f} TFLOP/s, "
+        f"SWA kernel {pre['kernels']['attn_swa']['gbs']:.0f} GB/s")
+    line = {
+        "metric": "attention tokens/s + % of MFMA/HBM roofline (16K SWA prefill; 256K decode)",
+        "value": pre["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "precision": "bf16 inputs, outputs and KV cache; fp16 MFMA operands; fp32 accumulation and softmax",
+        "data": "synthetic",
+        "config": {"workload": "32-layer attention schedule prefill (27 gated SWA + 5 global), 1 x 16384 tokens",
+                   "batch": 1, "seq_len": 16384, "layers": N_LAYERS, "global_layers": list(GLOBAL_LAYERS),
+                   "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "window": W, "rotary_dims": R, "rope_base": 1e4,
+                   "seed": 1003},
+        "roofline": pre["roofline"],
+        "schedule": {"tflops": pre["schedule_tflops"], "mfma_frac": pre["schedule_mfma_frac"]},
+        "kernels": pre["kernels"],
+    }
+    if not args.no_decode:
+        log("decode: allocating and filling the 256K KV cache of 32 sequences")
+        dec = run_decode(zg, args.steps, args.warmup)
+        log(f"decode: {dec['ms_per_step']:.3f} ms/step, {dec['tokens_per_s']:.1f} tokens/s, "
+            f"split-K kernel {dec['roofline']['achieved']:.0f} GB/s")
+        line["decode"] = {"metric": "decode tokens/s + % of HBM roofline", "value": dec["tokens_per_s"],
+                          "unit": "tokens/s", "ms_per_step": dec["ms_per_step"], "step_gbs": dec["step_gbs"],
+                          "step_hbm_frac": dec["step_hbm_frac"], "roofline": dec["roofline"],
+                          "kernels": dec["kernels"], "config": dec["config"],
+                          "kv_cache_device_bytes": dec["kv_cache_device_bytes"]}
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the fp64 oracle on a sample")
+        t0 = time.perf_counter()
+        cb = cpu_baseline()
+        cb["seconds"] = round(time.perf_counter() - t0, 1)
+        line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
