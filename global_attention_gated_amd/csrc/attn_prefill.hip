@@ -79,15 +79,14 @@ __global__ void __launch_bounds__(256) ring_write_kernel(RingWriteArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t half_of(const uint4& w, int e) {
-  const uint32_t d = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
-  return (e & 1) ? (d >> 16) : (d & 0xffffu);
+__device__ __forceinline__ uint32_t dword_of(const uint4& w, int i) {
+  return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
 }
 
 // Work-group: 256 threads = 4 waves; 128 query rows = G heads x P positions of one KV head; wave w
 // owns rows 32w..32w+31 (row r -> head r / P, position i0 + r % P).  The S^T = K Q^T formulation puts
 // one query per lane column, so the softmax statistics of a query live in lanes l and l+32 only.
-template <bool GATED, bool KA_BF16, bool VA_BF16>
+template <bool GATED, bool KA_BF16, bool VA_BF16, bool HAS_RING>
 __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * kKsStride];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kHeadDim * kVtStride];
@@ -158,42 +157,52 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < 16; j++) acc_o[db][j] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
 
-  // ---- tile loading roles
+  // ---- tile loading roles.  Rows past the key range are clamped to its last row: always initialised
+  // data, whose scores the causal mask removes.
   const int kc = tid & 15, kr = tid >> 4;   // K: 16-byte chunk kc of rows kr + 16 rr
   const int vq = tid & 15, vd = tid >> 4;   // V: keys 4vq..4vq+3, dims 8vd..8vd+7
+  const uint16_t* kplane = a.kA + b * a.kA_sb + kvh * a.kA_sh + 8 * kc;
+  const uint16_t* vplane = a.vA + b * a.vA_sb + kvh * a.vA_sh + 8 * vd;
+  const int kst = (int)a.kA_st, vst = (int)a.vA_st;
+  const int apos0 = (int)a.a_pos0;
+  const int klast = (int)khi - 1;
   uint4 kreg[4], vreg[4];
 
   auto load_tile = [&](int t) {
-    const int64_t kt = (int64_t)t * kBN;
+    const int kt = t * kBN;
+    if (HAS_RING && kt < apos0) {
+      // part of this tile precedes the chunk: those rows come from the SWA ring (bf16, slot pos mod W)
+      const uint16_t* kring = a.kR + b * a.R_sb + kvh * a.R_sh + 8 * kc;
+      const uint16_t* vring = a.vR + b * a.R_sb + kvh * a.R_sh + 8 * vd;
 #pragma unroll
-    for (int rr = 0; rr < 4; rr++) {
-      const int64_t pos = kt + kr + 16 * rr;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (pos < khi) {
-        if (pos < a.a_pos0) {   // SWA ring (bf16)
-          w = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.kR + b * a.R_sb + kvh * a.R_sh +
-                                                               (pos % a.window) * kHeadDim + 8 * kc));
-        } else {
-          w = *reinterpret_cast<const uint4*>(a.kA + b * a.kA_sb + kvh * a.kA_sh + (pos - a.a_pos0) * a.kA_st + 8 * kc);
-          if (KA_BF16) w = bf16x8_to_f16x8(w);
-        }
+      for (int rr = 0; rr < 4; rr++) {
+        const int pos = min(kt + kr + 16 * rr, klast);
+        const bool ring = pos < apos0;
+        const uint4 w = ring ? *reinterpret_cast<const uint4*>(kring + (pos % a.window) * kHeadDim)
+                             : *reinterpret_cast<const uint4*>(kplane + (pos - apos0) * kst);
+        kreg[rr] = (KA_BF16 || ring) ? bf16x8_to_f16x8(w) : w;
       }
-      kreg[rr] = w;
-    }
 #pragma unroll
-    for (int rr = 0; rr < 4; rr++) {
-      const int64_t pos = kt + 4 * vq + rr;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (pos < khi) {
-        if (pos < a.a_pos0) {
-          w = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.vR + b * a.R_sb + kvh * a.R_sh +
-                                                               (pos % a.window) * kHeadDim + 8 * vd));
-        } else {
-          w = *reinterpret_cast<const uint4*>(a.vA + b * a.vA_sb + kvh * a.vA_sh + (pos - a.a_pos0) * a.vA_st + 8 * vd);
-          if (VA_BF16) w = bf16x8_to_f16x8(w);
-        }
+      for (int rr = 0; rr < 4; rr++) {
+        const int pos = min(kt + 4 * vq + rr, klast);
+        const bool ring = pos < apos0;
+        const uint4 w = ring ? *reinterpret_cast<const uint4*>(vring + (pos % a.window) * kHeadDim)
+                             : *reinterpret_cast<const uint4*>(vplane + (pos - apos0) * vst);
+        vreg[rr] = (VA_BF16 || ring) ? bf16x8_to_f16x8(w) : w;
       }
-      vreg[rr] = w;
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) {
+        const int row = min(kt + kr + 16 * rr, klast) - apos0;
+        const uint4 w = *reinterpret_cast<const uint4*>(kplane + row * kst);
+        kreg[rr] = KA_BF16 ? bf16x8_to_f16x8(w) : w;
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) {
+        const int row = min(kt + 4 * vq + rr, klast) - apos0;
+        const uint4 w = *reinterpret_cast<const uint4*>(vplane + row * vst);
+        vreg[rr] = VA_BF16 ? bf16x8_to_f16x8(w) : w;
+      }
     }
   };
   // V^T column of key k within a tile: 16-key groups, inside a group the quads 1 and 2 swap places so
@@ -203,11 +212,13 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int rr = 0; rr < 4; rr++) *reinterpret_cast<uint4*>(&Ks[buf][(kr + 16 * rr) * kKsStride + 8 * kc]) = kreg[rr];
+    // transpose 4 keys x 8 dims: dim e of keys 0..3 -> one 8-byte LDS row segment (v_perm_b32 pairs halves)
 #pragma unroll
     for (int e = 0; e < 8; e++) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       uint2 w;
-      w.x = half_of(vreg[0], e) | (half_of(vreg[1], e) << 16);
-      w.y = half_of(vreg[2], e) | (half_of(vreg[3], e) << 16);
+      w.x = __builtin_amdgcn_perm(dword_of(vreg[1], e >> 1), dword_of(vreg[0], e >> 1), sel);
+      w.y = __builtin_amdgcn_perm(dword_of(vreg[3], e >> 1), dword_of(vreg[2], e >> 1), sel);
       *reinterpret_cast<uint2*>(&Vt[buf][(8 * vd + e) * kVtStride + vcol]) = w;
     }
   };
@@ -217,16 +228,20 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
     const int64_t kt = (int64_t)t * kBN;
     if (kt > whi) return;                                             // beyond every query of the wave
     if (GATED && kt + kBN - 1 < wlo - a.window + 1) return;           // before every window of the wave
+    // S^T = K Q^T for the two 32-key halves; the two accumulator chains are interleaved so consecutive
+    // MFMAs are independent.
     floatx16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
+    for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int j = 0; j < 16; j++) sacc[kb][j] = 0.f;
+    const uint16_t* kfrag = &Ks[buf][l32 * kKsStride + 8 * hi];
 #pragma unroll
-      for (int t8 = 0; t8 < 8; t8++) {
-        const half8 ka = *reinterpret_cast<const half8*>(&Ks[buf][(kb * 32 + l32) * kKsStride + 16 * t8 + 8 * hi]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[t8], sacc[kb], 0, 0, 0);
-      }
+    for (int t8 = 0; t8 < 8; t8++) {
+      const half8 k0 = *reinterpret_cast<const half8*>(kfrag + 16 * t8);
+      const half8 k1 = *reinterpret_cast<const half8*>(kfrag + 32 * kKsStride + 16 * t8);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[t8], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qf[t8], sacc[1], 0, 0, 0);
     }
     const bool full = (kt + kBN - 1 <= wlo) && (!GATED || kt >= whi - a.window + 1);
     if (!full) {
@@ -244,7 +259,7 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-      for (int j = 0; j < 16; j++) mx = fmaxf(mx, sacc[kb][j]);
+      for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(sacc[kb][j], sacc[kb][j + 1]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     // Rescale only when the running max grows by more than 2^8: exact (the max used is carried along)
@@ -266,23 +281,24 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int h2 = 0; h2 < 2; h2++) {
-        uint4 w;
-        uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+        uint32_t wp[4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int j = 8 * h2 + 2 * e;
           wp[e] = pack_f16(__builtin_amdgcn_exp2f(sacc[kb][j] - m_run), __builtin_amdgcn_exp2f(sacc[kb][j + 1] - m_run));
           l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2, wp[e]), ones, l_run, false);
         }
-        pf[kb][h2] = __builtin_bit_cast(half8, w);
+        pf[kb][h2] = __builtin_bit_cast(half8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
       }
+    // O^T += V^T P^T: four independent accumulators (32-dim blocks) per k-step
+    const uint16_t* vfrag = &Vt[buf][l32 * kVtStride + 8 * hi];
 #pragma unroll
-    for (int db = 0; db < 4; db++)
+    for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++)
+      for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; h2++) {
-          const half8 va = *reinterpret_cast<const half8*>(&Vt[buf][(db * 32 + l32) * kVtStride + kb * 32 + 16 * h2 + 8 * hi]);
+        for (int db = 0; db < 4; db++) {
+          const half8 va = *reinterpret_cast<const half8*>(vfrag + db * 32 * kVtStride + kb * 32 + 16 * h2);
           acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[kb][h2], acc_o[db], 0, 0, 0);
         }
   };
@@ -351,11 +367,14 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.gate) {
     // gated SWA: chunk keys come from the fp16 workspace, values from the bf16 input
     if (a.ka_bf16 || !a.va_bf16) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_prefill_kernel<true, false, true>), grid, block, 0, st, a);
+    if (a.kR)
+      hipLaunchKernelGGL((attn_prefill_kernel<true, false, true, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_prefill_kernel<true, false, true, false>), grid, block, 0, st, a);
   } else if (a.ka_bf16 && a.va_bf16) {
-    hipLaunchKernelGGL((attn_prefill_kernel<false, true, true>), grid, block, 0, st, a);    // from the KV cache
+    hipLaunchKernelGGL((attn_prefill_kernel<false, true, true, false>), grid, block, 0, st, a);    // from the KV cache
   } else if (!a.ka_bf16 && !a.va_bf16) {
-    hipLaunchKernelGGL((attn_prefill_kernel<false, false, false>), grid, block, 0, st, a);  // from the workspace
+    hipLaunchKernelGGL((attn_prefill_kernel<false, false, false, false>), grid, block, 0, st, a);  // from the workspace
   } else {
     return hipErrorInvalidValue;
   }

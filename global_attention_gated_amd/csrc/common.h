@@ -66,27 +66,30 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 
 // Rotary angle of pair i at absolute position pos, as (cos, sin).  The angle pos * base^(-2i/R) can
 // reach 2.6e5 rad at the 256K context, where an fp32 product loses ~1e-2 rad; the host supplies
-// inv_freq_rev[i] = base^(-2i/R) / (2 pi) in fp64, the product and its reduction to one revolution
-// are done in fp64, and only the reduced fraction goes through fp32 sin/cos.
+// inv_freq_rev[i] = base^(-2i/R) / (2 pi) in fp64, the product and its reduction to one revolution are
+// done in fp64, and the reduced fraction (24 bits, ~4e-7 rad) goes through v_sin_f32 / v_cos_f32, which
+// take their argument in revolutions.
 __device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq_rev, float& c, float& s) {
   double r = (double)pos * inv_freq_rev;
   r -= floor(r);
-  sincospif((float)(2.0 * r), &s, &c);
+  const float rf = (float)r;
+  s = __builtin_amdgcn_sinf(rf);
+  c = __builtin_amdgcn_cosf(rf);
 }
 
 // Rotate the pairs of 8 consecutive dims d0..d0+7 (d0 even) of a row at position pos; pairs at or
-// beyond rot_pairs are left alone.
+// beyond rot_pairs are left alone.  Whole chunks past the rotary dims skip the work.
 __device__ __forceinline__ void rope8(float* f, int d0, int64_t pos, int rot_pairs, const double* inv_freq_rev) {
+  if (d0 >= 2 * rot_pairs) return;
 #pragma unroll
   for (int m = 0; m < 4; m++) {
     const int i = d0 / 2 + m;
-    if (i < rot_pairs) {
-      float c, s;
-      rope_cs(pos, inv_freq_rev[i], c, s);
-      const float x0 = f[2 * m], x1 = f[2 * m + 1];
-      f[2 * m] = x0 * c - x1 * s;
-      f[2 * m + 1] = x0 * s + x1 * c;
-    }
+    float c, s;
+    rope_cs(pos, inv_freq_rev[i], c, s);
+    if (i >= rot_pairs) { c = 1.0f; s = 0.0f; }
+    const float x0 = f[2 * m], x1 = f[2 * m + 1];
+    f[2 * m] = x0 * c - x1 * s;
+    f[2 * m + 1] = x0 * s + x1 * c;
   }
 }
 

@@ -296,6 +296,9 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   if (pos0 < 0) return fail(ZG_EINVAL, "%s: pos0 must be >= 0", fn);
   if (!cache && pos0 != 0) return fail(ZG_EINVAL, "%s: pos0 > 0 needs a cache holding the earlier positions", fn);
   if ((int64_t)B * S * Hq >= (1ll << 40)) return fail(ZG_ERANGE, "%s: problem too large", fn);
+  // the kernels index positions and per-(b, head) rows with 32-bit integers
+  if (pos0 + S >= (1ll << 31) || (int64_t)S * Hkv * D >= (1ll << 31))
+    return fail(ZG_ERANGE, "%s: positions or chunk beyond the 32-bit row range", fn);
   if (cache) {
     int rc = check_layer(cache, layer);
     if (rc) return rc;
