@@ -128,25 +128,13 @@ def run_prefill(zg, steps, warmup, S=16384, B=1):
 
 # ------------------------------------------------------------------------------------------ decode
 def fill_cache(zg, cache, seed, P):
-    """Cache contents ~N(0,1) in the cache layout, as if positions 0..P-1 had been written: global row p
-    and ring slot p mod W hold position p; element value = stream (seed, layer, cacheK/V) at the flat index
-    ((b*Hkv + h)*P + p)*D + d."""
+    """Cache contents ~N(0,1) in the cache layout, as if positions 0..P-1 had been written."""
     import synth
-    B = cache.batch
     for l in range(1, cache.n_layers + 1):
         kp, vp, slots = cache.layer_view(l)
-        for ptr, tid in ((kp, synth.TENSOR_CACHE_K), (vp, synth.TENSOR_CACHE_V)):
-            if l in cache.global_layers:
-                synth.fill_device(ptr, seed, l, tid, B * HKV, P * D, slots * D, 0, P * D)
-            else:
-                # positions max(0, P-W)..P-1 live in slots p mod W: fill contiguous runs of slots
-                p = max(0, P - W)
-                while p < P:
-                    s = p % W
-                    run = min(P - p, W - s)
-                    synth.fill_device(ptr + s * D * 2, seed, l, tid, B * HKV, run * D, slots * D, p * D, P * D)
-                    p += run
-        for b in range(B):
+        synth.fill_kv_cache_layer(kp, vp, slots, seed=seed, layer=l, batch=cache.batch, n_kv_heads=HKV, head_dim=D,
+                                  n_positions=P, is_global=l in cache.global_layers, window=W)
+        for b in range(cache.batch):
             cache.set_length(l, b, P)
 
 

@@ -173,3 +173,32 @@ def normal_bf16_device(seed: int, layer: int, tensor: int, shape, index_offset: 
     if n:
         fill_device(t.data_ptr(), seed, layer, tensor, 1, n, n, index_offset, n, device=t.device)
     return t
+
+
+def fill_kv_cache_layer(k_ptr: int, v_ptr: int, slots: int, *, seed: int, layer: int, batch: int, n_kv_heads: int,
+                        head_dim: int, n_positions: int, is_global: bool, window: int, device=None):
+    """Fill one layer of a KV cache in device memory as if positions 0..P-1 (P = n_positions) had been
+    stored: K/V arrays [batch][n_kv_heads][slots][head_dim] (bf16); a global layer holds position p in
+    row p, an SWA ring holds positions max(0, P-W)..P-1 in slot p mod W.  The value of (b, h, p, d) is
+    stream (seed, layer, cached K = 6 / cached V = 7) at flat index ((b*n_kv_heads + h)*P + p)*head_dim + d.
+    """
+    P, D, W = n_positions, head_dim, window
+    rows = batch * n_kv_heads
+    for ptr, tid in ((k_ptr, TENSOR_CACHE_K), (v_ptr, TENSOR_CACHE_V)):
+        if is_global:
+            fill_device(ptr, seed, layer, tid, rows, P * D, slots * D, 0, P * D, device=device)
+        else:
+            p = max(0, P - W)
+            while p < P:                      # contiguous runs of positions land in contiguous slots
+                s = p % W
+                run = min(P - p, W - s)
+                fill_device(ptr + s * D * 2, seed, layer, tid, rows, run * D, slots * D, p * D, P * D, device=device)
+                p += run
+
+
+def kv_cache_values(seed: int, layer: int, tensor: int, b: int, h: int, positions, *, n_kv_heads: int,
+                    head_dim: int, n_positions: int) -> np.ndarray:
+    """Host bits [len(positions), head_dim] of the values fill_kv_cache_layer stores for (b, h)."""
+    pos = np.asarray(positions, dtype=np.int64)
+    idx = ((b * n_kv_heads + h) * n_positions + pos)[:, None] * head_dim + np.arange(head_dim)[None, :]
+    return normal_bf16_at(seed, layer, tensor, idx)
