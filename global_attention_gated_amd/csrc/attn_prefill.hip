@@ -28,6 +28,7 @@ namespace {
 constexpr int kBN = 64;         // keys per LDS tile
 constexpr int kKsStride = 136;  // halfs per K row in LDS: 128 + 8 pad (272 B keeps 16-B lane reads conflict-free)
 constexpr int kVtStride = 72;   // halfs per V^T row in LDS: 64 keys + 8 pad
+constexpr int kOsStride = 132;  // floats per output row staged in LDS (epilogue): 128 + 4 pad
 
 // ---------------------------------------------------------------------------------------------
 // k_hat prologue: one 16-lane group per (b, s, kv head) row, 8 dims per lane.
@@ -88,8 +89,12 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& w, int i) {
 // one query per lane column, so the softmax statistics of a query live in lanes l and l+32 only.
 template <bool GATED, bool KA_BF16, bool VA_BF16, bool HAS_RING>
 __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * kKsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kHeadDim * kVtStride];
+  // one LDS block: K tiles [2][64][136] and V^T tiles [2][128][72] (fp16) during the loop, the fp32
+  // output rows [128][132] in the epilogue
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBN * kKsStride + 2 * kHeadDim * kVtStride];
+  static_assert(128 * kOsStride * 4 <= sizeof(smem), "epilogue staging exceeds the tile buffers");
+  uint16_t (*Ks)[kBN * kKsStride] = reinterpret_cast<uint16_t (*)[kBN * kKsStride]>(smem);
+  uint16_t (*Vt)[kHeadDim * kVtStride] = reinterpret_cast<uint16_t (*)[kHeadDim * kVtStride]>(smem + 2 * kBN * kKsStride);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -150,6 +155,20 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
     }
   }
 
+  // SWA: fetch the gate logits of the work-group's 128 rows now, coalesced (16 lanes per 256-byte row,
+  // 8 chunks of 16 bytes per thread), so their latency overlaps the whole tile loop.
+  uint4 gate_pre[8];
+  if (GATED) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int c = tid + 256 * k;
+      const int orow = c >> 4, oc = c & 15;
+      const int ipos = min(i0 + orow % a.P, a.S - 1);
+      gate_pre[k] = *reinterpret_cast<const uint4*>(
+          a.gate + (((int64_t)b * a.S + ipos) * a.Hq + kvh * a.G + orow / a.P) * kHeadDim + 8 * oc);
+    }
+  }
+
   floatx16 acc_o[4];
 #pragma unroll
   for (int db = 0; db < 4; db++)
@@ -167,6 +186,14 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
   const int apos0 = (int)a.a_pos0;
   const int klast = (int)khi - 1;
   uint4 kreg[4], vreg[4];
+  const uint16_t* kplane_u = a.kA + b * a.kA_sb + kvh * a.kA_sh;   // wave-uniform plane bases
+  const uint16_t* vplane_u = a.vA + b * a.vA_sb + kvh * a.vA_sh;
+  int kvoff[4], vvoff[4];   // per-lane byte offsets of this thread's rows within a tile
+#pragma unroll
+  for (int rr = 0; rr < 4; rr++) {
+    kvoff[rr] = ((kr + 16 * rr) * kst + 8 * kc) * 2;
+    vvoff[rr] = ((4 * vq + rr) * vst + 8 * vd) * 2;
+  }
 
   auto load_tile = [&](int t) {
     const int kt = t * kBN;
@@ -191,16 +218,21 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
         vreg[rr] = (VA_BF16 || ring) ? bf16x8_to_f16x8(w) : w;
       }
     } else {
+      // Buffer loads: the descriptor base moves with the tile (scalar), the per-lane byte offsets stay
+      // constant, and rows past the key range fall outside num_records and read as zero.
+      const int rows = min(kBN, klast + 1 - kt);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kplane_u + (int64_t)(kt - apos0) * kst), (short)0, rows * kst * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vplane_u + (int64_t)(kt - apos0) * vst), (short)0, rows * vst * 2, 0x00020000);
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
-        const int row = min(kt + kr + 16 * rr, klast) - apos0;
-        const uint4 w = *reinterpret_cast<const uint4*>(kplane + row * kst);
+        const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kvoff[rr], 0, 0));
         kreg[rr] = KA_BF16 ? bf16x8_to_f16x8(w) : w;
       }
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
-        const int row = min(kt + 4 * vq + rr, klast) - apos0;
-        const uint4 w = *reinterpret_cast<const uint4*>(vplane + row * vst);
+        const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vvoff[rr], 0, 0));
         vreg[rr] = VA_BF16 ? bf16x8_to_f16x8(w) : w;
       }
     }
@@ -317,31 +349,44 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: O^T lane layout: acc_o[db][j] is d = 32db + 8(j/4) + 4hi + j%4 of query l32.
+  // ---- epilogue: normalise, stage the 128 rows through LDS as fp32 (the K/V buffers are free after the
+  // loop's last barrier), then each thread finishes 8 consecutive dims of a row (gate for SWA, bf16
+  // rounding) and 16 consecutive lanes store a whole 256-byte row.
+  // O^T lane layout: acc_o[db][j] is d = 32db + 8(j/4) + 4hi + j%4 of query row r.
   l_run += __shfl_xor(l_run, 32);
   const float inv_l = 1.0f / l_run;
-  if (qvalid) {
-    const int64_t rowoff = (((int64_t)b * a.S + i) * a.Hq + hq) * kHeadDim;
+  float* Os = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int db = 0; db < 4; db++)
+  for (int db = 0; db < 4; db++)
 #pragma unroll
-      for (int jq = 0; jq < 4; jq++) {
-        const int d = db * 32 + 8 * jq + 4 * hi;
-        float o[4];
+    for (int jq = 0; jq < 4; jq++) {
+      const int d = db * 32 + 8 * jq + 4 * hi;
+      float4 o;
+      o.x = acc_o[db][4 * jq] * inv_l;
+      o.y = acc_o[db][4 * jq + 1] * inv_l;
+      o.z = acc_o[db][4 * jq + 2] * inv_l;
+      o.w = acc_o[db][4 * jq + 3] * inv_l;
+      *reinterpret_cast<float4*>(&Os[r * kOsStride + d]) = o;
+    }
+  __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 4; e++) o[e] = acc_o[db][4 * jq + e] * inv_l;
-        if (GATED) {
-          const uint2 g = *reinterpret_cast<const uint2*>(a.gate + rowoff + d);
-          o[0] *= 1.0f / (1.0f + __expf(-bf16lo(g.x)));
-          o[1] *= 1.0f / (1.0f + __expf(-bf16hi(g.x)));
-          o[2] *= 1.0f / (1.0f + __expf(-bf16lo(g.y)));
-          o[3] *= 1.0f / (1.0f + __expf(-bf16hi(g.y)));
-        }
-        uint2 w;
-        w.x = pack_bf16(o[0], o[1]);
-        w.y = pack_bf16(o[2], o[3]);
-        *reinterpret_cast<uint2*>(a.out + rowoff + d) = w;
+  for (int k = 0; k < 8; k++) {
+    const int c = tid + 256 * k;
+    const int orow = c >> 4, oc = c & 15;
+    const int ipos = i0 + orow % a.P;
+    if (ipos < a.S) {
+      const int64_t goff = (((int64_t)b * a.S + ipos) * a.Hq + kvh * a.G + orow / a.P) * kHeadDim + 8 * oc;
+      const float4 o0 = *reinterpret_cast<const float4*>(&Os[orow * kOsStride + 8 * oc]);
+      const float4 o1 = *reinterpret_cast<const float4*>(&Os[orow * kOsStride + 8 * oc + 4]);
+      float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+      if (GATED) {
+        float g[8];
+        unpack8(gate_pre[k], g);
+#pragma unroll
+        for (int e = 0; e < 8; e++) o[e] *= 1.0f / (1.0f + __expf(-g[e]));
       }
+      *reinterpret_cast<uint4*>(a.out + goff) = pack8(o);
+    }
   }
 }
 
