@@ -34,6 +34,23 @@ GLOBAL_LAYERS = (6, 12, 18, 24, 30)
 N_LAYERS, HQ, HKV, D, W, R = 32, 32, 8, 128, 128, 42
 
 
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None when
+    the kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_16k_decode_256k.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.split()
+        if len(f) == 5 and f[0] == "traffic" and f[1] == kernel:
+            kv = dict(x.split("=", 1) for x in f[2:])
+            src = os.path.join(ROOT, kv["source"])
+            if os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest() == kv["sha256"]:
+                return int(kv["bytes"])
+    return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -113,12 +130,14 @@ def run_prefill(zg, steps, warmup, S=16384, B=1):
             "attn_swa": {"avg_ms": s_avg, "launches": s_n, "algorithmic_bytes_per_launch": bytes_swa,
                          "gbs": bytes_swa / (s_avg / 1e3) / 1e9,
                          "hbm_frac": bytes_swa / (s_avg / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": stored_traffic("attn_swa"),
                          "tflops": flop_swa / (s_avg / 1e3) / 1e12},
             "kv_prologue": {"avg_ms": p_ms / max(p_n, 1), "launches": p_n},
         },
         "roofline": {"bound": "mfma", "achieved": flop_global / (g_avg / 1e3) / 1e12, "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flop_global / (g_avg / 1e3) / 1e12 / MFMA_PEAK_TFLOPS,
-                     "traffic": None, "kernel": "attn_prefill_kernel<global> (one global layer per launch)"},
+                     "traffic": stored_traffic("attn_global"),
+                     "kernel": "attn_prefill_kernel<global> (one global layer per launch)"},
     }
     del layers, ws
     import torch
@@ -192,7 +211,7 @@ def run_decode(zg, steps, warmup, B=32, P=262144, seed=1004):
         "kv_cache_device_bytes": cache.device_bytes,
         "kernels": {n: {"avg_ms": t / max(c, 1), "launches": c} for n, (t, c) in kt.items()},
         "roofline": {"bound": "hbm", "achieved": glob_bytes / (g_avg / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": glob_bytes / (g_avg / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "frac": glob_bytes / (g_avg / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": stored_traffic("decode_global"),
                      "kernel": "decode_attn_kernel<global split-K> (5 global layers per launch)",
                      "algorithmic_bytes_per_launch": glob_bytes},
         "config": {"workload": "hybrid decode step, 32 seqs at position 262144, 32 layers (27 SWA ring + 5 global)",
@@ -257,7 +276,11 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill workload (profiling the decode alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="also copy a GIB-sized device tensor 3 times (a plain copy kernel of known traffic, for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention core here runs on a single MI355X "
@@ -266,6 +289,22 @@ def main():
     import torch
     import global_attention_gated_amd as zg
     torch.cuda.set_device(0)
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * 2**30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 2.0, out=dst)      # one elementwise kernel: reads n*4 bytes, writes n*4 bytes
+        sync()
+        log(f"copy calibration: 3 elementwise copies of {n * 4} bytes (read {n * 4} B + write {n * 4} B each)")
+        del src, dst
+        torch.cuda.empty_cache()
+    if args.no_prefill:
+        dec = run_decode(zg, args.steps, args.warmup)
+        log(f"decode: {dec['ms_per_step']:.3f} ms/step, {dec['tokens_per_s']:.1f} tokens/s, "
+            f"split-K kernel {dec['roofline']['achieved']:.0f} GB/s")
+        print(json.dumps({"decode": dec}), flush=True)
+        return
     log("prefill: setting up 32 layers of 1x16384 inputs")
     pre = run_prefill(zg, args.steps, args.warmup)
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step, {pre['tokens_per_s']:.0f} tokens/s, "
