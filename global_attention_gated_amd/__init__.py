@@ -19,7 +19,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libzgattn.so")
+# ZGATTN_LIB selects another build of the same library (for A/B timing of kernel variants)
+LIB_PATH = os.environ.get("ZGATTN_LIB") or os.path.join(_HERE, "libzgattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m global_attention_gated_amd.build`")

@@ -26,11 +26,21 @@ __device__ __forceinline__ float dot8(const uint4& k, const uint32_t* q, float d
   return d;
 }
 
+// Sum over each row of 16 lanes, result in every lane of the row: DPP row rotations by 8, 4, 2, 1 (no LDS
+// crossbar traffic).
+__device__ __forceinline__ float ror16(float x, int n) {
+  switch (n) {
+    case 8: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    case 4: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  }
+}
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 1);
+  x += ror16(x, 8);
+  x += ror16(x, 4);
+  x += ror16(x, 2);
+  x += ror16(x, 1);
   return x;
 }
 
@@ -117,8 +127,11 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecodeArgs a, int32_t 
     for (int e = 0; e < 8; e++) acc[hh][e] = 0.f;
   }
 
-  const uint16_t* kbase = ld.k + ((int64_t)b * a.Hkv + h) * ld.slots * kHeadDim + 8 * c;
-  const uint16_t* vbase = ld.v + ((int64_t)b * a.Hkv + h) * ld.slots * kHeadDim + 8 * c;
+  // buffer descriptors over this (sequence, KV head)'s rows r0..r1-1 (uniform); lanes add byte offsets
+  const int64_t plane = ((int64_t)b * a.Hkv + h) * ld.slots + r0;
+  const int nbytes = (int)((r1 - r0) * kHeadDim * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(ld.k + plane * kHeadDim), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(ld.v + plane * kHeadDim), (short)0, nbytes, 0x00020000);
 
   constexpr int U = 4;   // rows in flight per group
   for (int64_t rb = r0 + g; rb < r1; rb += 16 * U) {
@@ -133,37 +146,48 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecodeArgs a, int32_t 
         const int64_t back = ((p - row) % a.W + a.W) % a.W;
         ok[u] = p - back >= 0;
       }
-      const int64_t rr = row < r1 ? row : r0;
-      kw[u] = *reinterpret_cast<const uint4*>(kbase + rr * kHeadDim);
-      vw[u] = *reinterpret_cast<const uint4*>(vbase + rr * kHeadDim);
+      // rows past r1 fall outside the descriptor and read as zero (masked below)
+      const int off = (int)((row - r0) * kHeadDim + 8 * c) * 2;
+      kw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      vw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+    // scores of the U rows, then one running-max check for the block (lazy: the max is raised only when a
+    // score exceeds it by more than 2^8, which keeps p <= 256 and the result exact)
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int hh = 0; hh < G; hh++) {
+        const float x = sum16(dot8(kw[u], qhi[hh], dot8(kw[u], qlo[hh], 0.f)));
+        s[u][hh] = ok[u] ? x : -INFINITY;
+      }
+    float bmax[G];
+    bool need = false;
+#pragma unroll
+    for (int hh = 0; hh < G; hh++) {
+      bmax[hh] = s[0][hh];
+#pragma unroll
+      for (int u = 1; u < U; u++) bmax[hh] = fmaxf(bmax[hh], s[u][hh]);
+      need = need || (bmax[hh] > m[hh] + 8.0f);
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int hh = 0; hh < G; hh++) {
+        const bool nd = bmax[hh] > m[hh] + 8.0f;
+        const float alpha = nd ? __builtin_amdgcn_exp2f(m[hh] - bmax[hh]) : 1.0f;
+        m[hh] = nd ? bmax[hh] : m[hh];
+        l[hh] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[hh][e] *= alpha;
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      float s[G];
-#pragma unroll
-      for (int hh = 0; hh < G; hh++) s[hh] = sum16(dot8(kw[u], qhi[hh], dot8(kw[u], qlo[hh], 0.f)));
-      bool need = false;
-#pragma unroll
-      for (int hh = 0; hh < G; hh++) {
-        if (!ok[u]) s[hh] = -INFINITY;
-        need = need || (s[hh] > m[hh] + 8.0f);
-      }
-      if (__any(need)) {
-#pragma unroll
-        for (int hh = 0; hh < G; hh++) {
-          const bool nd = s[hh] > m[hh] + 8.0f;
-          const float alpha = nd ? __builtin_amdgcn_exp2f(m[hh] - s[hh]) : 1.0f;
-          m[hh] = nd ? s[hh] : m[hh];
-          l[hh] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 8; e++) acc[hh][e] *= alpha;
-        }
-      }
       float vf[8];
       unpack8(vw[u], vf);
 #pragma unroll
       for (int hh = 0; hh < G; hh++) {
-        const float pr = __builtin_amdgcn_exp2f(s[hh] - m[hh]);
+        const float pr = __builtin_amdgcn_exp2f(s[u][hh] - m[hh]);
         l[hh] += pr;
 #pragma unroll
         for (int e = 0; e < 8; e++) acc[hh][e] += pr * vf[e];
