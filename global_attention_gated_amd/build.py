@@ -21,6 +21,9 @@ ARCH = "gfx950"
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I" + os.path.join(ROOT, "include")]
+# Device sources assume finite-or-infinite, never NaN, operands (NaN inputs are outside the library's
+# contract); this lets fmaxf compile to plain v_max without quieting canonicalisations.
+DEVICE_FLAGS = ["-fno-honor-nans"]
 SOURCES = ["attn_prefill.hip", "decode.hip", "zgattn_api.cpp"]
 
 
@@ -40,7 +43,7 @@ def build(verbose: bool = False) -> str:
         src = os.path.join(CSRC, s)
         obj = os.path.join(BUILD, s + ".o")
         objs.append(obj)
-        lang = ["-x", "hip"] if s.endswith(".cpp") else []
+        lang = ["-x", "hip"] if s.endswith(".cpp") else DEVICE_FLAGS
         cmds.append([HIPCC] + HIP_FLAGS + lang + ["-c", src, "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         outs = list(ex.map(_run, cmds))

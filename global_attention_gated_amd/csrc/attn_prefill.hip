@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; e++) ss += f[t][e] * f[t][e];
     }
-    ss += __shfl_xor(ss, 32);
+    ss = xor32_sum(ss);
     const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps);
 #pragma unroll
     for (int t = 0; t < 8; t++) {
@@ -174,7 +174,15 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
   for (int db = 0; db < 4; db++)
 #pragma unroll
     for (int j = 0; j < 16; j++) acc_o[db][j] = 0.f;
-  float m_run = -1e30f, l_run = 0.f;
+  // Running max m (log2 units) and sum l of this lane's query.  The global layer keeps -m in a whole
+  // accumulator block and starts each score chain from it, so its MFMAs yield s - m directly (the SWA
+  // layer, short of registers, subtracts m afterwards).  m is set by the first tile that shows the query a
+  // visible key (m_set) and raised lazily after that.
+  float m_run = 0.f, l_run = 0.f;
+  bool m_set = false;
+  floatx16 negm;
+#pragma unroll
+  for (int j = 0; j < 16; j++) negm[j] = 0.f;
 
   // ---- tile loading roles.  Rows past the key range are clamped to its last row: always initialised
   // data, whose scores the causal mask removes.
@@ -263,17 +271,22 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
     // S^T = K Q^T for the two 32-key halves; the two accumulator chains are interleaved so consecutive
     // MFMAs are independent.
     floatx16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int j = 0; j < 16; j++) sacc[kb][j] = 0.f;
     const uint16_t* kfrag = &Ks[buf][l32 * kKsStride + 8 * hi];
 #pragma unroll
     for (int t8 = 0; t8 < 8; t8++) {
       const half8 k0 = *reinterpret_cast<const half8*>(kfrag + 16 * t8);
       const half8 k1 = *reinterpret_cast<const half8*>(kfrag + 32 * kKsStride + 16 * t8);
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[t8], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qf[t8], sacc[1], 0, 0, 0);
+      floatx16 c0 = sacc[0], c1 = sacc[1];
+      if (t8 == 0) {
+        if constexpr (GATED) {
+#pragma unroll
+          for (int j = 0; j < 16; j++) c0[j] = c1[j] = 0.f;
+        } else {
+          c0 = c1 = negm;
+        }
+      }
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[t8], c0, 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qf[t8], c1, 0, 0, 0);
     }
     const bool full = (kt + kBN - 1 <= wlo) && (!GATED || kt >= whi - a.window + 1);
     if (!full) {
@@ -292,19 +305,36 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
       for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(sacc[kb][j], sacc[kb][j + 1]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    // Rescale only when the running max grows by more than 2^8: exact (the max used is carried along)
-    // and keeps every p <= 256.
-    const bool need = m_new > m_run + 8.0f;
+    mx = xor32_max(mx);
+    // mx is the tile's max relative to m (global) or absolute (SWA).  m is raised only when the scores
+    // exceed it by more than 2^8 (exact: the m used is carried along; every p stays <= 256), or set on the
+    // query's first visible key.
+    if constexpr (GATED) mx -= m_run;   // the global layer's sacc already holds s - m
+    const bool need = m_set ? mx > 8.0f : mx > -INFINITY;
     if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = need ? m_new : m_run;
+      const float sh = need ? mx : 0.0f;
+      const float alpha = m_set ? __builtin_amdgcn_exp2f(-sh) : 1.0f;   // l and acc are still 0 before
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; db++)
 #pragma unroll
         for (int j = 0; j < 16; j++) acc_o[db][j] *= alpha;
+      m_run += sh;
+      m_set = m_set || need;
+      if constexpr (!GATED) {
+#pragma unroll
+        for (int j = 0; j < 16; j++) negm[j] = -m_run;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+          for (int j = 0; j < 16; j++) sacc[kb][j] -= sh;
+      }
+    }
+    if constexpr (GATED) {
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) sacc[kb][j] -= m_run;
     }
     // P = exp2(s - m) rounded to fp16; the row sum adds the same rounded values (v_dot2 with ones), so
     // numerator and denominator use identical weights.
@@ -317,7 +347,7 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const int j = 8 * h2 + 2 * e;
-          wp[e] = pack_f16(__builtin_amdgcn_exp2f(sacc[kb][j] - m_run), __builtin_amdgcn_exp2f(sacc[kb][j + 1] - m_run));
+          wp[e] = pack_f16(__builtin_amdgcn_exp2f(sacc[kb][j]), __builtin_amdgcn_exp2f(sacc[kb][j + 1]));
           l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2, wp[e]), ones, l_run, false);
         }
         pf[kb][h2] = __builtin_bit_cast(half8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
@@ -353,7 +383,7 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
   // loop's last barrier), then each thread finishes 8 consecutive dims of a row (gate for SWA, bf16
   // rounding) and 16 consecutive lanes store a whole 256-byte row.
   // O^T lane layout: acc_o[db][j] is d = 32db + 8(j/4) + 4hi + j%4 of query row r.
-  l_run += __shfl_xor(l_run, 32);
+  l_run = xor32_sum(l_run);
   const float inv_l = 1.0f / l_run;
   float* Os = reinterpret_cast<float*>(smem);
 #pragma unroll

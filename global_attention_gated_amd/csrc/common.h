@@ -47,6 +47,25 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& w) {
   return r;
 }
 
+// Combine a value with the one held by lane l ^ 32 (the other half of the wave): v_permlane32_swap
+// returns {x[l & 31], x[32 + (l & 31)]} in every lane, so both lanes of a pair get bit-identical results.
+__device__ __forceinline__ void xor32_pair(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  lo = __builtin_bit_cast(float, (unsigned)r[0]);
+  hi = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  float lo, hi;
+  xor32_pair(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  float lo, hi;
+  xor32_pair(x, lo, hi);
+  return lo + hi;
+}
+
 // Unpack 8 bf16 (one 16-byte load) into fp32.
 __device__ __forceinline__ void unpack8(const uint4& w, float* f) {
   f[0] = bf16lo(w.x); f[1] = bf16hi(w.x);

@@ -73,6 +73,11 @@ def _bf16_bits_rne_from_f64(x: np.ndarray) -> np.ndarray:
     return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Hand-made inputs: bf16 bits (nearest-even) of float values."""
+    return _bf16_bits_rne_from_f64(np.asarray(x, dtype=np.float64))
+
+
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Decode bf16 bit patterns (uint16) to float64 exactly."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)

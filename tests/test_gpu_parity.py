@@ -82,6 +82,29 @@ def test_prefill_shapes(zg, gated, B, S, Hq, Hkv, W, R):
     compare(got, oracle_prefill(L, gated, W, R, 1e4, 1e-6), f"{'swa' if gated else 'global'} B{B} S{S} {Hq}/{Hkv} W{W} R{R}")
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_prefill_running_max_jumps(zg, gated):
+    """Scores that jump late in the sequence: every query is one vector u (zero on the rotary dims, so
+    RoPE leaves it alone) and the keys at a few positions are blends of u and noise, up to u itself. A
+    query that reaches such a key sees its score max rise by more than 8 in log2 units over the keys
+    before it, several times along the sequence, which drives the online softmax's rescaling paths."""
+    B, S, Hq, Hkv, W, R = 1, 2500, 4, 1, 128, 42
+    L = Layer(4242, 2, B, S, Hq, Hkv, gated=gated, w_spread=0.0)
+    rng = np.random.default_rng(7)
+    u = rng.standard_normal(128)
+    u[:R] = 0.0
+    q = np.broadcast_to(u, (B, S, Hq, 128))
+    k = synth.bf16_bits_to_f64(L.k).copy()
+    for pos, a in ((90, 0.45), (700, 0.7), (1500, 0.9), (2300, 1.0), (2310, 0.5)):
+        k[:, pos, :, :] = a * u + (1.0 - a) * k[:, pos, :, :]
+    L.q = synth.f64_to_bf16_bits(q)
+    L.k = synth.f64_to_bf16_bits(k)
+    L.wq = synth.f64_to_bf16_bits(np.full(128, 2.0))   # doubles every score: the max jumps by 13.6, then 10.5
+    L.dq, L.dk, L.dwq = to_dev(L.q), to_dev(L.k), to_dev(L.wq)
+    got = to_host_f64(gpu_prefill(zg, L, gated, W, R, 1e4, 1e-6))
+    compare(got, oracle_prefill(L, gated, W, R, 1e4, 1e-6), f"{'swa' if gated else 'global'} max jumps")
+
+
 def test_gate_infinities(zg):
     import torch
     L = Layer(77, 1, 1, 300, 8, 2)
@@ -90,7 +113,13 @@ def test_gate_infinities(zg):
     o_plus = zg.swa_prefill(L.dq, L.dk, L.dv, plus, L.dwq, L.dwk, window=1 << 20, rotary_dims=42, rope_base=1e4, eps=1e-6)
     o_glob = zg.global_prefill(L.dq, L.dk, L.dv, L.dwq, L.dwk, rotary_dims=42, rope_base=1e4, eps=1e-6)
     o_minus = zg.swa_prefill(L.dq, L.dk, L.dv, minus, L.dwq, L.dwk, window=128, rotary_dims=42, rope_base=1e4, eps=1e-6)
-    np.testing.assert_array_equal(to_host_bits(o_plus), to_host_bits(o_glob))
+    # sigma(+inf) = 1 exactly: the gated layer with a window covering the sequence is the global layer.  The
+    # two kernels round the softmax differently (the global one folds -m into the score accumulators), so
+    # both are held to the oracle's global layer and to each other at the parity bar.
+    ref = oracle_prefill(L, False, None, 42, 1e4, 1e-6)
+    compare(to_host_f64(o_plus), ref, "swa, gate +inf, window >= S")
+    compare(to_host_f64(o_glob), ref, "global")
+    compare(to_host_f64(o_plus), to_host_f64(o_glob), "swa with gate +inf against global")
     assert np.all(to_host_f64(o_minus) == 0.0)
 
 
