@@ -16,6 +16,7 @@ Inputs are generated on the GPU before the timed region.  The CPU baseline times
 bounded sample of the prefill workload (see cpu_baseline.sample in the output).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-decode] [--no-cpu-baseline]
+       python bench.py --schedule-sweep   (per-layer times at 4K..256K composed into 5:1, 3:1, 1:1, all-global)
 """
 from __future__ import annotations
 
@@ -224,6 +225,85 @@ def run_decode(zg, steps, warmup, B=32, P=262144, seed=1004):
     return res
 
 
+# ------------------------------------------------------------------------------------------ schedule sweep
+SCHEDULES = ("5:1", "3:1", "1:1", "all-global")
+
+
+def schedule_globals(name: str, n_layers: int = N_LAYERS):
+    """1-based global layers of a 32-layer stack.  "5:1" is the pages' placement (one global layer after every
+    five gated-SWA layers: 6, 12, ..., 30); "3:1" and "1:1" put one after every three or every one SWA layer;
+    "all-global" is full attention everywhere."""
+    period = {"5:1": 6, "3:1": 4, "1:1": 2, "all-global": 1}[name]
+    return tuple(l for l in range(1, n_layers + 1) if l % period == 0)
+
+
+def compose_schedules(per_layer_ms, footprint):
+    """Attention time of one prefill pass through the 32-layer stack for each schedule, from measured
+    per-layer times {S: {"swa": ms, "global": ms}} (layers of one kind cost the same at one length);
+    footprint(S, globals) gives the KV-cache bytes."""
+    out = {}
+    for name in SCHEDULES:
+        g = schedule_globals(name)
+        rows = []
+        for S in sorted(per_layer_ms):
+            t = per_layer_ms[S]
+            ms = (N_LAYERS - len(g)) * t["swa"] + len(g) * t["global"]
+            rows.append({"seq_len": S, "attention_ms": ms, "tokens_per_s": S / (ms / 1e3),
+                         "kv_cache_bytes": footprint(S, g)})
+        out[name] = {"global_layers": list(g), "n_global": len(g), "by_length": rows}
+    ref = {r["seq_len"]: r["attention_ms"] for r in out["all-global"]["by_length"]}
+    for name in SCHEDULES:
+        for r, rg in zip(out[name]["by_length"], out["all-global"]["by_length"]):
+            r["speedup_vs_all_global"] = ref[r["seq_len"]] / r["attention_ms"]
+            r["kv_ratio_all_global"] = rg["kv_cache_bytes"] / r["kv_cache_bytes"]
+    return out
+
+
+def run_schedule_sweep(zg, lengths=(4096, 16384, 65536, 262144), reps=3, seed=1006):
+    """Per-layer prefill time of one gated-SWA and one global layer (batch 1, 32q/8kv, D 128, W 128, R 42) at
+    each length, median of `reps` HIP-event timings after one warm-up call, composed into the schedules."""
+    import statistics
+    import torch
+    import synth
+    per_layer = {}
+    for S in lengths:
+        t = {n: synth.normal_bf16_device(seed, 1, tid, (1, S, H, D)) for n, tid, H in
+             (("q", synth.TENSOR_Q, HQ), ("k", synth.TENSOR_K, HKV), ("v", synth.TENSOR_V, HKV),
+              ("gate", synth.TENSOR_GATE, HQ))}
+        wq, wk = (torch.from_numpy(synth.norm_weight_bf16(seed, 1, tid, D).view("int16")).cuda().view(torch.bfloat16)
+                  for tid in (synth.TENSOR_WQ, synth.TENSOR_WK))
+        out = torch.empty_like(t["q"])
+        ws = torch.empty(zg.workspace_bytes(1, S, HKV, D), dtype=torch.uint8, device="cuda")
+        base = 1e4 if S <= 16384 else 1e7
+
+        def swa():
+            zg.swa_prefill(t["q"], t["k"], t["v"], t["gate"], wq, wk, out, window=W, rotary_dims=R, rope_base=base,
+                           eps=1e-6, workspace=ws)
+
+        def glob():
+            zg.global_prefill(t["q"], t["k"], t["v"], wq, wk, out, rotary_dims=R, rope_base=base, eps=1e-6,
+                              workspace=ws)
+
+        per_layer[S] = {}
+        for name, fn in (("swa", swa), ("global", glob)):
+            fn()
+            sync()
+            ms = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                e1.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            per_layer[S][name] = statistics.median(ms)
+        log(f"sweep: S={S}: SWA layer {per_layer[S]['swa']:.3f} ms, global layer {per_layer[S]['global']:.3f} ms")
+        del t, out, ws
+        torch.cuda.empty_cache()
+    sched = compose_schedules(per_layer, lambda S, g: zg.footprint_bytes(S, global_layers=g))
+    return per_layer, sched
+
+
 # ------------------------------------------------------------------------------------------ CPU baseline
 def cpu_baseline(S=16384, n_rows=1024, seed=1003):
     """The fp64 oracle on a sample of the prefill workload: n_rows random positions, all 32 query heads, in
@@ -278,6 +358,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill workload (profiling the decode alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule-sweep", action="store_true",
+                    help="instead of the benchmark: time one SWA and one global prefill layer at 4K..256K tokens and "
+                         "compose the 5:1, 3:1, 1:1 and all-global 32-layer schedules (one JSON line)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="also copy a GIB-sized device tensor 3 times (a plain copy kernel of known traffic, for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -299,6 +382,22 @@ def main():
         log(f"copy calibration: 3 elementwise copies of {n * 4} bytes (read {n * 4} B + write {n * 4} B each)")
         del src, dst
         torch.cuda.empty_cache()
+    if args.schedule_sweep:
+        per_layer, sched = run_schedule_sweep(zg)
+        for name in SCHEDULES:
+            log(f"sweep: {name:10s} " + "  ".join(
+                f"{r['seq_len'] // 1024}K {r['attention_ms']:.1f} ms x{r['speedup_vs_all_global']:.2f} "
+                f"KV {r['kv_cache_bytes'] / 2**30:.3f} GiB" for r in sched[name]["by_length"]))
+        print(json.dumps({
+            "metric": "attention time of one 32-layer prefill pass per schedule (sum of measured per-layer times)",
+            "unit": "ms", "n_gpus": 1, "data": "synthetic", "higher_is_better": False,
+            "config": {"workload": "schedule sweep, batch 1, 4K..256K tokens", "q_heads": HQ, "kv_heads": HKV,
+                       "head_dim": D, "window": W, "rotary_dims": R, "rope_base": "1e4 up to 16K, 1e7 above",
+                       "seed": 1006, "reps": 3},
+            "per_layer_ms": {str(S): v for S, v in per_layer.items()},
+            "schedules": sched,
+        }), flush=True)
+        return
     if args.no_prefill:
         dec = run_decode(zg, args.steps, args.warmup)
         log(f"decode: {dec['ms_per_step']:.3f} ms/step, {dec['tokens_per_s']:.1f} tokens/s, "

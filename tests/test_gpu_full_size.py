@@ -135,6 +135,32 @@ def test_schedule_1x16384_sampled_layers(zg):
             compare(got[0, p][:, kvh * G:(kvh + 1) * G], ref, f"16K layer {layer} kvh={kvh}")
 
 
+# ------------------------------------------------------------------------------------------ one shot at 256K
+def test_one_shot_prefill_1x262144_sampled(zg):
+    """The schedule sweep's longest point: one gated-SWA and one global layer prefilled in one call over
+    262,144 tokens (RoPE base 1e7), checked on sampled rows (the global layer on two KV heads)."""
+    import torch
+    B, S, Hq, Hkv, R, base, seed = 1, 262144, 32, 8, 42, 1e7, 1006
+    G = Hq // Hkv
+    rng = np.random.default_rng(5)
+    ws = torch.empty(zg.workspace_bytes(B, S, Hkv, D), dtype=torch.uint8, device="cuda")
+    for layer, gated, heads in ((1, True, range(Hkv)), (6, False, (0, Hkv - 1))):
+        t = dev_layer(seed, layer, B, S, Hq, Hkv, gated)
+        if gated:
+            out = zg.swa_prefill(t["q"], t["k"], t["v"], t["gate"], t["wq"], t["wk"], window=W, rotary_dims=R,
+                                 rope_base=base, eps=1e-6, workspace=ws)
+        else:
+            out = zg.global_prefill(t["q"], t["k"], t["v"], t["wq"], t["wk"], rotary_dims=R, rope_base=base, eps=1e-6,
+                                    workspace=ws)
+        pos = sample_positions(S, rng, 12 if gated else 6, extra=(65535, 65536, 131071, 200000))
+        got = to_host_f64(out[0, torch.tensor(pos, device="cuda")])
+        del t, out
+        torch.cuda.empty_cache()
+        for kvh in heads:
+            p, ref = oracle_rows(seed, layer, 0, kvh, pos, S_total=S, Hq=Hq, Hkv=Hkv, gated=gated, R=R, base=base)
+            compare(got[:, kvh * G:(kvh + 1) * G], ref, f"262144 one-shot layer {layer} kvh={kvh}")
+
+
 # ------------------------------------------------------------------------------------------ decode at 256K
 def test_hybrid_decode_32x262144_sampled(zg):
     import torch
