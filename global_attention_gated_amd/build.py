@@ -24,7 +24,11 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-
 # Device sources assume finite-or-infinite, never NaN, operands (NaN inputs are outside the library's
 # contract); this lets fmaxf compile to plain v_max without quieting canonicalisations.
 DEVICE_FLAGS = ["-fno-honor-nans"]
-SOURCES = ["attn_prefill.hip", "decode.hip", "zgattn_api.cpp"]
+# The streaming SWA kernel fits one work-group per CU (LDS), which would let the compiler hand it 512 vector
+# registers and put every MFMA accumulator in AGPRs; its softmax reads the score accumulators with VALU
+# instructions, so its MFMAs are kept in VGPR form.
+SOURCE_FLAGS = {"attn_swa_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCES = ["attn_prefill.hip", "attn_swa_stream.hip", "decode.hip", "zgattn_api.cpp"]
 
 
 def _run(cmd):
@@ -43,7 +47,7 @@ def build(verbose: bool = False) -> str:
         src = os.path.join(CSRC, s)
         obj = os.path.join(BUILD, s + ".o")
         objs.append(obj)
-        lang = ["-x", "hip"] if s.endswith(".cpp") else DEVICE_FLAGS
+        lang = ["-x", "hip"] if s.endswith(".cpp") else DEVICE_FLAGS + SOURCE_FLAGS.get(s, [])
         cmds.append([HIPCC] + HIP_FLAGS + lang + ["-c", src, "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         outs = list(ex.map(_run, cmds))

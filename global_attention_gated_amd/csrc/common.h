@@ -113,10 +113,11 @@ __device__ __forceinline__ void rope8(float* f, int d0, int64_t pos, int rot_pai
 }
 
 // RMSNorm * w then partial RoPE at position pos, for the 8 dims 8c..8c+7 of a 128-dim row held by a
-// group of 16 consecutive lanes (c = lane within the group; every lane of the group must be active).
-// Used for every k_hat (and the decode q_hat), so all kernels produce the same bits for the same row.
-__device__ __forceinline__ void norm_rope8_g16(float* f, const uint16_t* w, int c, int64_t pos, float eps,
-                                               int rot_pairs, const double* inv_freq_rev) {
+// group of 16 consecutive lanes (c = lane within the group; every lane of the group must be active), with
+// the lane's 8 weights wf already unpacked.  Used for every k_hat (and the decode q_hat), so all kernels
+// produce the same bits for the same row.
+__device__ __forceinline__ void norm_rope8_g16_w(float* f, const float* wf, int c, int64_t pos, float eps,
+                                                 int rot_pairs, const double* inv_freq_rev) {
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; e++) ss += f[e] * f[e];
@@ -125,11 +126,15 @@ __device__ __forceinline__ void norm_rope8_g16(float* f, const uint16_t* w, int 
   ss += __shfl_xor(ss, 2);
   ss += __shfl_xor(ss, 1);
   const float inv = rsqrtf(ss * (1.0f / kHeadDim) + eps);
-  float wf[8];
-  unpack8(*reinterpret_cast<const uint4*>(w + 8 * c), wf);
 #pragma unroll
   for (int e = 0; e < 8; e++) f[e] = f[e] * inv * wf[e];
   rope8(f, 8 * c, pos, rot_pairs, inv_freq_rev);
+}
+__device__ __forceinline__ void norm_rope8_g16(float* f, const uint16_t* w, int c, int64_t pos, float eps,
+                                               int rot_pairs, const double* inv_freq_rev) {
+  float wf[8];
+  unpack8(*reinterpret_cast<const uint4*>(w + 8 * c), wf);
+  norm_rope8_g16_w(f, wf, c, pos, eps, rot_pairs, inv_freq_rev);
 }
 
 }  // namespace zg

@@ -71,6 +71,26 @@ struct PrefillArgs {
   double inv_freq_rev[64];
 };
 
+// Streaming gated-SWA prefill without a cache (GQA group 4, window <= 128): one work-group per run of
+// `run` consecutive positions (a multiple of 32) of one (b, kv head); k_hat is computed in the kernel.
+struct SwaStreamArgs {
+  const uint16_t* q;     // [B][S][Hq][D]
+  const uint16_t* k;     // [B][S][Hkv][D] (raw k)
+  const uint16_t* v;     // [B][S][Hkv][D]
+  const uint16_t* gate;  // [B][S][Hq][D]
+  const uint16_t* qw;    // [D]
+  const uint16_t* kw;    // [D]
+  uint16_t* out;         // [B][S][Hq][D]
+  int32_t B, S, Hq, Hkv, G;
+  int32_t window;
+  int32_t rot_pairs;
+  float eps;
+  float q_scale;         // log2(e) / sqrt(D)
+  int32_t n_units;       // B * Hkv
+  int32_t run;           // positions per work-group
+  double inv_freq_rev[64];
+};
+
 // One entry per layer of a KV cache, in device memory.
 struct LayerDesc {
   uint16_t* k;
@@ -106,6 +126,8 @@ struct DecodeArgs {
 hipError_t launch_kv_prologue(const KvPrologueArgs& a, hipStream_t st);
 hipError_t launch_ring_write(const RingWriteArgs& a, hipStream_t st);
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st);
+int swa_stream_run_length(int S, int n_units);
 hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_global(const DecodeArgs& a, int32_t chunks_needed, hipStream_t st);

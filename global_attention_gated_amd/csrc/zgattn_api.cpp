@@ -336,6 +336,29 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rot_pairs = R / 2;
+  if (gated && !cache && G == 4 && window <= 128) {
+    // streaming SWA kernel: k_hat computed in its tile loader, no workspace pass
+    SwaStreamArgs sa{};
+    sa.q = static_cast<const uint16_t*>(q);
+    sa.k = static_cast<const uint16_t*>(k);
+    sa.v = static_cast<const uint16_t*>(v);
+    sa.gate = static_cast<const uint16_t*>(gate);
+    sa.qw = static_cast<const uint16_t*>(qw);
+    sa.kw = static_cast<const uint16_t*>(kw);
+    sa.out = static_cast<uint16_t*>(out);
+    sa.B = B; sa.S = S; sa.Hq = Hq; sa.Hkv = Hkv; sa.G = G;
+    sa.window = window;
+    sa.rot_pairs = rot_pairs;
+    sa.eps = eps;
+    sa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
+    sa.n_units = B * Hkv;
+    sa.run = swa_stream_run_length(S, sa.n_units);
+    fill_inv_freq(sa.inv_freq_rev, rot_pairs, R, base);
+    ScopedTimer tm("attn_swa", st);
+    hipError_t e = launch_swa_stream(sa, st);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ZG_OK;
+  }
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   const int64_t D64 = kHeadDim;

@@ -66,6 +66,15 @@ SHAPES = [
     (True, 1, 100, 4, 1, 4, 128),
     (True, 1, 97, 4, 1, 1000, 0),
     (True, 3, 33, 32, 8, 128, 42),
+    # streaming SWA kernel (GQA group 4, window <= 128): multi-step runs, several units, window edges
+    (True, 1, 9000, 4, 1, 128, 42),
+    (True, 2, 3000, 8, 2, 100, 42),
+    (True, 1, 1500, 4, 1, 1, 42),
+    (True, 1, 1537, 4, 1, 16, 42),
+    (True, 1, 1029, 4, 1, 33, 42),
+    (True, 1, 700, 4, 1, 64, 128),
+    (True, 1, 65, 4, 1, 127, 42),
+    (True, 1, 31, 4, 1, 128, 42),
     (False, 2, 300, 8, 2, None, 42),
     (False, 1, 700, 4, 1, None, 42),
     (False, 1, 257, 16, 2, None, 42),
