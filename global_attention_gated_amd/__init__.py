@@ -10,6 +10,9 @@ Entry points (C ABI in include/zgattn.h):
   global_prefill     ungated global causal layer prefill
   hybrid_decode_step one new token per sequence through every layer of a KVCache
   KVCache            kv_cache_alloc / kv_cache_free / footprint / layer views / lengths
+  linear_bf16        y = x W^T on hipBLASLt (the projections around the core)
+  gated_swa_layer    q/k/v/g projections + swa_prefill + o_proj, from the hidden state
+  global_layer       q/k/v projections + global_prefill + o_proj
 """
 from __future__ import annotations
 
@@ -51,13 +54,19 @@ _lib.prefill_workspace_bytes.restype = _u64
 _lib.swa_prefill.argtypes = [_vp] * 7 + [_i32] * 7 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
 _lib.global_prefill.argtypes = [_vp] * 6 + [_i32] * 6 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
 _lib.hybrid_decode_step.argtypes = [_vp] * 7 + [ctypes.POINTER(_i64), _i32, _i32, _f64, _f32, _vp, _vp]
+_lib.linear_bf16.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp]
+_lib.layer_workspace_bytes.argtypes = [_i32] * 5
+_lib.layer_workspace_bytes.restype = _u64
+_lib.gated_swa_layer.argtypes = [_vp] * 9 + [_i32] * 8 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
+_lib.global_layer.argtypes = [_vp] * 8 + [_i32] * 7 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
 _lib.zg_last_error.restype = ctypes.c_char_p
 _lib.zg_kernel_timer_enable.argtypes = [_i32]
 _lib.zg_kernel_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_f64), ctypes.POINTER(_i64)]
 
 EXPORTED = ["kv_cache_alloc", "kv_cache_free", "kv_cache_footprint_bytes", "kv_cache_layer_view", "kv_cache_length",
             "kv_cache_set_length", "prefill_workspace_bytes", "swa_prefill", "global_prefill", "hybrid_decode_step",
-            "zg_last_error", "zg_kernel_timer_enable", "zg_kernel_timer_read"]
+            "linear_bf16", "layer_workspace_bytes", "gated_swa_layer", "global_layer", "zg_last_error",
+            "zg_kernel_timer_enable", "zg_kernel_timer_read"]
 
 
 class ZgError(RuntimeError):
@@ -211,6 +220,66 @@ def global_prefill(q, k, v, q_norm_w, k_norm_w, out=None, *, rotary_dims=42, rop
     """Ungated global causal layer: q [B,S,Hq,D], k/v [B,S,Hkv,D], weights [D] (bf16); returns out."""
     return _prefill(False, q, k, v, None, q_norm_w, k_norm_w, out, 0, rotary_dims, rope_base, eps, pos0, cache,
                     layer, workspace)
+
+
+# ------------------------------------------------------------------------------------------- projections, layers
+def linear_bf16(x, w, y=None):
+    """y = x W^T: x [..., K], w [N, K] (bf16); returns y [..., N]."""
+    _bf16(x, "x"), _bf16(w, "w")
+    N, K = w.shape
+    if x.shape[-1] != K:
+        raise ValueError(f"x has {x.shape[-1]} features, w expects {K}")
+    T = x.numel() // K
+    if y is None:
+        y = torch.empty((*x.shape[:-1], N), dtype=torch.bfloat16, device=x.device)
+    _bf16(y, "y")
+    _check(_lib.linear_bf16(_ptr(x), _ptr(w), _ptr(y), T, K, N, _stream()))
+    return y
+
+
+def layer_workspace_bytes(B, S, Hq, Hkv, D=128) -> int:
+    return int(_lib.layer_workspace_bytes(B, S, Hq, Hkv, D))
+
+
+def _layer(gated, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, window, rotary_dims, rope_base, eps,
+           pos0, cache, layer, workspace):
+    for t, n in ((h, "h"), (w_q, "w_q"), (w_k, "w_k"), (w_v, "w_v"), (w_g, "w_g"), (w_o, "w_o"), (q_norm_w, "q_norm_w"),
+                 (k_norm_w, "k_norm_w")):
+        _bf16(t, n)
+    B, S, d_model = h.shape
+    D = q_norm_w.shape[0]
+    if y is None:
+        y = torch.empty_like(h)
+    _bf16(y, "y")
+    if workspace is None:
+        workspace = torch.empty(max(16, layer_workspace_bytes(B, S, Hq, Hkv, D)), dtype=torch.uint8, device=h.device)
+    ws_n = workspace.numel() * workspace.element_size()
+    ch = None if cache is None else cache.handle
+    if gated:
+        rc = _lib.gated_swa_layer(_ptr(h), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_g), _ptr(w_o), _ptr(q_norm_w),
+                                  _ptr(k_norm_w), _ptr(y), B, S, d_model, Hq, Hkv, D, window, rotary_dims, rope_base, eps,
+                                  pos0, ch, layer, workspace.data_ptr(), ws_n, _stream())
+    else:
+        rc = _lib.global_layer(_ptr(h), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(q_norm_w), _ptr(k_norm_w),
+                               _ptr(y), B, S, d_model, Hq, Hkv, D, rotary_dims, rope_base, eps, pos0, ch, layer,
+                               workspace.data_ptr(), ws_n, _stream())
+    _check(rc)
+    return y
+
+
+def gated_swa_layer(h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y=None, *, Hq=32, Hkv=8, window=128, rotary_dims=42,
+                    rope_base=1e4, eps=1e-6, pos0=0, cache: KVCache | None = None, layer=0, workspace=None):
+    """o_proj(A_SWA(q, k, v) (.) sigmoid(g)) with q/k/v/g = h W^T: h [B,S,d_model], W_q/W_g [Hq*D, d_model],
+    W_k/W_v [Hkv*D, d_model], W_o [d_model, Hq*D] (bf16); returns y [B,S,d_model]."""
+    return _layer(True, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, window, rotary_dims, rope_base, eps,
+                  pos0, cache, layer, workspace)
+
+
+def global_layer(h, w_q, w_k, w_v, w_o, q_norm_w, k_norm_w, y=None, *, Hq=32, Hkv=8, rotary_dims=42, rope_base=1e4,
+                 eps=1e-6, pos0=0, cache: KVCache | None = None, layer=0, workspace=None):
+    """o_proj(global causal attention of q, k, v) with q/k/v = h W^T; shapes as gated_swa_layer."""
+    return _layer(False, h, w_q, w_k, w_v, None, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, 0, rotary_dims, rope_base, eps,
+                  pos0, cache, layer, workspace)
 
 
 # ------------------------------------------------------------------------------------------- decode

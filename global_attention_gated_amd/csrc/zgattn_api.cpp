@@ -15,6 +15,7 @@
 #include "../../include/zgattn.h"
 #include "common.h"
 #include "launch.h"
+#include "linear.h"
 
 using namespace zg;
 
@@ -279,10 +280,12 @@ extern "C" uint64_t prefill_workspace_bytes(int32_t B, int32_t S, int32_t Hkv, i
 // ---------------------------------------------------------------------------------- prefill
 namespace {
 
+// validate_only: check every argument (the tensor pointers need only be non-null) and return without
+// enqueueing anything (used by the layer entry points before they launch the projections).
 int prefill_common(bool gated, const void* q, const void* k, const void* v, const void* gate, const void* qw,
                    const void* kw, void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
                    int32_t window, int32_t R, double base, float eps, int64_t pos0, zg_kv_cache* cache,
-                   int32_t layer, void* ws, uint64_t ws_bytes, void* stream) {
+                   int32_t layer, void* ws, uint64_t ws_bytes, void* stream, bool validate_only = false) {
   const char* fn = gated ? "swa_prefill" : "global_prefill";
   if (B < 0 || S < 0) return fail(ZG_EINVAL, "%s: negative B or S", fn);
   if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(ZG_EINVAL, "%s: Hq (%d) must be a positive multiple of Hkv (%d)", fn, Hq, Hkv);
@@ -334,6 +337,7 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
       return fail(ZG_EINVAL, "%s: the cache lives on device %d, the current device is %d", fn, cache->device, cur);
   }
 
+  if (validate_only) return ZG_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rot_pairs = R / 2;
   if (gated && !cache && G == 4 && window <= 128) {
@@ -477,6 +481,93 @@ extern "C" int global_prefill(const void* q, const void* k, const void* v, const
                               int32_t layer, void* workspace, uint64_t workspace_bytes, void* stream) {
   return prefill_common(false, q, k, v, nullptr, q_norm_w, k_norm_w, out, B, S, Hq, Hkv, D, 0, rotary_dims, rope_base,
                         eps, pos0, cache, layer, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------------- projections, layers
+extern "C" int linear_bf16(const void* x, const void* w, void* y, int64_t T, int32_t K, int32_t N, void* stream) {
+  const char* fn = "linear_bf16";
+  if (T < 0 || K < 1 || N < 1) return fail(ZG_EINVAL, "%s: T must be >= 0, K and N >= 1", fn);
+  if (T == 0) return ZG_OK;
+  if (!x || !w || !y) return fail(ZG_EINVAL, "%s: null tensor pointer", fn);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(ZG_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ScopedTimer tm("linear", st);
+  const int s = linear_bf16_run(x, w, y, T, K, N, st);
+  if (s) return fail(ZG_EHIP, "%s: hipBLASLt %s (T=%lld K=%d N=%d)", fn, blas_status_name(s), (long long)T, K, N);
+  return ZG_OK;
+}
+
+namespace {
+uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
+uint64_t layer_activation_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D) {
+  const uint64_t T = (uint64_t)B * (uint64_t)S;
+  return align256(T * (3ull * Hq + 2ull * Hkv) * (uint64_t)D * 2ull);   // q, g, o and k, v (bf16)
+}
+}  // namespace
+
+extern "C" uint64_t layer_workspace_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (B < 0 || S < 0 || Hq < 0 || Hkv < 0 || D < 0) return 0;
+  return layer_activation_bytes(B, S, Hq, Hkv, D) + prefill_workspace_bytes(B, S, Hkv, D);
+}
+
+namespace {
+int layer_common(bool gated, const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+                 const void* w_o, const void* qw, const void* kw, void* y, int32_t B, int32_t S, int32_t d_model,
+                 int32_t Hq, int32_t Hkv, int32_t D, int32_t window, int32_t R, double base, float eps, int64_t pos0,
+                 zg_kv_cache* cache, int32_t layer, void* ws, uint64_t ws_bytes, void* stream) {
+  const char* fn = gated ? "gated_swa_layer" : "global_layer";
+  if (d_model < 1) return fail(ZG_EINVAL, "%s: d_model must be >= 1", fn);
+  if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || D < 1) return fail(ZG_EINVAL, "%s: bad shape", fn);
+  if (B == 0 || S == 0) return ZG_OK;
+  if (!h || !w_q || !w_k || !w_v || !w_o || !y || (gated && !w_g)) return fail(ZG_EINVAL, "%s: null tensor pointer", fn);
+  if (!aligned16(h) || !aligned16(w_q) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(w_o) || !aligned16(y) ||
+      (gated && !aligned16(w_g)))
+    return fail(ZG_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+  if (!ws || !aligned16(ws)) return fail(ZG_EINVAL, "%s: a 16-byte aligned workspace is required", fn);
+  if (ws_bytes < layer_workspace_bytes(B, S, Hq, Hkv, D))
+    return fail(ZG_ERANGE, "%s: workspace of %llu bytes < %llu needed", fn, (unsigned long long)ws_bytes,
+                (unsigned long long)layer_workspace_bytes(B, S, Hq, Hkv, D));
+  // carve the activations: q [T][Hq*D], k, v [T][Hkv*D], g, o [T][Hq*D], then the attention workspace
+  const int64_t T = (int64_t)B * S;
+  uint16_t* q = static_cast<uint16_t*>(ws);
+  uint16_t* k = q + T * Hq * D;
+  uint16_t* v = k + T * Hkv * D;
+  uint16_t* g = v + T * Hkv * D;
+  uint16_t* o = g + T * Hq * D;
+  const uint64_t act = layer_activation_bytes(B, S, Hq, Hkv, D);
+  void* aws = static_cast<unsigned char*>(ws) + act;
+  const uint64_t aws_bytes = ws_bytes - act;
+  // the attention's arguments first, so a bad one enqueues nothing
+  int rc = prefill_common(gated, q, k, v, gated ? g : nullptr, qw, kw, o, B, S, Hq, Hkv, D, window, R, base, eps, pos0,
+                          cache, layer, aws, aws_bytes, stream, /*validate_only=*/true);
+  if (rc) return rc;
+  if ((rc = linear_bf16(h, w_q, q, T, d_model, Hq * D, stream))) return rc;
+  if ((rc = linear_bf16(h, w_k, k, T, d_model, Hkv * D, stream))) return rc;
+  if ((rc = linear_bf16(h, w_v, v, T, d_model, Hkv * D, stream))) return rc;
+  if (gated && (rc = linear_bf16(h, w_g, g, T, d_model, Hq * D, stream))) return rc;
+  rc = prefill_common(gated, q, k, v, gated ? g : nullptr, qw, kw, o, B, S, Hq, Hkv, D, window, R, base, eps, pos0, cache,
+                      layer, aws, aws_bytes, stream);
+  if (rc) return rc;
+  return linear_bf16(o, w_o, y, T, Hq * D, d_model, stream);
+}
+}  // namespace
+
+extern "C" int gated_swa_layer(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+                               const void* w_o, const void* q_norm_w, const void* k_norm_w, void* y, int32_t B,
+                               int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t window,
+                               int32_t rotary_dims, double rope_base, float eps, int64_t pos0, zg_kv_cache* cache,
+                               int32_t layer, void* workspace, uint64_t workspace_bytes, void* stream) {
+  return layer_common(true, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, B, S, d_model, Hq, Hkv, D, window,
+                      rotary_dims, rope_base, eps, pos0, cache, layer, workspace, workspace_bytes, stream);
+}
+
+extern "C" int global_layer(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                            const void* q_norm_w, const void* k_norm_w, void* y, int32_t B, int32_t S, int32_t d_model,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t rotary_dims, double rope_base, float eps,
+                            int64_t pos0, zg_kv_cache* cache, int32_t layer, void* workspace, uint64_t workspace_bytes,
+                            void* stream) {
+  return layer_common(false, h, w_q, w_k, w_v, nullptr, w_o, q_norm_w, k_norm_w, y, B, S, d_model, Hq, Hkv, D, 0,
+                      rotary_dims, rope_base, eps, pos0, cache, layer, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------------- decode

@@ -142,13 +142,45 @@ int hybrid_decode_step(const void* q, const void* k, const void* v, const void* 
                        const void* k_norm_w, void* out, const int64_t* positions, int32_t Hq,
                        int32_t rotary_dims, double rope_base, float eps, zg_kv_cache* cache, void* stream);
 
+/* ---- Projections around the core (onedev.kr "How it works": GatedSWA(h) = o_proj(A_SWA(q,k,v) (.)
+ * sigmoid(g_proj(h))), with q/k/v/g projections of the hidden state h).  Plain GEMMs on hipBLASLt. */
+
+/* y = x . W^T, a linear layer's forward: x [T][K], W [N][K] (out_features x in_features), y [T][N], device
+ * bf16, fp32 accumulation, result rounded to bf16.  The library keeps one hipBLASLt handle, a 64 MiB
+ * workspace and a cached plan per (T, K, N) per device, created on first use.  T == 0 is a no-op.
+ * Errors: EINVAL (shape, null, alignment), EHIP (hipBLASLt failure, message names the status). */
+int linear_bf16(const void* x, const void* w, void* y, int64_t T, int32_t K, int32_t N, void* stream);
+
+/* Workspace bytes for gated_swa_layer / global_layer on B x S tokens: the bf16 activations q, g, o [T][Hq*D] and
+ * k, v [T][Hkv*D] (T = B*S), 256-byte aligned, followed by prefill_workspace_bytes(B, S, Hkv, D). */
+uint64_t layer_workspace_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D);
+
+/* A gated-SWA attention layer from the hidden state: q = h W_q^T, k = h W_k^T, v = h W_v^T, g = h W_g^T, then
+ * swa_prefill (QK-RMSNorm, partial RoPE, windowed attention, sigmoid(g) gate), then y = o W_o^T.
+ *   h [B][S][d_model]; W_q, W_g [Hq*D][d_model]; W_k, W_v [Hkv*D][d_model]; W_o [d_model][Hq*D];
+ *   q_norm_w, k_norm_w [D]; y [B][S][d_model]   (device bf16).  The head layout of q/k/v/g/o is that of
+ *   swa_prefill ([token][head][D]).  Other arguments as swa_prefill; workspace of layer_workspace_bytes.
+ * Every argument (the attention's included) is validated before anything is enqueued.
+ * Errors: as linear_bf16 and swa_prefill. */
+int gated_swa_layer(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_g, const void* w_o,
+                    const void* q_norm_w, const void* k_norm_w, void* y, int32_t B, int32_t S, int32_t d_model,
+                    int32_t Hq, int32_t Hkv, int32_t D, int32_t window, int32_t rotary_dims, double rope_base, float eps,
+                    int64_t pos0, zg_kv_cache* cache, int32_t layer, void* workspace, uint64_t workspace_bytes,
+                    void* stream);
+
+/* The global layer: as gated_swa_layer without the gate projection and the window (global_prefill). */
+int global_layer(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                 const void* q_norm_w, const void* k_norm_w, void* y, int32_t B, int32_t S, int32_t d_model, int32_t Hq,
+                 int32_t Hkv, int32_t D, int32_t rotary_dims, double rope_base, float eps, int64_t pos0,
+                 zg_kv_cache* cache, int32_t layer, void* workspace, uint64_t workspace_bytes, void* stream);
+
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char* zg_last_error(void);
 
 /* Kernel timer: while enabled, every launch of the main attention kernels records a pair of HIP
  * events on the launch stream.  zg_kernel_timer_read synchronises on the recorded events and returns,
  * for the kernel family `name` ("attn_swa", "attn_global", "decode_global", "decode_swa",
- * "kv_prologue", "decode_merge", "decode_append"), the summed device time in ms and the launch count
+ * "kv_prologue", "decode_merge", "decode_append", "linear"), the summed device time in ms and the launch count
  * since the last reset.  Enabling resets the counters. */
 int zg_kernel_timer_enable(int32_t on);
 int zg_kernel_timer_read(const char* name, double* total_ms, int64_t* launches);

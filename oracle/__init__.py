@@ -22,7 +22,10 @@ jaehun.me, "New Approach" and "How Gated SWA Behaves"):
      in decode; q_hat, the scores, the softmax and the output stay in float64.
 Layer schedule: 32 layers, global at 6, 12, 18, 24, 30 (1-indexed), the other 27 gated SWA.
 
-Readings where the pages are silent are listed in the design doc of this repository.
+Readings where the pages are silent: softmax scale 1/sqrt(D); one RMSNorm weight vector for q and one for k per
+layer, shared by the heads, eps 1e-6; RMSNorm before RoPE; RoFormer's adjacent pairs (2i, 2i+1) rotated by
+p * base^(-2i/R); query head h reads KV head h // (Hq / Hkv); the gate is element-wise.  Around the core (the
+projections of ``attention_layer``) the layer's tensors are bf16 between operations.
 """
 from __future__ import annotations
 
@@ -278,6 +281,30 @@ def prefill_layer(q, k, v, gate, wq, wk, *, window: int | None, rotary_dims: int
             o = attend(qrows, qp, kk, vv, kp, window, grows)
             out[b][:, heads, :] = o.reshape(G, S, D).transpose(1, 0, 2)
     return out
+
+
+# ---------------------------------------------------------------------------- projections around the core
+def linear(x, w) -> np.ndarray:
+    """A linear layer's forward y = x W^T in float64: x [..., K], w [N, K] (W stored out x in)."""
+    return _as_f64(x) @ _as_f64(w).T
+
+
+def attention_layer(h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, *, Hq: int, Hkv: int, window: int | None,
+                    rotary_dims: int, base: float, eps: float) -> np.ndarray:
+    """The layer around the core (onedev.kr "How it works": o_proj(A_SWA(q, k, v) (.) sigmoid(g_proj(h))); the
+    global layer without the gate): q, k, v, g = h W^T, the attention of prefill_layer, y = o W_o^T.
+
+    The layer's tensors are bf16 between its operations (bf16 I/O, fp32 or better accumulation), so q, k, v, g
+    and the attention output o are rounded once to bf16 (nearest-even) before the next operation reads them;
+    everything else is float64.  h [B,S,d_model]; returns y float64 [B,S,d_model]."""
+    B, S, dm = np.asarray(h).shape
+    D = np.asarray(q_norm_w).shape[-1]
+    def proj(w, H):
+        return round_bf16(linear(h, w)).reshape(B, S, H, D)
+    q, k, v = proj(w_q, Hq), proj(w_k, Hkv), proj(w_v, Hkv)
+    g = None if w_g is None else proj(w_g, Hq)
+    o = prefill_layer(q, k, v, g, q_norm_w, k_norm_w, window=window, rotary_dims=rotary_dims, base=base, eps=eps)
+    return linear(round_bf16(o).reshape(B, S, Hq * D), w_o)
 
 
 def decode_step(q, k, v, gate, wq, wk, positions, cache: OracleCache, *, rotary_dims: int, base: float,

@@ -85,3 +85,39 @@ def test_decode_and_cache_reject_bad_arguments(zg):
     bad = zg._desc(32, [33], 1, 8, 128, 128, 1024)
     assert lib.kv_cache_alloc(ctypes.byref(bad), ctypes.byref(h), None) == 1
     assert lib.kv_cache_free(None) == 0
+
+
+def test_layer_workspace_bytes_closed_form(zg):
+    B, S, Hq, Hkv, D = 2, 300, 32, 8, 128
+    act = B * S * (3 * Hq + 2 * Hkv) * D * 2
+    act = (act + 255) // 256 * 256
+    assert zg.layer_workspace_bytes(B, S, Hq, Hkv, D) == act + zg.workspace_bytes(B, S, Hkv, D)
+
+
+def _layer(zg, **over):
+    a = dict(h=16, wq=16, wk=16, wv=16, wg=16, wo=16, qw=16, kw=16, y=16, B=1, S=4, dm=4096, Hq=4, Hkv=1, D=128,
+             window=128, R=42, base=1e4, eps=1e-6, pos0=0, cache=None, layer=0, ws=256, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return zg._lib.gated_swa_layer(a["h"], a["wq"], a["wk"], a["wv"], a["wg"], a["wo"], a["qw"], a["kw"], a["y"], a["B"],
+                                   a["S"], a["dm"], a["Hq"], a["Hkv"], a["D"], a["window"], a["R"], a["base"], a["eps"],
+                                   a["pos0"], a["cache"], a["layer"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dm=0), 1), (dict(wg=None), 1), (dict(h=24), 1), (dict(ws=None), 1), (dict(ws_bytes=1000), 3),
+    # the attention's own arguments are checked before any projection is enqueued
+    (dict(window=0), 1), (dict(D=64), 2), (dict(R=41), 1), (dict(pos0=3), 1), (dict(Hq=12, Hkv=1), 2),
+])
+def test_layer_rejects_bad_arguments_before_enqueueing(zg, over, status):
+    assert _layer(zg, **over) == status
+    assert zg._lib.zg_last_error()
+
+
+def test_linear_rejects_bad_arguments(zg):
+    lib = zg._lib
+    assert lib.linear_bf16(16, 16, 16, 10, 0, 4, None) == 1
+    assert lib.linear_bf16(16, 16, 16, -1, 4, 4, None) == 1
+    assert lib.linear_bf16(None, 16, 16, 10, 4, 4, None) == 1
+    assert lib.linear_bf16(16, 24, 16, 10, 4, 4, None) == 1
+    assert lib.linear_bf16(16, 16, 16, 0, 4, 4, None) == 0     # no tokens: no-op
+    assert _layer(zg, S=0) == 0

@@ -1,0 +1,71 @@
+"""GPU parity of the projections around the core (hipBLASLt bf16 GEMMs) and of whole attention layers from the
+hidden state, against the fp64 oracle on the same seeded inputs.
+
+Bars: a projection alone is within its own rounding: |y - y_64| <= 2^-8 |y_64| (the bf16 rounding of the
+result) + 1e-3 rms(y_64) (fp32 accumulation over K = 4096 products); a whole layer is held to the attention
+core's bar (max-abs 1e-2, mean-abs 1e-3), its output being o W_o^T of an attention output within that bar.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _inputs import TOL_MAX_ABS, TOL_MEAN_ABS, compare, to_dev, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+D_MODEL, HQ, HKV, D = 4096, 32, 8, 128
+
+
+@pytest.fixture(scope="module")
+def zg():
+    import torch
+    assert torch.cuda.is_available()
+    import global_attention_gated_amd as m
+    return m
+
+
+def weight_bits(seed, tensor, n_out, n_in):
+    """N(0,1) / sqrt(n_in) in bf16 (n_in a power of 4, so the scale is an exact power of two)."""
+    w = synth.bf16_bits_to_f64(synth.normal_bf16(seed, 0, tensor, (n_out, n_in)))
+    return synth.f64_to_bf16_bits(w / np.sqrt(n_in))
+
+
+@pytest.mark.parametrize("T,K,N", [(300, 4096, 1024), (513, 4096, 4096), (1, 4096, 4096), (64, 256, 96)])
+def test_linear_bf16_matches_oracle(zg, T, K, N):
+    x = synth.normal_bf16(11, 0, synth.TENSOR_H, (T, K))
+    w = weight_bits(11, synth.TENSOR_PQ, N, K)
+    y = to_host_f64(zg.linear_bf16(to_dev(x), to_dev(w)))
+    ref = oracle.linear(x, w)
+    err = np.abs(y - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-3 * np.sqrt(np.mean(ref ** 2))
+    assert np.all(err <= bound), f"max excess {float((err - bound).max()):.3e}"
+
+
+def _layer_inputs(seed, B, S, gated):
+    h = synth.normal_bf16(seed, 0, synth.TENSOR_H, (B, S, D_MODEL))
+    w = {"q": weight_bits(seed, synth.TENSOR_PQ, HQ * D, D_MODEL), "k": weight_bits(seed, synth.TENSOR_PK, HKV * D, D_MODEL),
+         "v": weight_bits(seed, synth.TENSOR_PV, HKV * D, D_MODEL),
+         "g": weight_bits(seed, synth.TENSOR_PG, HQ * D, D_MODEL) if gated else None,
+         "o": weight_bits(seed, synth.TENSOR_PO, D_MODEL, HQ * D)}
+    qn = synth.norm_weight_bf16(seed, 1, synth.TENSOR_WQ, D)
+    kn = synth.norm_weight_bf16(seed, 1, synth.TENSOR_WK, D)
+    return h, w, qn, kn
+
+
+@pytest.mark.parametrize("gated,B,S", [(True, 1, 400), (False, 1, 300), (True, 2, 129)])
+def test_attention_layer_from_hidden_state_matches_oracle(zg, gated, B, S):
+    h, w, qn, kn = _layer_inputs(21 + S, B, S, gated)
+    dv = {k: (None if v is None else to_dev(v)) for k, v in w.items()}
+    if gated:
+        y = zg.gated_swa_layer(to_dev(h), dv["q"], dv["k"], dv["v"], dv["g"], dv["o"], to_dev(qn), to_dev(kn), Hq=HQ,
+                               Hkv=HKV, window=128, rotary_dims=42, rope_base=1e4, eps=1e-6)
+    else:
+        y = zg.global_layer(to_dev(h), dv["q"], dv["k"], dv["v"], dv["o"], to_dev(qn), to_dev(kn), Hq=HQ, Hkv=HKV,
+                            rotary_dims=42, rope_base=1e4, eps=1e-6)
+    ref = oracle.attention_layer(h, w["q"], w["k"], w["v"], w["g"], w["o"], qn, kn, Hq=HQ, Hkv=HKV,
+                                 window=128 if gated else None, rotary_dims=42, base=1e4, eps=1e-6)
+    got = to_host_f64(y)
+    print(f"layer {'swa' if gated else 'global'} B{B} S{S}: max_abs {np.abs(got - ref).max():.3e} "
+          f"mean_abs {np.abs(got - ref).mean():.3e} rms(y) {np.sqrt(np.mean(ref ** 2)):.3f}")
+    compare(got, ref, f"{'gated SWA' if gated else 'global'} layer B{B} S{S}")

@@ -293,3 +293,34 @@ def test_bf16_rounding_ties_to_even_and_matches_torch():
     ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(oracle.round_bf16(x), ref)
     np.testing.assert_array_equal(oracle.bf16_to_f64(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+# ------------------------------------------------------------------------------------------ projections
+def test_linear_is_x_times_w_transposed_brute_force():
+    """y = x W^T with W stored out x in: against explicit fsum loops, the identity and one-hot rows."""
+    x = RNG.standard_normal((3, 5))
+    w = RNG.standard_normal((4, 5))
+    y = oracle.linear(x, w)
+    for t in range(3):
+        for n in range(4):
+            assert y[t, n] == pytest.approx(math.fsum(x[t, k] * w[n, k] for k in range(5)), rel=1e-14, abs=1e-14)
+    np.testing.assert_array_equal(oracle.linear(x, np.eye(5)), x)
+    onehot = np.zeros((1, 5)); onehot[0, 2] = 1.0
+    np.testing.assert_array_equal(oracle.linear(onehot, w)[0], w[:, 2])
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_attention_layer_with_identity_projections_is_the_core(gated):
+    """With every projection the identity (d_model = Hq*D, one query head per KV head), the layer is the
+    attention of prefill_layer on h itself, its output rounded to bf16 (the bf16 hand-off between ops)."""
+    import synth
+    B, S, H, D = 1, 40, 2, 128
+    h = synth.normal_bf16(7, 1, synth.TENSOR_H, (B, S, H * D))
+    eye = synth.f64_to_bf16_bits(np.eye(H * D))
+    wn = synth.norm_weight_bf16(7, 1, synth.TENSOR_WQ, D)
+    y = oracle.attention_layer(h, eye, eye, eye, eye if gated else None, eye, wn, wn, Hq=H, Hkv=H,
+                               window=16 if gated else None, rotary_dims=42, base=1e4, eps=1e-6)
+    hq = h.reshape(B, S, H, D)
+    o = oracle.prefill_layer(hq, hq, hq, hq if gated else None, wn, wn, window=16 if gated else None, rotary_dims=42,
+                             base=1e4, eps=1e-6)
+    np.testing.assert_array_equal(y, oracle.bf16_to_f64(oracle.round_bf16(o)).reshape(B, S, H * D))
