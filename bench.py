@@ -304,6 +304,65 @@ def run_schedule_sweep(zg, lengths=(4096, 16384, 65536, 262144), reps=3, seed=10
     return per_layer, sched
 
 
+# ------------------------------------------------------------------------------------------ whole layers
+D_MODEL = 4096
+
+
+def run_layers(zg, steps=5, warmup=2, S=16384, seed=1007):
+    """One gated-SWA and one global layer from the hidden state (q/k/v(/g) projections, attention core, o_proj),
+    batch 1 x S tokens, d_model 4096, 32q/8kv, random-init weights N(0,1)/sqrt(fan_in); HIP-event time per
+    layer call and the hipBLASLt GEMM time within it (kernel timer "linear")."""
+    import numpy as np
+    import torch
+    import synth
+
+    def weight(tensor, n_out, n_in):
+        w = synth.normal_bf16_device(seed, 0, tensor, (n_out, n_in))
+        return (w.float() / float(np.sqrt(n_in))).to(torch.bfloat16)   # power-of-two scale: exact
+
+    h = synth.normal_bf16_device(seed, 0, synth.TENSOR_H, (1, S, D_MODEL))
+    w = {"q": weight(synth.TENSOR_PQ, HQ * D, D_MODEL), "k": weight(synth.TENSOR_PK, HKV * D, D_MODEL),
+         "v": weight(synth.TENSOR_PV, HKV * D, D_MODEL), "g": weight(synth.TENSOR_PG, HQ * D, D_MODEL),
+         "o": weight(synth.TENSOR_PO, D_MODEL, HQ * D)}
+    nw = torch.from_numpy(synth.norm_weight_bf16(seed, 1, synth.TENSOR_WQ, D).view("int16")).cuda().view(torch.bfloat16)
+    y = torch.empty_like(h)
+    ws = torch.empty(zg.layer_workspace_bytes(1, S, HQ, HKV, D), dtype=torch.uint8, device="cuda")
+    calls = {
+        "gated_swa_layer": lambda: zg.gated_swa_layer(h, w["q"], w["k"], w["v"], w["g"], w["o"], nw, nw, y, Hq=HQ,
+                                                      Hkv=HKV, window=W, rotary_dims=R, rope_base=1e4, workspace=ws),
+        "global_layer": lambda: zg.global_layer(h, w["q"], w["k"], w["v"], w["o"], nw, nw, y, Hq=HQ, Hkv=HKV,
+                                                rotary_dims=R, rope_base=1e4, workspace=ws),
+    }
+    gemm_flop = {"gated_swa_layer": 2 * S * D_MODEL * (3 * HQ * D + 2 * HKV * D),
+                 "global_layer": 2 * S * D_MODEL * (2 * HQ * D + 2 * HKV * D)}
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        sync()
+        zg.kernel_timer_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        sync()
+        lin_ms, lin_n = zg.kernel_timer_read("linear")
+        zg.kernel_timer_enable(False)
+        ms = e0.elapsed_time(e1) / steps
+        gms = lin_ms / steps
+        res[name] = {"ms_per_layer": ms, "gemm_ms_per_layer": gms, "gemm_launches_per_layer": lin_n // steps,
+                     "gemm_tflop_per_layer": gemm_flop[name] / 1e12,
+                     "gemm_tflops": gemm_flop[name] / (gms / 1e3) / 1e12,
+                     "gemm_mfma_frac": gemm_flop[name] / (gms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS}
+        log(f"layers: {name}: {ms:.3f} ms/layer, GEMMs {gms:.3f} ms ({res[name]['gemm_tflops']:.0f} TFLOP/s)")
+    stack_ms = 27 * res["gated_swa_layer"]["ms_per_layer"] + 5 * res["global_layer"]["ms_per_layer"]
+    res["stack"] = {"ms": stack_ms, "tokens_per_s": S / (stack_ms / 1e3)}
+    del h, w, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------------------------------ CPU baseline
 def cpu_baseline(S=16384, n_rows=4096, seed=1003):
     """The fp64 oracle on a sample of the prefill workload: n_rows random positions, all 32 query heads, in
@@ -361,6 +420,9 @@ def main():
     ap.add_argument("--schedule-sweep", action="store_true",
                     help="instead of the benchmark: time one SWA and one global prefill layer at 4K..256K tokens and "
                          "compose the 5:1, 3:1, 1:1 and all-global 32-layer schedules (one JSON line)")
+    ap.add_argument("--layers", action="store_true",
+                    help="instead of the benchmark: time whole layers from the hidden state (projections on hipBLASLt, "
+                         "attention core, o_proj) at 1 x 16384 tokens, d_model 4096 (one JSON line)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="also copy a GIB-sized device tensor 3 times (a plain copy kernel of known traffic, for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -382,6 +444,16 @@ def main():
         log(f"copy calibration: 3 elementwise copies of {n * 4} bytes (read {n * 4} B + write {n * 4} B each)")
         del src, dst
         torch.cuda.empty_cache()
+    if args.layers:
+        res = run_layers(zg, steps=args.steps, warmup=args.warmup)
+        print(json.dumps({
+            "metric": "attention-layer time from the hidden state (q/k/v/g projections + core + o_proj)",
+            "unit": "ms", "n_gpus": 1, "data": "synthetic", "higher_is_better": False, "dtype": "bf16",
+            "config": {"workload": "one gated-SWA and one global layer, 1 x 16384 tokens", "d_model": D_MODEL,
+                       "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "window": W, "rotary_dims": R, "seed": 1007},
+            "layers": res,
+        }), flush=True)
+        return
     if args.schedule_sweep:
         per_layer, sched = run_schedule_sweep(zg)
         for name in SCHEDULES:

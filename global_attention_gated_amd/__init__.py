@@ -59,13 +59,20 @@ _lib.layer_workspace_bytes.argtypes = [_i32] * 5
 _lib.layer_workspace_bytes.restype = _u64
 _lib.gated_swa_layer.argtypes = [_vp] * 9 + [_i32] * 8 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
 _lib.global_layer.argtypes = [_vp] * 8 + [_i32] * 7 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
+_lib.fp8_linear_alloc.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_vp)]
+_lib.fp8_linear_free.argtypes = [_vp]
+_lib.fp8_linear_scales.argtypes = [_vp, ctypes.POINTER(_f32)]
+_lib.fp8_linear_workspace_bytes.argtypes = [_i64, _i32, _i32]
+_lib.fp8_linear_workspace_bytes.restype = _u64
+_lib.linear_fp8_delayed.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _u64, _vp]
 _lib.zg_last_error.restype = ctypes.c_char_p
 _lib.zg_kernel_timer_enable.argtypes = [_i32]
 _lib.zg_kernel_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_f64), ctypes.POINTER(_i64)]
 
 EXPORTED = ["kv_cache_alloc", "kv_cache_free", "kv_cache_footprint_bytes", "kv_cache_layer_view", "kv_cache_length",
             "kv_cache_set_length", "prefill_workspace_bytes", "swa_prefill", "global_prefill", "hybrid_decode_step",
-            "linear_bf16", "layer_workspace_bytes", "gated_swa_layer", "global_layer", "zg_last_error",
+            "linear_bf16", "layer_workspace_bytes", "gated_swa_layer", "global_layer", "fp8_linear_alloc",
+            "fp8_linear_free", "fp8_linear_scales", "fp8_linear_workspace_bytes", "linear_fp8_delayed", "zg_last_error",
             "zg_kernel_timer_enable", "zg_kernel_timer_read"]
 
 
@@ -235,6 +242,53 @@ def linear_bf16(x, w, y=None):
     _bf16(y, "y")
     _check(_lib.linear_bf16(_ptr(x), _ptr(w), _ptr(y), T, K, N, _stream()))
     return y
+
+
+class Fp8Linear:
+    """y = x W^T with E4M3 operands under delayed scaling (fp8_linear_alloc / linear_fp8_delayed): the state holds
+    each operand's amax history and current scale.  After a call, ``workspace`` holds the operands' E4M3 codes."""
+
+    def __init__(self, K: int, N: int, history: int = 1024):
+        h = _vp()
+        _check(_lib.fp8_linear_alloc(K, N, history, ctypes.byref(h)))
+        self.handle, self.K, self.N, self.history = h, K, N, history
+        self.workspace = None
+
+    def scales(self):
+        """(s_x, s_w): the scales the next call will use."""
+        out = (_f32 * 2)()
+        _check(_lib.fp8_linear_scales(self.handle, out))
+        return float(out[0]), float(out[1])
+
+    def __call__(self, x, w, y=None):
+        _bf16(x, "x"), _bf16(w, "w")
+        T = x.numel() // self.K
+        if y is None:
+            y = torch.empty((*x.shape[:-1], self.N), dtype=torch.bfloat16, device=x.device)
+        _bf16(y, "y")
+        need = int(_lib.fp8_linear_workspace_bytes(T, self.K, self.N))
+        if self.workspace is None or self.workspace.numel() < need:
+            self.workspace = torch.empty(max(16, need), dtype=torch.uint8, device=x.device)
+        _check(_lib.linear_fp8_delayed(_ptr(x), _ptr(w), _ptr(y), T, self.K, self.N, self.handle,
+                                       self.workspace.data_ptr(), self.workspace.numel(), _stream()))
+        return y
+
+    def codes(self, T: int):
+        """The E4M3 codes of the last call's x [T][K] and W [N][K] (uint8 CPU tensors)."""
+        off = (T * self.K + 255) // 256 * 256
+        ws = self.workspace.cpu()
+        return ws[:T * self.K].reshape(T, self.K), ws[off:off + self.N * self.K].reshape(self.N, self.K)
+
+    def close(self):
+        if self.handle:
+            _lib.fp8_linear_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def layer_workspace_bytes(B, S, Hq, Hkv, D=128) -> int:

@@ -1,7 +1,7 @@
 // Dense projections around the attention core (ZGCM-1 paper summaries: onedev.kr "How it works": the gated
 // layer is o_proj(A_SWA(q, k, v) (.) sigmoid(g_proj(h))), with q/k/v/g projections of the hidden state h).
 // These are plain GEMMs, run on hipBLASLt: y[T][N] = x[T][K] . W[N][K]^T (a linear layer's forward, W stored
-// out_features x in_features), bf16 operands, fp32 accumulation, bf16 result.
+// out_features x in_features), fp32 accumulation, bf16 result; operands bf16, or E4M3 with per-tensor scales.
 //
 // hipBLASLt is column-major: the row-major y[T][N] is the column-major N x T matrix D = op(A) op(B) with A = W
 // read as the column-major K x N matrix (transposed: op(A) = W, N x K) and B = x read as the column-major
@@ -29,7 +29,7 @@ struct Plan {
 struct DeviceBlas {
   hipblasLtHandle_t handle = nullptr;
   void* ws = nullptr;
-  std::map<std::tuple<int64_t, int32_t, int32_t>, Plan> plans;   // (T, K, N)
+  std::map<std::tuple<int, int64_t, int32_t, int32_t>, Plan> plans;   // (fp8?, T, K, N)
 };
 
 std::mutex g_mu;
@@ -37,7 +37,7 @@ std::map<int, DeviceBlas> g_dev;
 
 // Handle, workspace and plan for this device and shape, created on first use and kept until the process
 // ends.  Returns a hipblasStatus_t value (0 = success).
-int get_plan(int64_t T, int32_t K, int32_t N, DeviceBlas** dev_out, const Plan** plan_out) {
+int get_plan(bool fp8, int64_t T, int32_t K, int32_t N, DeviceBlas** dev_out, Plan** plan_out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return HIPBLAS_STATUS_NOT_INITIALIZED;
   std::lock_guard<std::mutex> lk(g_mu);
@@ -52,7 +52,7 @@ int get_plan(int64_t T, int32_t K, int32_t N, DeviceBlas** dev_out, const Plan**
       return HIPBLAS_STATUS_ALLOC_FAILED;
     }
   }
-  const auto key = std::make_tuple(T, K, N);
+  const auto key = std::make_tuple(fp8 ? 1 : 0, T, K, N);
   auto it = d.plans.find(key);
   if (it == d.plans.end()) {
     Plan p;
@@ -60,8 +60,17 @@ int get_plan(int64_t T, int32_t K, int32_t N, DeviceBlas** dev_out, const Plan**
     const int32_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
     if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof opT);
     if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof opN);
-    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, (uint64_t)K, (uint64_t)N, (int64_t)K);
-    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, (uint64_t)K, (uint64_t)T, (int64_t)K);
+    const hipDataType in = fp8 ? HIP_R_8F_E4M3 : HIP_R_16BF;
+    if (fp8 && s == HIPBLAS_STATUS_SUCCESS) {
+      // placeholder scale pointers so the heuristic sees a scaled FP8 problem; each call sets its own
+      static float one = 1.0f;
+      const void* pa = &one;
+      s = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_A_SCALE_POINTER, &pa, sizeof pa);
+      if (s == HIPBLAS_STATUS_SUCCESS)
+        s = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_B_SCALE_POINTER, &pa, sizeof pa);
+    }
+    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&p.la, in, (uint64_t)K, (uint64_t)N, (int64_t)K);
+    if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&p.lb, in, (uint64_t)K, (uint64_t)T, (int64_t)K);
     if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatrixLayoutCreate(&p.ld, HIP_R_16BF, (uint64_t)N, (uint64_t)T, (int64_t)N);
     hipblasLtMatmulPreference_t pref = nullptr;
     if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatmulPreferenceCreate(&pref);
@@ -93,11 +102,29 @@ int get_plan(int64_t T, int32_t K, int32_t N, DeviceBlas** dev_out, const Plan**
 
 int linear_bf16_run(const void* x, const void* w, void* y, int64_t T, int32_t K, int32_t N, hipStream_t st) {
   DeviceBlas* d = nullptr;
-  const Plan* p = nullptr;
-  int s = get_plan(T, K, N, &d, &p);
+  Plan* p = nullptr;
+  int s = get_plan(false, T, K, N, &d, &p);
   if (s != HIPBLAS_STATUS_SUCCESS) return s;
   const float alpha = 1.0f, beta = 0.0f;
   return hipblasLtMatmul(d->handle, p->desc, &alpha, w, p->la, x, p->lb, &beta, y, p->ld, y, p->ld, &p->algo, d->ws,
+                         kBlasWorkspace, st);
+}
+
+int linear_fp8_run(const void* xq, const void* wq, void* y, int64_t T, int32_t K, int32_t N, const float* x_scale_inv,
+                   const float* w_scale_inv, hipStream_t st) {
+  DeviceBlas* d = nullptr;
+  Plan* p = nullptr;
+  int s = get_plan(true, T, K, N, &d, &p);
+  if (s != HIPBLAS_STATUS_SUCCESS) return s;
+  // the scale pointers live in the shared plan: set them and enqueue under the lock
+  std::lock_guard<std::mutex> lk(g_mu);
+  const void* pa = w_scale_inv;   // A = W
+  const void* pb = x_scale_inv;   // B = x
+  s = hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_A_SCALE_POINTER, &pa, sizeof pa);
+  if (s == HIPBLAS_STATUS_SUCCESS) s = hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_B_SCALE_POINTER, &pb, sizeof pb);
+  if (s != HIPBLAS_STATUS_SUCCESS) return s;
+  const float alpha = 1.0f, beta = 0.0f;
+  return hipblasLtMatmul(d->handle, p->desc, &alpha, wq, p->la, xq, p->lb, &beta, y, p->ld, y, p->ld, &p->algo, d->ws,
                          kBlasWorkspace, st);
 }
 

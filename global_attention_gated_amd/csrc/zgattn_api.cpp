@@ -497,6 +497,15 @@ extern "C" int linear_bf16(const void* x, const void* w, void* y, int64_t T, int
   return ZG_OK;
 }
 
+// ---- FP8 projections with delayed scaling
+struct zg_fp8_linear {
+  int device = -1;
+  int32_t K = 0, N = 0, H = 0;
+  int32_t idx = 0;       // history slot of the next call
+  void* mem = nullptr;   // device: hist [2][H], amax [2], scale [2], scale_inv [2]
+  zg::Fp8State st{};
+};
+
 namespace {
 uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
 uint64_t layer_activation_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -551,6 +560,93 @@ int layer_common(bool gated, const void* h, const void* w_q, const void* w_k, co
   return linear_bf16(o, w_o, y, T, Hq * D, d_model, stream);
 }
 }  // namespace
+
+extern "C" int fp8_linear_alloc(int32_t K, int32_t N, int32_t history, zg_fp8_linear** out) {
+  const char* fn = "fp8_linear_alloc";
+  if (!out) return fail(ZG_EINVAL, "%s: null output handle", fn);
+  *out = nullptr;
+  if (K < 1 || N < 1 || history < 1) return fail(ZG_EINVAL, "%s: K, N and history must be >= 1", fn);
+  if (K % 8) return fail(ZG_EUNSUPPORTED, "%s: K = %d must be a multiple of 8", fn, K);
+  auto* f = new (std::nothrow) zg_fp8_linear();
+  if (!f) return fail(ZG_ENOMEM, "%s: host allocation failed", fn);
+  f->K = K; f->N = N; f->H = history;
+  if (hipGetDevice(&f->device) != hipSuccess) { delete f; return fail(ZG_EHIP, "%s: no current device", fn); }
+  const size_t bytes = (2 * (size_t)history + 6) * 4;
+  if (hipMalloc(&f->mem, bytes) != hipSuccess) { delete f; return fail(ZG_ENOMEM, "%s: device allocation failed", fn); }
+  float* base = static_cast<float*>(f->mem);
+  f->st.hist = base;
+  f->st.amax = reinterpret_cast<uint32_t*>(base + 2 * (size_t)history);
+  f->st.scale = base + 2 * (size_t)history + 2;
+  f->st.scale_inv = base + 2 * (size_t)history + 4;
+  f->st.H = history;
+  std::vector<float> init(2 * (size_t)history + 6, 0.0f);
+  init[2 * (size_t)history + 2] = init[2 * (size_t)history + 3] = 1.0f;   // scales
+  init[2 * (size_t)history + 4] = init[2 * (size_t)history + 5] = 1.0f;   // their inverses
+  if (hipMemcpy(f->mem, init.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(f->mem);
+    delete f;
+    return fail(ZG_EHIP, "%s: initialising the state failed", fn);
+  }
+  *out = f;
+  return ZG_OK;
+}
+
+extern "C" int fp8_linear_free(zg_fp8_linear* f) {
+  if (!f) return ZG_OK;
+  (void)hipDeviceSynchronize();
+  (void)hipFree(f->mem);
+  delete f;
+  return ZG_OK;
+}
+
+extern "C" int fp8_linear_scales(const zg_fp8_linear* f, float* scales_out) {
+  if (!f || !scales_out) return fail(ZG_EINVAL, "fp8_linear_scales: null argument");
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(scales_out, f->st.scale, 2 * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(ZG_EHIP, "fp8_linear_scales: reading the device state failed");
+  return ZG_OK;
+}
+
+extern "C" uint64_t fp8_linear_workspace_bytes(int64_t T, int32_t K, int32_t N) {
+  if (T < 0 || K < 0 || N < 0) return 0;
+  return align256((uint64_t)T * (uint64_t)K) + align256((uint64_t)N * (uint64_t)K);
+}
+
+extern "C" int linear_fp8_delayed(const void* x, const void* w, void* y, int64_t T, int32_t K, int32_t N,
+                                  zg_fp8_linear* f, void* workspace, uint64_t workspace_bytes, void* stream) {
+  const char* fn = "linear_fp8_delayed";
+  if (!f) return fail(ZG_EINVAL, "%s: null state", fn);
+  if (T < 0 || K != f->K || N != f->N) return fail(ZG_EINVAL, "%s: shape (T=%lld, K=%d, N=%d) does not match the state (K=%d, N=%d)", fn, (long long)T, K, N, f->K, f->N);
+  if (T == 0) return ZG_OK;
+  if (!x || !w || !y) return fail(ZG_EINVAL, "%s: null tensor pointer", fn);
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return fail(ZG_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+  if (!workspace || !aligned16(workspace)) return fail(ZG_EINVAL, "%s: a 16-byte aligned workspace is required", fn);
+  if (workspace_bytes < fp8_linear_workspace_bytes(T, K, N))
+    return fail(ZG_ERANGE, "%s: workspace of %llu bytes < %llu needed", fn, (unsigned long long)workspace_bytes,
+                (unsigned long long)fp8_linear_workspace_bytes(T, K, N));
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != f->device)
+    return fail(ZG_EINVAL, "%s: the state lives on device %d, the current device is %d", fn, f->device, cur);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  uint8_t* wq = xq + align256((uint64_t)T * K);
+  hipError_t e;
+  {
+    ScopedTimer tm("fp8_quantize", st);
+    e = launch_fp8_quantize(static_cast<const uint16_t*>(x), xq, T * K, f->st.scale + 0, f->st.amax + 0, st);
+    if (e == hipSuccess) e = launch_fp8_quantize(static_cast<const uint16_t*>(w), wq, (int64_t)N * K, f->st.scale + 1, f->st.amax + 1, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
+  {
+    ScopedTimer tm("linear", st);
+    const int s = linear_fp8_run(xq, wq, y, T, K, N, f->st.scale_inv + 0, f->st.scale_inv + 1, st);
+    if (s) return fail(ZG_EHIP, "%s: hipBLASLt %s (T=%lld K=%d N=%d)", fn, blas_status_name(s), (long long)T, K, N);
+  }
+  e = launch_fp8_finalize(f->st, f->idx, st);
+  if (e != hipSuccess) return hip_fail(e, "fp8 finalize launch");
+  f->idx = (f->idx + 1) % f->H;
+  return ZG_OK;
+}
 
 extern "C" int gated_swa_layer(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_g,
                                const void* w_o, const void* q_norm_w, const void* k_norm_w, void* y, int32_t B,

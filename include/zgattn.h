@@ -151,6 +151,31 @@ int hybrid_decode_step(const void* q, const void* k, const void* v, const void* 
  * Errors: EINVAL (shape, null, alignment), EHIP (hipBLASLt failure, message names the status). */
 int linear_bf16(const void* x, const void* w, void* y, int64_t T, int32_t K, int32_t N, void* stream);
 
+/* ---- FP8 projections with delayed scaling (onedev.kr "What differs": FP8 matmuls, E4M3 in the forward pass,
+ * delayed scaling over a 1,024-step amax history).  E4M3 is the OCP format: largest finite value 448,
+ * 3 mantissa bits, subnormals down to 2^-9.  A state keeps, for the input x and the weight W, an amax
+ * history of `history` calls and the scale in use, s = 448 / max(history) (1 while the history is zero).
+ * Each call quantises x and W with the current scales (code = E4M3(v * s), nearest-even, saturating at +-448),
+ * runs the GEMM on the codes with fp32 accumulation and multiplies by 1/(s_x s_w), then records this call's
+ * max |x| and max |W| in the histories and derives the next scales: the scales lag the data by one call. */
+typedef struct zg_fp8_linear zg_fp8_linear;
+
+/* Allocate a state for y[T][N] = x[T][K] . W[N][K]^T on the current device: histories zero, scales 1.
+ * K must be a multiple of 8.  Errors: EINVAL, EUNSUPPORTED, ENOMEM, EHIP. */
+int fp8_linear_alloc(int32_t K, int32_t N, int32_t history, zg_fp8_linear** out);
+/* Release a state (synchronises the device first).  NULL is accepted. */
+int fp8_linear_free(zg_fp8_linear* state);
+/* The scales the next call will use, {s_x, s_w} (HOST float[2]); synchronises the device. */
+int fp8_linear_scales(const zg_fp8_linear* state, float* scales_out);
+/* Workspace bytes of linear_fp8_delayed: the E4M3 codes of x (T*K bytes), then those of W (N*K bytes), each
+ * starting on a 256-byte boundary.  After a call the workspace holds both code arrays. */
+uint64_t fp8_linear_workspace_bytes(int64_t T, int32_t K, int32_t N);
+/* One FP8 projection: x [T][K], W [N][K], y [T][N] device bf16; state as allocated for (K, N).  Calls that
+ * share a state must be ordered on one stream.  T == 0 is a no-op (the state does not advance).
+ * Errors: EINVAL (shape or device mismatch, null, alignment), ERANGE (workspace), EHIP. */
+int linear_fp8_delayed(const void* x, const void* w, void* y, int64_t T, int32_t K, int32_t N, zg_fp8_linear* state,
+                       void* workspace, uint64_t workspace_bytes, void* stream);
+
 /* Workspace bytes for gated_swa_layer / global_layer on B x S tokens: the bf16 activations q, g, o [T][Hq*D] and
  * k, v [T][Hkv*D] (T = B*S), 256-byte aligned, followed by prefill_workspace_bytes(B, S, Hkv, D). */
 uint64_t layer_workspace_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D);
@@ -180,7 +205,7 @@ const char* zg_last_error(void);
 /* Kernel timer: while enabled, every launch of the main attention kernels records a pair of HIP
  * events on the launch stream.  zg_kernel_timer_read synchronises on the recorded events and returns,
  * for the kernel family `name` ("attn_swa", "attn_global", "decode_global", "decode_swa",
- * "kv_prologue", "decode_merge", "decode_append", "linear"), the summed device time in ms and the launch count
+ * "kv_prologue", "decode_merge", "decode_append", "linear", "fp8_quantize"), the summed device time in ms and the launch count
  * since the last reset.  Enabling resets the counters. */
 int zg_kernel_timer_enable(int32_t on);
 int zg_kernel_timer_read(const char* name, double* total_ms, int64_t* launches);

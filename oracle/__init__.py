@@ -289,6 +289,64 @@ def linear(x, w) -> np.ndarray:
     return _as_f64(x) @ _as_f64(w).T
 
 
+# FP8 E4M3 (OCP) from its definition: sign, 4 exponent bits (bias 7), 3 mantissa bits; normals
+# 2^(e-7) (1 + m/8) for e = 1..15 except e = 15, m = 7 (NaN), largest finite 448; subnormals m 2^-9.
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Codes (uint8) of float32 values, nearest-even, saturating at +-448 (finite inputs).  The decision is
+    taken on the float32 value itself (what the quantised product is before encoding)."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v).astype(np.float64)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sat = a >= E4M3_MAX
+    sub = a < 2.0 ** -6
+    nrm = ~sat & ~sub
+    code[sat] = 0x7E
+    code[sub] = np.rint(a[sub] * 512.0).astype(np.int64)              # 0..8 (8 = the smallest normal)
+    f, p = np.frexp(a[nrm])                                            # a = f 2^p, f in [0.5, 1)
+    e = p - 1
+    q = np.rint((a[nrm] / np.ldexp(1.0, e) - 1.0) * 8.0).astype(np.int64)   # 0..8, nearest-even
+    code[nrm] = np.minimum((e + 7) * 8 + q, 0x7E)                    # q = 8 carries into the exponent
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 values of E4M3 codes (the NaN code is not produced by e4m3_encode)."""
+    c = np.asarray(codes, dtype=np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where(c & 0x80, -mag, mag)
+
+
+class Fp8DelayedLinear:
+    """y = x W^T with both operands in E4M3 under delayed scaling (onedev.kr "What differs": FP8 matmuls with
+    delayed scaling over a 1,024-step amax history).  Per tensor (0 = x, 1 = W): the scale in use s (float32, 1 at
+    first), codes = E4M3(v * s) in float32, y = (codes_x . codes_w^T) * (1/s_x) * (1/s_w); then this call's max |v|
+    enters the tensor's history and the next scale is 448 / max(history) in float32 (1 if the history is zero)."""
+
+    def __init__(self, K: int, N: int, history: int = 1024):
+        self.K, self.N, self.H = K, N, history
+        self.hist = np.zeros((2, history), dtype=np.float32)
+        self.idx = 0
+        self.scale = np.ones(2, dtype=np.float32)
+
+    def __call__(self, x, w):
+        xf = _as_f64(x).astype(np.float32)          # bf16 values are exact in float32
+        wf = _as_f64(w).astype(np.float32)
+        cx = e4m3_encode(xf * self.scale[0])        # float32 products, as the kernels form them
+        cw = e4m3_encode(wf * self.scale[1])
+        inv = np.float32(1.0) / self.scale          # the dequantisation factors, float32
+        y = (e4m3_decode(cx) @ e4m3_decode(cw).T) * np.float64(inv[0]) * np.float64(inv[1])
+        self.hist[0, self.idx] = np.max(np.abs(xf))
+        self.hist[1, self.idx] = np.max(np.abs(wf))
+        self.idx = (self.idx + 1) % self.H
+        m = self.hist.max(axis=1)
+        self.scale = np.where(m > 0, np.float32(E4M3_MAX) / np.where(m > 0, m, np.float32(1)), np.float32(1)).astype(np.float32)
+        return y, cx, cw
+
+
 def attention_layer(h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, *, Hq: int, Hkv: int, window: int | None,
                     rotary_dims: int, base: float, eps: float) -> np.ndarray:
     """The layer around the core (onedev.kr "How it works": o_proj(A_SWA(q, k, v) (.) sigmoid(g_proj(h))); the

@@ -69,3 +69,27 @@ def test_attention_layer_from_hidden_state_matches_oracle(zg, gated, B, S):
     print(f"layer {'swa' if gated else 'global'} B{B} S{S}: max_abs {np.abs(got - ref).max():.3e} "
           f"mean_abs {np.abs(got - ref).mean():.3e} rms(y) {np.sqrt(np.mean(ref ** 2)):.3f}")
     compare(got, ref, f"{'gated SWA' if gated else 'global'} layer B{B} S{S}")
+
+
+def test_fp8_delayed_scaling_matches_oracle_over_calls(zg):
+    """Five FP8 projections through one state whose input magnitude changes by powers of two: the E4M3 codes of
+    x and W equal the oracle's byte for byte, the scales in use equal its float32 scales, and y is within its
+    rounding bound (the codes' products are exact; fp32 accumulation; bf16 result)."""
+    T, K, N = 300, 4096, 1024
+    f = zg.Fp8Linear(K, N, history=1024)
+    ref = oracle.Fp8DelayedLinear(K, N, history=1024)
+    w = weight_bits(31, synth.TENSOR_PK, N, K)
+    x0 = synth.bf16_bits_to_f64(synth.normal_bf16(31, 0, synth.TENSOR_H, (T, K)))
+    for call, mag in enumerate((1.0, 4.0, 0.25, 16.0, 1.0)):
+        x = synth.f64_to_bf16_bits(x0 * mag)                     # exact: power-of-two factors
+        sx, sw = f.scales()
+        assert (np.float32(sx), np.float32(sw)) == (ref.scale[0], ref.scale[1]), f"call {call}"
+        y = to_host_f64(f(to_dev(x), to_dev(w)))
+        yr, cx, cw = ref(x, w)
+        gx, gw = f.codes(T)
+        np.testing.assert_array_equal(gx.numpy(), cx, err_msg=f"x codes, call {call}")
+        np.testing.assert_array_equal(gw.numpy(), cw, err_msg=f"W codes, call {call}")
+        err = np.abs(y - yr)
+        bound = 2.0 ** -8 * np.abs(yr) + 1e-3 * np.sqrt(np.mean(yr ** 2))
+        assert np.all(err <= bound), f"call {call}: max excess {float((err - bound).max()):.3e}"
+    f.close()

@@ -324,3 +324,51 @@ def test_attention_layer_with_identity_projections_is_the_core(gated):
     o = oracle.prefill_layer(hq, hq, hq, hq if gated else None, wn, wn, window=16 if gated else None, rotary_dims=42,
                              base=1e4, eps=1e-6)
     np.testing.assert_array_equal(y, oracle.bf16_to_f64(oracle.round_bf16(o)).reshape(B, S, H * D))
+
+
+# ------------------------------------------------------------------------------------------ FP8 E4M3
+def test_e4m3_codes_of_defining_values():
+    """OCP E4M3: bias 7, 3 mantissa bits, largest finite 448 (0x7E), smallest subnormal 2^-9 (0x01)."""
+    cases = {0.0: 0x00, 1.0: 0x38, -1.0: 0xB8, 448.0: 0x7E, -448.0: 0xFE, 2.0 ** -9: 0x01, 2.0 ** -6: 0x08,
+             1.75: 0x3E, 240.0: 0x77, 0.5: 0x30,
+             1.0 + 1 / 16: 0x38,          # tie -> even mantissa (0)
+             1.0 + 3 / 16: 0x3A,          # tie -> even mantissa (2)
+             3 * 2.0 ** -10: 0x02,        # subnormal tie 1.5 -> 2
+             2.0 ** -10: 0x00,            # half the smallest subnormal: tie -> 0
+             1000.0: 0x7E, -1e6: 0xFE,    # saturation
+             15.5: 0x58,                  # 15.5 = 2^3 * 1.9375: mantissa tie 7.5 -> 8, carries into 16 = 2^4
+             56.0: 0x66}                  # 56 = 2^5 * 1.75
+    for v, code in cases.items():
+        assert int(oracle.e4m3_encode(np.array([v]))[0]) == code, v
+    for code in range(256):
+        if code & 0x7F == 0x7F:
+            continue                       # NaN codes
+        val = oracle.e4m3_decode(np.array([code]))[0]
+        back = int(oracle.e4m3_encode(np.array([val]))[0])
+        assert back == code or (val == 0.0 and back & 0x7F == 0), code
+
+
+def test_e4m3_matches_torch_float8_in_range():
+    """Against torch's float8_e4m3fn cast (nearest-even) for finite values inside +-448."""
+    v = np.concatenate([RNG.standard_normal(20000) * s for s in (1e-3, 0.05, 1.0, 30.0, 150.0)]).astype(np.float32)
+    v = v[np.abs(v) < 448.0]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_encode(v), ref)
+
+
+def test_fp8_delayed_scaling_lags_by_one_call():
+    """Scales start at 1, then follow 448 / max(amax history) of the calls before (history of 2 here)."""
+    f = oracle.Fp8DelayedLinear(K=8, N=2, history=2)
+    w = np.full((2, 8), 0.5)
+    for amax_x, expect_scale_x in ((2.0, 1.0), (8.0, 448.0 / 2.0), (1.0, 448.0 / 8.0), (1.0, 448.0 / 8.0)):
+        x = np.zeros((1, 8)); x[0, 3] = amax_x
+        assert float(f.scale[0]) == np.float32(expect_scale_x)
+        y, cx, cw = f(x, w)
+        assert float(f.scale[1]) == np.float32(448.0 / 0.5)
+    # after the fourth call the history holds {1, 1}: the next scale is 448
+    assert float(f.scale[0]) == 448.0
+    # with the scale 448/8 = 56 in use, x = 1 is coded as 56 -> E4M3(56) = 0x66 and dequantised exactly
+    f2 = oracle.Fp8DelayedLinear(K=8, N=1, history=4)
+    f2(np.full((1, 8), 8.0), np.full((1, 8), 1.0))
+    y, cx, cw = f2(np.full((1, 8), 1.0), np.full((1, 8), 1.0))
+    assert int(cx[0, 0]) == 0x66 and y[0, 0] == pytest.approx(8.0)
