@@ -358,7 +358,37 @@ def run_layers(zg, steps=5, warmup=2, S=16384, seed=1007):
         log(f"layers: {name}: {ms:.3f} ms/layer, GEMMs {gms:.3f} ms ({res[name]['gemm_tflops']:.0f} TFLOP/s)")
     stack_ms = 27 * res["gated_swa_layer"]["ms_per_layer"] + 5 * res["global_layer"]["ms_per_layer"]
     res["stack"] = {"ms": stack_ms, "tokens_per_s": S / (stack_ms / 1e3)}
-    del h, w, y, ws
+
+    # one 4096 -> 4096 projection of the S tokens: bf16 against FP8 with delayed scaling (quantisation of x and
+    # W, GEMM and scale update all inside the timed call)
+    x, wq = h.view(S, D_MODEL), w["q"]
+    fp8 = zg.Fp8Linear(D_MODEL, HQ * D)
+    yp = torch.empty((S, HQ * D), dtype=torch.bfloat16, device="cuda")
+    flop = 2 * S * D_MODEL * HQ * D
+    for name, fn in (("bf16", lambda: zg.linear_bf16(x, wq, yp)), ("fp8_delayed", lambda: fp8(x, wq, yp))):
+        for _ in range(warmup):
+            fn()
+        sync()
+        zg.kernel_timer_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        sync()
+        g_ms, _ = zg.kernel_timer_read("linear")
+        q_ms, _ = zg.kernel_timer_read("fp8_quantize")
+        zg.kernel_timer_enable(False)
+        ms = e0.elapsed_time(e1) / steps
+        peak = MFMA_PEAK_TFLOPS * (2 if name == "fp8_delayed" else 1)        # dense fp8 MFMA: 5.0 PFLOP/s
+        res.setdefault("projection_4096x4096", {"tokens": S, "tflop": flop / 1e12})[name] = {
+            "ms": ms, "gemm_ms": g_ms / steps, "quantize_ms": q_ms / steps, "tflops": flop / (ms / 1e3) / 1e12,
+            "gemm_tflops": flop / (g_ms / steps / 1e3) / 1e12, "gemm_peak_tflops": peak,
+            "gemm_frac": flop / (g_ms / steps / 1e3) / 1e12 / peak}
+        log(f"layers: projection {name}: {ms:.3f} ms (GEMM {g_ms / steps:.3f} ms, "
+            f"{flop / (g_ms / steps / 1e3) / 1e12:.0f} TFLOP/s; quantise {q_ms / steps:.3f} ms)")
+    fp8.close()
+    del h, w, y, ws, x, yp
     torch.cuda.empty_cache()
     return res
 

@@ -16,80 +16,82 @@
 namespace zg {
 namespace {
 
-// fp32 -> E4M3 code, nearest-even, saturating at +-448 (finite inputs).  Works on the fp32 bits: the three
-// kept mantissa bits are rounded on the 20 dropped ones; a carry out of the mantissa moves into the exponent
-// field of the code, which is the correct next binade.
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(x);
-  uint32_t mag;
-  if (a >= 448.0f) {
-    mag = 0x7E;                                        // saturate
-  } else if (a < 0.015625f) {                          // below 2^-6: multiples of 2^-9 (the scaling is exact)
-    mag = (uint32_t)__builtin_rintf(a * 512.0f);       // 0..8 (8 is the smallest normal, code 0x08)
-  } else {
-    const uint32_t ua = u & 0x7fffffffu;
-    const int e = (int)(ua >> 23) - 127;               // -6 .. 8
-    uint32_t q = (ua >> 20) & 7u;
-    const uint32_t rem = ua & 0xfffffu;
-    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) q += 1;
-    mag = ((uint32_t)(e + 7) << 3) + q;
-    if (mag > 0x7Eu) mag = 0x7E;
+// E4M3 codes of 8 bf16 values times s: the product clamped to +-448 (v_med3) and converted by v_cvt_pk_fp8_f32
+// (nearest-even into OCP E4M3), which together give the saturating nearest-even code.  Raises m to max |x|.
+__device__ __forceinline__ uint2 e4m3x8(uint4 w, float s, float& m) {
+  float f[8];
+  unpack8(w, f);
+  uint32_t out[2];
+#pragma unroll
+  for (int d = 0; d < 2; d++) {
+    float a[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      m = fmaxf(m, fabsf(f[4 * d + e]));
+      a[e] = __builtin_amdgcn_fmed3f(f[4 * d + e] * s, -448.0f, 448.0f);
+    }
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a[0], a[1], 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(a[2], a[3], r, true);
+    out[d] = (uint32_t)r;
   }
-  return sign | mag;
+  return make_uint2(out[0], out[1]);
 }
 
-// Quantise n bf16 values (n a multiple of 8) with the scale in *scale; atomically raise *amax (fp32 bits, a
-// non-negative float compares like its bits) to this tensor's max |x|.
+// Quantise n bf16 values (n8 = n / 8 groups of 8) with the scale in *scale: codes = E4M3(x * s).  Grid stride,
+// two groups in flight per lane, every access a lane-contiguous 16-byte load / 8-byte store.  Each work-group
+// writes the max |x| of what it covered to partial[blockIdx.x] (no atomics: a same-address atomic per wave
+// serialises at the L2); the finalize kernel reduces the partials.
 __global__ void __launch_bounds__(256) fp8_quantize_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
                                                           int64_t n8, const float* __restrict__ scale,
-                                                          uint32_t* __restrict__ amax) {
+                                                          float* __restrict__ partial) {
   const float s = *scale;
   float m = 0.f;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
-    float f[8];
-    unpack8(*reinterpret_cast<const uint4*>(x + 8 * i), f);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      m = fmaxf(m, fabsf(f[e]));
-      lo |= e4m3_code(f[e] * s) << (8 * e);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      m = fmaxf(m, fabsf(f[4 + e]));
-      hi |= e4m3_code(f[4 + e] * s) << (8 * e);
-    }
-    *reinterpret_cast<uint2*>(q + 8 * i) = make_uint2(lo, hi);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint2* qv = reinterpret_cast<uint2*>(q);
+  for (; u + stride < n8; u += 2 * stride) {
+    const uint4 a = xv[u], b = xv[u + stride];
+    qv[u] = e4m3x8(a, s, m);
+    qv[u + stride] = e4m3x8(b, s, m);
   }
-  // wave max, then one atomic per wave
+  if (u < n8) qv[u] = e4m3x8(xv[u], s, m);
+  __shared__ float red[4];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) atomicMax(amax, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// After a call: push each tensor's amax into its history (slot idx), clear it, and derive the next scale
-// s = 448 / max(history) (1 if the history is all zero) and its inverse (the GEMM's dequantisation factor).
-// One work-group; state layout as Fp8State.
-__global__ void __launch_bounds__(256) fp8_finalize_kernel(Fp8State st, int32_t idx) {
-  __shared__ float red[2][4];
+// After a call: reduce each tensor's partial maxima (nblk[t] of them) to this call's amax, push it into the
+// history (slot idx), and derive the next scale s = 448 / max(history) (1 if the history is all zero) and its
+// inverse (the GEMM's dequantisation factor).  One work-group; state layout as Fp8State.
+__global__ void __launch_bounds__(256) fp8_finalize_kernel(Fp8State st, int32_t idx, int32_t nblk0, int32_t nblk1) {
+  __shared__ float red[4];
   for (int t = 0; t < 2; t++) {
+    const float* part = st.partial + (int64_t)t * kFp8MaxBlocks;
+    const int nb = t == 0 ? nblk0 : nblk1;
     float* hist = st.hist + (int64_t)t * st.H;
-    if (threadIdx.x == 0) hist[idx] = __uint_as_float(st.amax[t]);
-    __syncthreads();
     float m = 0.f;
+    for (int i = threadIdx.x; i < nb; i += blockDim.x) m = fmaxf(m, part[i]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) hist[idx] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    m = 0.f;
     for (int i = threadIdx.x; i < st.H; i += blockDim.x) m = fmaxf(m, hist[i]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if ((threadIdx.x & 63) == 0) red[t][threadIdx.x >> 6] = m;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
-      const float mm = fmaxf(fmaxf(red[t][0], red[t][1]), fmaxf(red[t][2], red[t][3]));
-      const float s = mm > 0.f ? 448.0f / mm : 1.0f;
-      st.scale[t] = s;
-      st.scale_inv[t] = 1.0f / s;
-      st.amax[t] = 0u;
+      const float mm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      const float sc = mm > 0.f ? 448.0f / mm : 1.0f;
+      st.scale[t] = sc;
+      st.scale_inv[t] = 1.0f / sc;
     }
     __syncthreads();
   }
@@ -97,18 +99,20 @@ __global__ void __launch_bounds__(256) fp8_finalize_kernel(Fp8State st, int32_t 
 
 }  // namespace
 
-hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const float* scale, uint32_t* amax,
+int32_t fp8_quantize_blocks(int64_t n) {
+  const int64_t b = (n / 8 + 255) / 256;
+  return (int32_t)(b < 1 ? 1 : (b > kFp8MaxBlocks ? kFp8MaxBlocks : b));
+}
+
+hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const float* scale, float* partial,
                                hipStream_t st) {
-  const int64_t n8 = n / 8;
-  int64_t blocks = (n8 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(fp8_quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, q, n8, scale, amax);
+  hipLaunchKernelGGL(fp8_quantize_kernel, dim3((unsigned)fp8_quantize_blocks(n)), dim3(256), 0, st, x, q, n / 8,
+                     scale, partial);
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, hipStream_t st) {
-  hipLaunchKernelGGL(fp8_finalize_kernel, dim3(1), dim3(256), 0, st, s, idx);
+hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, int32_t nblk0, int32_t nblk1, hipStream_t st) {
+  hipLaunchKernelGGL(fp8_finalize_kernel, dim3(1), dim3(256), 0, st, s, idx, nblk0, nblk1);
   return hipGetLastError();
 }
 

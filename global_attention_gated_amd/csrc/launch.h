@@ -92,10 +92,12 @@ struct SwaStreamArgs {
 };
 
 // Device state of an FP8 projection with delayed scaling: two tensors (0 = the input x, 1 = the weight W),
-// each with an amax history of H floats, this call's amax (fp32 bits), the scale in use and its inverse.
+// each with an amax history of H floats, the per-work-group maxima of the current call's quantisation, the
+// scale in use and its inverse.
+constexpr int32_t kFp8MaxBlocks = 2048;   // work-groups of one quantisation launch (8 per CU)
 struct Fp8State {
   float* hist;        // [2][H]
-  uint32_t* amax;     // [2]
+  float* partial;     // [2][kFp8MaxBlocks]
   float* scale;       // [2]
   float* scale_inv;   // [2]
   int32_t H;
@@ -137,9 +139,10 @@ hipError_t launch_kv_prologue(const KvPrologueArgs& a, hipStream_t st);
 hipError_t launch_ring_write(const RingWriteArgs& a, hipStream_t st);
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st);
-hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const float* scale, uint32_t* amax,
+int32_t fp8_quantize_blocks(int64_t n);   // work-groups launch_fp8_quantize uses for n values
+hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const float* scale, float* partial,
                                hipStream_t st);
-hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, hipStream_t st);
+hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, int32_t nblk0, int32_t nblk1, hipStream_t st);
 int swa_stream_run_length(int S, int n_units);
 hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t st);

@@ -502,7 +502,7 @@ struct zg_fp8_linear {
   int device = -1;
   int32_t K = 0, N = 0, H = 0;
   int32_t idx = 0;       // history slot of the next call
-  void* mem = nullptr;   // device: hist [2][H], amax [2], scale [2], scale_inv [2]
+  void* mem = nullptr;   // device: hist [2][H], partial [2][kFp8MaxBlocks], scale [2], scale_inv [2]
   zg::Fp8State st{};
 };
 
@@ -571,17 +571,17 @@ extern "C" int fp8_linear_alloc(int32_t K, int32_t N, int32_t history, zg_fp8_li
   if (!f) return fail(ZG_ENOMEM, "%s: host allocation failed", fn);
   f->K = K; f->N = N; f->H = history;
   if (hipGetDevice(&f->device) != hipSuccess) { delete f; return fail(ZG_EHIP, "%s: no current device", fn); }
-  const size_t bytes = (2 * (size_t)history + 6) * 4;
+  const size_t P = 2 * (size_t)history + 2 * (size_t)zg::kFp8MaxBlocks;   // floats before the scales
+  const size_t bytes = (P + 4) * 4;
   if (hipMalloc(&f->mem, bytes) != hipSuccess) { delete f; return fail(ZG_ENOMEM, "%s: device allocation failed", fn); }
   float* base = static_cast<float*>(f->mem);
   f->st.hist = base;
-  f->st.amax = reinterpret_cast<uint32_t*>(base + 2 * (size_t)history);
-  f->st.scale = base + 2 * (size_t)history + 2;
-  f->st.scale_inv = base + 2 * (size_t)history + 4;
+  f->st.partial = base + 2 * (size_t)history;
+  f->st.scale = base + P;
+  f->st.scale_inv = base + P + 2;
   f->st.H = history;
-  std::vector<float> init(2 * (size_t)history + 6, 0.0f);
-  init[2 * (size_t)history + 2] = init[2 * (size_t)history + 3] = 1.0f;   // scales
-  init[2 * (size_t)history + 4] = init[2 * (size_t)history + 5] = 1.0f;   // their inverses
+  std::vector<float> init(P + 4, 0.0f);
+  init[P] = init[P + 1] = init[P + 2] = init[P + 3] = 1.0f;   // scales and their inverses
   if (hipMemcpy(f->mem, init.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(f->mem);
     delete f;
@@ -633,8 +633,10 @@ extern "C" int linear_fp8_delayed(const void* x, const void* w, void* y, int64_t
   hipError_t e;
   {
     ScopedTimer tm("fp8_quantize", st);
-    e = launch_fp8_quantize(static_cast<const uint16_t*>(x), xq, T * K, f->st.scale + 0, f->st.amax + 0, st);
-    if (e == hipSuccess) e = launch_fp8_quantize(static_cast<const uint16_t*>(w), wq, (int64_t)N * K, f->st.scale + 1, f->st.amax + 1, st);
+    e = launch_fp8_quantize(static_cast<const uint16_t*>(x), xq, T * K, f->st.scale + 0, f->st.partial, st);
+    if (e == hipSuccess)
+      e = launch_fp8_quantize(static_cast<const uint16_t*>(w), wq, (int64_t)N * K, f->st.scale + 1,
+                              f->st.partial + zg::kFp8MaxBlocks, st);
   }
   if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
   {
@@ -642,7 +644,7 @@ extern "C" int linear_fp8_delayed(const void* x, const void* w, void* y, int64_t
     const int s = linear_fp8_run(xq, wq, y, T, K, N, f->st.scale_inv + 0, f->st.scale_inv + 1, st);
     if (s) return fail(ZG_EHIP, "%s: hipBLASLt %s (T=%lld K=%d N=%d)", fn, blas_status_name(s), (long long)T, K, N);
   }
-  e = launch_fp8_finalize(f->st, f->idx, st);
+  e = launch_fp8_finalize(f->st, f->idx, fp8_quantize_blocks(T * K), fp8_quantize_blocks((int64_t)N * K), st);
   if (e != hipSuccess) return hip_fail(e, "fp8 finalize launch");
   f->idx = (f->idx + 1) % f->H;
   return ZG_OK;
