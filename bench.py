@@ -326,15 +326,23 @@ def run_layers(zg, steps=5, warmup=2, S=16384, seed=1007):
          "o": weight(synth.TENSOR_PO, D_MODEL, HQ * D)}
     nw = torch.from_numpy(synth.norm_weight_bf16(seed, 1, synth.TENSOR_WQ, D).view("int16")).cuda().view(torch.bfloat16)
     y = torch.empty_like(h)
-    ws = torch.empty(zg.layer_workspace_bytes(1, S, HQ, HKV, D), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(zg.fp8_layer_workspace_bytes(1, S, D_MODEL, HQ, HKV, D), dtype=torch.uint8, device="cuda")
+    f8 = {"gated_swa_layer_fp8": zg.Fp8Layer(D_MODEL, HQ, HKV, D), "global_layer_fp8": zg.Fp8Layer(D_MODEL, HQ, HKV, D)}
     calls = {
         "gated_swa_layer": lambda: zg.gated_swa_layer(h, w["q"], w["k"], w["v"], w["g"], w["o"], nw, nw, y, Hq=HQ,
                                                       Hkv=HKV, window=W, rotary_dims=R, rope_base=1e4, workspace=ws),
         "global_layer": lambda: zg.global_layer(h, w["q"], w["k"], w["v"], w["o"], nw, nw, y, Hq=HQ, Hkv=HKV,
                                                 rotary_dims=R, rope_base=1e4, workspace=ws),
+        "gated_swa_layer_fp8": lambda: zg.gated_swa_layer_fp8(
+            h, w["q"], w["k"], w["v"], w["g"], w["o"], nw, nw, y, fp8=f8["gated_swa_layer_fp8"], Hq=HQ, Hkv=HKV,
+            window=W, rotary_dims=R, rope_base=1e4, workspace=ws),
+        "global_layer_fp8": lambda: zg.global_layer_fp8(
+            h, w["q"], w["k"], w["v"], w["o"], nw, nw, y, fp8=f8["global_layer_fp8"], Hq=HQ, Hkv=HKV, rotary_dims=R,
+            rope_base=1e4, workspace=ws),
     }
     gemm_flop = {"gated_swa_layer": 2 * S * D_MODEL * (3 * HQ * D + 2 * HKV * D),
                  "global_layer": 2 * S * D_MODEL * (2 * HQ * D + 2 * HKV * D)}
+    gemm_flop["gated_swa_layer_fp8"], gemm_flop["global_layer_fp8"] = gemm_flop["gated_swa_layer"], gemm_flop["global_layer"]
     res = {}
     for name, fn in calls.items():
         for _ in range(warmup):
@@ -348,16 +356,23 @@ def run_layers(zg, steps=5, warmup=2, S=16384, seed=1007):
         e1.record()
         sync()
         lin_ms, lin_n = zg.kernel_timer_read("linear")
+        q_ms, _ = zg.kernel_timer_read("fp8_quantize")
         zg.kernel_timer_enable(False)
         ms = e0.elapsed_time(e1) / steps
         gms = lin_ms / steps
+        peak = MFMA_PEAK_TFLOPS * (2 if name.endswith("_fp8") else 1)        # dense fp8 MFMA: 5.0 PFLOP/s
         res[name] = {"ms_per_layer": ms, "gemm_ms_per_layer": gms, "gemm_launches_per_layer": lin_n // steps,
-                     "gemm_tflop_per_layer": gemm_flop[name] / 1e12,
-                     "gemm_tflops": gemm_flop[name] / (gms / 1e3) / 1e12,
-                     "gemm_mfma_frac": gemm_flop[name] / (gms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS}
-        log(f"layers: {name}: {ms:.3f} ms/layer, GEMMs {gms:.3f} ms ({res[name]['gemm_tflops']:.0f} TFLOP/s)")
-    stack_ms = 27 * res["gated_swa_layer"]["ms_per_layer"] + 5 * res["global_layer"]["ms_per_layer"]
-    res["stack"] = {"ms": stack_ms, "tokens_per_s": S / (stack_ms / 1e3)}
+                     "quantize_ms_per_layer": q_ms / steps, "gemm_tflop_per_layer": gemm_flop[name] / 1e12,
+                     "gemm_tflops": gemm_flop[name] / (gms / 1e3) / 1e12, "gemm_peak_tflops": peak,
+                     "gemm_mfma_frac": gemm_flop[name] / (gms / 1e3) / 1e12 / peak}
+        log(f"layers: {name}: {ms:.3f} ms/layer, GEMMs {gms:.3f} ms ({res[name]['gemm_tflops']:.0f} TFLOP/s), "
+            f"quantise {q_ms / steps:.3f} ms")
+    for sfx in ("", "_fp8"):
+        stack_ms = 27 * res["gated_swa_layer" + sfx]["ms_per_layer"] + 5 * res["global_layer" + sfx]["ms_per_layer"]
+        res["stack" + sfx] = {"ms": stack_ms, "tokens_per_s": S / (stack_ms / 1e3)}
+        log(f"layers: 27 gated + 5 global{sfx or ' (bf16)'}: {stack_ms:.2f} ms, {S / (stack_ms / 1e3):.0f} tokens/s")
+    for st in f8.values():
+        st.close()
 
     # one 4096 -> 4096 projection of the S tokens: bf16 against FP8 with delayed scaling (quantisation of x and
     # W, GEMM and scale update all inside the timed call)

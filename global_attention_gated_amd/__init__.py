@@ -65,6 +65,13 @@ _lib.fp8_linear_scales.argtypes = [_vp, ctypes.POINTER(_f32)]
 _lib.fp8_linear_workspace_bytes.argtypes = [_i64, _i32, _i32]
 _lib.fp8_linear_workspace_bytes.restype = _u64
 _lib.linear_fp8_delayed.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _u64, _vp]
+_lib.fp8_layer_alloc.argtypes = [_i32] * 5 + [ctypes.POINTER(_vp)]
+_lib.fp8_layer_free.argtypes = [_vp]
+_lib.fp8_layer_scales.argtypes = [_vp, ctypes.POINTER(_f32)]
+_lib.fp8_layer_workspace_bytes.argtypes = [_i32] * 6
+_lib.fp8_layer_workspace_bytes.restype = _u64
+_lib.gated_swa_layer_fp8.argtypes = [_vp] * 9 + [_i32] * 8 + [_f64, _f32, _i64, _vp, _i32, _vp, _vp, _u64, _vp]
+_lib.global_layer_fp8.argtypes = [_vp] * 8 + [_i32] * 7 + [_f64, _f32, _i64, _vp, _i32, _vp, _vp, _u64, _vp]
 _lib.zg_last_error.restype = ctypes.c_char_p
 _lib.zg_kernel_timer_enable.argtypes = [_i32]
 _lib.zg_kernel_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_f64), ctypes.POINTER(_i64)]
@@ -72,8 +79,9 @@ _lib.zg_kernel_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_f64), cty
 EXPORTED = ["kv_cache_alloc", "kv_cache_free", "kv_cache_footprint_bytes", "kv_cache_layer_view", "kv_cache_length",
             "kv_cache_set_length", "prefill_workspace_bytes", "swa_prefill", "global_prefill", "hybrid_decode_step",
             "linear_bf16", "layer_workspace_bytes", "gated_swa_layer", "global_layer", "fp8_linear_alloc",
-            "fp8_linear_free", "fp8_linear_scales", "fp8_linear_workspace_bytes", "linear_fp8_delayed", "zg_last_error",
-            "zg_kernel_timer_enable", "zg_kernel_timer_read"]
+            "fp8_linear_free", "fp8_linear_scales", "fp8_linear_workspace_bytes", "linear_fp8_delayed",
+            "fp8_layer_alloc", "fp8_layer_free", "fp8_layer_scales", "fp8_layer_workspace_bytes", "gated_swa_layer_fp8",
+            "global_layer_fp8", "zg_last_error", "zg_kernel_timer_enable", "zg_kernel_timer_read"]
 
 
 class ZgError(RuntimeError):
@@ -295,8 +303,42 @@ def layer_workspace_bytes(B, S, Hq, Hkv, D=128) -> int:
     return int(_lib.layer_workspace_bytes(B, S, Hq, Hkv, D))
 
 
+class Fp8Layer:
+    """Delayed-scaling state of one attention layer with FP8 projections (fp8_layer_alloc): tensors h, W_q, W_k,
+    W_v, W_g, o, W_o, each with its own amax history and scale.  Pass it as ``fp8=`` to gated_swa_layer_fp8 /
+    global_layer_fp8."""
+
+    TENSORS = ("h", "w_q", "w_k", "w_v", "w_g", "o", "w_o")
+
+    def __init__(self, d_model: int, Hq: int = 32, Hkv: int = 8, D: int = 128, history: int = 1024):
+        h = _vp()
+        _check(_lib.fp8_layer_alloc(d_model, Hq, Hkv, D, history, ctypes.byref(h)))
+        self.handle, self.d_model, self.Hq, self.Hkv, self.D, self.history = h, d_model, Hq, Hkv, D, history
+
+    def scales(self):
+        """The seven scales the next call will use, in the order of TENSORS."""
+        out = (_f32 * 7)()
+        _check(_lib.fp8_layer_scales(self.handle, out))
+        return tuple(float(x) for x in out)
+
+    def close(self):
+        if self.handle:
+            _lib.fp8_layer_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def fp8_layer_workspace_bytes(B, S, d_model, Hq, Hkv, D=128) -> int:
+    return int(_lib.fp8_layer_workspace_bytes(B, S, d_model, Hq, Hkv, D))
+
+
 def _layer(gated, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, window, rotary_dims, rope_base, eps,
-           pos0, cache, layer, workspace):
+           pos0, cache, layer, workspace, fp8=None):
     for t, n in ((h, "h"), (w_q, "w_q"), (w_k, "w_k"), (w_v, "w_v"), (w_g, "w_g"), (w_o, "w_o"), (q_norm_w, "q_norm_w"),
                  (k_norm_w, "k_norm_w")):
         _bf16(t, n)
@@ -306,17 +348,23 @@ def _layer(gated, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, wi
         y = torch.empty_like(h)
     _bf16(y, "y")
     if workspace is None:
-        workspace = torch.empty(max(16, layer_workspace_bytes(B, S, Hq, Hkv, D)), dtype=torch.uint8, device=h.device)
+        need = (layer_workspace_bytes(B, S, Hq, Hkv, D) if fp8 is None
+                else fp8_layer_workspace_bytes(B, S, d_model, Hq, Hkv, D))
+        workspace = torch.empty(max(16, need), dtype=torch.uint8, device=h.device)
     ws_n = workspace.numel() * workspace.element_size()
     ch = None if cache is None else cache.handle
+    common = (B, S, d_model, Hq, Hkv, D)
     if gated:
-        rc = _lib.gated_swa_layer(_ptr(h), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_g), _ptr(w_o), _ptr(q_norm_w),
-                                  _ptr(k_norm_w), _ptr(y), B, S, d_model, Hq, Hkv, D, window, rotary_dims, rope_base, eps,
-                                  pos0, ch, layer, workspace.data_ptr(), ws_n, _stream())
+        args = (_ptr(h), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_g), _ptr(w_o), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(y),
+                *common, window, rotary_dims, rope_base, eps, pos0, ch, layer)
     else:
-        rc = _lib.global_layer(_ptr(h), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(q_norm_w), _ptr(k_norm_w),
-                               _ptr(y), B, S, d_model, Hq, Hkv, D, rotary_dims, rope_base, eps, pos0, ch, layer,
-                               workspace.data_ptr(), ws_n, _stream())
+        args = (_ptr(h), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(y),
+                *common, rotary_dims, rope_base, eps, pos0, ch, layer)
+    tail = (workspace.data_ptr(), ws_n, _stream())
+    if fp8 is None:
+        rc = (_lib.gated_swa_layer if gated else _lib.global_layer)(*args, *tail)
+    else:
+        rc = (_lib.gated_swa_layer_fp8 if gated else _lib.global_layer_fp8)(*args, fp8.handle, *tail)
     _check(rc)
     return y
 
@@ -334,6 +382,21 @@ def global_layer(h, w_q, w_k, w_v, w_o, q_norm_w, k_norm_w, y=None, *, Hq=32, Hk
     """o_proj(global causal attention of q, k, v) with q/k/v = h W^T; shapes as gated_swa_layer."""
     return _layer(False, h, w_q, w_k, w_v, None, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, 0, rotary_dims, rope_base, eps,
                   pos0, cache, layer, workspace)
+
+
+def gated_swa_layer_fp8(h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y=None, *, fp8: Fp8Layer, Hq=32, Hkv=8,
+                        window=128, rotary_dims=42, rope_base=1e4, eps=1e-6, pos0=0, cache: KVCache | None = None,
+                        layer=0, workspace=None):
+    """gated_swa_layer with every projection on E4M3 operands under the delayed-scaling state ``fp8``."""
+    return _layer(True, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, window, rotary_dims, rope_base, eps,
+                  pos0, cache, layer, workspace, fp8=fp8)
+
+
+def global_layer_fp8(h, w_q, w_k, w_v, w_o, q_norm_w, k_norm_w, y=None, *, fp8: Fp8Layer, Hq=32, Hkv=8, rotary_dims=42,
+                     rope_base=1e4, eps=1e-6, pos0=0, cache: KVCache | None = None, layer=0, workspace=None):
+    """global_layer with every projection on E4M3 operands under the delayed-scaling state ``fp8``."""
+    return _layer(False, h, w_q, w_k, w_v, None, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, 0, rotary_dims, rope_base, eps,
+                  pos0, cache, layer, workspace, fp8=fp8)
 
 
 # ------------------------------------------------------------------------------------------- decode

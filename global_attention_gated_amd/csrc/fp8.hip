@@ -64,36 +64,40 @@ __global__ void __launch_bounds__(256) fp8_quantize_kernel(const uint16_t* __res
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// After a call: reduce each tensor's partial maxima (nblk[t] of them) to this call's amax, push it into the
-// history (slot idx), and derive the next scale s = 448 / max(history) (1 if the history is all zero) and its
-// inverse (the GEMM's dequantisation factor).  One work-group; state layout as Fp8State.
-__global__ void __launch_bounds__(256) fp8_finalize_kernel(Fp8State st, int32_t idx, int32_t nblk0, int32_t nblk1) {
+// After a call: reduce each quantised tensor's partial maxima (nb.n[t] of them) to this call's amax, push it into
+// the tensor's history (slot idx), and derive the next scale s = 448 / max(history) (1 if the history is all
+// zero) and its inverse (the GEMM's dequantisation factor).  One work-group per tensor; a tensor with
+// nb.n[t] = 0 was not quantised in this call and keeps its state.
+__global__ void __launch_bounds__(256) fp8_finalize_kernel(Fp8State st, int32_t idx, Fp8Blocks nb) {
   __shared__ float red[4];
-  for (int t = 0; t < 2; t++) {
-    const float* part = st.partial + (int64_t)t * kFp8MaxBlocks;
-    const int nb = t == 0 ? nblk0 : nblk1;
-    float* hist = st.hist + (int64_t)t * st.H;
-    float m = 0.f;
-    for (int i = threadIdx.x; i < nb; i += blockDim.x) m = fmaxf(m, part[i]);
+  const int t = blockIdx.x;
+  int cnt = 0;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) hist[idx] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    m = 0.f;
-    for (int i = threadIdx.x; i < st.H; i += blockDim.x) m = fmaxf(m, hist[i]);
+  for (int i = 0; i < kFp8MaxTensors; i++)
+    if (i == t) cnt = nb.n[i];
+  if (cnt == 0) return;
+  const float* part = st.partial + (int64_t)t * kFp8MaxBlocks;
+  float* hist = st.hist + (int64_t)t * st.H;
+  float m = 0.f;
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) m = fmaxf(m, part[i]);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const float mm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-      const float sc = mm > 0.f ? 448.0f / mm : 1.0f;
-      st.scale[t] = sc;
-      st.scale_inv[t] = 1.0f / sc;
-    }
-    __syncthreads();
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) hist[idx] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  m = 0.f;
+  for (int i = threadIdx.x; i < st.H; i += blockDim.x) m = fmaxf(m, hist[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float mm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sc = mm > 0.f ? 448.0f / mm : 1.0f;
+    st.scale[t] = sc;
+    st.scale_inv[t] = 1.0f / sc;
   }
 }
 
@@ -111,8 +115,8 @@ hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const f
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, int32_t nblk0, int32_t nblk1, hipStream_t st) {
-  hipLaunchKernelGGL(fp8_finalize_kernel, dim3(1), dim3(256), 0, st, s, idx, nblk0, nblk1);
+hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, const Fp8Blocks& nb, hipStream_t st) {
+  hipLaunchKernelGGL(fp8_finalize_kernel, dim3((unsigned)s.n), dim3(256), 0, st, s, idx, nb);
   return hipGetLastError();
 }
 

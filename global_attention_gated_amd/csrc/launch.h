@@ -91,16 +91,22 @@ struct SwaStreamArgs {
   double inv_freq_rev[64];
 };
 
-// Device state of an FP8 projection with delayed scaling: two tensors (0 = the input x, 1 = the weight W),
-// each with an amax history of H floats, the per-work-group maxima of the current call's quantisation, the
-// scale in use and its inverse.
+// Device state of FP8 operands under delayed scaling: n tensors (a projection: 0 = the input x, 1 = the weight
+// W), each with an amax history of H floats, the per-work-group maxima of the current call's quantisation,
+// the scale in use and its inverse.
 constexpr int32_t kFp8MaxBlocks = 2048;   // work-groups of one quantisation launch (8 per CU)
+constexpr int32_t kFp8MaxTensors = 8;
 struct Fp8State {
-  float* hist;        // [2][H]
-  float* partial;     // [2][kFp8MaxBlocks]
-  float* scale;       // [2]
-  float* scale_inv;   // [2]
+  float* hist;        // [n][H]
+  float* partial;     // [n][kFp8MaxBlocks]
+  float* scale;       // [n]
+  float* scale_inv;   // [n]
   int32_t H;
+  int32_t n;
+};
+// Work-groups of each tensor's quantisation in the current call (0 = not quantised: state left unchanged).
+struct Fp8Blocks {
+  int32_t n[kFp8MaxTensors];
 };
 
 // One entry per layer of a KV cache, in device memory.
@@ -142,7 +148,7 @@ hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st);
 int32_t fp8_quantize_blocks(int64_t n);   // work-groups launch_fp8_quantize uses for n values
 hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const float* scale, float* partial,
                                hipStream_t st);
-hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, int32_t nblk0, int32_t nblk1, hipStream_t st);
+hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, const Fp8Blocks& nb, hipStream_t st);
 int swa_stream_run_length(int S, int n_units);
 hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_swa(const DecodeArgs& a, hipStream_t st);

@@ -506,6 +506,41 @@ struct zg_fp8_linear {
   zg::Fp8State st{};
 };
 
+// The FP8 state of a whole layer: tensors 0 = h, 1..4 = W_q, W_k, W_v, W_g, 5 = the attention output o,
+// 6 = W_o (W_g unused by a global layer).
+enum { kF8H = 0, kF8Wq = 1, kF8Wk = 2, kF8Wv = 3, kF8Wg = 4, kF8O = 5, kF8Wo = 6, kF8LayerTensors = 7 };
+struct zg_fp8_layer {
+  int device = -1;
+  int32_t d_model = 0, Hq = 0, Hkv = 0, D = 0, H = 0;
+  int32_t idx = 0;
+  void* mem = nullptr;   // device: hist [7][H], partial [7][kFp8MaxBlocks], scale [7], scale_inv [7]
+  zg::Fp8State st{};
+};
+
+namespace {
+// Device memory for n tensors' delayed-scaling state: histories zero, scales and their inverses one.
+int fp8_state_alloc(const char* fn, int32_t n, int32_t history, void** mem, zg::Fp8State* st) {
+  const size_t P = (size_t)n * ((size_t)history + (size_t)zg::kFp8MaxBlocks);   // floats before the scales
+  const size_t bytes = (P + 2 * (size_t)n) * 4;
+  if (hipMalloc(mem, bytes) != hipSuccess) { *mem = nullptr; return fail(ZG_ENOMEM, "%s: device allocation failed", fn); }
+  float* base = static_cast<float*>(*mem);
+  st->hist = base;
+  st->partial = base + (size_t)n * history;
+  st->scale = base + P;
+  st->scale_inv = base + P + n;
+  st->H = history;
+  st->n = n;
+  std::vector<float> init(P + 2 * (size_t)n, 0.0f);
+  for (size_t i = P; i < init.size(); i++) init[i] = 1.0f;
+  if (hipMemcpy(*mem, init.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(*mem);
+    *mem = nullptr;
+    return fail(ZG_EHIP, "%s: initialising the state failed", fn);
+  }
+  return ZG_OK;
+}
+}  // namespace
+
 namespace {
 uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
 uint64_t layer_activation_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -519,24 +554,44 @@ extern "C" uint64_t layer_workspace_bytes(int32_t B, int32_t S, int32_t Hq, int3
   return layer_activation_bytes(B, S, Hq, Hkv, D) + prefill_workspace_bytes(B, S, Hkv, D);
 }
 
+extern "C" uint64_t fp8_layer_workspace_bytes(int32_t B, int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv,
+                                              int32_t D) {
+  if (B < 0 || S < 0 || d_model < 0 || Hq < 0 || Hkv < 0 || D < 0) return 0;
+  const uint64_t T = (uint64_t)B * (uint64_t)S, dm = (uint64_t)d_model, qd = (uint64_t)Hq * D, kd = (uint64_t)Hkv * D;
+  return layer_workspace_bytes(B, S, Hq, Hkv, D) + align256(T * dm) + align256(T * qd) + 2 * align256(qd * dm) +
+         2 * align256(kd * dm) + align256(dm * qd);
+}
+
 namespace {
+// q/k/v(/g) = h W^T, the attention core, y = o W_o^T.  With f8, every projection runs on E4M3 operands under
+// delayed scaling (h quantised once for the four input projections, o once for o_proj).
 int layer_common(bool gated, const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_g,
                  const void* w_o, const void* qw, const void* kw, void* y, int32_t B, int32_t S, int32_t d_model,
                  int32_t Hq, int32_t Hkv, int32_t D, int32_t window, int32_t R, double base, float eps, int64_t pos0,
-                 zg_kv_cache* cache, int32_t layer, void* ws, uint64_t ws_bytes, void* stream) {
-  const char* fn = gated ? "gated_swa_layer" : "global_layer";
+                 zg_kv_cache* cache, int32_t layer, zg_fp8_layer* f8, void* ws, uint64_t ws_bytes, void* stream) {
+  const char* fn = f8 ? (gated ? "gated_swa_layer_fp8" : "global_layer_fp8") : (gated ? "gated_swa_layer" : "global_layer");
   if (d_model < 1) return fail(ZG_EINVAL, "%s: d_model must be >= 1", fn);
   if (B < 0 || S < 0 || Hq < 1 || Hkv < 1 || D < 1) return fail(ZG_EINVAL, "%s: bad shape", fn);
+  if (f8) {
+    if (f8->d_model != d_model || f8->Hq != Hq || f8->Hkv != Hkv || f8->D != D)
+      return fail(ZG_EINVAL, "%s: shape (d_model=%d, Hq=%d, Hkv=%d, D=%d) does not match the FP8 state (%d, %d, %d, %d)",
+                  fn, d_model, Hq, Hkv, D, f8->d_model, f8->Hq, f8->Hkv, f8->D);
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != f8->device)
+      return fail(ZG_EINVAL, "%s: the FP8 state lives on device %d, the current device is %d", fn, f8->device, cur);
+  }
   if (B == 0 || S == 0) return ZG_OK;
   if (!h || !w_q || !w_k || !w_v || !w_o || !y || (gated && !w_g)) return fail(ZG_EINVAL, "%s: null tensor pointer", fn);
   if (!aligned16(h) || !aligned16(w_q) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(w_o) || !aligned16(y) ||
       (gated && !aligned16(w_g)))
     return fail(ZG_EINVAL, "%s: tensors must be 16-byte aligned", fn);
   if (!ws || !aligned16(ws)) return fail(ZG_EINVAL, "%s: a 16-byte aligned workspace is required", fn);
-  if (ws_bytes < layer_workspace_bytes(B, S, Hq, Hkv, D))
+  const uint64_t need = f8 ? fp8_layer_workspace_bytes(B, S, d_model, Hq, Hkv, D) : layer_workspace_bytes(B, S, Hq, Hkv, D);
+  if (ws_bytes < need)
     return fail(ZG_ERANGE, "%s: workspace of %llu bytes < %llu needed", fn, (unsigned long long)ws_bytes,
-                (unsigned long long)layer_workspace_bytes(B, S, Hq, Hkv, D));
-  // carve the activations: q [T][Hq*D], k, v [T][Hkv*D], g, o [T][Hq*D], then the attention workspace
+                (unsigned long long)need);
+  // carve the activations: q [T][Hq*D], k, v [T][Hkv*D], g, o [T][Hq*D], then the attention workspace, then
+  // (FP8) the E4M3 codes of h, o, W_q, W_k, W_v, W_g and W_o
   const int64_t T = (int64_t)B * S;
   uint16_t* q = static_cast<uint16_t*>(ws);
   uint16_t* k = q + T * Hq * D;
@@ -545,21 +600,107 @@ int layer_common(bool gated, const void* h, const void* w_q, const void* w_k, co
   uint16_t* o = g + T * Hq * D;
   const uint64_t act = layer_activation_bytes(B, S, Hq, Hkv, D);
   void* aws = static_cast<unsigned char*>(ws) + act;
-  const uint64_t aws_bytes = ws_bytes - act;
+  const uint64_t aws_bytes = layer_workspace_bytes(B, S, Hq, Hkv, D) - act;
   // the attention's arguments first, so a bad one enqueues nothing
   int rc = prefill_common(gated, q, k, v, gated ? g : nullptr, qw, kw, o, B, S, Hq, Hkv, D, window, R, base, eps, pos0,
                           cache, layer, aws, aws_bytes, stream, /*validate_only=*/true);
   if (rc) return rc;
-  if ((rc = linear_bf16(h, w_q, q, T, d_model, Hq * D, stream))) return rc;
-  if ((rc = linear_bf16(h, w_k, k, T, d_model, Hkv * D, stream))) return rc;
-  if ((rc = linear_bf16(h, w_v, v, T, d_model, Hkv * D, stream))) return rc;
-  if (gated && (rc = linear_bf16(h, w_g, g, T, d_model, Hq * D, stream))) return rc;
+  if (!f8) {
+    if ((rc = linear_bf16(h, w_q, q, T, d_model, Hq * D, stream))) return rc;
+    if ((rc = linear_bf16(h, w_k, k, T, d_model, Hkv * D, stream))) return rc;
+    if ((rc = linear_bf16(h, w_v, v, T, d_model, Hkv * D, stream))) return rc;
+    if (gated && (rc = linear_bf16(h, w_g, g, T, d_model, Hq * D, stream))) return rc;
+    rc = prefill_common(gated, q, k, v, gated ? g : nullptr, qw, kw, o, B, S, Hq, Hkv, D, window, R, base, eps, pos0,
+                        cache, layer, aws, aws_bytes, stream);
+    if (rc) return rc;
+    return linear_bf16(o, w_o, y, T, Hq * D, d_model, stream);
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t dm = d_model, qd = (int64_t)Hq * D, kd = (int64_t)Hkv * D;
+  uint8_t* hc = static_cast<uint8_t*>(ws) + layer_workspace_bytes(B, S, Hq, Hkv, D);
+  uint8_t* oc = hc + align256(T * dm);
+  uint8_t* wc[kF8LayerTensors] = {};
+  wc[kF8Wq] = oc + align256(T * qd);
+  wc[kF8Wk] = wc[kF8Wq] + align256(qd * dm);
+  wc[kF8Wv] = wc[kF8Wk] + align256(kd * dm);
+  wc[kF8Wg] = wc[kF8Wv] + align256(kd * dm);
+  wc[kF8Wo] = wc[kF8Wg] + align256(qd * dm);
+  const Fp8State& fs = f8->st;
+  Fp8Blocks nb{};
+  auto quant = [&](int t, const void* src, uint8_t* dst, int64_t n) {
+    nb.n[t] = fp8_quantize_blocks(n);
+    return launch_fp8_quantize(static_cast<const uint16_t*>(src), dst, n, fs.scale + t, fs.partial + (int64_t)t * kFp8MaxBlocks, st);
+  };
+  auto gemm = [&](const uint8_t* xc, int tx, int tw, void* out, int32_t K, int32_t N) {
+    ScopedTimer tm("linear", st);
+    const int s = linear_fp8_run(xc, wc[tw], out, T, K, N, fs.scale_inv + tx, fs.scale_inv + tw, st);
+    return s ? fail(ZG_EHIP, "%s: hipBLASLt %s (T=%lld K=%d N=%d)", fn, blas_status_name(s), (long long)T, K, N) : ZG_OK;
+  };
+  hipError_t e;
+  {
+    ScopedTimer tm("fp8_quantize", st);
+    e = quant(kF8H, h, hc, T * dm);
+    if (e == hipSuccess) e = quant(kF8Wq, w_q, wc[kF8Wq], qd * dm);
+    if (e == hipSuccess) e = quant(kF8Wk, w_k, wc[kF8Wk], kd * dm);
+    if (e == hipSuccess) e = quant(kF8Wv, w_v, wc[kF8Wv], kd * dm);
+    if (e == hipSuccess && gated) e = quant(kF8Wg, w_g, wc[kF8Wg], qd * dm);
+  }
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
+  if ((rc = gemm(hc, kF8H, kF8Wq, q, d_model, (int32_t)qd))) return rc;
+  if ((rc = gemm(hc, kF8H, kF8Wk, k, d_model, (int32_t)kd))) return rc;
+  if ((rc = gemm(hc, kF8H, kF8Wv, v, d_model, (int32_t)kd))) return rc;
+  if (gated && (rc = gemm(hc, kF8H, kF8Wg, g, d_model, (int32_t)qd))) return rc;
   rc = prefill_common(gated, q, k, v, gated ? g : nullptr, qw, kw, o, B, S, Hq, Hkv, D, window, R, base, eps, pos0, cache,
                       layer, aws, aws_bytes, stream);
   if (rc) return rc;
-  return linear_bf16(o, w_o, y, T, Hq * D, d_model, stream);
+  {
+    ScopedTimer tm("fp8_quantize", st);
+    e = quant(kF8O, o, oc, T * qd);
+    if (e == hipSuccess) e = quant(kF8Wo, w_o, wc[kF8Wo], dm * qd);
+  }
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantize launch");
+  if ((rc = gemm(oc, kF8O, kF8Wo, y, (int32_t)qd, d_model))) return rc;
+  e = launch_fp8_finalize(fs, f8->idx, nb, st);
+  if (e != hipSuccess) return hip_fail(e, "fp8 finalize launch");
+  f8->idx = (f8->idx + 1) % f8->H;
+  return ZG_OK;
 }
 }  // namespace
+
+extern "C" int fp8_layer_alloc(int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t history,
+                               zg_fp8_layer** out) {
+  const char* fn = "fp8_layer_alloc";
+  if (!out) return fail(ZG_EINVAL, "%s: null output handle", fn);
+  *out = nullptr;
+  if (d_model < 1 || Hq < 1 || Hkv < 1 || D < 1 || history < 1)
+    return fail(ZG_EINVAL, "%s: d_model, Hq, Hkv, D and history must be >= 1", fn);
+  if (d_model % 8 || ((int64_t)Hq * D) % 8)
+    return fail(ZG_EUNSUPPORTED, "%s: d_model (%d) and Hq*D (%d) must be multiples of 8", fn, d_model, Hq * D);
+  auto* f = new (std::nothrow) zg_fp8_layer();
+  if (!f) return fail(ZG_ENOMEM, "%s: host allocation failed", fn);
+  f->d_model = d_model; f->Hq = Hq; f->Hkv = Hkv; f->D = D; f->H = history;
+  if (hipGetDevice(&f->device) != hipSuccess) { delete f; return fail(ZG_EHIP, "%s: no current device", fn); }
+  if (int rc = fp8_state_alloc(fn, kF8LayerTensors, history, &f->mem, &f->st)) { delete f; return rc; }
+  *out = f;
+  return ZG_OK;
+}
+
+extern "C" int fp8_layer_free(zg_fp8_layer* f) {
+  if (!f) return ZG_OK;
+  (void)hipDeviceSynchronize();
+  (void)hipFree(f->mem);
+  delete f;
+  return ZG_OK;
+}
+
+extern "C" int fp8_layer_scales(const zg_fp8_layer* f, float* scales_out) {
+  if (!f || !scales_out) return fail(ZG_EINVAL, "fp8_layer_scales: null argument");
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(scales_out, f->st.scale, kF8LayerTensors * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(ZG_EHIP, "fp8_layer_scales: reading the device state failed");
+  return ZG_OK;
+}
 
 extern "C" int fp8_linear_alloc(int32_t K, int32_t N, int32_t history, zg_fp8_linear** out) {
   const char* fn = "fp8_linear_alloc";
@@ -571,22 +712,7 @@ extern "C" int fp8_linear_alloc(int32_t K, int32_t N, int32_t history, zg_fp8_li
   if (!f) return fail(ZG_ENOMEM, "%s: host allocation failed", fn);
   f->K = K; f->N = N; f->H = history;
   if (hipGetDevice(&f->device) != hipSuccess) { delete f; return fail(ZG_EHIP, "%s: no current device", fn); }
-  const size_t P = 2 * (size_t)history + 2 * (size_t)zg::kFp8MaxBlocks;   // floats before the scales
-  const size_t bytes = (P + 4) * 4;
-  if (hipMalloc(&f->mem, bytes) != hipSuccess) { delete f; return fail(ZG_ENOMEM, "%s: device allocation failed", fn); }
-  float* base = static_cast<float*>(f->mem);
-  f->st.hist = base;
-  f->st.partial = base + 2 * (size_t)history;
-  f->st.scale = base + P;
-  f->st.scale_inv = base + P + 2;
-  f->st.H = history;
-  std::vector<float> init(P + 4, 0.0f);
-  init[P] = init[P + 1] = init[P + 2] = init[P + 3] = 1.0f;   // scales and their inverses
-  if (hipMemcpy(f->mem, init.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
-    (void)hipFree(f->mem);
-    delete f;
-    return fail(ZG_EHIP, "%s: initialising the state failed", fn);
-  }
+  if (int rc = fp8_state_alloc(fn, 2, history, &f->mem, &f->st)) { delete f; return rc; }
   *out = f;
   return ZG_OK;
 }
@@ -644,7 +770,10 @@ extern "C" int linear_fp8_delayed(const void* x, const void* w, void* y, int64_t
     const int s = linear_fp8_run(xq, wq, y, T, K, N, f->st.scale_inv + 0, f->st.scale_inv + 1, st);
     if (s) return fail(ZG_EHIP, "%s: hipBLASLt %s (T=%lld K=%d N=%d)", fn, blas_status_name(s), (long long)T, K, N);
   }
-  e = launch_fp8_finalize(f->st, f->idx, fp8_quantize_blocks(T * K), fp8_quantize_blocks((int64_t)N * K), st);
+  Fp8Blocks nb{};
+  nb.n[0] = fp8_quantize_blocks(T * K);
+  nb.n[1] = fp8_quantize_blocks((int64_t)N * K);
+  e = launch_fp8_finalize(f->st, f->idx, nb, st);
   if (e != hipSuccess) return hip_fail(e, "fp8 finalize launch");
   f->idx = (f->idx + 1) % f->H;
   return ZG_OK;
@@ -656,7 +785,7 @@ extern "C" int gated_swa_layer(const void* h, const void* w_q, const void* w_k, 
                                int32_t rotary_dims, double rope_base, float eps, int64_t pos0, zg_kv_cache* cache,
                                int32_t layer, void* workspace, uint64_t workspace_bytes, void* stream) {
   return layer_common(true, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, B, S, d_model, Hq, Hkv, D, window,
-                      rotary_dims, rope_base, eps, pos0, cache, layer, workspace, workspace_bytes, stream);
+                      rotary_dims, rope_base, eps, pos0, cache, layer, nullptr, workspace, workspace_bytes, stream);
 }
 
 extern "C" int global_layer(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_o,
@@ -665,7 +794,28 @@ extern "C" int global_layer(const void* h, const void* w_q, const void* w_k, con
                             int64_t pos0, zg_kv_cache* cache, int32_t layer, void* workspace, uint64_t workspace_bytes,
                             void* stream) {
   return layer_common(false, h, w_q, w_k, w_v, nullptr, w_o, q_norm_w, k_norm_w, y, B, S, d_model, Hq, Hkv, D, 0,
-                      rotary_dims, rope_base, eps, pos0, cache, layer, workspace, workspace_bytes, stream);
+                      rotary_dims, rope_base, eps, pos0, cache, layer, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gated_swa_layer_fp8(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+                                   const void* w_o, const void* q_norm_w, const void* k_norm_w, void* y, int32_t B,
+                                   int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t window,
+                                   int32_t rotary_dims, double rope_base, float eps, int64_t pos0, zg_kv_cache* cache,
+                                   int32_t layer, zg_fp8_layer* fp8, void* workspace, uint64_t workspace_bytes,
+                                   void* stream) {
+  if (!fp8) return fail(ZG_EINVAL, "gated_swa_layer_fp8: null FP8 state");
+  return layer_common(true, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, B, S, d_model, Hq, Hkv, D, window,
+                      rotary_dims, rope_base, eps, pos0, cache, layer, fp8, workspace, workspace_bytes, stream);
+}
+
+extern "C" int global_layer_fp8(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                                const void* q_norm_w, const void* k_norm_w, void* y, int32_t B, int32_t S,
+                                int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t rotary_dims,
+                                double rope_base, float eps, int64_t pos0, zg_kv_cache* cache, int32_t layer,
+                                zg_fp8_layer* fp8, void* workspace, uint64_t workspace_bytes, void* stream) {
+  if (!fp8) return fail(ZG_EINVAL, "global_layer_fp8: null FP8 state");
+  return layer_common(false, h, w_q, w_k, w_v, nullptr, w_o, q_norm_w, k_norm_w, y, B, S, d_model, Hq, Hkv, D, 0,
+                      rotary_dims, rope_base, eps, pos0, cache, layer, fp8, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------------- decode

@@ -199,6 +199,38 @@ int global_layer(const void* h, const void* w_q, const void* w_k, const void* w_
                  int32_t Hkv, int32_t D, int32_t rotary_dims, double rope_base, float eps, int64_t pos0,
                  zg_kv_cache* cache, int32_t layer, void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* ---- Whole layers with FP8 projections (onedev.kr "What differs": the matmuls run in FP8, E4M3 forward, delayed
+ * scaling over a 1,024-step amax history).  A layer state holds seven delayed-scaling tensors, each with its own
+ * history and scale as in zg_fp8_linear: 0 = h, 1 = W_q, 2 = W_k, 3 = W_v, 4 = W_g (unused by a global layer),
+ * 5 = the attention output o, 6 = W_o.  Per call h is quantised once and feeds the four input projections, o once
+ * for o_proj; every GEMM multiplies by the inverse scales of its two operands; after the call each quantised
+ * tensor's max |v| enters its history and its next scale is derived (the scales lag the data by one call). */
+typedef struct zg_fp8_layer zg_fp8_layer;
+
+/* Allocate a layer state on the current device (histories zero, scales 1).  d_model and Hq*D must be multiples
+ * of 8.  Errors: EINVAL, EUNSUPPORTED, ENOMEM, EHIP. */
+int fp8_layer_alloc(int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t history, zg_fp8_layer** out);
+/* Release a layer state (synchronises the device first).  NULL is accepted. */
+int fp8_layer_free(zg_fp8_layer* state);
+/* The seven scales the next call will use (HOST float[7], tensor order above); synchronises the device. */
+int fp8_layer_scales(const zg_fp8_layer* state, float* scales_out);
+/* Workspace bytes of the FP8 layers: layer_workspace_bytes(B, S, Hq, Hkv, D), then the E4M3 codes of h [T][d_model],
+ * o [T][Hq*D], W_q, W_k, W_v, W_g and W_o, each starting on a 256-byte boundary. */
+uint64_t fp8_layer_workspace_bytes(int32_t B, int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D);
+/* gated_swa_layer / global_layer with every projection on E4M3 operands under the layer state `fp8` (shapes must
+ * match the state's).  Calls that share a state must be ordered on one stream.  B*S == 0 is a no-op (the state
+ * does not advance).  Errors: as gated_swa_layer / global_layer, and EINVAL for a null or mismatched state. */
+int gated_swa_layer_fp8(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+                        const void* w_o, const void* q_norm_w, const void* k_norm_w, void* y, int32_t B, int32_t S,
+                        int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t window, int32_t rotary_dims,
+                        double rope_base, float eps, int64_t pos0, zg_kv_cache* cache, int32_t layer,
+                        zg_fp8_layer* fp8, void* workspace, uint64_t workspace_bytes, void* stream);
+int global_layer_fp8(const void* h, const void* w_q, const void* w_k, const void* w_v, const void* w_o,
+                     const void* q_norm_w, const void* k_norm_w, void* y, int32_t B, int32_t S, int32_t d_model,
+                     int32_t Hq, int32_t Hkv, int32_t D, int32_t rotary_dims, double rope_base, float eps, int64_t pos0,
+                     zg_kv_cache* cache, int32_t layer, zg_fp8_layer* fp8, void* workspace, uint64_t workspace_bytes,
+                     void* stream);
+
 /* Thread-local description of the last non-OK status returned on this thread ("" if none). */
 const char* zg_last_error(void);
 

@@ -320,30 +320,60 @@ def e4m3_decode(codes) -> np.ndarray:
     return np.where(c & 0x80, -mag, mag)
 
 
+class Fp8DelayedScaling:
+    """Delayed scaling of n FP8 tensors (onedev.kr "What differs": FP8 matmuls with delayed scaling over a
+    1,024-step amax history).  Per tensor t: the scale in use s_t (float32, 1 at first); encode(t, v) gives the codes
+    E4M3(v * s_t) of the float32 products and notes this call's max |v|; commit() ends a call: every tensor encoded
+    in it gets its max |v| in history slot idx and its next scale 448 / max(history) in float32 (1 if the history
+    is zero), then idx advances.  Tensors not encoded in a call keep their state."""
+
+    def __init__(self, n: int, history: int = 1024):
+        self.n, self.H = n, history
+        self.hist = np.zeros((n, history), dtype=np.float32)
+        self.idx = 0
+        self.scale = np.ones(n, dtype=np.float32)
+        self._amax = {}
+
+    def encode(self, t: int, v) -> np.ndarray:
+        vf = _as_f64(v).astype(np.float32)          # bf16 values are exact in float32
+        self._amax[t] = max(self._amax.get(t, np.float32(0)), np.float32(np.max(np.abs(vf))) if vf.size else np.float32(0))
+        return e4m3_encode(vf * self.scale[t])      # float32 products, as the kernels form them
+
+    def inv(self, t: int) -> np.float64:
+        """The dequantisation factor 1/s_t, formed in float32."""
+        return np.float64(np.float32(1.0) / self.scale[t])
+
+    def commit(self):
+        for t, a in self._amax.items():
+            self.hist[t, self.idx] = a
+            m = self.hist[t].max()
+            self.scale[t] = np.float32(E4M3_MAX) / m if m > 0 else np.float32(1.0)
+        self._amax = {}
+        self.idx = (self.idx + 1) % self.H
+
+
+def fp8_matmul(cx, cw, inv_x, inv_w) -> np.ndarray:
+    """x W^T from E4M3 codes: (decode(cx) . decode(cw)^T) * (1/s_x) * (1/s_w), float64."""
+    return (e4m3_decode(cx) @ e4m3_decode(cw).T) * inv_x * inv_w
+
+
 class Fp8DelayedLinear:
-    """y = x W^T with both operands in E4M3 under delayed scaling (onedev.kr "What differs": FP8 matmuls with
-    delayed scaling over a 1,024-step amax history).  Per tensor (0 = x, 1 = W): the scale in use s (float32, 1 at
-    first), codes = E4M3(v * s) in float32, y = (codes_x . codes_w^T) * (1/s_x) * (1/s_w); then this call's max |v|
-    enters the tensor's history and the next scale is 448 / max(history) in float32 (1 if the history is zero)."""
+    """y = x W^T with both operands in E4M3 under delayed scaling: tensors 0 = x, 1 = W of a
+    Fp8DelayedScaling state; one call encodes both with the current scales, multiplies and commits."""
 
     def __init__(self, K: int, N: int, history: int = 1024):
         self.K, self.N, self.H = K, N, history
-        self.hist = np.zeros((2, history), dtype=np.float32)
-        self.idx = 0
-        self.scale = np.ones(2, dtype=np.float32)
+        self.state = Fp8DelayedScaling(2, history)
+
+    @property
+    def scale(self):
+        return self.state.scale
 
     def __call__(self, x, w):
-        xf = _as_f64(x).astype(np.float32)          # bf16 values are exact in float32
-        wf = _as_f64(w).astype(np.float32)
-        cx = e4m3_encode(xf * self.scale[0])        # float32 products, as the kernels form them
-        cw = e4m3_encode(wf * self.scale[1])
-        inv = np.float32(1.0) / self.scale          # the dequantisation factors, float32
-        y = (e4m3_decode(cx) @ e4m3_decode(cw).T) * np.float64(inv[0]) * np.float64(inv[1])
-        self.hist[0, self.idx] = np.max(np.abs(xf))
-        self.hist[1, self.idx] = np.max(np.abs(wf))
-        self.idx = (self.idx + 1) % self.H
-        m = self.hist.max(axis=1)
-        self.scale = np.where(m > 0, np.float32(E4M3_MAX) / np.where(m > 0, m, np.float32(1)), np.float32(1)).astype(np.float32)
+        st = self.state
+        cx, cw = st.encode(0, x), st.encode(1, w)
+        y = fp8_matmul(cx, cw, st.inv(0), st.inv(1))
+        st.commit()
         return y, cx, cw
 
 
@@ -363,6 +393,41 @@ def attention_layer(h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, *, Hq: int, 
     g = None if w_g is None else proj(w_g, Hq)
     o = prefill_layer(q, k, v, g, q_norm_w, k_norm_w, window=window, rotary_dims=rotary_dims, base=base, eps=eps)
     return linear(round_bf16(o).reshape(B, S, Hq * D), w_o)
+
+
+FP8_LAYER_TENSORS = ("h", "w_q", "w_k", "w_v", "w_g", "o", "w_o")
+
+
+def attention_layer_fp8(h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, state: Fp8DelayedScaling, *, Hq: int, Hkv: int,
+                        window: int | None, rotary_dims: int, base: float, eps: float,
+                        codes: dict | None = None) -> np.ndarray:
+    """attention_layer with every projection on E4M3 operands (onedev.kr "What differs": FP8 matmuls, E4M3 in the
+    forward pass, delayed scaling).  state holds seven tensors in the order of FP8_LAYER_TENSORS; h is encoded once
+    for the four input projections and the bf16 attention output o once for o_proj, each weight once, all with the
+    scales in use before the call; the call ends with state.commit().  q, k, v, g and o are bf16 between the
+    operations as in attention_layer.  Returns y float64 [B,S,d_model]; a dict passed as codes receives every
+    tensor's E4M3 codes by name."""
+    B, S, dm = np.asarray(h).shape
+    D = np.asarray(q_norm_w).shape[-1]
+    t = {name: i for i, name in enumerate(FP8_LAYER_TENSORS)}
+    ch = state.encode(t["h"], np.asarray(h).reshape(B * S, dm))
+
+    got = {"h": ch}
+
+    def proj(name, w, H):
+        cw = got[name] = state.encode(t[name], w)
+        return round_bf16(fp8_matmul(ch, cw, state.inv(t["h"]), state.inv(t[name]))).reshape(B, S, H, D)
+
+    q, k, v = proj("w_q", w_q, Hq), proj("w_k", w_k, Hkv), proj("w_v", w_v, Hkv)
+    g = None if w_g is None else proj("w_g", w_g, Hq)
+    o = round_bf16(prefill_layer(q, k, v, g, q_norm_w, k_norm_w, window=window, rotary_dims=rotary_dims, base=base,
+                                 eps=eps)).reshape(B * S, Hq * D)
+    co, cwo = got["o"], got["w_o"] = state.encode(t["o"], o), state.encode(t["w_o"], w_o)
+    y = fp8_matmul(co, cwo, state.inv(t["o"]), state.inv(t["w_o"]))
+    state.commit()
+    if codes is not None:
+        codes.update(got)
+    return y.reshape(B, S, dm)
 
 
 def decode_step(q, k, v, gate, wq, wk, positions, cache: OracleCache, *, rotary_dims: int, base: float,

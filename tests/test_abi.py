@@ -94,6 +94,22 @@ def test_layer_workspace_bytes_closed_form(zg):
     assert zg.layer_workspace_bytes(B, S, Hq, Hkv, D) == act + zg.workspace_bytes(B, S, Hkv, D)
 
 
+
+def test_fp8_layer_workspace_bytes_closed_form(zg):
+    B, S, dm, Hq, Hkv, D = 2, 300, 4096, 32, 8, 128
+    T = B * S
+    a = lambda n: (n + 255) // 256 * 256
+    codes = a(T * dm) + a(T * Hq * D) + 2 * a(Hq * D * dm) + 2 * a(Hkv * D * dm) + a(dm * Hq * D)
+    assert zg.fp8_layer_workspace_bytes(B, S, dm, Hq, Hkv, D) == zg.layer_workspace_bytes(B, S, Hq, Hkv, D) + codes
+
+
+def test_fp8_layers_reject_a_null_state(zg):
+    args = [16] * 9 + [1, 4, 4096, 4, 1, 128, 128, 42, 1e4, 1e-6, 0, None, 0, None, 256, 1 << 30, None]
+    assert zg._lib.gated_swa_layer_fp8(*args) == zg.ZG_EINVAL
+    gargs = [16] * 8 + [1, 4, 4096, 4, 1, 128, 42, 1e4, 1e-6, 0, None, 0, None, 256, 1 << 30, None]
+    assert zg._lib.global_layer_fp8(*gargs) == zg.ZG_EINVAL
+    assert b"null FP8 state" in zg._lib.zg_last_error()
+
 def _layer(zg, **over):
     a = dict(h=16, wq=16, wk=16, wv=16, wg=16, wo=16, qw=16, kw=16, y=16, B=1, S=4, dm=4096, Hq=4, Hkv=1, D=128,
              window=128, R=42, base=1e4, eps=1e-6, pos0=0, cache=None, layer=0, ws=256, ws_bytes=1 << 30, stream=None)

@@ -93,3 +93,89 @@ def test_fp8_delayed_scaling_matches_oracle_over_calls(zg):
         bound = 2.0 ** -8 * np.abs(yr) + 1e-3 * np.sqrt(np.mean(yr ** 2))
         assert np.all(err <= bound), f"call {call}: max excess {float((err - bound).max()):.3e}"
     f.close()
+
+
+def _e4m3_step(a):
+    """Spacing of E4M3 values at magnitude a (normals: 2^(e-3) in [2^e, 2^(e+1)); subnormals 2^-9)."""
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.exp2(e - 3)
+
+
+def _fp8_layer_codes(ws, B, S, gated):
+    """The E4M3 codes the layer leaves in its workspace (layout of fp8_layer_workspace_bytes)."""
+    import global_attention_gated_amd as zgm
+    a = lambda n: (n + 255) // 256 * 256
+    T, qd, kd = B * S, HQ * D, HKV * D
+    off = zgm.layer_workspace_bytes(B, S, HQ, HKV, D)
+    mem = ws.cpu().numpy()
+    out = {}
+    for name, n, shape in (("h", T * D_MODEL, (T, D_MODEL)), ("o", T * qd, (T, qd)), ("w_q", qd * D_MODEL, (qd, D_MODEL)),
+                           ("w_k", kd * D_MODEL, (kd, D_MODEL)), ("w_v", kd * D_MODEL, (kd, D_MODEL)),
+                           ("w_g", qd * D_MODEL, (qd, D_MODEL)), ("w_o", D_MODEL * qd, (D_MODEL, qd))):
+        out[name] = mem[off:off + n].reshape(shape)
+        off += a(n)
+    if not gated:
+        del out["w_g"]
+    return out
+
+
+@pytest.mark.parametrize("gated,B,S", [(True, 1, 400), (False, 1, 300)])
+def test_fp8_layer_matches_oracle_over_calls(zg, gated, B, S):
+    """Three calls of a layer with FP8 projections through one delayed-scaling state, h scaled by 1, 1/2, 1 (exact
+    power-of-two factors).  Per call:
+    - the scales in use equal the oracle's float32 scales (h and the weights exactly; o, whose max |o| comes from
+      the attention output, within one bf16 step of the maximum, 2^-7 relative);
+    - the E4M3 codes of h and of every weight equal the oracle's byte for byte (same inputs, same float32 decision);
+    - the codes of the attention output o: the GPU's o is within the core's bar of the oracle's (and its scale
+      within 2^-7), so a code's value may differ from the oracle's by that bar plus one E4M3 step at its magnitude
+      (o s on a rounding boundary), and no more; such differences stay rare (<= 5% of the elements);
+    - y: mean-abs within the core's bar (1e-3); max-abs within the core's 1e-2 plus two such steps at the largest
+      |o| times the largest |W_o| entry (one flipped code moves y_j by its step times w_jk)."""
+    h, w, qn, kn = _layer_inputs(41 + S, B, S, gated)
+    h0 = synth.bf16_bits_to_f64(h)
+    dv = {k: (None if v is None else to_dev(v)) for k, v in w.items()}
+    st = zg.Fp8Layer(D_MODEL, HQ, HKV, D, history=1024)
+    ref = oracle.Fp8DelayedScaling(7, history=1024)
+    o_t = oracle.FP8_LAYER_TENSORS.index("o")
+    import torch
+    ws = torch.empty(zg.fp8_layer_workspace_bytes(B, S, D_MODEL, HQ, HKV, D), dtype=torch.uint8, device="cuda")
+    wo_max = float(np.abs(synth.bf16_bits_to_f64(w["o"])).max())
+    for call, mag in enumerate((1.0, 0.5, 1.0)):
+        hb = synth.f64_to_bf16_bits(h0 * mag)
+        got_s = np.asarray(st.scales(), dtype=np.float32)
+        for t, name in enumerate(oracle.FP8_LAYER_TENSORS):
+            if t == o_t:
+                assert abs(got_s[t] / ref.scale[t] - 1) <= 2.0 ** -7, f"call {call}: scale of o"
+            else:
+                assert got_s[t] == ref.scale[t], f"call {call}: scale of {name}"
+        s_o = float(ref.scale[o_t])
+        if gated:
+            y = zg.gated_swa_layer_fp8(to_dev(hb), dv["q"], dv["k"], dv["v"], dv["g"], dv["o"], to_dev(qn), to_dev(kn),
+                                       fp8=st, Hq=HQ, Hkv=HKV, window=128, rotary_dims=42, rope_base=1e4, eps=1e-6,
+                                       workspace=ws)
+        else:
+            y = zg.global_layer_fp8(to_dev(hb), dv["q"], dv["k"], dv["v"], dv["o"], to_dev(qn), to_dev(kn), fp8=st,
+                                    Hq=HQ, Hkv=HKV, rotary_dims=42, rope_base=1e4, eps=1e-6, workspace=ws)
+        rc = {}
+        yr = oracle.attention_layer_fp8(hb, w["q"], w["k"], w["v"], w["g"], w["o"], qn, kn, ref, Hq=HQ, Hkv=HKV,
+                                        window=128 if gated else None, rotary_dims=42, base=1e4, eps=1e-6, codes=rc)
+        gc = _fp8_layer_codes(ws, B, S, gated)
+        for name in gc:
+            if name != "o":
+                np.testing.assert_array_equal(gc[name], rc[name], err_msg=f"call {call}: codes of {name}")
+        diff = gc["o"] != rc["o"]
+        vg = oracle.e4m3_decode(gc["o"]) / float(got_s[o_t])
+        vr = oracle.e4m3_decode(rc["o"]) / s_o
+        lim = TOL_MAX_ABS + _e4m3_step(np.maximum(np.abs(vg), np.abs(vr)) * s_o) / s_o
+        assert np.all(np.abs(vg - vr) <= lim), f"call {call}: o codes beyond one step of the oracle's"
+        assert diff.mean() <= 0.05, f"call {call}: {diff.mean():.4f} of the o codes differ"
+        got = to_host_f64(y)
+        err = np.abs(got - yr)
+        o_max = float(np.abs(oracle.e4m3_decode(rc["o"])).max()) / s_o
+        allow = 2 * float(_e4m3_step(o_max * s_o)) / s_o * wo_max
+        print(f"fp8 layer {'swa' if gated else 'global'} call {call}: max_abs {err.max():.3e} mean_abs {err.mean():.3e} "
+              f"rms(y) {np.sqrt(np.mean(yr ** 2)):.3f}; o codes differing {diff.mean():.2e}; flip allowance {allow:.3e}; "
+              f"s_o {float(got_s[o_t]):.6g} vs {s_o:.6g}")
+        assert err.mean() <= TOL_MEAN_ABS, f"call {call}: mean_abs {err.mean():.3e}"
+        assert err.max() <= TOL_MAX_ABS + allow, f"call {call}: max_abs {err.max():.3e} > {TOL_MAX_ABS + allow:.3e}"
+    st.close()

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+import synth
 
 RNG = np.random.default_rng(12345)
 
@@ -372,3 +373,71 @@ def test_fp8_delayed_scaling_lags_by_one_call():
     f2(np.full((1, 8), 8.0), np.full((1, 8), 1.0))
     y, cx, cw = f2(np.full((1, 8), 1.0), np.full((1, 8), 1.0))
     assert int(cx[0, 0]) == 0x66 and y[0, 0] == pytest.approx(8.0)
+
+
+def _e4m3_grid(rng, shape, e_lo, e_hi, signed=True):
+    """Random values (1 + m/8) 2^e, e in [e_lo, e_hi]: normal E4M3 values, exact in bf16 too."""
+    m = rng.integers(0, 8, size=shape)
+    e = rng.integers(e_lo, e_hi + 1, size=shape)
+    v = (1.0 + m / 8.0) * np.exp2(e)
+    if signed:
+        v = v * rng.choice([-1.0, 1.0], size=shape)
+    return synth.f64_to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_fp8_layer_equals_bf16_layer_when_operands_are_e4m3_exact(gated):
+    """First call (all scales 1) with every quantised operand exactly representable in E4M3: h and the q/k/w_o
+    weights on the E4M3 grid, W_v picking columns of h that are constant over the tokens (so v, the attention
+    average and o are that constant, whatever the weights), W_g = 64 x picking positive columns (sigmoid(g) rounds
+    to 1).  Then quantisation changes nothing and the FP8 layer equals the bf16 layer exactly; afterwards each
+    quantised tensor's scale is 448 / its max |v|, and a global layer leaves W_g's state alone."""
+    rng = np.random.default_rng(11)
+    B, S, Hq, Hkv, D, dm = 1, 24, 2, 1, 128, 256
+    hv = oracle.bf16_to_f64(_e4m3_grid(rng, (B, S, dm), -1, 1, signed=False))
+    cols = rng.choice(dm, size=Hkv * D, replace=False)
+    hv[:, :, cols] = hv[:, :1, cols]                        # constant over the tokens
+    h = synth.f64_to_bf16_bits(hv)
+    onehot = np.zeros((Hkv * D, dm))
+    onehot[np.arange(Hkv * D), cols] = 1.0
+    w_q = _e4m3_grid(rng, (Hq * D, dm), -6, -3)
+    w_k = _e4m3_grid(rng, (Hkv * D, dm), -6, -3)
+    w_v = synth.f64_to_bf16_bits(onehot)
+    w_g = synth.f64_to_bf16_bits(64.0 * np.eye(Hq * D, dm)) if gated else None
+    w_o = _e4m3_grid(rng, (dm, Hq * D), -6, -3)
+    wn = synth.norm_weight_bf16(7, 1, synth.TENSOR_WQ, D)
+    kw = dict(Hq=Hq, Hkv=Hkv, window=4 if gated else None, rotary_dims=42, base=1e4, eps=1e-6)
+    st = oracle.Fp8DelayedScaling(7, history=16)
+    y8 = oracle.attention_layer_fp8(h, w_q, w_k, w_v, w_g, w_o, wn, wn, st, **kw)
+    y = oracle.attention_layer(h, w_q, w_k, w_v, w_g, w_o, wn, wn, **kw)
+    np.testing.assert_array_equal(y8, y)
+    o_max = np.max(np.abs(hv[0, 0, cols]))                 # o = v = the constant columns (each head repeats them)
+    for name, v in (("h", hv), ("w_q", w_q), ("w_k", w_k), ("w_v", onehot), ("w_g", w_g), ("o", o_max), ("w_o", w_o)):
+        t = oracle.FP8_LAYER_TENSORS.index(name)
+        if v is None:
+            assert st.scale[t] == 1.0 and not st.hist[t].any()
+            continue
+        m = np.float32(np.max(np.abs(oracle.bf16_to_f64(v) if np.asarray(v).dtype == np.uint16 else v)))
+        assert st.scale[t] == np.float32(448.0) / m, name
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_fp8_layer_tracks_bf16_layer_within_e4m3_precision(gated):
+    """Random operands over three calls: E4M3 keeps 3 mantissa bits, so each quantised operand is off by at most
+    2^-4 relative (normals) and the layer output by a few percent rms, at every call (scales 1, then fitted).
+    A dropped or misapplied dequantisation factor is off by the scale itself (factors of 10-10^4 here)."""
+    B, S, Hq, Hkv, D, dm = 1, 48, 2, 1, 128, 256
+    h = synth.normal_bf16(5, 1, synth.TENSOR_H, (B, S, dm))
+    def wt(t, n, k):
+        return synth.f64_to_bf16_bits(oracle.bf16_to_f64(synth.normal_bf16(5, 1, t, (n, k))) / np.sqrt(k))
+    w_q, w_k, w_v = wt(synth.TENSOR_PQ, Hq * D, dm), wt(synth.TENSOR_PK, Hkv * D, dm), wt(synth.TENSOR_PV, Hkv * D, dm)
+    w_g = wt(synth.TENSOR_PG, Hq * D, dm) if gated else None
+    w_o = wt(synth.TENSOR_PO, dm, Hq * D)
+    wn = synth.norm_weight_bf16(5, 1, synth.TENSOR_WQ, D)
+    kw = dict(Hq=Hq, Hkv=Hkv, window=16 if gated else None, rotary_dims=42, base=1e4, eps=1e-6)
+    y = oracle.attention_layer(h, w_q, w_k, w_v, w_g, w_o, wn, wn, **kw)
+    st = oracle.Fp8DelayedScaling(7, history=16)
+    for call in range(3):
+        y8 = oracle.attention_layer_fp8(h, w_q, w_k, w_v, w_g, w_o, wn, wn, st, **kw)
+        rel = np.sqrt(np.mean((y8 - y) ** 2) / np.mean(y ** 2))
+        assert 1e-4 < rel < 0.15, (call, rel)
