@@ -283,6 +283,99 @@ def prefill_layer(q, k, v, gate, wq, wk, *, window: int | None, rotary_dims: int
     return out
 
 
+# ---------------------------------------------------------------------------- backward (training)
+def _rope_transpose(dy, pos, rotary_dims: int, base: float) -> np.ndarray:
+    """The transpose of step 2 (a rotation per pair, so its inverse): (d0, d1) -> (d0 cos a + d1 sin a,
+    -d0 sin a + d1 cos a) with a = pos * base^(-2i/R).  dy [..., D]; pos broadcasts against dy.shape[:-1]."""
+    dx = np.array(dy, dtype=np.float64, copy=True)
+    p = np.broadcast_to(np.asarray(pos, dtype=np.float64), dx.shape[:-1])
+    for i in range(rotary_dims // 2):
+        a = p * base ** (-2.0 * i / rotary_dims)
+        c, sn = np.cos(a), np.sin(a)
+        d0, d1 = dx[..., 2 * i].copy(), dx[..., 2 * i + 1].copy()
+        dx[..., 2 * i] = d0 * c + d1 * sn
+        dx[..., 2 * i + 1] = -d0 * sn + d1 * c
+    return dx
+
+
+def _rmsnorm_backward(x, w, dy, eps: float):
+    """Derivatives of step 1, y = x w / r with r = sqrt(mean(x^2) + eps), over the last axis:
+    dx = (w dy) / r - x (sum_d w_d dy_d x_d) / (D r^3);  dw = sum over the rows of dy x / r."""
+    x = _as_f64(x)
+    w = _as_f64(w)
+    D = x.shape[-1]
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    wdy = w * dy
+    dx = wdy / r - x * np.sum(wdy * x, axis=-1, keepdims=True) / (D * r ** 3)
+    dw = np.sum((dy * x / r).reshape(-1, D), axis=0)
+    return dx, dw
+
+
+def prefill_layer_backward(q, k, v, gate, wq, wk, dout, *, window: int | None, rotary_dims: int, base: float,
+                           eps: float) -> dict:
+    """Gradients of one attention layer's output (prefill_layer without a cache, positions 0..S-1) with respect
+    to its inputs, given dout = dL/d(out) [B,S,Hq,D].  Returns float64 arrays: dq [B,S,Hq,D], dk, dv [B,S,Hkv,D],
+    dgate [B,S,Hq,D] (None for a global layer), dwq, dwk [D]; and the forward's out and lse [B,S,Hq] (natural log
+    of the softmax denominator: p_ij = exp(s_ij - lse_i)).
+
+    Chain rule through steps 5 to 1, per (sequence, query head) with dense masked score matrices:
+      A = p v, out = A (.) sigmoid(g):   dA = dout (.) sigmoid(g),  dg = dout (.) A (.) sigmoid(g) (1 - sigmoid(g))
+      p = softmax(s):                    dp = dA v^T,  ds = p (.) (dp - rowsum(p (.) dp))
+      s = q_hat k_hat^T / sqrt(D):       dq_hat = ds k_hat / sqrt(D),  dk_hat = ds^T q_hat / sqrt(D)
+      A = p v:                           dv = p^T dA
+    summed over the query heads that share a KV head; then through RoPE (its transpose) and RMSNorm.  The bf16
+    rounding of k_hat (the cache form keys are read in) passes its gradient through unchanged."""
+    q = np.asarray(q)
+    B, S, Hq, D = q.shape
+    Hkv = np.asarray(k).shape[2]
+    G = Hq // Hkv
+    pos = np.arange(S, dtype=np.int64)
+    qhat = qk_prologue(q, pos[None, :, None], wq, eps, rotary_dims, base)
+    khat = cache_key(qk_prologue(k, pos[None, :, None], wk, eps, rotary_dims, base))
+    vf = _as_f64(v)
+    gf = None if gate is None else _as_f64(gate)
+    do = _as_f64(dout)
+    i, j = np.meshgrid(pos, pos, indexing="ij")
+    vis = j <= i
+    if window is not None and window > 0:
+        vis &= (i - j) < window
+    scale = 1.0 / np.sqrt(D)
+    dqhat = np.zeros((B, S, Hq, D))
+    dkhat = np.zeros((B, S, Hkv, D))
+    dv = np.zeros((B, S, Hkv, D))
+    dg = None if gf is None else np.zeros((B, S, Hq, D))
+    out = np.zeros((B, S, Hq, D))
+    lse = np.zeros((B, S, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // G
+            sc = np.where(vis, (qhat[b, :, h] @ khat[b, :, kh].T) * scale, -np.inf)
+            m = sc.max(axis=1, keepdims=True)
+            e = np.exp(sc - m)
+            l = e.sum(axis=1, keepdims=True)
+            p = e / l
+            lse[b, :, h] = (m + np.log(l))[:, 0]
+            A = p @ vf[b, :, kh]
+            if gf is None:
+                out[b, :, h] = A
+                dA = do[b, :, h]
+            else:
+                sg = 1.0 / (1.0 + np.exp(-gf[b, :, h]))
+                out[b, :, h] = A * sg
+                dA = do[b, :, h] * sg
+                dg[b, :, h] = do[b, :, h] * A * sg * (1.0 - sg)
+            dp = dA @ vf[b, :, kh].T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dqhat[b, :, h] = ds @ khat[b, :, kh] * scale
+            dkhat[b, :, kh] += ds.T @ qhat[b, :, h] * scale
+            dv[b, :, kh] += p.T @ dA
+    dqn = _rope_transpose(dqhat, pos[None, :, None], rotary_dims, base)
+    dkn = _rope_transpose(dkhat, pos[None, :, None], rotary_dims, base)
+    dq, dwq = _rmsnorm_backward(q, wq, dqn, eps)
+    dk, dwk = _rmsnorm_backward(k, wk, dkn, eps)
+    return {"dq": dq, "dk": dk, "dv": dv, "dgate": dg, "dwq": dwq, "dwk": dwk, "out": out, "lse": lse}
+
+
 # ---------------------------------------------------------------------------- projections around the core
 def linear(x, w) -> np.ndarray:
     """A linear layer's forward y = x W^T in float64: x [..., K], w [N, K] (W stored out x in)."""

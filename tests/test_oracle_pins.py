@@ -441,3 +441,106 @@ def test_fp8_layer_tracks_bf16_layer_within_e4m3_precision(gated):
         y8 = oracle.attention_layer_fp8(h, w_q, w_k, w_v, w_g, w_o, wn, wn, st, **kw)
         rel = np.sqrt(np.mean((y8 - y) ** 2) / np.mean(y ** 2))
         assert 1e-4 < rel < 0.15, (call, rel)
+
+
+# ------------------------------------------------------------------------------------------ backward
+def _bwd_problem(seed, B, S, Hq, Hkv, D=128, gated=True):
+    q = synth.normal_bf16(seed, 1, synth.TENSOR_Q, (B, S, Hq, D))
+    k = synth.normal_bf16(seed, 1, synth.TENSOR_K, (B, S, Hkv, D))
+    v = synth.normal_bf16(seed, 1, synth.TENSOR_V, (B, S, Hkv, D))
+    g = synth.normal_bf16(seed, 1, synth.TENSOR_GATE, (B, S, Hq, D)) if gated else None
+    wq = synth.norm_weight_bf16(seed, 1, synth.TENSOR_WQ, D)
+    wk = synth.norm_weight_bf16(seed, 1, synth.TENSOR_WK, D)
+    do = np.random.default_rng(seed).standard_normal((B, S, Hq, D))
+    return q, k, v, g, wq, wk, do
+
+
+def _torch_layer(q, k, v, g, wq, wk, *, window, R, base, eps):
+    """The forward from library routines: torch's rms_norm, RoPE as a complex product (RoFormer), masked
+    scaled_dot_product_attention, sigmoid gate; k_hat rounded to bf16 with its gradient passed straight through."""
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    pos = torch.arange(S, dtype=torch.float64)
+    inv = base ** (-torch.arange(0, R, 2, dtype=torch.float64) / R)
+    rot = torch.polar(torch.ones(S, R // 2, dtype=torch.float64), pos[:, None] * inv[None, :])   # [S, R/2]
+
+    def rope(x):
+        xr = torch.view_as_complex(x[..., :R].reshape(*x.shape[:-1], R // 2, 2).contiguous())
+        xr = torch.view_as_real(xr * rot[None, :, None, :]).reshape(*x.shape[:-1], R)
+        return torch.cat([xr, x[..., R:]], dim=-1)
+
+    qh = rope(torch.nn.functional.rms_norm(q, (D,), wq, eps))
+    kh = rope(torch.nn.functional.rms_norm(k, (D,), wk, eps))
+    kh = kh + (kh.to(torch.bfloat16).to(torch.float64) - kh).detach()
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    vis = j <= i
+    if window:
+        vis = vis & (i - j < window)
+    G = Hq // Hkv
+    kr = kh.repeat_interleave(G, dim=2)
+    vr = v.repeat_interleave(G, dim=2)
+    a = torch.nn.functional.scaled_dot_product_attention(qh.transpose(1, 2), kr.transpose(1, 2), vr.transpose(1, 2),
+                                                         attn_mask=vis)
+    a = a.transpose(1, 2)
+    return a * torch.sigmoid(g) if g is not None else a
+
+
+@pytest.mark.parametrize("gated,window,B,S,Hq,Hkv", [(True, 8, 1, 24, 4, 1), (False, None, 2, 17, 4, 2),
+                                                     (True, 5, 1, 19, 2, 2)])
+def test_backward_matches_torch_autograd(gated, window, B, S, Hq, Hkv):
+    """The oracle's hand-derived gradients against torch autograd (float64) through the forward built from
+    library routines: every input, and the norm weights."""
+    q, k, v, g, wq, wk, do = _bwd_problem(3, B, S, Hq, Hkv, gated=gated)
+    ref = oracle.prefill_layer_backward(q, k, v, g, wq, wk, do, window=window, rotary_dims=42, base=1e4, eps=1e-6)
+    t = {n: torch.tensor(oracle.bf16_to_f64(x), requires_grad=True)
+         for n, x in (("q", q), ("k", k), ("v", v), ("wq", wq), ("wk", wk)) + ((("g", g),) if gated else ())}
+    out = _torch_layer(t["q"], t["k"], t["v"], t.get("g"), t["wq"], t["wk"], window=window, R=42, base=1e4, eps=1e-6)
+    np.testing.assert_allclose(out.detach().numpy(), ref["out"], rtol=0, atol=1e-12)
+    (out * torch.tensor(do)).sum().backward()
+    for n, r in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("wq", "dwq"), ("wk", "dwk")) + ((("g", "dgate"),) if gated else ()):
+        np.testing.assert_allclose(t[n].grad.numpy(), ref[r], rtol=1e-9, atol=1e-11, err_msg=n)
+
+
+def test_backward_matches_finite_differences():
+    """Central differences of the oracle's own forward (prefill_layer) on sampled elements of q, v, g and w_q (k
+    and w_k feed the bf16-rounded k_hat, whose true derivative is a step function: autograd pins those)."""
+    B, S, Hq, Hkv, D = 1, 10, 2, 1, 128
+    q, k, v, g, wq, wk, do = _bwd_problem(4, B, S, Hq, Hkv)
+    kw = dict(window=4, rotary_dims=42, base=1e4, eps=1e-6)
+    ref = oracle.prefill_layer_backward(q, k, v, g, wq, wk, do, **kw)
+    f = {n: oracle.bf16_to_f64(x) for n, x in (("q", q), ("k", k), ("v", v), ("g", g), ("wq", wq), ("wk", wk))}
+    rng = np.random.default_rng(9)
+
+    def loss(**over):
+        a = {**f, **over}
+        return float(np.sum(oracle.prefill_layer(a["q"], a["k"], a["v"], a["g"], a["wq"], a["wk"], **kw) * do))
+
+    h = 1e-5
+    for n, r in (("q", "dq"), ("v", "dv"), ("g", "dgate"), ("wq", "dwq")):
+        for _ in range(6):
+            idx = tuple(rng.integers(0, s) for s in f[n].shape)
+            xp, xm = f[n].copy(), f[n].copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd = (loss(**{n: xp}) - loss(**{n: xm})) / (2 * h)
+            assert abs(fd - ref[r][idx]) <= 1e-6 * max(1.0, abs(fd)), (n, idx, fd, ref[r][idx])
+
+
+def test_backward_window_one_and_closed_gate():
+    """W = 1: each query sees only itself, p = 1, so the scores carry no gradient (dq = dk = dw = 0) and
+    dv = sum over the group's heads of dout (.) sigmoid(g), dg = dout (.) v (.) sigmoid'(g).
+    g = -inf: the output is identically zero, so every gradient is zero."""
+    B, S, Hq, Hkv, D = 1, 9, 2, 1, 128
+    q, k, v, g, wq, wk, do = _bwd_problem(5, B, S, Hq, Hkv)
+    r = oracle.prefill_layer_backward(q, k, v, g, wq, wk, do, window=1, rotary_dims=42, base=1e4, eps=1e-6)
+    for n in ("dq", "dk", "dwq", "dwk"):
+        assert np.abs(r[n]).max() < 1e-13, n
+    sg = 1.0 / (1.0 + np.exp(-oracle.bf16_to_f64(g)))
+    vf = oracle.bf16_to_f64(v)
+    np.testing.assert_allclose(r["dv"][:, :, 0], (do * sg).sum(axis=2), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(r["dgate"], do * vf[:, :, [0, 0]] * sg * (1 - sg), rtol=1e-12, atol=1e-13)
+    gneg = synth.f64_to_bf16_bits(np.full(oracle.bf16_to_f64(g).shape, -np.inf))
+    z = oracle.prefill_layer_backward(q, k, v, gneg, wq, wk, do, window=4, rotary_dims=42, base=1e4, eps=1e-6)
+    for n in ("dq", "dk", "dv", "dgate", "dwq", "dwk"):
+        assert not np.any(z[n]), n
