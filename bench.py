@@ -408,6 +408,75 @@ def run_layers(zg, steps=5, warmup=2, S=16384, seed=1007):
     return res
 
 
+# ------------------------------------------------------------------------------------------ training backward
+def run_backward(zg, steps=5, warmup=2, S=16384, seed=1008):
+    """Training forward (with lse) and backward of one gated-SWA and one global layer, batch 1 x S tokens, 32q/8kv:
+    HIP-event time of each call and of each backward kernel family.  The global backward's algorithmic work is
+    2.5x the forward's (S, dP, dV, dQ, dK: 5 x 2D flop per visible (head, key) pair); the kernels execute 3.5x
+    (S and dP are formed in both the dK/dV and the dQ kernel)."""
+    import numpy as np
+    import torch
+    import synth
+    res = {}
+    for name, gated, layer in (("gated_swa", True, 1), ("global", False, 6)):
+        q = synth.normal_bf16_device(seed, layer, synth.TENSOR_Q, (1, S, HQ, D))
+        k = synth.normal_bf16_device(seed, layer, synth.TENSOR_K, (1, S, HKV, D))
+        v = synth.normal_bf16_device(seed, layer, synth.TENSOR_V, (1, S, HKV, D))
+        g = synth.normal_bf16_device(seed, layer, synth.TENSOR_GATE, (1, S, HQ, D)) if gated else None
+        dout = synth.normal_bf16_device(seed, layer, synth.TENSOR_DOUT, (1, S, HQ, D))
+        wq = torch.from_numpy(synth.norm_weight_bf16(seed, layer, synth.TENSOR_WQ, D).view("int16")).cuda().view(torch.bfloat16)
+        wk = torch.from_numpy(synth.norm_weight_bf16(seed, layer, synth.TENSOR_WK, D).view("int16")).cuda().view(torch.bfloat16)
+        out = torch.empty_like(q)
+        lse = torch.empty((1, HQ, S), dtype=torch.float32, device="cuda")
+        fws = torch.empty(zg.workspace_bytes(1, S, HKV, D), dtype=torch.uint8, device="cuda")
+        bws = torch.empty(zg.backward_workspace_bytes(1, S, HQ, HKV, D), dtype=torch.uint8, device="cuda")
+        grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+                 "dq_norm_w": torch.empty(D, dtype=torch.float32, device="cuda"),
+                 "dk_norm_w": torch.empty(D, dtype=torch.float32, device="cuda")}
+        if gated:
+            grads["dgate"] = torch.empty_like(g)
+
+        def fwd():
+            zg.prefill_train(q, k, v, g, wq, wk, window=W, rotary_dims=R, rope_base=1e4, out=out, lse=lse, workspace=fws)
+
+        def bwd():
+            zg.prefill_backward(q, k, v, g, wq, wk, out, lse, dout, window=W, rotary_dims=R, rope_base=1e4,
+                                grads=grads, workspace=bws)
+
+        times = {}
+        for tag, fn in (("forward", fwd), ("backward", bwd)):
+            for _ in range(warmup):
+                fn()
+            sync()
+            zg.kernel_timer_enable(True)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            sync()
+            times[tag] = e0.elapsed_time(e1) / steps
+            if tag == "backward":
+                times["kernels"] = {kn: zg.kernel_timer_read(kn)[0] / steps for kn in ("bwd_prep", "bwd_kv", "bwd_q", "bwd_post")}
+            zg.kernel_timer_enable(False)
+        pairs = S * (S + 1) // 2 if not gated else sum(min(i + 1, W) for i in range(S))
+        fwd_flop = 4 * D * HQ * pairs
+        r = {"forward_ms": times["forward"], "backward_ms": times["backward"], "backward_kernels_ms": times["kernels"],
+             "forward_tflop": fwd_flop / 1e12, "backward_algorithmic_tflop": 2.5 * fwd_flop / 1e12,
+             "backward_tflops": 2.5 * fwd_flop / (times["backward"] / 1e3) / 1e12}
+        mm = times["kernels"]["bwd_kv"] + times["kernels"]["bwd_q"]
+        r["mfma_kernels_tflops"] = 2.5 * fwd_flop / (mm / 1e3) / 1e12
+        r["mfma_kernels_frac"] = r["mfma_kernels_tflops"] / MFMA_PEAK_TFLOPS
+        res[name] = r
+        log(f"backward: {name}: forward {times['forward']:.3f} ms, backward {times['backward']:.3f} ms "
+            f"(prep {times['kernels']['bwd_prep']:.3f}, dK/dV {times['kernels']['bwd_kv']:.3f}, "
+            f"dQ {times['kernels']['bwd_q']:.3f}, norm/RoPE {times['kernels']['bwd_post']:.3f}); "
+            f"{r['backward_tflops']:.0f} TFLOP/s algorithmic, dK/dV + dQ kernels {r['mfma_kernels_tflops']:.0f} TFLOP/s")
+        del q, k, v, g, dout, out, lse, fws, bws, grads
+        torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------------------------------ CPU baseline
 def cpu_baseline(S=16384, n_rows=4096, seed=1003):
     """The fp64 oracle on a sample of the prefill workload: n_rows random positions, all 32 query heads, in
@@ -468,6 +537,9 @@ def main():
     ap.add_argument("--layers", action="store_true",
                     help="instead of the benchmark: time whole layers from the hidden state (projections on hipBLASLt, "
                          "attention core, o_proj) at 1 x 16384 tokens, d_model 4096 (one JSON line)")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the benchmark: time the training forward and backward of one gated-SWA and one "
+                         "global layer at 1 x 16384 tokens (one JSON line)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="also copy a GIB-sized device tensor 3 times (a plain copy kernel of known traffic, for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -489,6 +561,16 @@ def main():
         log(f"copy calibration: 3 elementwise copies of {n * 4} bytes (read {n * 4} B + write {n * 4} B each)")
         del src, dst
         torch.cuda.empty_cache()
+    if args.backward:
+        res = run_backward(zg, steps=args.steps, warmup=args.warmup)
+        print(json.dumps({
+            "metric": "training forward + backward time of one attention layer (gradients of q, k, v, gate, norm weights)",
+            "unit": "ms", "n_gpus": 1, "data": "synthetic", "higher_is_better": False, "dtype": "bf16",
+            "config": {"workload": "one gated-SWA and one global layer, 1 x 16384 tokens", "q_heads": HQ,
+                       "kv_heads": HKV, "head_dim": D, "window": W, "rotary_dims": R, "seed": 1008},
+            "backward": res,
+        }), flush=True)
+        return
     if args.layers:
         res = run_layers(zg, steps=args.steps, warmup=args.warmup)
         print(json.dumps({

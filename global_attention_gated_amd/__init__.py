@@ -72,6 +72,13 @@ _lib.fp8_layer_workspace_bytes.argtypes = [_i32] * 6
 _lib.fp8_layer_workspace_bytes.restype = _u64
 _lib.gated_swa_layer_fp8.argtypes = [_vp] * 9 + [_i32] * 8 + [_f64, _f32, _i64, _vp, _i32, _vp, _vp, _u64, _vp]
 _lib.global_layer_fp8.argtypes = [_vp] * 8 + [_i32] * 7 + [_f64, _f32, _i64, _vp, _i32, _vp, _vp, _u64, _vp]
+_fp = ctypes.POINTER(ctypes.c_float)
+_lib.swa_prefill_train.argtypes = [_vp] * 8 + [_i32] * 7 + [_f64, _f32, _vp, _u64, _vp]
+_lib.global_prefill_train.argtypes = [_vp] * 7 + [_i32] * 6 + [_f64, _f32, _vp, _u64, _vp]
+_lib.backward_workspace_bytes.argtypes = [_i32] * 5
+_lib.backward_workspace_bytes.restype = _u64
+_lib.swa_prefill_backward.argtypes = [_vp] * 15 + [_i32] * 7 + [_f64, _f32, _vp, _u64, _vp]
+_lib.global_prefill_backward.argtypes = [_vp] * 13 + [_i32] * 6 + [_f64, _f32, _vp, _u64, _vp]
 _lib.zg_last_error.restype = ctypes.c_char_p
 _lib.zg_kernel_timer_enable.argtypes = [_i32]
 _lib.zg_kernel_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_f64), ctypes.POINTER(_i64)]
@@ -81,7 +88,9 @@ EXPORTED = ["kv_cache_alloc", "kv_cache_free", "kv_cache_footprint_bytes", "kv_c
             "linear_bf16", "layer_workspace_bytes", "gated_swa_layer", "global_layer", "fp8_linear_alloc",
             "fp8_linear_free", "fp8_linear_scales", "fp8_linear_workspace_bytes", "linear_fp8_delayed",
             "fp8_layer_alloc", "fp8_layer_free", "fp8_layer_scales", "fp8_layer_workspace_bytes", "gated_swa_layer_fp8",
-            "global_layer_fp8", "zg_last_error", "zg_kernel_timer_enable", "zg_kernel_timer_read"]
+            "global_layer_fp8", "swa_prefill_train", "global_prefill_train", "backward_workspace_bytes",
+            "swa_prefill_backward", "global_prefill_backward", "zg_last_error", "zg_kernel_timer_enable",
+            "zg_kernel_timer_read"]
 
 
 class ZgError(RuntimeError):
@@ -235,6 +244,76 @@ def global_prefill(q, k, v, q_norm_w, k_norm_w, out=None, *, rotary_dims=42, rop
     """Ungated global causal layer: q [B,S,Hq,D], k/v [B,S,Hkv,D], weights [D] (bf16); returns out."""
     return _prefill(False, q, k, v, None, q_norm_w, k_norm_w, out, 0, rotary_dims, rope_base, eps, pos0, cache,
                     layer, workspace)
+
+
+# ------------------------------------------------------------------------------------------- training
+def _f32cuda(t, name):
+    if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous()):
+        raise TypeError(f"{name} must be a contiguous float32 CUDA tensor")
+    return t
+
+
+def prefill_train(q, k, v, gate, q_norm_w, k_norm_w, *, window=128, rotary_dims=42, rope_base=1e4, eps=1e-6,
+                  out=None, lse=None, workspace=None):
+    """Training forward (swa_prefill_train, or global_prefill_train when gate is None): returns (out, lse), out
+    [B,S,Hq,D] bf16 and lse [B,Hq,S] fp32 (natural log of each softmax denominator)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        _bf16(t, n)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    out = torch.empty_like(q) if out is None else _bf16(out, "out")
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if lse is None else _f32cuda(lse, "lse")
+    if workspace is None:
+        workspace = torch.empty(max(16, workspace_bytes(B, S, Hkv, D)), dtype=torch.uint8, device=q.device)
+    ws_n = workspace.numel() * workspace.element_size()
+    if gate is not None:
+        rc = _lib.swa_prefill_train(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out),
+                                    _ptr(lse), B, S, Hq, Hkv, D, window, rotary_dims, rope_base, eps,
+                                    workspace.data_ptr(), ws_n, _stream())
+    else:
+        rc = _lib.global_prefill_train(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), _ptr(lse),
+                                       B, S, Hq, Hkv, D, rotary_dims, rope_base, eps, workspace.data_ptr(), ws_n,
+                                       _stream())
+    _check(rc)
+    return out, lse
+
+
+def backward_workspace_bytes(B, S, Hq, Hkv, D=128) -> int:
+    return int(_lib.backward_workspace_bytes(B, S, Hq, Hkv, D))
+
+
+def prefill_backward(q, k, v, gate, q_norm_w, k_norm_w, out, lse, dout, *, window=128, rotary_dims=42, rope_base=1e4,
+                     eps=1e-6, grads=None, workspace=None):
+    """Backward (swa_prefill_backward, or global_prefill_backward when gate is None): returns a dict with dq, dk,
+    dv (bf16, shaped as q/k/v), dgate (bf16, None for a global layer) and dq_norm_w, dk_norm_w ([D] fp32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"),
+                 (out, "out"), (dout, "dout")):
+        _bf16(t, n)
+    _f32cuda(lse, "lse")
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    g = grads or {}
+    dq = g.get("dq", torch.empty_like(q))
+    dk = g.get("dk", torch.empty_like(k))
+    dv = g.get("dv", torch.empty_like(v))
+    dg = None if gate is None else g.get("dgate", torch.empty_like(gate))
+    dqw = g.get("dq_norm_w", torch.empty(D, dtype=torch.float32, device=q.device))
+    dkw = g.get("dk_norm_w", torch.empty(D, dtype=torch.float32, device=q.device))
+    if workspace is None:
+        workspace = torch.empty(max(16, backward_workspace_bytes(B, S, Hq, Hkv, D)), dtype=torch.uint8, device=q.device)
+    ws_n = workspace.numel() * workspace.element_size()
+    if gate is not None:
+        rc = _lib.swa_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out),
+                                       _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dqw),
+                                       _ptr(dkw), B, S, Hq, Hkv, D, window, rotary_dims, rope_base, eps,
+                                       workspace.data_ptr(), ws_n, _stream())
+    else:
+        rc = _lib.global_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out),
+                                          _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqw), _ptr(dkw),
+                                          B, S, Hq, Hkv, D, rotary_dims, rope_base, eps, workspace.data_ptr(), ws_n,
+                                          _stream())
+    _check(rc)
+    return {"dq": dq, "dk": dk, "dv": dv, "dgate": dg, "dq_norm_w": dqw, "dk_norm_w": dkw}
 
 
 # ------------------------------------------------------------------------------------------- projections, layers

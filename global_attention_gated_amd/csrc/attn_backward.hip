@@ -1,0 +1,560 @@
+// Backward of an attention layer for training (gradients of the gated-SWA or global layer output with respect to
+// q, k, v, the gate logits and the two RMSNorm weights), given the forward's output and log-sum-exp.
+//
+// The forward (ZGCM-1 summaries: onedev.kr "How it works"; jaehun.me "New Approach" and "How Gated SWA Behaves"),
+// per (sequence, query head, query i): q_hat = RoPE(RMSNorm(q) w_q), k_hat = bf16(RoPE(RMSNorm(k) w_k)),
+// s_ij = q_hat_i . k_hat_j / sqrt(D) over the visible keys (causal; SWA also i - j < W), p = softmax(s),
+// A = p v, out = A (.) sigmoid(g) (SWA) or A (global).  With dout given, the chain rule reads:
+//   dA = dout (.) sigmoid(g);  dg = dout (.) A (.) sigmoid(g)(1 - sigmoid(g)) = dout (.) out (.) (1 - sigmoid(g))
+//   Delta_i = sum_j p_ij dp_ij = dA_i . A_i = dout_i . out_i     (no division by sigmoid(g) anywhere)
+//   dp_ij = dA_i . v_j;  ds_ij = p_ij (dp_ij - Delta_i);  p_ij = exp(s_ij - lse_i)
+//   dq_hat_i = sum_j ds_ij k_hat_j / sqrt(D);  dk_hat_j = sum_i ds_ij q_hat_i / sqrt(D);  dv_j = sum_i p_ij dA_i
+// summed over the query heads of a GQA group for k and v; then back through RoPE (its transpose) and RMSNorm.
+// The bf16 rounding of k_hat passes its gradient through unchanged.
+//
+// Kernels, in launch order:
+//   bwd_prep_kernel  per 64-token block of one head: q_hat (fp16, pre-scaled by log2(e)/sqrt(D), the forward's
+//                    score operand) and q_hat^T (bf16); dA and dA^T (bf16), Delta, lse in log2 units, dgate;
+//                    for the KV heads k_hat (fp16) and k_hat^T (bf16).  Transposes go through LDS.
+//   bwd_kv_kernel    key-centric: a work-group owns 128 keys of one (sequence, KV head), one wave per 32 keys, and
+//                    walks the query tiles that see them for each head of the group; dV^T = dA^T P and
+//                    dK_hat^T = Q_hat^T dS accumulate in registers (MFMA 32x32x16, scores in fp16 as the forward,
+//                    gradient products in bf16 for their range).
+//   bwd_q_kernel     query-centric: a work-group owns 32 positions of the 4 heads of a group (one wave each) and
+//                    walks the key tiles they see: dQ_hat^T = K_hat^T dS^T.
+//   bwd_post_kernel  RoPE transpose and RMSNorm backward per (token, head) row; bf16 dq / dk and deterministic
+//                    per-work-group partial sums of the norm-weight gradients, reduced by bwd_dw_reduce_kernel.
+#include "common.h"
+#include "launch.h"
+
+namespace zg {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16v8;
+
+constexpr int kT = 32;          // query / key tile of the MFMA kernels
+constexpr int kRowS = 136;      // LDS row stride (halves) of [32][128] tiles: 16-byte pad
+constexpr int kTrS = 40;        // LDS row stride (halves) of [128][32] transposed tiles
+constexpr int kPrepTok = 64;    // tokens per prep work-group
+constexpr int kPrepTS = 72;     // LDS row stride (halves) of the prep transpose tiles [128][64]
+
+__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ bf16v8 as_bf16v8(const uint4& w) { return __builtin_bit_cast(bf16v8, w); }
+__device__ __forceinline__ half8 as_half8(const uint4& w) { return __builtin_bit_cast(half8, w); }
+
+// 8 fp32 of an MFMA C block (regs j0..j0+7) -> bf16 operand fragment
+__device__ __forceinline__ bf16v8 c8_to_bf16(const float* c) {
+  return as_bf16v8(make_uint4(pack_bf16(c[0], c[1]), pack_bf16(c[2], c[3]), pack_bf16(c[4], c[5]), pack_bf16(c[6], c[7])));
+}
+
+// A-operand fragment of a transposed [128][kTrS] tile for k-step t: row `row`, the 8 columns
+// 16t + 4hi + {0..3} and 16t + 8 + 4hi + {0..3} (the order in which an MFMA C block holds its rows, so the
+// fragment pairs with a B operand built from C registers 8t..8t+7).
+__device__ __forceinline__ bf16v8 tr_frag(const uint16_t* tile, int row, int t, int hi) {
+  const uint16_t* p = tile + row * kTrS + 16 * t + 4 * hi;
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hh = *reinterpret_cast<const uint2*>(p + 8);
+  return as_bf16v8(make_uint4(lo.x, lo.y, hh.x, hh.y));
+}
+
+// ------------------------------------------------------------------------------------------ prep
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t T1[kHeadDim * kPrepTS];
+  __shared__ __attribute__((aligned(16))) uint16_t T2[kHeadDim * kPrepTS];
+  const int tid = threadIdx.x;
+  const int c = tid & 15, rg = tid >> 4;   // 16 lanes per row, 8 dims each; 16 rows per pass
+  const int s0 = blockIdx.x * kPrepTok;
+  const bool qmode = (int)blockIdx.y < a.B * a.Hq;
+  const int bh = qmode ? (int)blockIdx.y : (int)blockIdx.y - a.B * a.Hq;
+  const int H = qmode ? a.Hq : a.Hkv;
+  const int b = bh / H, h = bh % H;
+  float wf[8];
+  unpack8(*reinterpret_cast<const uint4*>((qmode ? a.qw : a.kw) + 8 * c), wf);
+  const bool gated = a.gate != nullptr;
+
+  for (int pass = 0; pass < kPrepTok / 16; pass++) {
+    const int row = pass * 16 + rg;
+    const int s = s0 + row;
+    const int64_t wrow = ((int64_t)bh * a.Sp + s) * kHeadDim + 8 * c;   // [b][h][Sp][D] workspace row
+    uint4 t1 = make_uint4(0, 0, 0, 0), t2 = make_uint4(0, 0, 0, 0);
+    if (s < a.S) {
+      const int64_t irow = (((int64_t)b * a.S + s) * H + h) * kHeadDim + 8 * c;   // [B][S][H][D] input row
+      float f[8];
+      unpack8(*reinterpret_cast<const uint4*>((qmode ? a.q : a.k) + irow), f);
+      norm_rope8_g16_w(f, wf, c, s, a.eps, a.rot_pairs, a.inv_freq_rev);
+      if (qmode) {
+        float fs[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) fs[e] = f[e] * a.q_scale;
+        *reinterpret_cast<uint4*>(a.qh16 + wrow) = make_uint4(pack_f16(fs[0], fs[1]), pack_f16(fs[2], fs[3]),
+                                                              pack_f16(fs[4], fs[5]), pack_f16(fs[6], fs[7]));
+        t1 = pack8(f);
+        float d[8], o[8], g[8];
+        unpack8(*reinterpret_cast<const uint4*>(a.dout + irow), d);
+        unpack8(*reinterpret_cast<const uint4*>(a.out + irow), o);
+        float delta = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) delta += d[e] * o[e];
+        if (gated) {
+          unpack8(*reinterpret_cast<const uint4*>(a.gate + irow), g);
+          float dg[8];
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float sg = sigmoidf_(g[e]);
+            dg[e] = d[e] * o[e] * (1.0f - sg);
+            d[e] *= sg;
+          }
+          *reinterpret_cast<uint4*>(a.dgate + irow) = pack8(dg);
+        }
+        t2 = pack8(d);
+        *reinterpret_cast<uint4*>(a.da + wrow) = t2;
+        delta += __shfl_xor(delta, 8);
+        delta += __shfl_xor(delta, 4);
+        delta += __shfl_xor(delta, 2);
+        delta += __shfl_xor(delta, 1);
+        if (c == 0) {
+          a.delta[(int64_t)bh * a.Sp + s] = delta;
+          a.lse2[(int64_t)bh * a.Sp + s] = a.lse[(int64_t)bh * a.S + s] * kLog2e;
+        }
+      } else {
+        t1 = pack8(f);                                            // k_hat in its bf16 cache form
+        *reinterpret_cast<uint4*>(a.kh16 + wrow) = bf16x8_to_f16x8(t1);
+      }
+    } else {
+      if (qmode) {
+        *reinterpret_cast<uint4*>(a.qh16 + wrow) = t1;
+        *reinterpret_cast<uint4*>(a.da + wrow) = t2;
+        if (c == 0) {
+          a.delta[(int64_t)bh * a.Sp + s] = 0.f;
+          a.lse2[(int64_t)bh * a.Sp + s] = INFINITY;
+        }
+      } else {
+        *reinterpret_cast<uint4*>(a.kh16 + wrow) = t1;
+      }
+    }
+    const uint16_t* p1 = reinterpret_cast<const uint16_t*>(&t1);
+    const uint16_t* p2 = reinterpret_cast<const uint16_t*>(&t2);
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      T1[(8 * c + e) * kPrepTS + row] = p1[e];
+      if (qmode) T2[(8 * c + e) * kPrepTS + row] = p2[e];
+    }
+  }
+  __syncthreads();
+  // transposed stores: dim row d = tid / 2, tokens 32 (tid & 1) .. +31 (64 bytes)
+  const int d = tid >> 1, half = tid & 1;
+  const int64_t trow = ((int64_t)bh * kHeadDim + d) * a.Sp + s0 + 32 * half;
+  uint16_t* dst1 = qmode ? a.qt : a.kt;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    *reinterpret_cast<uint4*>(dst1 + trow + 8 * k) =
+        *reinterpret_cast<const uint4*>(&T1[d * kPrepTS + 32 * half + 8 * k]);
+    if (qmode)
+      *reinterpret_cast<uint4*>(a.dat + trow + 8 * k) =
+          *reinterpret_cast<const uint4*>(&T2[d * kPrepTS + 32 * half + 8 * k]);
+  }
+}
+
+// ------------------------------------------------------------------------------------------ dK, dV
+struct KvStage {
+  uint16_t qs[kT * kRowS];       // q_hat' fp16 [32 queries][128]
+  uint16_t das[kT * kRowS];      // dA bf16 [32][128]
+  uint16_t qts[kHeadDim * kTrS];   // q_hat^T bf16 [128][32]
+  uint16_t dats[kHeadDim * kTrS];  // dA^T bf16 [128][32]
+  float lse2[kT];
+  float dl[kT];
+};
+
+__global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) KvStage st[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int n_units = a.B * a.Hkv;
+  const int unit = blockIdx.x % n_units, kb = blockIdx.x / n_units;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const bool swa = a.window > 0;
+  const int jb0 = kb * 128;              // the work-group's keys jb0 .. jb0+127
+  const int j0 = jb0 + 32 * wave;        // this wave's keys j0 .. j0+31
+  const int key = j0 + l32;              // this lane's key (MFMA column)
+
+  // preload this lane's key row: k_hat fp16 (score operand) and v bf16 (dP operand), K-steps of 16 dims
+  uint4 kf[8], vf[8];
+  {
+    const uint16_t* kr = a.kh16 + ((int64_t)unit * a.Sp + key) * kHeadDim + 8 * hi;
+    const int kc = min(key, a.S - 1);
+    const uint16_t* vr = a.v + (((int64_t)b * a.S + kc) * a.Hkv + kvh) * kHeadDim + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      kf[t] = *reinterpret_cast<const uint4*>(kr + 16 * t);
+      vf[t] = *reinterpret_cast<const uint4*>(vr + 16 * t);
+    }
+  }
+  floatx16 dv[4], dk[4];
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) dv[db][j] = dk[db][j] = 0.f;
+
+  // query tiles that see some key of the work-group, per head
+  const int jb_last = min(jb0 + 127, a.S - 1);
+  const int q_end = swa ? min(a.S, jb_last + a.window) : a.S;   // exclusive
+  const int qt0 = jb0 / kT, qt1 = (q_end + kT - 1) / kT;
+  const int ntiles = max(qt1 - qt0, 0);
+  const int n_it = ntiles * a.G;
+  // this wave's visible queries [j0, wq_end)
+  const int wq_end = swa ? min(a.S, j0 + 31 + a.window) : a.S;
+
+  // staging roles: 2 x 16-byte chunks of each of the four tiles per thread, plus lse / Delta
+  uint4 pre[8];
+  float pre_f = 0.f;
+  auto load_stage = [&](int it) {
+    const int hq = kvh * a.G + it / ntiles;
+    const int q0 = (qt0 + it % ntiles) * kT;
+    const int64_t bh = (int64_t)b * a.Hq + hq;
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int cidx = tid + 256 * k;
+      const int r = cidx >> 4, cc = cidx & 15;            // row-major tiles: row r, chunk cc
+      const int64_t ro = (bh * a.Sp + q0 + r) * kHeadDim + 8 * cc;
+      pre[k] = *reinterpret_cast<const uint4*>(a.qh16 + ro);
+      pre[2 + k] = *reinterpret_cast<const uint4*>(a.da + ro);
+      const int d = cidx >> 2, part = cidx & 3;           // transposed tiles: dim d, 8 tokens
+      const int64_t to = (bh * kHeadDim + d) * a.Sp + q0 + 8 * part;
+      pre[4 + k] = *reinterpret_cast<const uint4*>(a.qt + to);
+      pre[6 + k] = *reinterpret_cast<const uint4*>(a.dat + to);
+    }
+    if (tid < 64) pre_f = (tid < 32 ? a.lse2 : a.delta)[bh * a.Sp + q0 + (tid & 31)];
+  };
+  auto store_stage = [&](int buf) {
+    KvStage& s = st[buf];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int cidx = tid + 256 * k;
+      const int r = cidx >> 4, cc = cidx & 15;
+      *reinterpret_cast<uint4*>(&s.qs[r * kRowS + 8 * cc]) = pre[k];
+      *reinterpret_cast<uint4*>(&s.das[r * kRowS + 8 * cc]) = pre[2 + k];
+      const int d = cidx >> 2, part = cidx & 3;
+      *reinterpret_cast<uint4*>(&s.qts[d * kTrS + 8 * part]) = pre[4 + k];
+      *reinterpret_cast<uint4*>(&s.dats[d * kTrS + 8 * part]) = pre[6 + k];
+    }
+    if (tid < 32) s.lse2[tid] = pre_f;
+    else if (tid < 64) s.dl[tid - 32] = pre_f;
+  };
+
+  auto compute = [&](int buf, int it) {
+    const int q0 = (qt0 + it % ntiles) * kT;
+    if (q0 + kT <= j0 || q0 >= wq_end) return;            // no query of the tile sees this wave's keys
+    const KvStage& s = st[buf];
+    floatx16 sacc, dpacc;
+#pragma unroll
+    for (int j = 0; j < 16; j++) sacc[j] = dpacc[j] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const uint4 qa = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 8 * hi]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(qa), as_half8(kf[t]), sacc, 0, 0, 0);
+      const uint4 da = *reinterpret_cast<const uint4*>(&s.das[l32 * kRowS + 16 * t + 8 * hi]);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16v8(da), as_bf16v8(vf[t]), dpacc, 0, 0, 0);
+    }
+    // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key.  P and dS replace S and dP.
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const int qr = 8 * (j >> 2) + 4 * hi + (j & 3);
+      const int qi = q0 + qr;
+      const bool vis = qi < a.S && key <= qi && (!swa || qi - key < a.window);
+      const float pj = vis ? __builtin_amdgcn_exp2f(sacc[j] - s.lse2[qr]) : 0.f;
+      sacc[j] = pj;
+      dpacc[j] = pj * (dpacc[j] - s.dl[qr]);
+    }
+    float pv[16], sv[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      pv[j] = sacc[j];
+      sv[j] = dpacc[j];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const bf16v8 pb = c8_to_bf16(pv + 8 * t);
+      const bf16v8 sb = c8_to_bf16(sv + 8 * t);
+#pragma unroll
+      for (int db = 0; db < 4; db++) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.dats, 32 * db + l32, t, hi), pb, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.qts, 32 * db + l32, t, hi), sb, dk[db], 0, 0, 0);
+      }
+    }
+  };
+
+  if (n_it > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_it; it++) {
+    const int buf = it & 1;
+    const bool more = it + 1 < n_it;
+    if (more) load_stage(it + 1);
+    compute(buf, it);
+    if (more) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // outputs: C layout reg j of block db is dim 32db + 8(j/4) + 4hi + j%4 of this lane's key
+  if (key < a.S) {
+    uint16_t* dvr = a.dv + (((int64_t)b * a.S + key) * a.Hkv + kvh) * kHeadDim;
+    float* dkr = a.dkh + ((int64_t)unit * a.Sp + key) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; db++)
+#pragma unroll
+      for (int jq = 0; jq < 4; jq++) {
+        const int d = 32 * db + 8 * jq + 4 * hi;
+        *reinterpret_cast<uint2*>(dvr + d) = make_uint2(pack_bf16(dv[db][4 * jq], dv[db][4 * jq + 1]),
+                                                        pack_bf16(dv[db][4 * jq + 2], dv[db][4 * jq + 3]));
+        *reinterpret_cast<float4*>(dkr + d) = make_float4(dk[db][4 * jq], dk[db][4 * jq + 1], dk[db][4 * jq + 2],
+                                                          dk[db][4 * jq + 3]);
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------ dQ
+struct QStage {
+  uint16_t ks[kT * kRowS];         // k_hat fp16 [32 keys][128]
+  uint16_t vs[kT * kRowS];         // v bf16 [32][128]
+  uint16_t kts[kHeadDim * kTrS];   // k_hat^T bf16 [128][32]
+};
+
+__global__ void __launch_bounds__(256) bwd_q_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) QStage st[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int n_units = a.B * a.Hkv;
+  const int n_qt = (a.S + kT - 1) / kT;
+  const int unit = blockIdx.x % n_units, rank = blockIdx.x / n_units;
+  const bool swa = a.window > 0;
+  const int qt = swa ? rank : n_qt - 1 - rank;            // global: longest rows first
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int hq = kvh * a.G + wave;
+  const int i0 = qt * kT;
+  const int qi = i0 + l32;                                 // this lane's query (MFMA column)
+  const int64_t bh = (int64_t)b * a.Hq + hq;
+
+  uint4 qf[8], daf[8];
+  {
+    const uint16_t* qr = a.qh16 + (bh * a.Sp + qi) * kHeadDim + 8 * hi;
+    const uint16_t* dr = a.da + (bh * a.Sp + qi) * kHeadDim + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      qf[t] = *reinterpret_cast<const uint4*>(qr + 16 * t);
+      daf[t] = *reinterpret_cast<const uint4*>(dr + 16 * t);
+    }
+  }
+  const float lse2 = a.lse2[bh * a.Sp + qi];
+  const float dl = a.delta[bh * a.Sp + qi];
+  floatx16 dq[4];
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) dq[db][j] = 0.f;
+
+  const int k_end = min(a.S, i0 + kT);
+  const int k_beg = swa ? max(0, i0 - a.window + 1) : 0;
+  const int kt0 = k_beg / kT, kt1 = (k_end + kT - 1) / kT;
+  const int n_it = kt1 - kt0;
+
+  uint4 pre[6];
+  auto load_stage = [&](int it) {
+    const int k0 = (kt0 + it) * kT;
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int cidx = tid + 256 * k;
+      const int r = cidx >> 4, cc = cidx & 15;
+      pre[k] = *reinterpret_cast<const uint4*>(a.kh16 + ((int64_t)unit * a.Sp + k0 + r) * kHeadDim + 8 * cc);
+      const int kc = min(k0 + r, a.S - 1);
+      pre[2 + k] = *reinterpret_cast<const uint4*>(a.v + (((int64_t)b * a.S + kc) * a.Hkv + kvh) * kHeadDim + 8 * cc);
+      const int d = cidx >> 2, part = cidx & 3;
+      pre[4 + k] = *reinterpret_cast<const uint4*>(a.kt + ((int64_t)unit * kHeadDim + d) * a.Sp + k0 + 8 * part);
+    }
+  };
+  auto store_stage = [&](int buf) {
+    QStage& s = st[buf];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int cidx = tid + 256 * k;
+      const int r = cidx >> 4, cc = cidx & 15;
+      *reinterpret_cast<uint4*>(&s.ks[r * kRowS + 8 * cc]) = pre[k];
+      *reinterpret_cast<uint4*>(&s.vs[r * kRowS + 8 * cc]) = pre[2 + k];
+      const int d = cidx >> 2, part = cidx & 3;
+      *reinterpret_cast<uint4*>(&s.kts[d * kTrS + 8 * part]) = pre[4 + k];
+    }
+  };
+  auto compute = [&](int buf, int it) {
+    const int k0 = (kt0 + it) * kT;
+    const QStage& s = st[buf];
+    floatx16 sacc, dpacc;
+#pragma unroll
+    for (int j = 0; j < 16; j++) sacc[j] = dpacc[j] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const uint4 ka = *reinterpret_cast<const uint4*>(&s.ks[l32 * kRowS + 16 * t + 8 * hi]);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(ka), as_half8(qf[t]), sacc, 0, 0, 0);
+      const uint4 va = *reinterpret_cast<const uint4*>(&s.vs[l32 * kRowS + 16 * t + 8 * hi]);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16v8(va), as_bf16v8(daf[t]), dpacc, 0, 0, 0);
+    }
+    // C layout: reg j is key k0 + 8(j/4) + 4hi + j%4, column = this lane's query
+    float ds[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const int kj = k0 + 8 * (j >> 2) + 4 * hi + (j & 3);
+      const bool vis = qi < a.S && kj <= qi && (!swa || qi - kj < a.window);
+      const float pj = vis ? __builtin_amdgcn_exp2f(sacc[j] - lse2) : 0.f;
+      ds[j] = pj * (dpacc[j] - dl);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const bf16v8 sb = c8_to_bf16(ds + 8 * t);
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.kts, 32 * db + l32, t, hi), sb, dq[db], 0, 0, 0);
+    }
+  };
+
+  if (n_it > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < n_it; it++) {
+    const int buf = it & 1;
+    const bool more = it + 1 < n_it;
+    if (more) load_stage(it + 1);
+    compute(buf, it);
+    if (more) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  float* dqr = a.dqh + (bh * a.Sp + qi) * kHeadDim;
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int jq = 0; jq < 4; jq++) {
+      const int d = 32 * db + 8 * jq + 4 * hi;
+      *reinterpret_cast<float4*>(dqr + d) = make_float4(dq[db][4 * jq], dq[db][4 * jq + 1], dq[db][4 * jq + 2],
+                                                        dq[db][4 * jq + 3]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------ norm / RoPE backward
+// Rows (b, s, h) with h fastest, 16 lanes per row (8 dims each, the chunk c = lane & 15 fixed per thread).
+// dy = RoPE^T(dX_hat / sqrt(D)); x = the raw input row; r = sqrt(mean(x^2) + eps):
+//   dx = w dy / r - x (sum_d w_d dy_d x_d) / (D r^3);   dw += dy x / r
+__global__ void __launch_bounds__(256) bwd_post_kernel(BwdArgs a, int kmode) {
+  __shared__ float red[16][kHeadDim];
+  const int tid = threadIdx.x, c = tid & 15, rg = tid >> 4;
+  const int H = kmode ? a.Hkv : a.Hq;
+  const float* dxh = kmode ? a.dkh : a.dqh;
+  const uint16_t* x = kmode ? a.k : a.q;
+  uint16_t* dx = kmode ? a.dk : a.dq;
+  float wf[8], acc[8];
+  unpack8(*reinterpret_cast<const uint4*>((kmode ? a.kw : a.qw) + 8 * c), wf);
+#pragma unroll
+  for (int e = 0; e < 8; e++) acc[e] = 0.f;
+  const float inv_sqrt_d = 0.08838834764831845f;   // 1/sqrt(128)
+  const int64_t rows = (int64_t)a.B * a.S * H;
+  for (int64_t row = (int64_t)blockIdx.x * 16 + rg; row < rows; row += (int64_t)gridDim.x * 16) {
+    const int h = (int)(row % H);
+    const int64_t bs = row / H;
+    const int s = (int)(bs % a.S), b = (int)(bs / a.S);
+    const float* src = dxh + (((int64_t)b * H + h) * a.Sp + s) * kHeadDim + 8 * c;
+    const float4 g0 = *reinterpret_cast<const float4*>(src);
+    const float4 g1 = *reinterpret_cast<const float4*>(src + 4);
+    float dy[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int e = 0; e < 8; e++) dy[e] *= inv_sqrt_d;
+    if (8 * c < 2 * a.rot_pairs) {
+#pragma unroll
+      for (int m = 0; m < 4; m++) {
+        const int i = 4 * c + m;
+        float cs, sn;
+        rope_cs(s, a.inv_freq_rev[i], cs, sn);
+        if (i >= a.rot_pairs) { cs = 1.0f; sn = 0.0f; }
+        const float d0 = dy[2 * m], d1 = dy[2 * m + 1];
+        dy[2 * m] = d0 * cs + d1 * sn;
+        dy[2 * m + 1] = -d0 * sn + d1 * cs;
+      }
+    }
+    float xf[8];
+    unpack8(*reinterpret_cast<const uint4*>(x + row * kHeadDim + 8 * c), xf);
+    float ss = 0.f, dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      ss += xf[e] * xf[e];
+      dot += wf[e] * dy[e] * xf[e];
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      ss += __shfl_xor(ss, o);
+      dot += __shfl_xor(dot, o);
+    }
+    const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps);
+    const float k3 = dot * inv * inv * inv * (1.0f / kHeadDim);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      o[e] = wf[e] * dy[e] * inv - xf[e] * k3;
+      acc[e] += dy[e] * xf[e] * inv;
+    }
+    *reinterpret_cast<uint4*>(dx + row * kHeadDim + 8 * c) = pack8(o);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e++) red[rg][8 * c + e] = acc[e];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float sum = 0.f;
+    for (int g = 0; g < 16; g++) sum += red[g][tid];
+    a.dw_part[((int64_t)kmode * kBwdPostBlocks + blockIdx.x) * kHeadDim + tid] = sum;
+  }
+}
+
+__global__ void __launch_bounds__(128) bwd_dw_zero_kernel(float* dqw, float* dkw) {
+  dqw[threadIdx.x] = 0.f;
+  dkw[threadIdx.x] = 0.f;
+}
+
+__global__ void __launch_bounds__(128) bwd_dw_reduce_kernel(BwdArgs a) {
+  const int kmode = blockIdx.x, d = threadIdx.x;
+  const float* part = a.dw_part + (int64_t)kmode * kBwdPostBlocks * kHeadDim;
+  float sum = 0.f;
+  for (int i = 0; i < kBwdPostBlocks; i++) sum += part[(int64_t)i * kHeadDim + d];
+  (kmode ? a.dkw : a.dqw)[d] = sum;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dw_zero(float* dqw, float* dkw, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_dw_zero_kernel, dim3(1), dim3(kHeadDim), 0, st, dqw, dkw);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(a.Sp / kPrepTok, a.B * (a.Hq + a.Hkv)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_kv_kernel, dim3(a.B * a.Hkv * ((a.S + 127) / 128)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_q_kernel, dim3(a.B * a.Hkv * ((a.S + kT - 1) / kT)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_post(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_post_kernel, dim3(kBwdPostBlocks), dim3(256), 0, st, a, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_post_kernel, dim3(kBwdPostBlocks), dim3(256), 0, st, a, 1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dw_reduce_kernel, dim3(2), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace zg

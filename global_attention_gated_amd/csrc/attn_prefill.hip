@@ -385,6 +385,9 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(PrefillArgs a) {
   // O^T lane layout: acc_o[db][j] is d = 32db + 8(j/4) + 4hi + j%4 of query row r.
   l_run = xor32_sum(l_run);
   const float inv_l = 1.0f / l_run;
+  // training: the log-sum-exp of the query's scores (natural log; scores in log2 units are s log2(e))
+  if (a.lse && hi == 0 && qvalid)
+    a.lse[((int64_t)b * a.Hq + hq) * a.S + i] = (m_run + __log2f(l_run)) * 0.6931471805599453f;
   float* Os = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int db = 0; db < 4; db++)

@@ -68,6 +68,7 @@ struct PrefillArgs {
   float q_scale;                // log2(e) / sqrt(D)
   int32_t n_units;              // B * Hkv
   int32_t n_qtiles;             // ceil(S / P)
+  float* lse;                   // [B][Hq][S] natural log of each softmax denominator (training), or null
   double inv_freq_rev[64];
 };
 
@@ -109,6 +110,45 @@ struct Fp8Blocks {
   int32_t n[kFp8MaxTensors];
 };
 
+// Backward of an attention layer (training), no cache, positions 0..S-1.  Sp = S rounded up to 128; the
+// workspace arrays are zero past S (and lse2 +inf), so tiles may run over the end.
+constexpr int32_t kBwdPostBlocks = 512;   // work-groups of the norm/RoPE backward (and dw partials per tensor)
+struct BwdArgs {
+  const uint16_t* q;      // [B][S][Hq][D] bf16
+  const uint16_t* k;      // [B][S][Hkv][D]
+  const uint16_t* v;      // [B][S][Hkv][D]
+  const uint16_t* gate;   // [B][S][Hq][D], null for a global layer
+  const uint16_t* qw;     // [D]
+  const uint16_t* kw;     // [D]
+  const uint16_t* out;    // [B][S][Hq][D] the forward's output
+  const uint16_t* dout;   // [B][S][Hq][D]
+  const float* lse;       // [B][Hq][S] natural log of the softmax denominators
+  uint16_t* dq;           // [B][S][Hq][D] bf16
+  uint16_t* dk;           // [B][S][Hkv][D]
+  uint16_t* dv;           // [B][S][Hkv][D]
+  uint16_t* dgate;        // [B][S][Hq][D], null for a global layer
+  float* dqw;             // [D]
+  float* dkw;             // [D]
+  // workspace
+  uint16_t* qh16;         // [B][Hq][Sp][D] fp16 q_hat * log2(e)/sqrt(D)
+  uint16_t* qt;           // [B][Hq][D][Sp] bf16 q_hat transposed
+  uint16_t* da;           // [B][Hq][Sp][D] bf16 dA
+  uint16_t* dat;          // [B][Hq][D][Sp] bf16 dA transposed
+  float* lse2;            // [B][Hq][Sp] lse * log2(e)
+  float* delta;           // [B][Hq][Sp] dout . out
+  uint16_t* kh16;         // [B][Hkv][Sp][D] fp16 k_hat (bf16 values)
+  uint16_t* kt;           // [B][Hkv][D][Sp] bf16 k_hat transposed
+  float* dqh;             // [B][Hq][Sp][D] sum_j ds_ij k_hat_j
+  float* dkh;             // [B][Hkv][Sp][D] sum_i ds_ij q_hat_i (over the group's heads)
+  float* dw_part;         // [2][kBwdPostBlocks][D]
+  int32_t B, S, Sp, Hq, Hkv, G;
+  int32_t window;         // 0 for a global layer
+  int32_t rot_pairs;
+  float eps;
+  float q_scale;          // log2(e) / sqrt(D)
+  double inv_freq_rev[64];
+};
+
 // One entry per layer of a KV cache, in device memory.
 struct LayerDesc {
   uint16_t* k;
@@ -148,6 +188,11 @@ hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st);
 int32_t fp8_quantize_blocks(int64_t n);   // work-groups launch_fp8_quantize uses for n values
 hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const float* scale, float* partial,
                                hipStream_t st);
+hipError_t launch_bwd_dw_zero(float* dqw, float* dkw, hipStream_t st);   // D = 128 floats each
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_post(const BwdArgs& a, hipStream_t st);
 hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, const Fp8Blocks& nb, hipStream_t st);
 int swa_stream_run_length(int S, int n_units);
 hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t st);

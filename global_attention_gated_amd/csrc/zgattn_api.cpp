@@ -285,8 +285,9 @@ namespace {
 int prefill_common(bool gated, const void* q, const void* k, const void* v, const void* gate, const void* qw,
                    const void* kw, void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
                    int32_t window, int32_t R, double base, float eps, int64_t pos0, zg_kv_cache* cache,
-                   int32_t layer, void* ws, uint64_t ws_bytes, void* stream, bool validate_only = false) {
-  const char* fn = gated ? "swa_prefill" : "global_prefill";
+                   int32_t layer, void* ws, uint64_t ws_bytes, void* stream, bool validate_only = false,
+                   float* lse = nullptr, const char* fn_name = nullptr) {
+  const char* fn = fn_name ? fn_name : (gated ? "swa_prefill" : "global_prefill");
   if (B < 0 || S < 0) return fail(ZG_EINVAL, "%s: negative B or S", fn);
   if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(ZG_EINVAL, "%s: Hq (%d) must be a positive multiple of Hkv (%d)", fn, Hq, Hkv);
   if (D != kHeadDim) return fail(ZG_EUNSUPPORTED, "%s: head dim %d, only 128 is implemented", fn, D);
@@ -340,7 +341,8 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   if (validate_only) return ZG_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rot_pairs = R / 2;
-  if (gated && !cache && G == 4 && window <= 128) {
+  if (lse && cache) return fail(ZG_EINVAL, "%s: the training forward takes no cache", fn);
+  if (gated && !cache && G == 4 && window <= 128 && !lse) {
     // streaming SWA kernel: k_hat computed in its tile loader, no workspace pass
     SwaStreamArgs sa{};
     sa.q = static_cast<const uint16_t*>(q);
@@ -411,6 +413,7 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
   a.n_units = B * Hkv;
   a.n_qtiles = (S + a.P - 1) / a.P;
+  a.lse = lse;
   std::memcpy(a.inv_freq_rev, pa.inv_freq_rev, sizeof a.inv_freq_rev);
   if (!gated && cache) {          // every key from the cache (bf16), absolute positions
     a.kA = ld->k; a.vA = ld->v;
@@ -481,6 +484,169 @@ extern "C" int global_prefill(const void* q, const void* k, const void* v, const
                               int32_t layer, void* workspace, uint64_t workspace_bytes, void* stream) {
   return prefill_common(false, q, k, v, nullptr, q_norm_w, k_norm_w, out, B, S, Hq, Hkv, D, 0, rotary_dims, rope_base,
                         eps, pos0, cache, layer, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------------- training: forward + backward
+extern "C" int swa_prefill_train(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
+                                 const void* k_norm_w, void* out, float* lse, int32_t B, int32_t S, int32_t Hq,
+                                 int32_t Hkv, int32_t D, int32_t window, int32_t rotary_dims, double rope_base,
+                                 float eps, void* workspace, uint64_t workspace_bytes, void* stream) {
+  if (B > 0 && S > 0 && !lse) return fail(ZG_EINVAL, "swa_prefill_train: null lse");
+  return prefill_common(true, q, k, v, gate, q_norm_w, k_norm_w, out, B, S, Hq, Hkv, D, window, rotary_dims, rope_base,
+                        eps, 0, nullptr, 0, workspace, workspace_bytes, stream, false, lse, "swa_prefill_train");
+}
+
+extern "C" int global_prefill_train(const void* q, const void* k, const void* v, const void* q_norm_w,
+                                    const void* k_norm_w, void* out, float* lse, int32_t B, int32_t S, int32_t Hq,
+                                    int32_t Hkv, int32_t D, int32_t rotary_dims, double rope_base, float eps,
+                                    void* workspace, uint64_t workspace_bytes, void* stream) {
+  if (B > 0 && S > 0 && !lse) return fail(ZG_EINVAL, "global_prefill_train: null lse");
+  return prefill_common(false, q, k, v, nullptr, q_norm_w, k_norm_w, out, B, S, Hq, Hkv, D, 0, rotary_dims, rope_base,
+                        eps, 0, nullptr, 0, workspace, workspace_bytes, stream, false, lse, "global_prefill_train");
+}
+
+namespace {
+struct BwdLayout {
+  uint64_t qh16, qt, da, dat, lse2, delta, kh16, kt, dqh, dkh, dw_part, total;
+};
+uint64_t a256(uint64_t x) { return (x + 255) & ~255ull; }
+BwdLayout bwd_layout(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D) {
+  const uint64_t Sp = ((uint64_t)S + 127) / 128 * 128;
+  const uint64_t q2 = (uint64_t)B * Hq * Sp * D * 2, k2 = (uint64_t)B * Hkv * Sp * D * 2;
+  const uint64_t rows = (uint64_t)B * Hq * Sp * 4;
+  BwdLayout l{};
+  uint64_t o = 0;
+  l.qh16 = o; o += a256(q2);
+  l.qt = o; o += a256(q2);
+  l.da = o; o += a256(q2);
+  l.dat = o; o += a256(q2);
+  l.lse2 = o; o += a256(rows);
+  l.delta = o; o += a256(rows);
+  l.kh16 = o; o += a256(k2);
+  l.kt = o; o += a256(k2);
+  l.dqh = o; o += a256(2 * q2);
+  l.dkh = o; o += a256(2 * k2);
+  l.dw_part = o; o += a256(2ull * zg::kBwdPostBlocks * D * 4);
+  l.total = o;
+  return l;
+}
+
+int backward_common(bool gated, const void* q, const void* k, const void* v, const void* gate, const void* qw,
+                    const void* kw, const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* dgate, float* dqw, float* dkw, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                    int32_t window, int32_t R, double base, float eps, void* ws, uint64_t ws_bytes, void* stream) {
+  const char* fn = gated ? "swa_prefill_backward" : "global_prefill_backward";
+  if (B < 0 || S < 0) return fail(ZG_EINVAL, "%s: negative B or S", fn);
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return fail(ZG_EINVAL, "%s: Hq (%d) must be a positive multiple of Hkv (%d)", fn, Hq, Hkv);
+  if (D != kHeadDim) return fail(ZG_EUNSUPPORTED, "%s: head dim %d, only 128 is implemented", fn, D);
+  if (Hq / Hkv != 4) return fail(ZG_EUNSUPPORTED, "%s: GQA group %d, only 4 is implemented", fn, Hq / Hkv);
+  if (gated && window < 1) return fail(ZG_EINVAL, "%s: window must be >= 1", fn);
+  if (R < 0 || R > D || (R & 1)) return fail(ZG_EINVAL, "%s: rotary_dims %d must be even and in 0..%d", fn, R, D);
+  if (!(base > 0.0) || !std::isfinite(base)) return fail(ZG_EINVAL, "%s: rope_base must be positive and finite", fn);
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(ZG_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if ((int64_t)S >= (1ll << 30) || (int64_t)B * Hq * (((int64_t)S + 127) / 128 * 128) * D >= (1ll << 40))
+    return fail(ZG_ERANGE, "%s: problem too large", fn);
+  if (!dqw || !dkw) return fail(ZG_EINVAL, "%s: null norm-weight gradient", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (B == 0 || S == 0) {   // empty: the norm-weight gradients are zero
+    hipError_t e = launch_bwd_dw_zero(dqw, dkw, st);
+    return e == hipSuccess ? ZG_OK : hip_fail(e, "clearing the norm-weight gradients");
+  }
+  if (!q || !k || !v || !qw || !kw || !out || !lse || !dout || !dq || !dk || !dv || (gated && (!gate || !dgate)))
+    return fail(ZG_EINVAL, "%s: null tensor pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(qw) || !aligned16(kw) || !aligned16(out) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse) ||
+      (gated && (!aligned16(gate) || !aligned16(dgate))))
+    return fail(ZG_EINVAL, "%s: tensors must be 16-byte aligned", fn);
+  const BwdLayout L = bwd_layout(B, S, Hq, Hkv, D);
+  if (!ws || !aligned16(ws)) return fail(ZG_EINVAL, "%s: a 16-byte aligned workspace is required", fn);
+  if (ws_bytes < L.total)
+    return fail(ZG_ERANGE, "%s: workspace of %llu bytes < %llu needed", fn, (unsigned long long)ws_bytes,
+                (unsigned long long)L.total);
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.gate = gated ? static_cast<const uint16_t*>(gate) : nullptr;
+  a.qw = static_cast<const uint16_t*>(qw);
+  a.kw = static_cast<const uint16_t*>(kw);
+  a.out = static_cast<const uint16_t*>(out);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.dgate = gated ? static_cast<uint16_t*>(dgate) : nullptr;
+  a.dqw = dqw;
+  a.dkw = dkw;
+  a.qh16 = reinterpret_cast<uint16_t*>(w + L.qh16);
+  a.qt = reinterpret_cast<uint16_t*>(w + L.qt);
+  a.da = reinterpret_cast<uint16_t*>(w + L.da);
+  a.dat = reinterpret_cast<uint16_t*>(w + L.dat);
+  a.lse2 = reinterpret_cast<float*>(w + L.lse2);
+  a.delta = reinterpret_cast<float*>(w + L.delta);
+  a.kh16 = reinterpret_cast<uint16_t*>(w + L.kh16);
+  a.kt = reinterpret_cast<uint16_t*>(w + L.kt);
+  a.dqh = reinterpret_cast<float*>(w + L.dqh);
+  a.dkh = reinterpret_cast<float*>(w + L.dkh);
+  a.dw_part = reinterpret_cast<float*>(w + L.dw_part);
+  a.B = B; a.S = S; a.Sp = (S + 127) / 128 * 128; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
+  a.window = gated ? window : 0;
+  a.rot_pairs = R / 2;
+  a.eps = eps;
+  a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
+  fill_inv_freq(a.inv_freq_rev, R / 2, R, base);
+  hipError_t e;
+  {
+    ScopedTimer tm("bwd_prep", st);
+    e = launch_bwd_prep(a, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "backward prep launch");
+  {
+    ScopedTimer tm("bwd_kv", st);
+    e = launch_bwd_kv(a, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "backward dK/dV launch");
+  {
+    ScopedTimer tm("bwd_q", st);
+    e = launch_bwd_q(a, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "backward dQ launch");
+  {
+    ScopedTimer tm("bwd_post", st);
+    e = launch_bwd_post(a, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "backward norm/RoPE launch");
+  return ZG_OK;
+}
+}  // namespace
+
+extern "C" uint64_t backward_workspace_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (B < 0 || S < 0 || Hq < 0 || Hkv < 0 || D < 0) return 0;
+  return bwd_layout(B, S, Hq, Hkv, D).total;
+}
+
+extern "C" int swa_prefill_backward(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
+                                    const void* k_norm_w, const void* out, const float* lse, const void* dout, void* dq,
+                                    void* dk, void* dv, void* dgate, float* dq_norm_w, float* dk_norm_w, int32_t B,
+                                    int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t window, int32_t rotary_dims,
+                                    double rope_base, float eps, void* workspace, uint64_t workspace_bytes,
+                                    void* stream) {
+  return backward_common(true, q, k, v, gate, q_norm_w, k_norm_w, out, lse, dout, dq, dk, dv, dgate, dq_norm_w,
+                         dk_norm_w, B, S, Hq, Hkv, D, window, rotary_dims, rope_base, eps, workspace, workspace_bytes,
+                         stream);
+}
+
+extern "C" int global_prefill_backward(const void* q, const void* k, const void* v, const void* q_norm_w,
+                                       const void* k_norm_w, const void* out, const float* lse, const void* dout,
+                                       void* dq, void* dk, void* dv, float* dq_norm_w, float* dk_norm_w, int32_t B,
+                                       int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t rotary_dims,
+                                       double rope_base, float eps, void* workspace, uint64_t workspace_bytes,
+                                       void* stream) {
+  return backward_common(false, q, k, v, nullptr, q_norm_w, k_norm_w, out, lse, dout, dq, dk, dv, nullptr, dq_norm_w,
+                         dk_norm_w, B, S, Hq, Hkv, D, 0, rotary_dims, rope_base, eps, workspace, workspace_bytes,
+                         stream);
 }
 
 // ---------------------------------------------------------------------------------- projections, layers

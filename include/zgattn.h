@@ -142,6 +142,48 @@ int hybrid_decode_step(const void* q, const void* k, const void* v, const void* 
                        const void* k_norm_w, void* out, const int64_t* positions, int32_t Hq,
                        int32_t rotary_dims, double rope_base, float eps, zg_kv_cache* cache, void* stream);
 
+/* ---- Training: forward with log-sum-exp, and the backward of an attention layer (no cache, positions 0..S-1).
+ * The forward is swa_prefill / global_prefill that also writes, per (sequence, query head, position), the natural
+ * log of its softmax denominator: lse_i = log sum_j exp(s_ij), s_ij = q_hat_i . k_hat_j / sqrt(D) over the visible
+ * keys.  lse [B][Hq][S] device fp32.  Other arguments and errors as swa_prefill (workspace of
+ * prefill_workspace_bytes). */
+int swa_prefill_train(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
+                      const void* k_norm_w, void* out, float* lse, int32_t B, int32_t S, int32_t Hq, int32_t Hkv,
+                      int32_t D, int32_t window, int32_t rotary_dims, double rope_base, float eps, void* workspace,
+                      uint64_t workspace_bytes, void* stream);
+int global_prefill_train(const void* q, const void* k, const void* v, const void* q_norm_w, const void* k_norm_w,
+                         void* out, float* lse, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t rotary_dims, double rope_base, float eps, void* workspace, uint64_t workspace_bytes,
+                         void* stream);
+
+/* Workspace bytes of the backward: staged q_hat (fp16 and transposed bf16), dA = dout (.) sigmoid(g) (bf16, also
+ * transposed), per-row Delta = dout . out and lse, k_hat (fp16 and transposed bf16), fp32 dq_hat / dk_hat and the
+ * norm-weight partial sums, with S rounded up to 128. */
+uint64_t backward_workspace_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D);
+
+/* Gradients of a gated-SWA layer's output (onedev.kr "How it works": A_SWA(q,k,v) (.) sigmoid(g), with the
+ * QK-RMSNorm and partial RoPE of jaehun.me "How Gated SWA Behaves") with respect to its inputs, given dout = dL/dout.
+ *   inputs as swa_prefill_train, plus out [B][S][Hq][D] and lse [B][Hq][S] from it, and dout [B][S][Hq][D];
+ *   outputs dq [B][S][Hq][D], dk, dv [B][S][Hkv][D], dgate [B][S][Hq][D] (device bf16, written) and
+ *   dq_norm_w, dk_norm_w [D] (device fp32, written: sums over every token and head).
+ * Chain rule: dA = dout (.) sigmoid(g); dgate = dout (.) out (.) (1 - sigmoid(g)); Delta_i = dout_i . out_i;
+ * ds_ij = p_ij (dA_i . v_j - Delta_i); dq_hat = ds k_hat / sqrt(D); dk_hat = ds^T q_hat / sqrt(D) and
+ * dv = p^T dA summed over the query heads of a KV head; then through RoPE and RMSNorm.  The bf16 rounding of
+ * k_hat passes its gradient through unchanged.  Score products in fp16 (as the forward), gradient products in
+ * bf16, fp32 accumulation.  D = 128 and GQA group 4 only.
+ * Errors: EINVAL, EUNSUPPORTED, ERANGE (workspace, size), EHIP. */
+int swa_prefill_backward(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
+                         const void* k_norm_w, const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                         void* dv, void* dgate, float* dq_norm_w, float* dk_norm_w, int32_t B, int32_t S, int32_t Hq,
+                         int32_t Hkv, int32_t D, int32_t window, int32_t rotary_dims, double rope_base, float eps,
+                         void* workspace, uint64_t workspace_bytes, void* stream);
+/* The global layer's backward: as swa_prefill_backward without the gate (dA = dout) and the window. */
+int global_prefill_backward(const void* q, const void* k, const void* v, const void* q_norm_w, const void* k_norm_w,
+                            const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            float* dq_norm_w, float* dk_norm_w, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                            int32_t rotary_dims, double rope_base, float eps, void* workspace, uint64_t workspace_bytes,
+                            void* stream);
+
 /* ---- Projections around the core (onedev.kr "How it works": GatedSWA(h) = o_proj(A_SWA(q,k,v) (.)
  * sigmoid(g_proj(h))), with q/k/v/g projections of the hidden state h).  Plain GEMMs on hipBLASLt. */
 
@@ -237,7 +279,8 @@ const char* zg_last_error(void);
 /* Kernel timer: while enabled, every launch of the main attention kernels records a pair of HIP
  * events on the launch stream.  zg_kernel_timer_read synchronises on the recorded events and returns,
  * for the kernel family `name` ("attn_swa", "attn_global", "decode_global", "decode_swa",
- * "kv_prologue", "decode_merge", "decode_append", "linear", "fp8_quantize"), the summed device time in ms and the launch count
+ * "kv_prologue", "decode_merge", "decode_append", "linear", "fp8_quantize", "bwd_prep", "bwd_kv", "bwd_q",
+ * "bwd_post"), the summed device time in ms and the launch count
  * since the last reset.  Enabling resets the counters. */
 int zg_kernel_timer_enable(int32_t on);
 int zg_kernel_timer_read(const char* name, double* total_ms, int64_t* launches);

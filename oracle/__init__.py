@@ -312,7 +312,7 @@ def _rmsnorm_backward(x, w, dy, eps: float):
 
 
 def prefill_layer_backward(q, k, v, gate, wq, wk, dout, *, window: int | None, rotary_dims: int, base: float,
-                           eps: float) -> dict:
+                           eps: float, delta_from_bf16_out: bool = False) -> dict:
     """Gradients of one attention layer's output (prefill_layer without a cache, positions 0..S-1) with respect
     to its inputs, given dout = dL/d(out) [B,S,Hq,D].  Returns float64 arrays: dq [B,S,Hq,D], dk, dv [B,S,Hkv,D],
     dgate [B,S,Hq,D] (None for a global layer), dwq, dwk [D]; and the forward's out and lse [B,S,Hq] (natural log
@@ -324,7 +324,11 @@ def prefill_layer_backward(q, k, v, gate, wq, wk, dout, *, window: int | None, r
       s = q_hat k_hat^T / sqrt(D):       dq_hat = ds k_hat / sqrt(D),  dk_hat = ds^T q_hat / sqrt(D)
       A = p v:                           dv = p^T dA
     summed over the query heads that share a KV head; then through RoPE (its transpose) and RMSNorm.  The bf16
-    rounding of k_hat (the cache form keys are read in) passes its gradient through unchanged."""
+    rounding of k_hat (the cache form keys are read in) passes its gradient through unchanged.
+
+    rowsum(p (.) dp) equals dout . out; delta_from_bf16_out=True forms it from the layer's bf16 output instead, as
+    a backward that is handed the bf16 output must (the exact result is the default; the variant measures what
+    that rounding alone costs)."""
     q = np.asarray(q)
     B, S, Hq, D = q.shape
     Hkv = np.asarray(k).shape[2]
@@ -365,7 +369,11 @@ def prefill_layer_backward(q, k, v, gate, wq, wk, dout, *, window: int | None, r
                 dA = do[b, :, h] * sg
                 dg[b, :, h] = do[b, :, h] * A * sg * (1.0 - sg)
             dp = dA @ vf[b, :, kh].T
-            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            if delta_from_bf16_out:
+                delta = np.sum(do[b, :, h] * bf16_to_f64(round_bf16(out[b, :, h])), axis=1, keepdims=True)
+            else:
+                delta = np.sum(p * dp, axis=1, keepdims=True)
+            ds = p * (dp - delta)
             dqhat[b, :, h] = ds @ khat[b, :, kh] * scale
             dkhat[b, :, kh] += ds.T @ qhat[b, :, h] * scale
             dv[b, :, kh] += p.T @ dA

@@ -31,6 +31,8 @@ TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_GATE = 0, 1, 2, 3
 TENSOR_WQ, TENSOR_WK, TENSOR_CACHE_K, TENSOR_CACHE_V = 4, 5, 6, 7
 # the hidden state and the projection weights around the core (q, k, v, g, o)
 TENSOR_H, TENSOR_PQ, TENSOR_PK, TENSOR_PV, TENSOR_PG, TENSOR_PO = 8, 9, 10, 11, 12, 13
+# the output gradient of the backward
+TENSOR_DOUT = 14
 
 
 def _mix(z: np.ndarray) -> np.ndarray:

@@ -137,3 +137,43 @@ def test_linear_rejects_bad_arguments(zg):
     assert lib.linear_bf16(16, 24, 16, 10, 4, 4, None) == 1
     assert lib.linear_bf16(16, 16, 16, 0, 4, 4, None) == 0     # no tokens: no-op
     assert _layer(zg, S=0) == 0
+
+
+def test_backward_workspace_bytes_closed_form(zg):
+    B, S, Hq, Hkv, D = 2, 300, 32, 8, 128
+    Sp = (S + 127) // 128 * 128
+    a = lambda n: (n + 255) // 256 * 256
+    q2, k2, rows = B * Hq * Sp * D * 2, B * Hkv * Sp * D * 2, B * Hq * Sp * 4
+    want = 4 * a(q2) + 2 * a(rows) + 2 * a(k2) + a(2 * q2) + a(2 * k2) + a(2 * 512 * D * 4)
+    assert zg.backward_workspace_bytes(B, S, Hq, Hkv, D) == want
+
+
+def _bwd(zg, gated=True, **over):
+    a = dict(B=1, S=4, Hq=4, Hkv=1, D=128, W=128, R=42, base=1e4, eps=1e-6, ws=256, ws_bytes=1 << 30, dqw=16, dkw=16,
+             ptr=16)
+    a.update(over)
+    p = a["ptr"]
+    if gated:
+        return zg._lib.swa_prefill_backward(p, p, p, p, p, p, p, p, p, p, p, p, p, a["dqw"], a["dkw"], a["B"], a["S"],
+                                            a["Hq"], a["Hkv"], a["D"], a["W"], a["R"], a["base"], a["eps"], a["ws"],
+                                            a["ws_bytes"], None)
+    return zg._lib.global_prefill_backward(p, p, p, p, p, p, p, p, p, p, p, a["dqw"], a["dkw"], a["B"], a["S"], a["Hq"],
+                                           a["Hkv"], a["D"], a["R"], a["base"], a["eps"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("gated", [True, False])
+@pytest.mark.parametrize("over,status", [
+    (dict(Hq=8, Hkv=1), 2), (dict(D=64), 2), (dict(Hq=6, Hkv=4), 1), (dict(R=43), 1), (dict(eps=-1.0), 1),
+    (dict(ptr=None), 1), (dict(dqw=None), 1), (dict(ws_bytes=1024), 3), (dict(ws=None), 1), (dict(ptr=8), 1)])
+def test_backward_rejects_bad_arguments_before_enqueueing(zg, gated, over, status):
+    assert _bwd(zg, gated, **over) == status, zg._lib.zg_last_error()
+
+
+def test_swa_backward_rejects_window_zero(zg):
+    assert _bwd(zg, True, W=0) == zg.ZG_EINVAL
+
+
+def test_training_forward_needs_lse(zg):
+    p = 16
+    rc = zg._lib.swa_prefill_train(p, p, p, p, p, p, p, None, 1, 4, 4, 1, 128, 128, 42, 1e4, 1e-6, 256, 1 << 30, None)
+    assert rc == zg.ZG_EINVAL and b"null lse" in zg._lib.zg_last_error()

@@ -1,0 +1,89 @@
+"""GPU parity of the training path: the forward's log-sum-exp and the backward of a gated-SWA or global layer
+(dq, dk, dv, dgate and the two norm-weight gradients), against the fp64 oracle's exact gradients on the same seeded
+inputs.
+
+Bar of the backward, per gradient X against the exact X_ref (elementwise, then the mean):
+    |err| <= 2 |D_X| + 2^-7 |X_ref| + 0.1 R_X,        mean |err| <= 0.005 R_X
+with R_X = rms(X_ref) (dv's rms where X_ref is identically zero: one visible key), and D_X the change in the
+exact gradient when Delta_i = dout_i . out_i is formed from the bf16 output, as this backward (the standard
+flash-attention form) must: out is handed over in bf16, 2^-9 relative per element.  The other terms: the bf16
+rounding of every result (2^-9 |X|, 2^-7 leaves margin), and the bf16 operands of the gradient products (dA, P,
+dS, q_hat: 2^-9 each, fp32 accumulation), whose errors scale with the summed terms rather than with the result:
+ds_ij = p_ij (dp_ij - Delta_i) subtracts two values of size ~sqrt(D) |dout| |v| to get a much smaller one.
+Measured: max 0.3-2.1 of (2|D_X| + 2^-7|X_ref| + 0.01 R_X), mean 0.1-0.3% of R_X.  A missed tile, wrong mask,
+head or scale errs by ~R_X on whole rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _inputs import Layer, compare, to_dev, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def zg():
+    import torch
+    assert torch.cuda.is_available()
+    import global_attention_gated_amd as m
+    return m
+
+
+def _problem(seed, gated, B, S, Hq, Hkv, W):
+    L = Layer(seed, 1, B, S, Hq, Hkv, gated=gated)
+    dout = synth.normal_bf16(seed, 1, synth.TENSOR_DOUT, (B, S, Hq, 128))
+    kw = dict(window=W if gated else None, rotary_dims=42, base=1e4, eps=1e-6)
+    ref = oracle.prefill_layer_backward(L.q, L.k, L.v, L.gate, L.wq, L.wk, dout, **kw)
+    ref16 = oracle.prefill_layer_backward(L.q, L.k, L.v, L.gate, L.wq, L.wk, dout, delta_from_bf16_out=True, **kw)
+    return L, dout, ref, ref16
+
+
+def _check(g, ref, ref16, gated, tag):
+    names = [("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dq_norm_w", "dwq"), ("dk_norm_w", "dwk")]
+    if gated:
+        names.append(("dgate", "dgate"))
+    rms_dv = float(np.sqrt(np.mean(ref["dv"] ** 2)))
+    for gn, rn in names:
+        got = to_host_f64(g[gn])
+        r, r16 = ref[rn], ref16[rn]
+        assert np.all(np.isfinite(got)), f"{tag} {gn}: non-finite"
+        err = np.abs(got - r)
+        dlt = np.abs(r16 - r)
+        rms = float(np.sqrt(np.mean(r ** 2)))
+        R = rms if rms > 0.01 * rms_dv else rms_dv
+        bound = 2 * dlt + 2.0 ** -7 * np.abs(r) + 0.1 * R
+        print(f"{tag} {gn}: max_abs {err.max():.3e} mean_abs {err.mean():.3e} R {R:.3e} "
+              f"max err/bound {np.max(err / bound):.3f} mean/R {err.mean() / R:.2e}")
+        assert np.all(err <= bound), f"{tag} {gn}: max err/bound {np.max(err / bound):.3f}"
+        assert err.mean() <= 0.005 * R, f"{tag} {gn}: mean_abs {err.mean():.3e} > {0.005 * R:.3e}"
+
+
+CASES = [(True, 1, 300, 8, 2, 128), (False, 1, 257, 8, 2, 0), (True, 2, 129, 4, 1, 16), (True, 1, 33, 4, 1, 128),
+         (False, 1, 1, 4, 1, 0), (True, 1, 1, 4, 1, 128)]
+
+
+@pytest.mark.parametrize("gated,B,S,Hq,Hkv,W", CASES)
+def test_backward_alone_matches_oracle(zg, gated, B, S, Hq, Hkv, W):
+    """The backward fed the oracle's own out (rounded to bf16) and lse (float32)."""
+    import torch
+    L, dout, ref, ref16 = _problem(61, gated, B, S, Hq, Hkv, W)
+    out = to_dev(oracle.round_bf16(ref["out"]))
+    lse = torch.from_numpy(np.ascontiguousarray(ref["lse"].transpose(0, 2, 1)).astype(np.float32)).cuda()
+    g = zg.prefill_backward(L.dq, L.dk, L.dv, L.dgate, L.dwq, L.dwk, out, lse, to_dev(dout), window=W,
+                            rotary_dims=42, rope_base=1e4, eps=1e-6)
+    _check(g, ref, ref16, gated, f"alone {'swa' if gated else 'global'} B{B} S{S}")
+
+
+@pytest.mark.parametrize("gated,B,S,Hq,Hkv,W", CASES)
+def test_training_forward_backward_matches_oracle(zg, gated, B, S, Hq, Hkv, W):
+    """The training pipeline: the GPU forward's out and lse feed the GPU backward."""
+    L, dout, ref, ref16 = _problem(61, gated, B, S, Hq, Hkv, W)
+    out, lse = zg.prefill_train(L.dq, L.dk, L.dv, L.dgate, L.dwq, L.dwk, window=W, rotary_dims=42, rope_base=1e4,
+                                eps=1e-6)
+    compare(to_host_f64(out), ref["out"], "training forward out")
+    compare(lse.detach().cpu().numpy().transpose(0, 2, 1).astype(np.float64), ref["lse"], "training forward lse")
+    g = zg.prefill_backward(L.dq, L.dk, L.dv, L.dgate, L.dwq, L.dwk, out, lse, to_dev(dout), window=W,
+                            rotary_dims=42, rope_base=1e4, eps=1e-6)
+    _check(g, ref, ref16, gated, f"train {'swa' if gated else 'global'} B{B} S{S}")
