@@ -16,10 +16,10 @@
 //   bwd_prep_kernel  per 64-token block of one head: q_hat (fp16, pre-scaled by log2(e)/sqrt(D), the forward's
 //                    score operand) and q_hat^T (bf16); dA and dA^T (bf16), Delta, lse in log2 units, dgate;
 //                    for the KV heads k_hat (fp16) and k_hat^T (bf16).  Transposes go through LDS.
-//   bwd_kv_kernel    key-centric: a work-group owns 128 keys of one (sequence, KV head), one wave per 32 keys, and
-//                    walks the query tiles that see them for each head of the group; dV^T = dA^T P and
-//                    dK_hat^T = Q_hat^T dS accumulate in registers (MFMA 32x32x16, scores in fp16 as the forward,
-//                    gradient products in bf16 for their range).
+//   bwd_kv_kernel    key-centric, in two launches (dV, then dK): a work-group owns 128 keys of one (sequence, KV
+//                    head), one wave per 32 keys, and walks the query tiles that see them for each head of the
+//                    group; dV^T = dA^T P or dK_hat^T = Q_hat^T dS accumulates in registers (MFMA 32x32x16, scores
+//                    in fp16 as the forward, gradient products in bf16 for their range).
 //   bwd_q_kernel     query-centric: a work-group owns 32 positions of the 4 heads of a group (one wave each) and
 //                    walks the key tiles they see: dQ_hat^T = K_hat^T dS^T.
 //   bwd_post_kernel  RoPE transpose and RMSNorm backward per (token, head) row; bf16 dq / dk and deterministic
@@ -34,7 +34,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16v8;
 
 constexpr int kT = 32;          // query / key tile of the MFMA kernels
 constexpr int kRowS = 136;      // LDS row stride (halves) of [32][128] tiles: 16-byte pad
-constexpr int kTrS = 40;        // LDS row stride (halves) of [128][32] transposed tiles
+constexpr int kTrS = 36;        // LDS row stride (halves) of [128][32] transposed tiles: 72 B, so 16 lanes'
+                                // 8-byte reads at consecutive rows cover all 128 bytes of the banks once
 constexpr int kPrepTok = 64;    // tokens per prep work-group
 constexpr int kPrepTS = 72;     // LDS row stride (halves) of the prep transpose tiles [128][64]
 
@@ -157,16 +158,28 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------ dK, dV
+// 8-byte halves of a 16-byte chunk into a transposed tile row (its rows are 8- but not 16-byte aligned)
+__device__ __forceinline__ void st_tr(uint16_t* dst, const uint4& v) {
+  reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+  reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+}
+
+// One query tile of the key-centric kernels.  The dV kernel needs q_hat' (scores) and dA^T; the dK kernel
+// q_hat' (scores), dA (dP) and q_hat^T.
 struct KvStage {
-  uint16_t qs[kT * kRowS];       // q_hat' fp16 [32 queries][128]
-  uint16_t das[kT * kRowS];      // dA bf16 [32][128]
-  uint16_t qts[kHeadDim * kTrS];   // q_hat^T bf16 [128][32]
-  uint16_t dats[kHeadDim * kTrS];  // dA^T bf16 [128][32]
+  uint16_t qs[kT * kRowS];         // q_hat' fp16 [32 queries][128]
+  uint16_t xs[kT * kRowS];         // dK: dA bf16 [32][128]
+  uint16_t xts[kHeadDim * kTrS];   // dV: dA^T, dK: q_hat^T, bf16 [128][32]
   float lse2[kT];
   float dl[kT];
 };
 
-__global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs a) {
+// Key-centric: a work-group owns 128 keys of one (sequence, KV head), one wave per 32 keys, and walks the query
+// tiles that see them for each head of the group.  DK = false: dV^T += dA^T P.  DK = true: dK_hat^T +=
+// q_hat^T dS with dS = P (dP - Delta), dP = dA V^T.  Every MFMA takes one operand from LDS and the other from
+// registers (the wave's key rows, or P / dS from the C registers), so two waves per SIMD fit.
+template <bool DK>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_kv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) KvStage st[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int n_units = a.B * a.Hkv;
@@ -177,23 +190,24 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs a) {
   const int j0 = jb0 + 32 * wave;        // this wave's keys j0 .. j0+31
   const int key = j0 + l32;              // this lane's key (MFMA column)
 
-  // preload this lane's key row: k_hat fp16 (score operand) and v bf16 (dP operand), K-steps of 16 dims
-  uint4 kf[8], vf[8];
+  // this lane's key row: k_hat fp16 (score operand) and, for dK, v bf16 (dP operand); K-steps of 16 dims
+  uint4 kf[8], vf[DK ? 8 : 1];
   {
     const uint16_t* kr = a.kh16 + ((int64_t)unit * a.Sp + key) * kHeadDim + 8 * hi;
-    const int kc = min(key, a.S - 1);
-    const uint16_t* vr = a.v + (((int64_t)b * a.S + kc) * a.Hkv + kvh) * kHeadDim + 8 * hi;
 #pragma unroll
-    for (int t = 0; t < 8; t++) {
-      kf[t] = *reinterpret_cast<const uint4*>(kr + 16 * t);
-      vf[t] = *reinterpret_cast<const uint4*>(vr + 16 * t);
+    for (int t = 0; t < 8; t++) kf[t] = *reinterpret_cast<const uint4*>(kr + 16 * t);
+    if constexpr (DK) {
+      const int kc = min(key, a.S - 1);
+      const uint16_t* vr = a.v + (((int64_t)b * a.S + kc) * a.Hkv + kvh) * kHeadDim + 8 * hi;
+#pragma unroll
+      for (int t = 0; t < 8; t++) vf[t] = *reinterpret_cast<const uint4*>(vr + 16 * t);
     }
   }
-  floatx16 dv[4], dk[4];
+  floatx16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; db++)
 #pragma unroll
-    for (int j = 0; j < 16; j++) dv[db][j] = dk[db][j] = 0.f;
+    for (int j = 0; j < 16; j++) acc[db][j] = 0.f;
 
   // query tiles that see some key of the work-group, per head
   const int jb_last = min(jb0 + 127, a.S - 1);
@@ -201,11 +215,11 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs a) {
   const int qt0 = jb0 / kT, qt1 = (q_end + kT - 1) / kT;
   const int ntiles = max(qt1 - qt0, 0);
   const int n_it = ntiles * a.G;
-  // this wave's visible queries [j0, wq_end)
-  const int wq_end = swa ? min(a.S, j0 + 31 + a.window) : a.S;
+  const int wq_end = swa ? min(a.S, j0 + 31 + a.window) : a.S;   // this wave's visible queries [j0, wq_end)
 
-  // staging roles: 2 x 16-byte chunks of each of the four tiles per thread, plus lse / Delta
-  uint4 pre[8];
+  // staging: 2 x 16-byte chunks per tile per thread, plus lse / Delta
+  constexpr int NPRE = DK ? 6 : 4;
+  uint4 pre[NPRE];
   float pre_f = 0.f;
   auto load_stage = [&](int it) {
     const int hq = kvh * a.G + it / ntiles;
@@ -217,13 +231,12 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs a) {
       const int r = cidx >> 4, cc = cidx & 15;            // row-major tiles: row r, chunk cc
       const int64_t ro = (bh * a.Sp + q0 + r) * kHeadDim + 8 * cc;
       pre[k] = *reinterpret_cast<const uint4*>(a.qh16 + ro);
-      pre[2 + k] = *reinterpret_cast<const uint4*>(a.da + ro);
       const int d = cidx >> 2, part = cidx & 3;           // transposed tiles: dim d, 8 tokens
       const int64_t to = (bh * kHeadDim + d) * a.Sp + q0 + 8 * part;
-      pre[4 + k] = *reinterpret_cast<const uint4*>(a.qt + to);
-      pre[6 + k] = *reinterpret_cast<const uint4*>(a.dat + to);
+      pre[2 + k] = *reinterpret_cast<const uint4*>((DK ? a.qt : a.dat) + to);
+      if constexpr (DK) pre[4 + k] = *reinterpret_cast<const uint4*>(a.da + ro);
     }
-    if (tid < 64) pre_f = (tid < 32 ? a.lse2 : a.delta)[bh * a.Sp + q0 + (tid & 31)];
+    if (tid < (DK ? 64 : 32)) pre_f = (tid < 32 ? a.lse2 : a.delta)[bh * a.Sp + q0 + (tid & 31)];
   };
   auto store_stage = [&](int buf) {
     KvStage& s = st[buf];
@@ -232,13 +245,12 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs a) {
       const int cidx = tid + 256 * k;
       const int r = cidx >> 4, cc = cidx & 15;
       *reinterpret_cast<uint4*>(&s.qs[r * kRowS + 8 * cc]) = pre[k];
-      *reinterpret_cast<uint4*>(&s.das[r * kRowS + 8 * cc]) = pre[2 + k];
       const int d = cidx >> 2, part = cidx & 3;
-      *reinterpret_cast<uint4*>(&s.qts[d * kTrS + 8 * part]) = pre[4 + k];
-      *reinterpret_cast<uint4*>(&s.dats[d * kTrS + 8 * part]) = pre[6 + k];
+      st_tr(&s.xts[d * kTrS + 8 * part], pre[2 + k]);
+      if constexpr (DK) *reinterpret_cast<uint4*>(&s.xs[r * kRowS + 8 * cc]) = pre[4 + k];
     }
     if (tid < 32) s.lse2[tid] = pre_f;
-    else if (tid < 64) s.dl[tid - 32] = pre_f;
+    else if (DK && tid < 64) s.dl[tid - 32] = pre_f;
   };
 
   auto compute = [&](int buf, int it) {
@@ -252,34 +264,39 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs a) {
     for (int t = 0; t < 8; t++) {
       const uint4 qa = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 8 * hi]);
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(qa), as_half8(kf[t]), sacc, 0, 0, 0);
-      const uint4 da = *reinterpret_cast<const uint4*>(&s.das[l32 * kRowS + 16 * t + 8 * hi]);
-      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16v8(da), as_bf16v8(vf[t]), dpacc, 0, 0, 0);
+      if constexpr (DK) {
+        const uint4 da = *reinterpret_cast<const uint4*>(&s.xs[l32 * kRowS + 16 * t + 8 * hi]);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16v8(da), as_bf16v8(vf[t]), dpacc, 0, 0, 0);
+      }
     }
-    // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key.  P and dS replace S and dP.
+    // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key.  P (dV) or dS (dK) replaces S.
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int qr = 8 * (j >> 2) + 4 * hi + (j & 3);
-      const int qi = q0 + qr;
-      const bool vis = qi < a.S && key <= qi && (!swa || qi - key < a.window);
-      const float pj = vis ? __builtin_amdgcn_exp2f(sacc[j] - s.lse2[qr]) : 0.f;
-      sacc[j] = pj;
-      dpacc[j] = pj * (dpacc[j] - s.dl[qr]);
-    }
-    float pv[16], sv[16];
+    for (int jq = 0; jq < 4; jq++) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&s.lse2[8 * jq + 4 * hi]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      float dlv[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (DK) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&s.dl[8 * jq + 4 * hi]);
+        dlv[0] = d4.x; dlv[1] = d4.y; dlv[2] = d4.z; dlv[3] = d4.w;
+      }
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      pv[j] = sacc[j];
-      sv[j] = dpacc[j];
+      for (int e = 0; e < 4; e++) {
+        const int j = 4 * jq + e;
+        const int qi = q0 + 8 * jq + 4 * hi + e;
+        const bool vis = qi < a.S && key <= qi && (!swa || qi - key < a.window);
+        const float pj = vis ? __builtin_amdgcn_exp2f(sacc[j] - lv[e]) : 0.f;
+        sacc[j] = DK ? pj * (dpacc[j] - dlv[e]) : pj;
+      }
     }
+    float xv[16];
+#pragma unroll
+    for (int j = 0; j < 16; j++) xv[j] = sacc[j];
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-      const bf16v8 pb = c8_to_bf16(pv + 8 * t);
-      const bf16v8 sb = c8_to_bf16(sv + 8 * t);
+      const bf16v8 xb = c8_to_bf16(xv + 8 * t);
 #pragma unroll
-      for (int db = 0; db < 4; db++) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.dats, 32 * db + l32, t, hi), pb, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.qts, 32 * db + l32, t, hi), sb, dk[db], 0, 0, 0);
-      }
+      for (int db = 0; db < 4; db++)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.xts, 32 * db + l32, t, hi), xb, acc[db], 0, 0, 0);
     }
   };
 
@@ -299,17 +316,20 @@ __global__ void __launch_bounds__(256) bwd_kv_kernel(BwdArgs a) {
 
   // outputs: C layout reg j of block db is dim 32db + 8(j/4) + 4hi + j%4 of this lane's key
   if (key < a.S) {
-    uint16_t* dvr = a.dv + (((int64_t)b * a.S + key) * a.Hkv + kvh) * kHeadDim;
-    float* dkr = a.dkh + ((int64_t)unit * a.Sp + key) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; db++)
 #pragma unroll
       for (int jq = 0; jq < 4; jq++) {
         const int d = 32 * db + 8 * jq + 4 * hi;
-        *reinterpret_cast<uint2*>(dvr + d) = make_uint2(pack_bf16(dv[db][4 * jq], dv[db][4 * jq + 1]),
-                                                        pack_bf16(dv[db][4 * jq + 2], dv[db][4 * jq + 3]));
-        *reinterpret_cast<float4*>(dkr + d) = make_float4(dk[db][4 * jq], dk[db][4 * jq + 1], dk[db][4 * jq + 2],
-                                                          dk[db][4 * jq + 3]);
+        if constexpr (DK) {
+          float* dkr = a.dkh + ((int64_t)unit * a.Sp + key) * kHeadDim;
+          *reinterpret_cast<float4*>(dkr + d) = make_float4(acc[db][4 * jq], acc[db][4 * jq + 1],
+                                                            acc[db][4 * jq + 2], acc[db][4 * jq + 3]);
+        } else {
+          uint16_t* dvr = a.dv + (((int64_t)b * a.S + key) * a.Hkv + kvh) * kHeadDim;
+          *reinterpret_cast<uint2*>(dvr + d) = make_uint2(pack_bf16(acc[db][4 * jq], acc[db][4 * jq + 1]),
+                                                          pack_bf16(acc[db][4 * jq + 2], acc[db][4 * jq + 3]));
+        }
       }
   }
 }
@@ -321,7 +341,7 @@ struct QStage {
   uint16_t kts[kHeadDim * kTrS];   // k_hat^T bf16 [128][32]
 };
 
-__global__ void __launch_bounds__(256) bwd_q_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) bwd_q_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) QStage st[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int n_units = a.B * a.Hkv;
@@ -381,7 +401,7 @@ __global__ void __launch_bounds__(256) bwd_q_kernel(BwdArgs a) {
       *reinterpret_cast<uint4*>(&s.ks[r * kRowS + 8 * cc]) = pre[k];
       *reinterpret_cast<uint4*>(&s.vs[r * kRowS + 8 * cc]) = pre[2 + k];
       const int d = cidx >> 2, part = cidx & 3;
-      *reinterpret_cast<uint4*>(&s.kts[d * kTrS + 8 * part]) = pre[4 + k];
+      st_tr(&s.kts[d * kTrS + 8 * part], pre[4 + k]);
     }
   };
   auto compute = [&](int buf, int it) {
@@ -538,7 +558,11 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_kv_kernel, dim3(a.B * a.Hkv * ((a.S + 127) / 128)), dim3(256), 0, st, a);
+  const dim3 grid(a.B * a.Hkv * ((a.S + 127) / 128));
+  hipLaunchKernelGGL(bwd_kv_kernel<false>, grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_kv_kernel<true>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
