@@ -384,6 +384,74 @@ def prefill_layer_backward(q, k, v, gate, wq, wk, dout, *, window: int | None, r
     return {"dq": dq, "dk": dk, "dv": dv, "dgate": dg, "dwq": dwq, "dwk": dwk, "out": out, "lse": lse}
 
 
+def prefill_layer_backward_rows(q, k, v, gate, wq, wk, dout, *, window: int | None, rotary_dims: int, base: float,
+                                eps: float, b: int, kv_head: int, query_rows, key_rows, block: int = 512) -> dict:
+    """prefill_layer_backward at full size, for one (sequence b, KV head) on sampled rows: the gradients of the
+    group's query heads at query_rows (dq, dgate [n_q, G, D]) and of the KV head at key_rows (dk, dv [n_k, D]).
+    Each query row's scores, softmax, output and Delta are formed whole, exactly as in prefill_layer_backward; rows
+    are taken `block` at a time only to bound memory, and the key-side sums add every row block's terms.  Each
+    result comes twice: exact, and with Delta from the bf16 output ("*_d16")."""
+    q = np.asarray(q)
+    B, S, Hq, D = q.shape
+    Hkv = np.asarray(k).shape[2]
+    G = Hq // Hkv
+    heads = list(range(kv_head * G, (kv_head + 1) * G))
+    pos = np.arange(S, dtype=np.int64)
+    qhat = qk_prologue(q[b][:, heads], pos[:, None], wq, eps, rotary_dims, base)             # [S, G, D]
+    khat = cache_key(qk_prologue(np.asarray(k)[b][:, kv_head], pos, wk, eps, rotary_dims, base))   # [S, D]
+    vf = _as_f64(np.asarray(v)[b][:, kv_head])
+    gf = None if gate is None else _as_f64(np.asarray(gate)[b][:, heads])
+    do = _as_f64(np.asarray(dout)[b][:, heads])
+    qr = np.asarray(query_rows, dtype=np.int64)
+    kr = np.asarray(key_rows, dtype=np.int64)
+    scale = 1.0 / np.sqrt(D)
+    res = {n: np.zeros((len(qr), G, D)) for n in ("dqhat", "dqhat_d16", "dgate")}
+    for n in ("dkhat", "dkhat_d16", "dv"):
+        res[n] = np.zeros((len(kr), D))
+    for r0 in range(0, S, block):
+        r1 = min(S, r0 + block)
+        c0 = 0 if window is None or window <= 0 else max(0, r0 - window + 1)
+        i = pos[r0:r1, None]
+        j = pos[None, c0:r1]
+        vis = j <= i
+        if window is not None and window > 0:
+            vis &= (i - j) < window
+        kin = (kr >= c0) & (kr < r1)
+        qin = (qr >= r0) & (qr < r1)
+        for g in range(G):
+            sc = np.where(vis, (qhat[r0:r1, g] @ khat[c0:r1].T) * scale, -np.inf)
+            m = sc.max(axis=1, keepdims=True)
+            e = np.exp(sc - m)
+            p = e / e.sum(axis=1, keepdims=True)
+            A = p @ vf[c0:r1]
+            if gf is None:
+                out, dA = A, do[r0:r1, g]
+            else:
+                sg = 1.0 / (1.0 + np.exp(-gf[r0:r1, g]))
+                out, dA = A * sg, do[r0:r1, g] * sg
+                res["dgate"][qin, g] = (do[r0:r1, g] * A * sg * (1.0 - sg))[qr[qin] - r0]
+            delta = {"": np.sum(p * (dA @ vf[c0:r1].T), axis=1, keepdims=True),
+                     "_d16": np.sum(do[r0:r1, g] * bf16_to_f64(round_bf16(out)), axis=1, keepdims=True)}
+            if kin.any():
+                jj = kr[kin] - c0
+                dpJ = dA @ vf[kr[kin]].T                       # [rows, nJ]
+                res["dv"][kin] += p[:, jj].T @ dA
+                for sfx, dl in delta.items():
+                    res["dkhat" + sfx][kin] += (p[:, jj] * (dpJ - dl)).T @ qhat[r0:r1, g] * scale
+            if qin.any():
+                ii = qr[qin] - r0
+                dpI = dA[ii] @ vf[c0:r1].T
+                for sfx, dl in delta.items():
+                    res["dqhat" + sfx][qin, g] = (p[ii] * (dpI - dl[ii])) @ khat[c0:r1] * scale
+    out = {"dv": res["dv"], "dgate": None if gf is None else res["dgate"]}
+    for sfx in ("", "_d16"):
+        dqn = _rope_transpose(res["dqhat" + sfx], qr[:, None], rotary_dims, base)
+        out["dq" + sfx], _ = _rmsnorm_backward(q[b][qr][:, heads], wq, dqn, eps)
+        dkn = _rope_transpose(res["dkhat" + sfx], kr, rotary_dims, base)
+        out["dk" + sfx], _ = _rmsnorm_backward(np.asarray(k)[b][kr, kv_head], wk, dkn, eps)
+    return out
+
+
 # ---------------------------------------------------------------------------- projections around the core
 def linear(x, w) -> np.ndarray:
     """A linear layer's forward y = x W^T in float64: x [..., K], w [N, K] (W stored out x in)."""

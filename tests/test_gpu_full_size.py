@@ -257,3 +257,53 @@ def test_chunked_prefill_262144_in_16384_chunks(zg):
             compare(got[:, kvh * G:(kvh + 1) * G], ref, f"262144-token chunked prefill layer {layer} kvh={kvh}")
     cache.close()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_backward_1x16384_sampled(zg, gated):
+    """Training forward and backward at 1 x 16384, 32 query / 8 KV heads (the backward benchmark's launch
+    configuration): sampled query rows (dq, dgate) and key rows (dk, dv) of one KV head's group against the
+    row-sampled oracle, to the bar of test_gpu_backward (2 |D_X| + 2^-7 |X_ref| + 0.1 R_X, mean 0.005 R_X)."""
+    import torch
+    seed, layer, S, Hq, Hkv, kvh = 1009, 2 if gated else 6, 16384, 32, 8, 5
+    G = Hq // Hkv
+    L = dev_layer(seed, layer, 1, S, Hq, Hkv, gated)
+    dout = torch.empty((1, S, Hq, D), dtype=torch.bfloat16, device="cuda")
+    synth.fill_device(dout.data_ptr(), seed, layer, synth.TENSOR_DOUT, 1, S * Hq * D, S * Hq * D, 0, S * Hq * D)
+    out, lse = zg.prefill_train(L["q"], L["k"], L["v"], L.get("gate"), L["wq"], L["wk"], window=W, rotary_dims=42,
+                                rope_base=1e4, eps=1e-6)
+    g = zg.prefill_backward(L["q"], L["k"], L["v"], L.get("gate"), L["wq"], L["wk"], out, lse, dout, window=W,
+                            rotary_dims=42, rope_base=1e4, eps=1e-6)
+    rng = np.random.default_rng(3)
+    qr = np.unique(np.concatenate([[0, 1, 31, 127, 128, 4095, 8191, S - 1], rng.integers(0, S, 24)]))
+    kr = np.unique(np.concatenate([[0, 1, 32, 127, 128, 8192, S - 2, S - 1], rng.integers(0, S, 24)]))
+    heads = np.arange(kvh * G, (kvh + 1) * G)
+    tok = np.arange(S)
+
+    def host(tid, H, hs):
+        idx = ((tok[:, None, None] * H + hs[None, :, None]) * D + np.arange(D)[None, None, :])
+        return synth.normal_bf16_at(seed, layer, tid, idx)[None]              # [1, S, len(hs), D]
+
+    q, gt, do = host(synth.TENSOR_Q, Hq, heads), (host(synth.TENSOR_GATE, Hq, heads) if gated else None), \
+        host(synth.TENSOR_DOUT, Hq, heads)
+    k, v = host(synth.TENSOR_K, Hkv, np.array([kvh])), host(synth.TENSOR_V, Hkv, np.array([kvh]))
+    ref = oracle.prefill_layer_backward_rows(q, k, v, gt, L["wq_bits"], L["wk_bits"], do, window=W if gated else None,
+                                             rotary_dims=42, base=1e4, eps=1e-6, b=0, kv_head=0, query_rows=qr,
+                                             key_rows=kr)
+    got = {"dq": to_host_f64(g["dq"][0, qr][:, heads]), "dk": to_host_f64(g["dk"][0, kr, kvh]),
+           "dv": to_host_f64(g["dv"][0, kr, kvh])}
+    if gated:
+        got["dgate"] = to_host_f64(g["dgate"][0, qr][:, heads])
+    rms_dv = float(np.sqrt(np.mean(ref["dv"] ** 2)))
+    for n, x in got.items():
+        r = ref[n]
+        d = np.abs(ref[n + "_d16"] - r) if n in ("dq", "dk") else 0.0
+        err = np.abs(x - r)
+        rms = float(np.sqrt(np.mean(r ** 2)))
+        R = rms if rms > 0.01 * rms_dv else rms_dv
+        bound = 2 * d + 2.0 ** -7 * np.abs(r) + 0.1 * R
+        print(f"backward 16K {'swa' if gated else 'global'} {n}: max_abs {err.max():.3e} mean_abs {err.mean():.3e} "
+              f"R {R:.3e} max err/bound {np.max(err / bound):.3f}")
+        assert np.all(np.isfinite(x)), n
+        assert np.all(err <= bound), f"{n}: max err/bound {np.max(err / bound):.3f}"
+        assert err.mean() <= 0.005 * R, f"{n}: mean {err.mean():.3e}"

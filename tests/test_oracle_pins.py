@@ -544,3 +544,25 @@ def test_backward_window_one_and_closed_gate():
     z = oracle.prefill_layer_backward(q, k, v, gneg, wq, wk, do, window=4, rotary_dims=42, base=1e4, eps=1e-6)
     for n in ("dq", "dk", "dv", "dgate", "dwq", "dwk"):
         assert not np.any(z[n]), n
+
+
+@pytest.mark.parametrize("window", [7, None])
+def test_backward_rows_equals_full_backward(window):
+    """The row-sampled backward (row blocks, one KV head) against the whole-layer backward at a small size, for
+    sampled query and key rows spanning several blocks, both with the exact Delta and with Delta from the bf16
+    output."""
+    B, S, Hq, Hkv = 2, 45, 4, 2
+    q, k, v, g, wq, wk, do = _bwd_problem(6, B, S, Hq, Hkv, gated=window is not None)
+    kw = dict(window=window, rotary_dims=42, base=1e4, eps=1e-6)
+    full = oracle.prefill_layer_backward(q, k, v, g, wq, wk, do, **kw)
+    full16 = oracle.prefill_layer_backward(q, k, v, g, wq, wk, do, delta_from_bf16_out=True, **kw)
+    qr, kr = np.array([0, 3, 16, 31, 44]), np.array([0, 5, 15, 16, 40, 44])
+    r = oracle.prefill_layer_backward_rows(q, k, v, g, wq, wk, do, b=1, kv_head=1, query_rows=qr, key_rows=kr,
+                                           block=16, **kw)
+    np.testing.assert_allclose(r["dq"], full["dq"][1][qr][:, 2:4], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["dq_d16"], full16["dq"][1][qr][:, 2:4], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["dk"], full["dk"][1][kr][:, 1], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["dk_d16"], full16["dk"][1][kr][:, 1], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["dv"], full["dv"][1][kr][:, 1], rtol=1e-10, atol=1e-12)
+    if window is not None:
+        np.testing.assert_allclose(r["dgate"], full["dgate"][1][qr][:, 2:4], rtol=1e-10, atol=1e-12)
