@@ -221,9 +221,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int NPRE = DK ? 6 : 4;
   uint4 pre[NPRE];
   float pre_f = 0.f;
+  // Tiles are walked from the last one down: every work-group of a (sequence, KV head) ends its sweep at the
+  // same last tile, so the work-groups running together on an XCD read the same tiles at about the same time
+  // and share them through its L2.
+  auto tile_q0 = [&](int it) { return (qt1 - 1 - it % ntiles) * kT; };
   auto load_stage = [&](int it) {
     const int hq = kvh * a.G + it / ntiles;
-    const int q0 = (qt0 + it % ntiles) * kT;
+    const int q0 = tile_q0(it);
     const int64_t bh = (int64_t)b * a.Hq + hq;
 #pragma unroll
     for (int k = 0; k < 2; k++) {
@@ -254,12 +258,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
 
   auto compute = [&](int buf, int it) {
-    const int q0 = (qt0 + it % ntiles) * kT;
+    const int q0 = tile_q0(it);
     if (q0 + kT <= j0 || q0 >= wq_end) return;            // no query of the tile sees this wave's keys
     const KvStage& s = st[buf];
+    // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key.  The accumulators start from
+    // -lse (scores) and -Delta (dP), so the MFMAs return s - lse and dP - Delta.
     floatx16 sacc, dpacc;
 #pragma unroll
-    for (int j = 0; j < 16; j++) sacc[j] = dpacc[j] = 0.f;
+    for (int jq = 0; jq < 4; jq++) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&s.lse2[8 * jq + 4 * hi]);
+      sacc[4 * jq] = -l4.x; sacc[4 * jq + 1] = -l4.y; sacc[4 * jq + 2] = -l4.z; sacc[4 * jq + 3] = -l4.w;
+      if constexpr (DK) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&s.dl[8 * jq + 4 * hi]);
+        dpacc[4 * jq] = -d4.x; dpacc[4 * jq + 1] = -d4.y; dpacc[4 * jq + 2] = -d4.z; dpacc[4 * jq + 3] = -d4.w;
+      }
+    }
 #pragma unroll
     for (int t = 0; t < 8; t++) {
       const uint4 qa = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 8 * hi]);
@@ -269,23 +282,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16v8(da), as_bf16v8(vf[t]), dpacc, 0, 0, 0);
       }
     }
-    // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key.  P (dV) or dS (dK) replaces S.
+    // P (dV) or dS = P (dP - Delta) (dK) replaces S; the mask only where the diagonal, the window edge or the
+    // sequence end cuts the tile (wave-uniform test)
+    const bool inside = q0 >= j0 + 31 && q0 + 31 < a.S && (!swa || q0 + 31 - j0 < a.window) && j0 + 31 < a.S;
+    if (inside) {
 #pragma unroll
-    for (int jq = 0; jq < 4; jq++) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&s.lse2[8 * jq + 4 * hi]);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      float dlv[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (DK) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&s.dl[8 * jq + 4 * hi]);
-        dlv[0] = d4.x; dlv[1] = d4.y; dlv[2] = d4.z; dlv[3] = d4.w;
+      for (int j = 0; j < 16; j++) {
+        const float pj = __builtin_amdgcn_exp2f(sacc[j]);
+        sacc[j] = DK ? pj * dpacc[j] : pj;
       }
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int j = 4 * jq + e;
-        const int qi = q0 + 8 * jq + 4 * hi + e;
+      for (int j = 0; j < 16; j++) {
+        const int qi = q0 + 8 * (j >> 2) + 4 * hi + (j & 3);
         const bool vis = qi < a.S && key <= qi && (!swa || qi - key < a.window);
-        const float pj = vis ? __builtin_amdgcn_exp2f(sacc[j] - lv[e]) : 0.f;
-        sacc[j] = DK ? pj * (dpacc[j] - dlv[e]) : pj;
+        const float pj = vis ? __builtin_amdgcn_exp2f(sacc[j]) : 0.f;
+        sacc[j] = DK ? pj * dpacc[j] : pj;
       }
     }
     float xv[16];
@@ -341,7 +353,7 @@ struct QStage {
   uint16_t kts[kHeadDim * kTrS];   // k_hat^T bf16 [128][32]
 };
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) bwd_q_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_q_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) QStage st[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int n_units = a.B * a.Hkv;
@@ -407,9 +419,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
   auto compute = [&](int buf, int it) {
     const int k0 = (kt0 + it) * kT;
     const QStage& s = st[buf];
+    // C layout: reg j is key k0 + 8(j/4) + 4hi + j%4, column = this lane's query; the accumulators start from
+    // -lse and -Delta (this lane's query), so the MFMAs return s - lse and dP - Delta
     floatx16 sacc, dpacc;
 #pragma unroll
-    for (int j = 0; j < 16; j++) sacc[j] = dpacc[j] = 0.f;
+    for (int j = 0; j < 16; j++) {
+      sacc[j] = -lse2;
+      dpacc[j] = -dl;
+    }
 #pragma unroll
     for (int t = 0; t < 8; t++) {
       const uint4 ka = *reinterpret_cast<const uint4*>(&s.ks[l32 * kRowS + 16 * t + 8 * hi]);
@@ -417,14 +434,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))
       const uint4 va = *reinterpret_cast<const uint4*>(&s.vs[l32 * kRowS + 16 * t + 8 * hi]);
       dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16v8(va), as_bf16v8(daf[t]), dpacc, 0, 0, 0);
     }
-    // C layout: reg j is key k0 + 8(j/4) + 4hi + j%4, column = this lane's query
+    // the mask only where the diagonal, the window edge or the sequence end cuts the tile (wave-uniform test)
+    const bool inside = k0 + 31 <= i0 && i0 + 31 < a.S && (!swa || i0 + 31 - k0 < a.window);
     float ds[16];
+    if (inside) {
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      const int kj = k0 + 8 * (j >> 2) + 4 * hi + (j & 3);
-      const bool vis = qi < a.S && kj <= qi && (!swa || qi - kj < a.window);
-      const float pj = vis ? __builtin_amdgcn_exp2f(sacc[j] - lse2) : 0.f;
-      ds[j] = pj * (dpacc[j] - dl);
+      for (int j = 0; j < 16; j++) ds[j] = __builtin_amdgcn_exp2f(sacc[j]) * dpacc[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        const int kj = k0 + 8 * (j >> 2) + 4 * hi + (j & 3);
+        const bool vis = qi < a.S && kj <= qi && (!swa || qi - kj < a.window);
+        ds[j] = vis ? __builtin_amdgcn_exp2f(sacc[j]) * dpacc[j] : 0.f;
+      }
     }
 #pragma unroll
     for (int t = 0; t < 2; t++) {
