@@ -478,7 +478,7 @@ def run_backward(zg, steps=5, warmup=2, S=16384, seed=1008):
 
 
 # ------------------------------------------------------------------------------------------ CPU baseline
-def cpu_baseline(S=16384, n_rows=4096, seed=1003):
+def cpu_baseline(S=16384, n_rows=8192, seed=1003):
     """The fp64 oracle on a sample of the prefill workload: n_rows random positions, all 32 query heads, in
     one gated-SWA layer (layer 1) and one global layer (layer 6).  Per-token time = 27 x (SWA row time +
     SWA key-prologue time / S) + 5 x (global row time + global key-prologue time / S).  Input generation
