@@ -38,6 +38,8 @@ constexpr int kTrS = 36;        // LDS row stride (halves) of [128][32] transpos
                                 // 8-byte reads at consecutive rows cover all 128 bytes of the banks once
 constexpr int kPrepTok = 64;    // tokens per prep work-group
 constexpr int kPrepTS = 72;     // LDS row stride (halves) of the prep transpose tiles [128][64]
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima (no wait)
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
 
 __device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + __expf(-g)); }
 
@@ -47,6 +49,10 @@ __device__ __forceinline__ half8 as_half8(const uint4& w) { return __builtin_bit
 // 8 fp32 of an MFMA C block (regs j0..j0+7) -> bf16 operand fragment
 __device__ __forceinline__ bf16v8 c8_to_bf16(const float* c) {
   return as_bf16v8(make_uint4(pack_bf16(c[0], c[1]), pack_bf16(c[2], c[3]), pack_bf16(c[4], c[5]), pack_bf16(c[6], c[7])));
+}
+__device__ __forceinline__ bf16v8 c8_to_bf16(const floatx16& c, int j0) {
+  return as_bf16v8(make_uint4(pack_bf16(c[j0], c[j0 + 1]), pack_bf16(c[j0 + 2], c[j0 + 3]), pack_bf16(c[j0 + 4], c[j0 + 5]),
+                              pack_bf16(c[j0 + 6], c[j0 + 7])));
 }
 
 // A-operand fragment of a transposed [128][kTrS] tile for k-step t: row `row`, the 8 columns
@@ -166,10 +172,11 @@ __device__ __forceinline__ void st_tr(uint16_t* dst, const uint4& v) {
 
 // One query tile of the key-centric kernels.  The dV kernel needs q_hat' (scores) and dA^T; the dK kernel
 // q_hat' (scores), dA (dP) and q_hat^T.
+template <bool DK>
 struct KvStage {
-  uint16_t qs[kT * kRowS];         // q_hat' fp16 [32 queries][128]
-  uint16_t xs[kT * kRowS];         // dK: dA bf16 [32][128]
-  uint16_t xts[kHeadDim * kTrS];   // dV: dA^T, dK: q_hat^T, bf16 [128][32]
+  uint16_t qs[kT * kRowS];              // q_hat' fp16 [32 queries][128]
+  uint16_t xs[DK ? kT * kRowS : 8];     // dK: dA bf16 [32][128]
+  uint16_t xts[kHeadDim * kTrS];        // dV: dA^T, dK: q_hat^T, bf16 [128][32]
   float lse2[kT];
   float dl[kT];
 };
@@ -179,8 +186,9 @@ struct KvStage {
 // q_hat^T dS with dS = P (dP - Delta), dP = dA V^T.  Every MFMA takes one operand from LDS and the other from
 // registers (the wave's key rows, or P / dS from the C registers), so two waves per SIMD fit.
 template <bool DK>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_kv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) KvStage st[2];
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bwd_kv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) KvStage<DK> st[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int n_units = a.B * a.Hkv;
   const int unit = blockIdx.x % n_units, kb = blockIdx.x / n_units;
@@ -203,6 +211,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int t = 0; t < 8; t++) vf[t] = *reinterpret_cast<const uint4*>(vr + 16 * t);
     }
   }
+  // The key rows feed the MFMAs straight from these loads.  Retire them here: otherwise the compiler, unable to
+  // prove them complete across the loop's back edge, waits for every load in flight (the next tile's prefetch
+  // included; the vector-memory counter retires in order) in front of each MFMA that reads them.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   floatx16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; db++)
@@ -217,50 +229,52 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int n_it = ntiles * a.G;
   const int wq_end = swa ? min(a.S, j0 + 31 + a.window) : a.S;   // this wave's visible queries [j0, wq_end)
 
-  // staging: 2 x 16-byte chunks per tile per thread, plus lse / Delta
-  constexpr int NPRE = DK ? 6 : 4;
-  uint4 pre[NPRE];
-  float pre_f = 0.f;
-  // Tiles are walked from the last one down: every work-group of a (sequence, KV head) ends its sweep at the
-  // same last tile, so the work-groups running together on an XCD read the same tiles at about the same time
-  // and share them through its L2.
-  auto tile_q0 = [&](int it) { return (qt1 - 1 - it % ntiles) * kT; };
+  // staging: 2 x 16-byte chunks per tile per thread, plus lse / Delta.  Named registers, not an array: an array
+  // captured by the lambdas is left in memory (LDS or scratch) by the compiler, which makes every prefetch
+  // synchronous.
+  uint4 pq0, pq1, pt0, pt1, px0, px1;
+  float pf = 0.f;
+  const int r0 = tid >> 4, r1 = (tid + 256) >> 4, cc = tid & 15;   // row-major chunks (rows r0, r1; chunk cc)
+  const int d0 = tid >> 2, d1 = (tid + 256) >> 2, pt = tid & 3;    // transposed chunks (dims d0, d1; part pt)
+  // Tiles are walked from the last one down, the group's heads inside each tile: every work-group of a
+  // (sequence, KV head) starts at the same last tile and advances at the same pace, so the work-groups running
+  // together on an XCD read the same tiles at about the same time and share them through its L2.
+  auto tile_q0 = [&](int it) { return (qt1 - 1 - it / a.G) * kT; };
   auto load_stage = [&](int it) {
-    const int hq = kvh * a.G + it / ntiles;
+    const int hq = kvh * a.G + it % a.G;
     const int q0 = tile_q0(it);
     const int64_t bh = (int64_t)b * a.Hq + hq;
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      const int cidx = tid + 256 * k;
-      const int r = cidx >> 4, cc = cidx & 15;            // row-major tiles: row r, chunk cc
-      const int64_t ro = (bh * a.Sp + q0 + r) * kHeadDim + 8 * cc;
-      pre[k] = *reinterpret_cast<const uint4*>(a.qh16 + ro);
-      const int d = cidx >> 2, part = cidx & 3;           // transposed tiles: dim d, 8 tokens
-      const int64_t to = (bh * kHeadDim + d) * a.Sp + q0 + 8 * part;
-      pre[2 + k] = *reinterpret_cast<const uint4*>((DK ? a.qt : a.dat) + to);
-      if constexpr (DK) pre[4 + k] = *reinterpret_cast<const uint4*>(a.da + ro);
+    const uint16_t* qrow = a.qh16 + (bh * a.Sp + q0) * kHeadDim + 8 * cc;
+    pq0 = *reinterpret_cast<const uint4*>(qrow + r0 * kHeadDim);
+    pq1 = *reinterpret_cast<const uint4*>(qrow + r1 * kHeadDim);
+    const uint16_t* trow = (DK ? a.qt : a.dat) + (bh * kHeadDim) * a.Sp + q0 + 8 * pt;
+    pt0 = *reinterpret_cast<const uint4*>(trow + (int64_t)d0 * a.Sp);
+    pt1 = *reinterpret_cast<const uint4*>(trow + (int64_t)d1 * a.Sp);
+    if constexpr (DK) {
+      const uint16_t* xrow = a.da + (bh * a.Sp + q0) * kHeadDim + 8 * cc;
+      px0 = *reinterpret_cast<const uint4*>(xrow + r0 * kHeadDim);
+      px1 = *reinterpret_cast<const uint4*>(xrow + r1 * kHeadDim);
     }
-    if (tid < (DK ? 64 : 32)) pre_f = (tid < 32 ? a.lse2 : a.delta)[bh * a.Sp + q0 + (tid & 31)];
+    if (tid < (DK ? 64 : 32)) pf = (tid < 32 ? a.lse2 : a.delta)[bh * a.Sp + q0 + (tid & 31)];
   };
   auto store_stage = [&](int buf) {
-    KvStage& s = st[buf];
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      const int cidx = tid + 256 * k;
-      const int r = cidx >> 4, cc = cidx & 15;
-      *reinterpret_cast<uint4*>(&s.qs[r * kRowS + 8 * cc]) = pre[k];
-      const int d = cidx >> 2, part = cidx & 3;
-      st_tr(&s.xts[d * kTrS + 8 * part], pre[2 + k]);
-      if constexpr (DK) *reinterpret_cast<uint4*>(&s.xs[r * kRowS + 8 * cc]) = pre[4 + k];
+    KvStage<DK>& s = st[buf];
+    *reinterpret_cast<uint4*>(&s.qs[r0 * kRowS + 8 * cc]) = pq0;
+    *reinterpret_cast<uint4*>(&s.qs[r1 * kRowS + 8 * cc]) = pq1;
+    st_tr(&s.xts[d0 * kTrS + 8 * pt], pt0);
+    st_tr(&s.xts[d1 * kTrS + 8 * pt], pt1);
+    if constexpr (DK) {
+      *reinterpret_cast<uint4*>(&s.xs[r0 * kRowS + 8 * cc]) = px0;
+      *reinterpret_cast<uint4*>(&s.xs[r1 * kRowS + 8 * cc]) = px1;
     }
-    if (tid < 32) s.lse2[tid] = pre_f;
-    else if (DK && tid < 64) s.dl[tid - 32] = pre_f;
+    if (tid < 32) s.lse2[tid] = pf;
+    else if (DK && tid < 64) s.dl[tid - 32] = pf;
   };
 
   auto compute = [&](int buf, int it) {
     const int q0 = tile_q0(it);
     if (q0 + kT <= j0 || q0 >= wq_end) return;            // no query of the tile sees this wave's keys
-    const KvStage& s = st[buf];
+    const KvStage<DK>& s = st[buf];
     // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key.  The accumulators start from
     // -lse (scores) and -Delta (dP), so the MFMAs return s - lse and dP - Delta.
     floatx16 sacc, dpacc;
@@ -300,12 +314,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         sacc[j] = DK ? pj * dpacc[j] : pj;
       }
     }
-    float xv[16];
-#pragma unroll
-    for (int j = 0; j < 16; j++) xv[j] = sacc[j];
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-      const bf16v8 xb = c8_to_bf16(xv + 8 * t);
+      const bf16v8 xb = c8_to_bf16(sacc, 8 * t);
 #pragma unroll
       for (int db = 0; db < 4; db++)
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.xts, 32 * db + l32, t, hi), xb, acc[db], 0, 0, 0);
@@ -322,6 +333,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool more = it + 1 < n_it;
     if (more) load_stage(it + 1);
     compute(buf, it);
+    // Keep the stores of the prefetched tile after the compute: they go to the other buffer, so the compiler
+    // would otherwise move them (and the waits for their loads) up against the loads, which makes the prefetch
+    // synchronous.
+    asm volatile("" ::: "memory");
     if (more) store_stage(buf ^ 1);
     __syncthreads();
   }
@@ -379,6 +394,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   const float lse2 = a.lse2[bh * a.Sp + qi];
   const float dl = a.delta[bh * a.Sp + qi];
+  // retire the preloads (see bwd_kv_kernel)
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   floatx16 dq[4];
 #pragma unroll
   for (int db = 0; db < 4; db++)
@@ -390,31 +407,36 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int kt0 = k_beg / kT, kt1 = (k_end + kT - 1) / kT;
   const int n_it = kt1 - kt0;
 
-  uint4 pre[6];
+  // staging in named registers (see bwd_kv_kernel): 2 x 16-byte chunks per tile per thread; wave-uniform bases
+  // plus 32-bit lane offsets
+  uint4 pk0, pk1, pv0, pv1, pt0, pt1;
+  const int r0 = tid >> 4, r1 = (tid + 256) >> 4, cc = tid & 15;
+  const int d0 = tid >> 2, d1 = (tid + 256) >> 2, pt = tid & 3;
+  const uint16_t* kbase = a.kh16 + (int64_t)unit * a.Sp * kHeadDim;
+  const uint16_t* tbase = a.kt + (int64_t)unit * kHeadDim * a.Sp;
+  const uint16_t* vbase = a.v + ((int64_t)b * a.S * a.Hkv + kvh) * kHeadDim;
+  const int ok0 = r0 * kHeadDim + 8 * cc, ok1 = r1 * kHeadDim + 8 * cc;
+  const int ot0 = d0 * a.Sp + 8 * pt, ot1 = d1 * a.Sp + 8 * pt;
+  const int vrow = a.Hkv * kHeadDim;
   auto load_stage = [&](int it) {
     const int k0 = (kt0 + it) * kT;
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      const int cidx = tid + 256 * k;
-      const int r = cidx >> 4, cc = cidx & 15;
-      pre[k] = *reinterpret_cast<const uint4*>(a.kh16 + ((int64_t)unit * a.Sp + k0 + r) * kHeadDim + 8 * cc);
-      const int kc = min(k0 + r, a.S - 1);
-      pre[2 + k] = *reinterpret_cast<const uint4*>(a.v + (((int64_t)b * a.S + kc) * a.Hkv + kvh) * kHeadDim + 8 * cc);
-      const int d = cidx >> 2, part = cidx & 3;
-      pre[4 + k] = *reinterpret_cast<const uint4*>(a.kt + ((int64_t)unit * kHeadDim + d) * a.Sp + k0 + 8 * part);
-    }
+    const uint16_t* kb = kbase + k0 * kHeadDim;
+    pk0 = *reinterpret_cast<const uint4*>(kb + ok0);
+    pk1 = *reinterpret_cast<const uint4*>(kb + ok1);
+    pv0 = *reinterpret_cast<const uint4*>(vbase + (int64_t)min(k0 + r0, a.S - 1) * vrow + 8 * cc);
+    pv1 = *reinterpret_cast<const uint4*>(vbase + (int64_t)min(k0 + r1, a.S - 1) * vrow + 8 * cc);
+    const uint16_t* tb = tbase + k0;
+    pt0 = *reinterpret_cast<const uint4*>(tb + ot0);
+    pt1 = *reinterpret_cast<const uint4*>(tb + ot1);
   };
   auto store_stage = [&](int buf) {
     QStage& s = st[buf];
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      const int cidx = tid + 256 * k;
-      const int r = cidx >> 4, cc = cidx & 15;
-      *reinterpret_cast<uint4*>(&s.ks[r * kRowS + 8 * cc]) = pre[k];
-      *reinterpret_cast<uint4*>(&s.vs[r * kRowS + 8 * cc]) = pre[2 + k];
-      const int d = cidx >> 2, part = cidx & 3;
-      st_tr(&s.kts[d * kTrS + 8 * part], pre[4 + k]);
-    }
+    *reinterpret_cast<uint4*>(&s.ks[r0 * kRowS + 8 * cc]) = pk0;
+    *reinterpret_cast<uint4*>(&s.ks[r1 * kRowS + 8 * cc]) = pk1;
+    *reinterpret_cast<uint4*>(&s.vs[r0 * kRowS + 8 * cc]) = pv0;
+    *reinterpret_cast<uint4*>(&s.vs[r1 * kRowS + 8 * cc]) = pv1;
+    st_tr(&s.kts[d0 * kTrS + 8 * pt], pt0);
+    st_tr(&s.kts[d1 * kTrS + 8 * pt], pt1);
   };
   auto compute = [&](int buf, int it) {
     const int k0 = (kt0 + it) * kT;
@@ -436,21 +458,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     // the mask only where the diagonal, the window edge or the sequence end cuts the tile (wave-uniform test)
     const bool inside = k0 + 31 <= i0 && i0 + 31 < a.S && (!swa || i0 + 31 - k0 < a.window);
-    float ds[16];
     if (inside) {
 #pragma unroll
-      for (int j = 0; j < 16; j++) ds[j] = __builtin_amdgcn_exp2f(sacc[j]) * dpacc[j];
+      for (int j = 0; j < 16; j++) sacc[j] = __builtin_amdgcn_exp2f(sacc[j]) * dpacc[j];
     } else {
 #pragma unroll
       for (int j = 0; j < 16; j++) {
         const int kj = k0 + 8 * (j >> 2) + 4 * hi + (j & 3);
         const bool vis = qi < a.S && kj <= qi && (!swa || qi - kj < a.window);
-        ds[j] = vis ? __builtin_amdgcn_exp2f(sacc[j]) * dpacc[j] : 0.f;
+        sacc[j] = vis ? __builtin_amdgcn_exp2f(sacc[j]) * dpacc[j] : 0.f;
       }
     }
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-      const bf16v8 sb = c8_to_bf16(ds + 8 * t);
+      const bf16v8 sb = c8_to_bf16(sacc, 8 * t);
 #pragma unroll
       for (int db = 0; db < 4; db++)
         dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.kts, 32 * db + l32, t, hi), sb, dq[db], 0, 0, 0);
@@ -467,6 +488,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool more = it + 1 < n_it;
     if (more) load_stage(it + 1);
     compute(buf, it);
+    // Keep the stores of the prefetched tile after the compute: they go to the other buffer, so the compiler
+    // would otherwise move them (and the waits for their loads) up against the loads, which makes the prefetch
+    // synchronous.
+    asm volatile("" ::: "memory");
     if (more) store_stage(buf ^ 1);
     __syncthreads();
   }
