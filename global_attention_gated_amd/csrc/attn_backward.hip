@@ -287,14 +287,28 @@ bwd_kv_kernel(BwdArgs a) {
         dpacc[4 * jq] = -d4.x; dpacc[4 * jq + 1] = -d4.y; dpacc[4 * jq + 2] = -d4.z; dpacc[4 * jq + 3] = -d4.w;
       }
     }
+    if constexpr (DK) {
 #pragma unroll
-    for (int t = 0; t < 8; t++) {
-      const uint4 qa = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 8 * hi]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(qa), as_half8(kf[t]), sacc, 0, 0, 0);
-      if constexpr (DK) {
+      for (int t = 0; t < 8; t++) {
+        const uint4 qa = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 8 * hi]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(qa), as_half8(kf[t]), sacc, 0, 0, 0);
         const uint4 da = *reinterpret_cast<const uint4*>(&s.xs[l32 * kRowS + 16 * t + 8 * hi]);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16v8(da), as_bf16v8(vf[t]), dpacc, 0, 0, 0);
       }
+    } else {
+      // two independent chains (even and odd k-steps) so consecutive MFMAs do not wait on each other
+      floatx16 s2;
+#pragma unroll
+      for (int j = 0; j < 16; j++) s2[j] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        const uint4 qa = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 8 * hi]);
+        const uint4 qb = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 16 + 8 * hi]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(qa), as_half8(kf[t]), sacc, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(qb), as_half8(kf[t + 1]), s2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; j++) sacc[j] += s2[j];
     }
     // P (dV) or dS = P (dP - Delta) (dK) replaces S; the mask only where the diagonal, the window edge or the
     // sequence end cuts the tile (wave-uniform test)
