@@ -33,6 +33,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16v8;
 
 constexpr int kT = 32;          // query / key tile of the MFMA kernels
+constexpr int kG = 4;           // GQA group (query heads per KV head), the one shape the host accepts
 constexpr int kRowS = 136;      // LDS row stride (halves) of [32][128] tiles: 16-byte pad
 constexpr int kTrS = 36;        // LDS row stride (halves) of [128][32] transposed tiles: 72 B, so 16 lanes'
                                 // 8-byte reads at consecutive rows cover all 128 bytes of the banks once
@@ -226,7 +227,7 @@ bwd_kv_kernel(BwdArgs a) {
   const int q_end = swa ? min(a.S, jb_last + a.window) : a.S;   // exclusive
   const int qt0 = jb0 / kT, qt1 = (q_end + kT - 1) / kT;
   const int ntiles = max(qt1 - qt0, 0);
-  const int n_it = ntiles * a.G;
+  const int n_it = ntiles * kG;
   const int wq_end = swa ? min(a.S, j0 + 31 + a.window) : a.S;   // this wave's visible queries [j0, wq_end)
 
   // staging: 2 x 16-byte chunks per tile per thread, plus lse / Delta.  Named registers, not an array: an array
@@ -239,9 +240,9 @@ bwd_kv_kernel(BwdArgs a) {
   // Tiles are walked from the last one down, the group's heads inside each tile: every work-group of a
   // (sequence, KV head) starts at the same last tile and advances at the same pace, so the work-groups running
   // together on an XCD read the same tiles at about the same time and share them through its L2.
-  auto tile_q0 = [&](int it) { return (qt1 - 1 - it / a.G) * kT; };
+  auto tile_q0 = [&](int it) { return (qt1 - 1 - it / kG) * kT; };
   auto load_stage = [&](int it) {
-    const int hq = kvh * a.G + it % a.G;
+    const int hq = kvh * kG + it % kG;
     const int q0 = tile_q0(it);
     const int64_t bh = (int64_t)b * a.Hq + hq;
     const uint16_t* qrow = a.qh16 + (bh * a.Sp + q0) * kHeadDim + 8 * cc;
@@ -391,7 +392,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const bool swa = a.window > 0;
   const int qt = swa ? rank : n_qt - 1 - rank;            // global: longest rows first
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
-  const int hq = kvh * a.G + wave;
+  const int hq = kvh * kG + wave;
   const int i0 = qt * kT;
   const int qi = i0 + l32;                                 // this lane's query (MFMA column)
   const int64_t bh = (int64_t)b * a.Hq + hq;
