@@ -3,7 +3,7 @@
 inputs.
 
 Bar of the backward, per gradient X against the exact X_ref (elementwise, then the mean):
-    |err| <= 2 |D_X| + 2^-7 |X_ref| + 0.1 R_X,        mean |err| <= 0.005 R_X
+    |err| <= 2 |D_X| + 2^-7 |X_ref| + 0.1 R_X,        mean |err| <= 2 mean |D_X| + 0.005 R_X
 with R_X = rms(X_ref) (dv's rms where X_ref is identically zero: one visible key), and D_X the change in the
 exact gradient when Delta_i = dout_i . out_i is formed from the bf16 output, as this backward (the standard
 flash-attention form) must: out is handed over in bf16, 2^-9 relative per element.  The other terms: the bf16
@@ -57,11 +57,14 @@ def _check(g, ref, ref16, gated, tag):
         print(f"{tag} {gn}: max_abs {err.max():.3e} mean_abs {err.mean():.3e} R {R:.3e} "
               f"max err/bound {np.max(err / bound):.3f} mean/R {err.mean() / R:.2e}")
         assert np.all(err <= bound), f"{tag} {gn}: max err/bound {np.max(err / bound):.3f}"
-        assert err.mean() <= 0.005 * R, f"{tag} {gn}: mean_abs {err.mean():.3e} > {0.005 * R:.3e}"
+        mean_bound = 2 * float(np.mean(dlt)) + 0.005 * R
+        assert err.mean() <= mean_bound, f"{tag} {gn}: mean_abs {err.mean():.3e} > {mean_bound:.3e}"
 
 
 CASES = [(True, 1, 300, 8, 2, 128), (False, 1, 257, 8, 2, 0), (True, 2, 129, 4, 1, 16), (True, 1, 33, 4, 1, 128),
-         (False, 1, 1, 4, 1, 0), (True, 1, 1, 4, 1, 128)]
+         (False, 1, 1, 4, 1, 0), (True, 1, 1, 4, 1, 128),
+         # window 1 (no score gradient), a window wider than the tile ring, 3 sequences x 4 KV heads, ragged ends
+         (True, 1, 97, 4, 1, 1), (True, 1, 400, 4, 1, 256), (True, 3, 70, 16, 4, 32), (False, 3, 161, 16, 4, 0)]
 
 
 @pytest.mark.parametrize("gated,B,S,Hq,Hkv,W", CASES)

@@ -263,7 +263,7 @@ def test_chunked_prefill_262144_in_16384_chunks(zg):
 def test_backward_1x16384_sampled(zg, gated):
     """Training forward and backward at 1 x 16384, 32 query / 8 KV heads (the backward benchmark's launch
     configuration): sampled query rows (dq, dgate) and key rows (dk, dv) of one KV head's group against the
-    row-sampled oracle, to the bar of test_gpu_backward (2 |D_X| + 2^-7 |X_ref| + 0.1 R_X, mean 0.005 R_X)."""
+    row-sampled oracle, to the bar of test_gpu_backward (2 |D_X| + 2^-7 |X_ref| + 0.1 R_X; mean 2 mean|D_X| + 0.005 R_X)."""
     import torch
     seed, layer, S, Hq, Hkv, kvh = 1009, 2 if gated else 6, 16384, 32, 8, 5
     G = Hq // Hkv
@@ -306,4 +306,4 @@ def test_backward_1x16384_sampled(zg, gated):
               f"R {R:.3e} max err/bound {np.max(err / bound):.3f}")
         assert np.all(np.isfinite(x)), n
         assert np.all(err <= bound), f"{n}: max err/bound {np.max(err / bound):.3f}"
-        assert err.mean() <= 0.005 * R, f"{n}: mean {err.mean():.3e}"
+        assert err.mean() <= 2 * float(np.mean(d)) + 0.005 * R, f"{n}: mean {err.mean():.3e}"
