@@ -54,7 +54,8 @@ def test_single_gated_swa_layer_1x512_4q1kv(zg):
     42 dims with base 10,000, seed 1001 -- compared in full."""
     L = Layer(1001, 0, 1, 512, 4, 1, w_spread=0.0)
     got = to_host_f64(gpu_prefill(zg, L, True, 128, 42, 1e4, 1e-6))
-    compare(got, oracle_prefill(L, True, 128, 42, 1e4, 1e-6), "swa 1x512")
+    mx, mean = compare(got, oracle_prefill(L, True, 128, 42, 1e4, 1e-6), "swa 1x512")
+    print(f"swa 1x512 4q/1kv: max_abs {mx:.3e} mean_abs {mean:.3e}")
 
 
 SHAPES = [
