@@ -22,8 +22,9 @@
 //                    in fp16 as the forward, gradient products in bf16 for their range).
 //   bwd_q_kernel     query-centric: a work-group owns 32 positions of the 4 heads of a group (one wave each) and
 //                    walks the key tiles they see: dQ_hat^T = K_hat^T dS^T.
-//   bwd_post_kernel  RoPE transpose and RMSNorm backward per (token, head) row; bf16 dq / dk and deterministic
-//                    per-work-group partial sums of the norm-weight gradients, reduced by bwd_dw_reduce_kernel.
+//   epilogues        the dK and dQ kernels take their rows back through RoPE (its transpose) and RMSNorm in their
+//                    epilogues, write bf16 dk / dq and a per-work-group partial of dw_k / dw_q, which
+//                    bwd_dw_reduce_kernel sums in a fixed order.
 #include "common.h"
 #include "launch.h"
 
@@ -165,6 +166,89 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------ dK, dV
+// Epilogue of the dK and dQ kernels: the norm / RoPE backward of one row per lane pair, from the MFMA C layout
+// (acc[db][j] holds dim d = 32db + 8(j/4) + 4hi + j%4 of the lane's row; lanes l and l ^ 32 hold the two halves).
+// acc is sum_j ds k_hat (or sum_i ds q_hat); dy = acc / sqrt(D) goes back through RoPE (its transpose at
+// position pos) and RMSNorm (x re-read, r recomputed):
+//   dx = w dy / r - x (sum_d w_d dy_d x_d) / (D r^3),   and this row's share of the weight gradient dy x / r.
+// dx is written as bf16 at dxrow (null for a row past the sequence, whose acc is zero).  The weight-gradient shares
+// of the wave's 32 rows are summed by a butterfly that halves each lane's list at every exchange, leaving dims
+// n = 2 l32 and 2 l32 + 1 of the list in lane l32, and stored in red (this wave's 128 floats).
+__device__ __forceinline__ void norm_rope_bwd_rows(const floatx16 (&acc)[4], const uint16_t* xrow, const uint16_t* w,
+                                                   uint16_t* dxrow, int pos, const BwdArgs& a, int hi, int l32,
+                                                   float* red) {
+  constexpr float kInvSqrtD = 0.08838834764831845f;   // 1/sqrt(128)
+  float dy[64], xv[64], wv[64];
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int jq = 0; jq < 4; jq++) {
+      const int d = 32 * db + 8 * jq + 4 * hi, n = 16 * db + 4 * jq;
+      const uint2 x4 = xrow ? *reinterpret_cast<const uint2*>(xrow + d) : make_uint2(0, 0);
+      const uint2 w4 = *reinterpret_cast<const uint2*>(w + d);
+      xv[n] = bf16lo(x4.x); xv[n + 1] = bf16hi(x4.x); xv[n + 2] = bf16lo(x4.y); xv[n + 3] = bf16hi(x4.y);
+      wv[n] = bf16lo(w4.x); wv[n + 1] = bf16hi(w4.x); wv[n + 2] = bf16lo(w4.y); wv[n + 3] = bf16hi(w4.y);
+#pragma unroll
+      for (int e = 0; e < 4; e++) dy[n + e] = acc[db][4 * jq + e] * kInvSqrtD;
+    }
+  // RoPE transpose: pairs (d, d + 1), d even, rotated back by the angle of position pos
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int jq = 0; jq < 4; jq++)
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const int d = 32 * db + 8 * jq + 4 * hi + e, n = 16 * db + 4 * jq + e;
+        if ((d >> 1) < a.rot_pairs) {
+          float c, sn;
+          rope_cs(pos, a.inv_freq_rev[d >> 1], c, sn);
+          const float d0 = dy[n], d1 = dy[n + 1];
+          dy[n] = d0 * c + d1 * sn;
+          dy[n + 1] = -d0 * sn + d1 * c;
+        }
+      }
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int n = 0; n < 64; n++) {
+    ss += xv[n] * xv[n];
+    dot += wv[n] * dy[n] * xv[n];
+  }
+  ss = xor32_sum(ss);
+  dot = xor32_sum(dot);
+  const float r = rsqrtf(ss * (1.0f / kHeadDim) + a.eps);
+  const float k3 = dot * r * r * r * (1.0f / kHeadDim);
+  if (dxrow) {
+#pragma unroll
+    for (int db = 0; db < 4; db++)
+#pragma unroll
+      for (int jq = 0; jq < 4; jq++) {
+        const int d = 32 * db + 8 * jq + 4 * hi, n = 16 * db + 4 * jq;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = wv[n + e] * dy[n + e] * r - xv[n + e] * k3;
+        *reinterpret_cast<uint2*>(dxrow + d) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
+      }
+  }
+  // weight-gradient shares, summed over the wave's 32 rows (lane bits 4..0, one exchange each)
+#pragma unroll
+  for (int n = 0; n < 64; n++) dy[n] = dy[n] * xv[n] * r;
+#pragma unroll
+  for (int step = 0; step < 5; step++) {
+    const int o = 16 >> step, half = 32 >> step;
+    const bool up = (l32 & o) != 0;
+#pragma unroll
+    for (int i = 0; i < half; i++) {
+      const float send = up ? dy[i] : dy[i + half];
+      const float keep = up ? dy[i + half] : dy[i];
+      dy[i] = keep + __shfl_xor(send, o);
+    }
+  }
+  const int n0 = 2 * l32, db0 = n0 >> 4, j0 = n0 & 15;
+  const int d0 = 32 * db0 + 8 * (j0 >> 2) + 4 * hi + (j0 & 3);
+  red[d0] = dy[0];
+  red[d0 + 1] = dy[1];
+}
+
 // 8-byte halves of a 16-byte chunk into a transposed tile row (its rows are 8- but not 16-byte aligned)
 __device__ __forceinline__ void st_tr(uint16_t* dst, const uint4& v) {
   reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
@@ -357,21 +441,25 @@ bwd_kv_kernel(BwdArgs a) {
   }
 
   // outputs: C layout reg j of block db is dim 32db + 8(j/4) + 4hi + j%4 of this lane's key
-  if (key < a.S) {
+  if constexpr (DK) {
+    // dk: back through RoPE and the key RMSNorm here; the work-group's 128 keys' share of dw_k into its partial
+    __shared__ float red[4][kHeadDim];
+    const int64_t row = ((int64_t)b * a.S + key) * a.Hkv + kvh;
+    const bool valid = key < a.S;
+    norm_rope_bwd_rows(acc, valid ? a.k + row * kHeadDim : nullptr, a.kw, valid ? a.dk + row * kHeadDim : nullptr,
+                       key, a, hi, l32, red[wave]);
+    __syncthreads();
+    if (tid < kHeadDim)
+      a.dw_part[((int64_t)a.n_qblk + blockIdx.x) * kHeadDim + tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+  } else if (key < a.S) {
+    uint16_t* dvr = a.dv + (((int64_t)b * a.S + key) * a.Hkv + kvh) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 4; db++)
 #pragma unroll
       for (int jq = 0; jq < 4; jq++) {
         const int d = 32 * db + 8 * jq + 4 * hi;
-        if constexpr (DK) {
-          float* dkr = a.dkh + ((int64_t)unit * a.Sp + key) * kHeadDim;
-          *reinterpret_cast<float4*>(dkr + d) = make_float4(acc[db][4 * jq], acc[db][4 * jq + 1],
-                                                            acc[db][4 * jq + 2], acc[db][4 * jq + 3]);
-        } else {
-          uint16_t* dvr = a.dv + (((int64_t)b * a.S + key) * a.Hkv + kvh) * kHeadDim;
-          *reinterpret_cast<uint2*>(dvr + d) = make_uint2(pack_bf16(acc[db][4 * jq], acc[db][4 * jq + 1]),
-                                                          pack_bf16(acc[db][4 * jq + 2], acc[db][4 * jq + 3]));
-        }
+        *reinterpret_cast<uint2*>(dvr + d) = make_uint2(pack_bf16(acc[db][4 * jq], acc[db][4 * jq + 1]),
+                                                        pack_bf16(acc[db][4 * jq + 2], acc[db][4 * jq + 3]));
       }
   }
 }
@@ -511,87 +599,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
   }
 
-  float* dqr = a.dqh + (bh * a.Sp + qi) * kHeadDim;
-#pragma unroll
-  for (int db = 0; db < 4; db++)
-#pragma unroll
-    for (int jq = 0; jq < 4; jq++) {
-      const int d = 32 * db + 8 * jq + 4 * hi;
-      *reinterpret_cast<float4*>(dqr + d) = make_float4(dq[db][4 * jq], dq[db][4 * jq + 1], dq[db][4 * jq + 2],
-                                                        dq[db][4 * jq + 3]);
-    }
-}
-
-// ------------------------------------------------------------------------------------------ norm / RoPE backward
-// Rows (b, s, h) with h fastest, 16 lanes per row (8 dims each, the chunk c = lane & 15 fixed per thread).
-// dy = RoPE^T(dX_hat / sqrt(D)); x = the raw input row; r = sqrt(mean(x^2) + eps):
-//   dx = w dy / r - x (sum_d w_d dy_d x_d) / (D r^3);   dw += dy x / r
-__global__ void __launch_bounds__(256) bwd_post_kernel(BwdArgs a, int kmode) {
-  __shared__ float red[16][kHeadDim];
-  const int tid = threadIdx.x, c = tid & 15, rg = tid >> 4;
-  const int H = kmode ? a.Hkv : a.Hq;
-  const float* dxh = kmode ? a.dkh : a.dqh;
-  const uint16_t* x = kmode ? a.k : a.q;
-  uint16_t* dx = kmode ? a.dk : a.dq;
-  float wf[8], acc[8];
-  unpack8(*reinterpret_cast<const uint4*>((kmode ? a.kw : a.qw) + 8 * c), wf);
-#pragma unroll
-  for (int e = 0; e < 8; e++) acc[e] = 0.f;
-  const float inv_sqrt_d = 0.08838834764831845f;   // 1/sqrt(128)
-  const int64_t rows = (int64_t)a.B * a.S * H;
-  for (int64_t row = (int64_t)blockIdx.x * 16 + rg; row < rows; row += (int64_t)gridDim.x * 16) {
-    const int h = (int)(row % H);
-    const int64_t bs = row / H;
-    const int s = (int)(bs % a.S), b = (int)(bs / a.S);
-    const float* src = dxh + (((int64_t)b * H + h) * a.Sp + s) * kHeadDim + 8 * c;
-    const float4 g0 = *reinterpret_cast<const float4*>(src);
-    const float4 g1 = *reinterpret_cast<const float4*>(src + 4);
-    float dy[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-    for (int e = 0; e < 8; e++) dy[e] *= inv_sqrt_d;
-    if (8 * c < 2 * a.rot_pairs) {
-#pragma unroll
-      for (int m = 0; m < 4; m++) {
-        const int i = 4 * c + m;
-        float cs, sn;
-        rope_cs(s, a.inv_freq_rev[i], cs, sn);
-        if (i >= a.rot_pairs) { cs = 1.0f; sn = 0.0f; }
-        const float d0 = dy[2 * m], d1 = dy[2 * m + 1];
-        dy[2 * m] = d0 * cs + d1 * sn;
-        dy[2 * m + 1] = -d0 * sn + d1 * cs;
-      }
-    }
-    float xf[8];
-    unpack8(*reinterpret_cast<const uint4*>(x + row * kHeadDim + 8 * c), xf);
-    float ss = 0.f, dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      ss += xf[e] * xf[e];
-      dot += wf[e] * dy[e] * xf[e];
-    }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      ss += __shfl_xor(ss, o);
-      dot += __shfl_xor(dot, o);
-    }
-    const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps);
-    const float k3 = dot * inv * inv * inv * (1.0f / kHeadDim);
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      o[e] = wf[e] * dy[e] * inv - xf[e] * k3;
-      acc[e] += dy[e] * xf[e] * inv;
-    }
-    *reinterpret_cast<uint4*>(dx + row * kHeadDim + 8 * c) = pack8(o);
-  }
-#pragma unroll
-  for (int e = 0; e < 8; e++) red[rg][8 * c + e] = acc[e];
+  // dq: back through RoPE and the query RMSNorm here; the work-group's 4 x 32 rows' share of dw_q into its partial
+  __shared__ float red[4][kHeadDim];
+  const int64_t row = ((int64_t)b * a.S + qi) * a.Hq + hq;
+  const bool valid = qi < a.S;
+  norm_rope_bwd_rows(dq, valid ? a.q + row * kHeadDim : nullptr, a.qw, valid ? a.dq + row * kHeadDim : nullptr, qi, a,
+                     hi, l32, red[wave]);
   __syncthreads();
-  if (tid < kHeadDim) {
-    float sum = 0.f;
-    for (int g = 0; g < 16; g++) sum += red[g][tid];
-    a.dw_part[((int64_t)kmode * kBwdPostBlocks + blockIdx.x) * kHeadDim + tid] = sum;
-  }
+  if (tid < kHeadDim)
+    a.dw_part[(int64_t)blockIdx.x * kHeadDim + tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
 }
 
 __global__ void __launch_bounds__(128) bwd_dw_zero_kernel(float* dqw, float* dkw) {
@@ -599,12 +615,39 @@ __global__ void __launch_bounds__(128) bwd_dw_zero_kernel(float* dqw, float* dkw
   dkw[threadIdx.x] = 0.f;
 }
 
-__global__ void __launch_bounds__(128) bwd_dw_reduce_kernel(BwdArgs a) {
-  const int kmode = blockIdx.x, d = threadIdx.x;
-  const float* part = a.dw_part + (int64_t)kmode * kBwdPostBlocks * kHeadDim;
-  float sum = 0.f;
-  for (int i = 0; i < kBwdPostBlocks; i++) sum += part[(int64_t)i * kHeadDim + d];
-  (kmode ? a.dkw : a.dqw)[d] = sum;
+// dw_q = sum of the dQ work-groups' partials, dw_k = sum of the dK work-groups'.  Thread t sums the rows
+// i = t/128 (mod 8) of dim t%128, sixteen loads in flight, each into its own accumulator; accumulators and then
+// the eight slices are added in a fixed order, so the result is deterministic.
+__global__ void __launch_bounds__(1024) bwd_dw_reduce_kernel(BwdArgs a) {
+  constexpr int kSlices = 8, kLanes = 16;
+  __shared__ float red[kSlices][kHeadDim];
+  const int kmode = blockIdx.x, d = threadIdx.x & (kHeadDim - 1), slice = threadIdx.x >> 7;
+  const float* part = a.dw_part + (kmode ? (int64_t)a.n_qblk * kHeadDim : 0);
+  const int n = kmode ? a.n_kblk : a.n_qblk;
+  float acc[kLanes];
+#pragma unroll
+  for (int u = 0; u < kLanes; u++) acc[u] = 0.f;
+  int i = slice;
+  for (; i + (kLanes - 1) * kSlices < n; i += kLanes * kSlices) {
+    float v[kLanes];
+#pragma unroll
+    for (int u = 0; u < kLanes; u++) v[u] = part[(int64_t)(i + u * kSlices) * kHeadDim + d];
+#pragma unroll
+    for (int u = 0; u < kLanes; u++) acc[u] += v[u];
+  }
+  for (int u = 0; i < n; i += kSlices, u++) acc[u] += part[(int64_t)i * kHeadDim + d];
+#pragma unroll
+  for (int w = kLanes / 2; w > 0; w /= 2)
+#pragma unroll
+    for (int u = 0; u < w; u++) acc[u] += acc[u + w];
+  red[slice][d] = acc[0];
+  __syncthreads();
+  if (threadIdx.x < kHeadDim) {
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSlices; k++) sum += red[k][d];
+    (kmode ? a.dkw : a.dqw)[d] = sum;
+  }
 }
 
 }  // namespace
@@ -633,13 +676,8 @@ hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_post(const BwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_post_kernel, dim3(kBwdPostBlocks), dim3(256), 0, st, a, 0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_post_kernel, dim3(kBwdPostBlocks), dim3(256), 0, st, a, 1);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dw_reduce_kernel, dim3(2), dim3(128), 0, st, a);
+hipError_t launch_bwd_dw_reduce(const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_dw_reduce_kernel, dim3(2), dim3(1024), 0, st, a);
   return hipGetLastError();
 }
 

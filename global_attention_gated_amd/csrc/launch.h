@@ -112,7 +112,6 @@ struct Fp8Blocks {
 
 // Backward of an attention layer (training), no cache, positions 0..S-1.  Sp = S rounded up to 128; the
 // workspace arrays are zero past S (and lse2 +inf), so tiles may run over the end.
-constexpr int32_t kBwdPostBlocks = 512;   // work-groups of the norm/RoPE backward (and dw partials per tensor)
 struct BwdArgs {
   const uint16_t* q;      // [B][S][Hq][D] bf16
   const uint16_t* k;      // [B][S][Hkv][D]
@@ -138,9 +137,9 @@ struct BwdArgs {
   float* delta;           // [B][Hq][Sp] dout . out
   uint16_t* kh16;         // [B][Hkv][Sp][D] fp16 k_hat (bf16 values)
   uint16_t* kt;           // [B][Hkv][D][Sp] bf16 k_hat transposed
-  float* dqh;             // [B][Hq][Sp][D] sum_j ds_ij k_hat_j
-  float* dkh;             // [B][Hkv][Sp][D] sum_i ds_ij q_hat_i (over the group's heads)
-  float* dw_part;         // [2][kBwdPostBlocks][D]
+  float* dw_part;         // [n_qblk + n_kblk][D]: per-work-group partials of dw_q (dQ kernel), then of dw_k (dK)
+  int32_t n_qblk;         // work-groups of the dQ kernel: B * Hkv * ceil(S / 32)
+  int32_t n_kblk;         // work-groups of the dK kernel: B * Hkv * ceil(S / 128)
   int32_t B, S, Sp, Hq, Hkv, G;
   int32_t window;         // 0 for a global layer
   int32_t rot_pairs;
@@ -192,7 +191,7 @@ hipError_t launch_bwd_dw_zero(float* dqw, float* dkw, hipStream_t st);   // D = 
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st);
-hipError_t launch_bwd_post(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_dw_reduce(const BwdArgs& a, hipStream_t st);
 hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, const Fp8Blocks& nb, hipStream_t st);
 int swa_stream_run_length(int S, int n_units);
 hipError_t launch_decode_append(const DecodeArgs& a, hipStream_t st);

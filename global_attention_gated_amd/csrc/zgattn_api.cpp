@@ -507,7 +507,7 @@ extern "C" int global_prefill_train(const void* q, const void* k, const void* v,
 
 namespace {
 struct BwdLayout {
-  uint64_t qh16, qt, da, dat, lse2, delta, kh16, kt, dqh, dkh, dw_part, total;
+  uint64_t qh16, qt, da, dat, lse2, delta, kh16, kt, dw_part, total;
 };
 uint64_t a256(uint64_t x) { return (x + 255) & ~255ull; }
 BwdLayout bwd_layout(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D) {
@@ -524,9 +524,8 @@ BwdLayout bwd_layout(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D) {
   l.delta = o; o += a256(rows);
   l.kh16 = o; o += a256(k2);
   l.kt = o; o += a256(k2);
-  l.dqh = o; o += a256(2 * q2);
-  l.dkh = o; o += a256(2 * k2);
-  l.dw_part = o; o += a256(2ull * zg::kBwdPostBlocks * D * 4);
+  const uint64_t n_blk = (uint64_t)B * Hkv * (((uint64_t)S + 31) / 32 + ((uint64_t)S + 127) / 128);
+  l.dw_part = o; o += a256(n_blk * D * 4);
   l.total = o;
   return l;
 }
@@ -588,9 +587,9 @@ int backward_common(bool gated, const void* q, const void* k, const void* v, con
   a.delta = reinterpret_cast<float*>(w + L.delta);
   a.kh16 = reinterpret_cast<uint16_t*>(w + L.kh16);
   a.kt = reinterpret_cast<uint16_t*>(w + L.kt);
-  a.dqh = reinterpret_cast<float*>(w + L.dqh);
-  a.dkh = reinterpret_cast<float*>(w + L.dkh);
   a.dw_part = reinterpret_cast<float*>(w + L.dw_part);
+  a.n_qblk = B * Hkv * ((S + 31) / 32);
+  a.n_kblk = B * Hkv * ((S + 127) / 128);
   a.B = B; a.S = S; a.Sp = (S + 127) / 128 * 128; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.window = gated ? window : 0;
   a.rot_pairs = R / 2;
@@ -613,11 +612,8 @@ int backward_common(bool gated, const void* q, const void* k, const void* v, con
     e = launch_bwd_q(a, st);
   }
   if (e != hipSuccess) return hip_fail(e, "backward dQ launch");
-  {
-    ScopedTimer tm("bwd_post", st);
-    e = launch_bwd_post(a, st);
-  }
-  if (e != hipSuccess) return hip_fail(e, "backward norm/RoPE launch");
+  e = launch_bwd_dw_reduce(a, st);
+  if (e != hipSuccess) return hip_fail(e, "backward dw reduction launch");
   return ZG_OK;
 }
 }  // namespace

@@ -157,8 +157,8 @@ int global_prefill_train(const void* q, const void* k, const void* v, const void
                          void* stream);
 
 /* Workspace bytes of the backward: staged q_hat (fp16 and transposed bf16), dA = dout (.) sigmoid(g) (bf16, also
- * transposed), per-row Delta = dout . out and lse, k_hat (fp16 and transposed bf16), fp32 dq_hat / dk_hat and the
- * norm-weight partial sums, with S rounded up to 128. */
+ * transposed), per-row Delta = dout . out and lse, k_hat (fp16 and transposed bf16), with S rounded up to 128, and
+ * the per-work-group partial sums of the norm-weight gradients. */
 uint64_t backward_workspace_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D);
 
 /* Gradients of a gated-SWA layer's output (onedev.kr "How it works": A_SWA(q,k,v) (.) sigmoid(g), with the
@@ -279,8 +279,8 @@ const char* zg_last_error(void);
 /* Kernel timer: while enabled, every launch of the main attention kernels records a pair of HIP
  * events on the launch stream.  zg_kernel_timer_read synchronises on the recorded events and returns,
  * for the kernel family `name` ("attn_swa", "attn_global", "decode_global", "decode_swa",
- * "kv_prologue", "decode_merge", "decode_append", "linear", "fp8_quantize", "bwd_prep", "bwd_kv", "bwd_q",
- * "bwd_post"), the summed device time in ms and the launch count
+ * "kv_prologue", "decode_merge", "decode_append", "linear", "fp8_quantize", "bwd_prep", "bwd_kv", "bwd_q"),
+ * the summed device time in ms and the launch count
  * since the last reset.  Enabling resets the counters. */
 int zg_kernel_timer_enable(int32_t on);
 int zg_kernel_timer_read(const char* name, double* total_ms, int64_t* launches);

@@ -144,7 +144,8 @@ def test_backward_workspace_bytes_closed_form(zg):
     Sp = (S + 127) // 128 * 128
     a = lambda n: (n + 255) // 256 * 256
     q2, k2, rows = B * Hq * Sp * D * 2, B * Hkv * Sp * D * 2, B * Hq * Sp * 4
-    want = 4 * a(q2) + 2 * a(rows) + 2 * a(k2) + a(2 * q2) + a(2 * k2) + a(2 * 512 * D * 4)
+    n_blk = B * Hkv * ((S + 31) // 32 + (S + 127) // 128)      # dQ and dK work-groups: dw partials
+    want = 4 * a(q2) + 2 * a(rows) + 2 * a(k2) + a(n_blk * D * 4)
     assert zg.backward_workspace_bytes(B, S, Hq, Hkv, D) == want
 
 
