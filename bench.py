@@ -138,7 +138,7 @@ def run_prefill(zg, steps, warmup, S=16384, B=1):
         "roofline": {"bound": "mfma", "achieved": flop_global / (g_avg / 1e3) / 1e12, "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flop_global / (g_avg / 1e3) / 1e12 / MFMA_PEAK_TFLOPS,
                      "traffic": stored_traffic("attn_global"),
-                     "kernel": "attn_prefill_kernel<global> (one global layer per launch)"},
+                     "kernel": "attn_global_kernel (one global layer per launch)"},
     }
     del layers, ws
     import torch

@@ -72,6 +72,39 @@ struct PrefillArgs {
   double inv_freq_rev[64];
 };
 
+// Global causal prefill without a cache.  The tile prologue writes the keys and values once, in the layout the
+// attention kernel copies into LDS with direct (buffer-to-LDS) loads:
+//   kt: k_hat fp16 [B][Hkv][S_pad][D]
+//   vt: v^T fp16 [B][Hkv][D][S_pad], inside each group of 16 keys the quads of 4 keys in the order 0, 2, 1, 3
+// S_pad = S rounded up to a whole 64-key tile; the padding keys are zero in both.
+struct KvTilesArgs {
+  const uint16_t* k;   // [B][S][Hkv][D] bf16
+  const uint16_t* v;   // [B][S][Hkv][D] bf16
+  const uint16_t* kw;  // [D]
+  uint16_t* kt;
+  uint16_t* vt;
+  int32_t B, S, S_pad, Hkv;
+  int32_t rot_pairs;
+  float eps;
+  double inv_freq_rev[64];
+};
+
+struct GlobalArgs {
+  const uint16_t* q;    // [B][S][Hq][D]
+  const uint16_t* qw;   // [D]
+  uint16_t* out;        // [B][S][Hq][D]
+  float* lse;           // [B][Hq][S] or null
+  const uint16_t* kt;   // tile workspace, layouts as above
+  const uint16_t* vt;
+  int32_t B, S, S_pad, Hq, Hkv, G, P;  // P = 128 / G query positions per work-group
+  int32_t rot_pairs;
+  float eps;
+  float q_scale;        // log2(e) / sqrt(D)
+  int32_t n_units;      // B * Hkv
+  int32_t n_qtiles;     // ceil(S / P)
+  double inv_freq_rev[64];
+};
+
 // Streaming gated-SWA prefill without a cache (GQA group 4, window <= 128): one work-group per run of
 // `run` consecutive positions (a multiple of 32) of one (b, kv head); k_hat is computed in the kernel.
 struct SwaStreamArgs {
@@ -183,6 +216,8 @@ struct DecodeArgs {
 hipError_t launch_kv_prologue(const KvPrologueArgs& a, hipStream_t st);
 hipError_t launch_ring_write(const RingWriteArgs& a, hipStream_t st);
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_kv_tiles(const KvTilesArgs& a, hipStream_t st);
+hipError_t launch_attn_global(const GlobalArgs& a, hipStream_t st);
 hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st);
 int32_t fp8_quantize_blocks(int64_t n);   // work-groups launch_fp8_quantize uses for n values
 hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const float* scale, float* partial,

@@ -274,7 +274,8 @@ extern "C" int kv_cache_set_length(zg_kv_cache* c, int32_t layer, int32_t b, int
 
 extern "C" uint64_t prefill_workspace_bytes(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
   if (B < 0 || S < 0 || Hkv < 0 || D < 0) return 0;
-  return 2ull * (uint64_t)B * (uint64_t)S * (uint64_t)Hkv * (uint64_t)D * 2ull;
+  const uint64_t s_pad = ((uint64_t)S + 63) / 64 * 64;   // whole 64-key tiles
+  return 2ull * (uint64_t)B * s_pad * (uint64_t)Hkv * (uint64_t)D * 2ull;
 }
 
 // ---------------------------------------------------------------------------------- prefill
@@ -368,6 +369,40 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
   const int64_t D64 = kHeadDim;
+  if (!gated && !cache) {
+    // global layer without a cache: k_hat and v^T into the tile workspace, then the direct-load kernel
+    const int32_t S_pad = (S + 63) / 64 * 64;
+    KvTilesArgs ta{};
+    ta.k = k16;
+    ta.v = v16;
+    ta.kw = static_cast<const uint16_t*>(kw);
+    ta.kt = static_cast<uint16_t*>(ws);
+    ta.vt = ta.kt + (int64_t)B * Hkv * S_pad * D64;
+    ta.B = B; ta.S = S; ta.S_pad = S_pad; ta.Hkv = Hkv; ta.rot_pairs = rot_pairs; ta.eps = eps;
+    fill_inv_freq(ta.inv_freq_rev, rot_pairs, R, base);
+    {
+      ScopedTimer tm("kv_prologue", st);
+      hipError_t e = launch_kv_tiles(ta, st);
+      if (e != hipSuccess) return hip_fail(e, "kv_tiles launch");
+    }
+    GlobalArgs ga{};
+    ga.q = static_cast<const uint16_t*>(q);
+    ga.qw = static_cast<const uint16_t*>(qw);
+    ga.out = static_cast<uint16_t*>(out);
+    ga.lse = lse;
+    ga.kt = ta.kt; ga.vt = ta.vt;
+    ga.B = B; ga.S = S; ga.S_pad = S_pad; ga.Hq = Hq; ga.Hkv = Hkv; ga.G = G; ga.P = 128 / G;
+    ga.rot_pairs = rot_pairs;
+    ga.eps = eps;
+    ga.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
+    ga.n_units = B * Hkv;
+    ga.n_qtiles = (S + ga.P - 1) / ga.P;
+    std::memcpy(ga.inv_freq_rev, ta.inv_freq_rev, sizeof ga.inv_freq_rev);
+    ScopedTimer tm("attn_global", st);
+    hipError_t e = launch_attn_global(ga, st);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ZG_OK;
+  }
   const LayerDesc* ld = cache ? &cache->layers[layer - 1] : nullptr;
 
   // 1. k_hat of the chunk, rounded to the bf16 cache format: into the cache (global layer with a cache,

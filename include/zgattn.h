@@ -99,8 +99,9 @@ int kv_cache_length(const zg_kv_cache* cache, int32_t layer, int32_t b, int64_t*
 int kv_cache_set_length(zg_kv_cache* cache, int32_t layer, int32_t b, int64_t len);
 
 /* Device workspace bytes that swa_prefill / global_prefill need for a chunk of S tokens:
- * 2 * B*Hkv*S*D 16-bit elements (the chunk's normalised, rotated keys and, for a global layer without a
- * cache, its values, staged as fp16 for the MFMAs). */
+ * 2 * B*Hkv*S_pad*D 16-bit elements, S_pad = S rounded up to a multiple of 64 (the chunk's normalised, rotated
+ * keys and, for a global layer without a cache, its transposed values, staged as fp16 for the MFMAs in whole
+ * 64-key tiles). */
 uint64_t prefill_workspace_bytes(int32_t B, int32_t S, int32_t Hkv, int32_t D);
 
 /* Gated sliding-window attention layer, prefill of S new tokens per sequence at absolute positions

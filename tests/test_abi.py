@@ -48,6 +48,9 @@ def test_footprint_closed_form_matches_oracle_and_page(zg):
 
 def test_workspace_bytes(zg):
     assert zg.workspace_bytes(1, 16384, 8) == 2 * 16384 * 8 * 128 * 2
+    # whole 64-key tiles
+    assert zg.workspace_bytes(2, 100, 8) == 2 * 2 * 128 * 8 * 128 * 2
+    assert zg.workspace_bytes(1, 1, 1) == 2 * 64 * 128 * 2
 
 
 def _swa(zg, **over):
