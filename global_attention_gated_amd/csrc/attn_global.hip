@@ -210,15 +210,30 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
     const uint16_t* kb_ = Ks + buf * kTileHalves;
     const uint16_t* vb_ = Vt + buf * kTileHalves;
     // S^T = K Q^T for the two 32-key halves; the two accumulator chains are interleaved so consecutive MFMAs are
-    // independent, and both start from -m.
+    // independent, and both start from -m.  All 16 K fragments are read first (the scheduler would otherwise put
+    // each read right before its MFMA and expose the LDS latency), and the same registers then take the 16 V^T
+    // fragments of the PV product, read while the softmax runs.
+    half8 op[16];
+#pragma unroll
+    for (int t8 = 0; t8 < 8; t8++) {
+      op[2 * t8] = *reinterpret_cast<const half8*>(kb_ + kfo[t8]);
+      op[2 * t8 + 1] = *reinterpret_cast<const half8*>(kb_ + 32 * kHeadDim + kfo[t8]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     floatx16 sacc[2];
 #pragma unroll
     for (int t8 = 0; t8 < 8; t8++) {
-      const half8 k0 = *reinterpret_cast<const half8*>(kb_ + kfo[t8]);
-      const half8 k1 = *reinterpret_cast<const half8*>(kb_ + 32 * kHeadDim + kfo[t8]);
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k0, qf[t8], t8 == 0 ? negm : sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(k1, qf[t8], t8 == 0 ? negm : sacc[1], 0, 0, 0);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[2 * t8], qf[t8], t8 == 0 ? negm : sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[2 * t8 + 1], qf[t8], t8 == 0 ? negm : sacc[1], 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+        for (int db = 0; db < 4; db++)
+          op[8 * kb + 4 * h2 + db] = *reinterpret_cast<const half8*>(vb_ + db * 32 * kBN + vfo[2 * kb + h2]);
     if (kt + kBN - 1 > wlo) {   // the diagonal cuts this tile for some row of the wave
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
@@ -276,10 +291,8 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; h2++)
 #pragma unroll
-        for (int db = 0; db < 4; db++) {
-          const half8 va = *reinterpret_cast<const half8*>(vb_ + db * 32 * kBN + vfo[2 * kb + h2]);
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[kb][h2], acc_o[db], 0, 0, 0);
-        }
+        for (int db = 0; db < 4; db++)
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[8 * kb + 4 * h2 + db], pf[kb][h2], acc_o[db], 0, 0, 0);
   };
 
   // One step: start the next tile's copy into the other buffer (free: every wave passed the barrier after its
