@@ -62,8 +62,6 @@ __device__ __forceinline__ int vt_col(int k) {
 
 __device__ __forceinline__ uint32_t dw(const uint4& w, int i) { return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w; }
 
-template <int N> struct Tiles { static constexpr int n = N; };
-
 // Chunks 2t + hi (t = 0..7) of row r of a swizzled 256-byte-row LDS buffer that this wave filled with
 // global_load_lds, in one asm block that also waits for the reads.  Written out because the compiler,
 // seeing LDS reads after loads into LDS, would otherwise wait for every memory operation in flight
@@ -210,6 +208,9 @@ __global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_num_vgpr(256))) 
 
   // ---- the norm weights and RoPE frequencies, once, into LDS (global loads issued later would wait behind
   // the streaming loads: the vector-memory counter retires in order)
+  // the ring starts as zeros: the slots of tiles before position 0 are read (and masked) by the first steps
+  for (int x = tid; x < kRing * kKTile / 16; x += 256) reinterpret_cast<uint4*>(Ks)[x] = make_uint4(0u, 0u, 0u, 0u);
+  for (int x = tid; x < kRing * kVTile / 16; x += 256) reinterpret_cast<uint4*>(Vt)[x] = make_uint4(0u, 0u, 0u, 0u);
   if (tid < 32) reinterpret_cast<uint4*>(Wn)[tid] = *reinterpret_cast<const uint4*>((tid < 16 ? a.qw : a.kw) + 8 * (tid & 15));
   if (tid < kMaxRotPairs) Fr[tid] = a.inv_freq_rev[tid];
   lds_barrier();
@@ -274,88 +275,77 @@ __global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_num_vgpr(256))) 
     if (next_tile) load_kv(T + 1);
     if (more) load_q(i0 + kStep);
 
-    // ---- attention over the ring tiles T-jmax .. T (from tile 0 on), two 32-key tiles per pass
-    // (interleaved MFMA chains), the last pass possibly one
+    // ---- attention over the whole window of the step at once: its 32 queries see keys of the ring tiles
+    // T-4 .. T only, so all their scores fit in registers and one exact max per query replaces the online
+    // rescaling.  The five score chains are independent (S^T = K Q^T per tile, interleaved over the k-steps).
+    // Tiles before the window or before position 0 are masked out (their slots hold older keys or zeros).
+    int slot_k[kRing], slot_v[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; j++) {
+      const int sl = (T - (kRing - 1) + j + kRing) % kRing;   // ring slot of tile T-4+j (T-4 >= -4)
+      slot_k[j] = sl * kKTile;
+      slot_v[j] = sl * kVTile;
+    }
+    floatx16 sacc[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) sacc[j][e] = 0.f;
+#pragma unroll
+    for (int t8 = 0; t8 < 8; t8++)
+#pragma unroll
+      for (int j = 0; j < kRing; j++) {
+        const half8 kf = *reinterpret_cast<const half8*>(Ks + slot_k[j] + k_off(0, l32, 2 * t8 + hi));
+        sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[t8], sacc[j], 0, 0, 0);
+      }
+    // mask: key visible iff 0 <= i - key < min(W, i + 1) (one unsigned compare); tiles wholly inside every
+    // window of the step skip it
+    {
+      const unsigned lim = (unsigned)min(a.window, i + 1);
+#pragma unroll
+      for (int j = 0; j < kRing; j++) {
+        const int kt = (T - (kRing - 1) + j) * kTK;
+        if (!(kt >= 0 && kt + kTK - 1 <= i0 && kt >= i0 + kStep - a.window)) {
+#pragma unroll
+          for (int e = 0; e < 16; e++) {
+            const int key = kt + 8 * (e >> 2) + 4 * hi + (e & 3);
+            if ((unsigned)(i - key) >= lim) sacc[j][e] = -INFINITY;
+          }
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRing; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sacc[j][e], sacc[j][e + 1]));
+    mx = xor32_max(mx);   // finite: every query sees its own key
+    // P = exp2(s - m) rounded to fp16; the row sum adds the same rounded values.  O^T = V^T P^T (lane: dim
+    // l32 of block db; keys 16h2 + 8hi .. +8 of the tile)
     floatx16 acc_o[4];
 #pragma unroll
     for (int db = 0; db < 4; db++)
 #pragma unroll
-      for (int j = 0; j < 16; j++) acc_o[db][j] = 0.f;
-    float m_run = 0.f, l_run = 0.f;
-    bool m_set = false;
-    auto pass = [&](auto tiles, int ta) {
-      constexpr int NT = decltype(tiles)::n;
-      const int sl[2] = {ta % kRing, (ta + 1) % kRing};
-      floatx16 sacc[NT];
+      for (int e = 0; e < 16; e++) acc_o[db][e] = 0.f;
+    float l_run = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < NT; kb++)
+    for (int j = 0; j < kRing; j++)
 #pragma unroll
-        for (int j = 0; j < 16; j++) sacc[kb][j] = 0.f;
+      for (int h2 = 0; h2 < 2; h2++) {
+        uint32_t wp[4];
 #pragma unroll
-      for (int t8 = 0; t8 < 8; t8++)
-#pragma unroll
-        for (int kb = 0; kb < NT; kb++) {
-          const half8 kf = *reinterpret_cast<const half8*>(Ks + k_off(sl[kb], l32, 2 * t8 + hi));
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[t8], sacc[kb], 0, 0, 0);
+        for (int e = 0; e < 4; e++) {
+          const int x = 8 * h2 + 2 * e;
+          wp[e] = pack_f16(__builtin_amdgcn_exp2f(sacc[j][x] - mx), __builtin_amdgcn_exp2f(sacc[j][x + 1] - mx));
+          l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2, wp[e]), ones, l_run, false);
         }
-      // mask: key visible iff 0 <= i - key < W (one unsigned compare); passes wholly inside every window of
-      // the step skip it
-      const int key0 = ta * kTK;
-      if (!(key0 + NT * kTK - 1 <= i0 && key0 >= i0 + kStep - a.window)) {
+        const half8 pf = __builtin_bit_cast(half8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
 #pragma unroll
-        for (int kb = 0; kb < NT; kb++)
-#pragma unroll
-          for (int j = 0; j < 16; j++) {
-            const int key = key0 + kb * kTK + 8 * (j >> 2) + 4 * hi + (j & 3);
-            if ((unsigned)(i - key) >= (unsigned)a.window) sacc[kb][j] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NT; kb++)
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(sacc[kb][j], sacc[kb][j + 1]));
-      mx = xor32_max(mx) - m_run;
-      // m is set on the query's first visible key and raised only when the scores exceed it by more than
-      // 2^8 (exact: the m used is carried along; every p stays <= 256)
-      const bool need = m_set ? mx > 8.0f : mx > -INFINITY;
-      if (__any(need)) {
-        const float sh = need ? mx : 0.0f;
-        const float alpha = m_set ? __builtin_amdgcn_exp2f(-sh) : 1.0f;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; db++)
-#pragma unroll
-          for (int j = 0; j < 16; j++) acc_o[db][j] *= alpha;
-        m_run += sh;
-        m_set = m_set || need;
-      }
-      // P = exp2(s - m) rounded to fp16; the row sum adds the same rounded values.  O^T += V^T P^T (lane:
-      // dim l32 of block db; keys 16h2 + 8hi .. +8 of the tile)
-#pragma unroll
-      for (int kb = 0; kb < NT; kb++)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; h2++) {
-          uint32_t wp[4];
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const int j = 8 * h2 + 2 * e;
-            wp[e] = pack_f16(__builtin_amdgcn_exp2f(sacc[kb][j] - m_run), __builtin_amdgcn_exp2f(sacc[kb][j + 1] - m_run));
-            l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2, wp[e]), ones, l_run, false);
-          }
-          const half8 pf = __builtin_bit_cast(half8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
-#pragma unroll
-          for (int db = 0; db < 4; db++) {
-            const half8 va = *reinterpret_cast<const half8*>(Vt + vt_off(sl[kb], 32 * db + l32, 2 * h2 + hi));
-            acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf, acc_o[db], 0, 0, 0);
-          }
+        for (int db = 0; db < 4; db++) {
+          const half8 va = *reinterpret_cast<const half8*>(Vt + slot_v[j] + vt_off(0, 32 * db + l32, 2 * h2 + hi));
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf, acc_o[db], 0, 0, 0);
         }
-    };
-    {
-      int ta = max(T - jmax, 0);
-      for (; ta + 1 <= T; ta += 2) pass(Tiles<2>{}, ta);
-      if (ta == T) pass(Tiles<1>{}, ta);
-    }
+      }
 
     // ---- epilogue.  acc_o[db][j] is dim d = 32db + 8(j/4) + 4hi + j%4 of row r = 32w + l32.
     const float inv_l = 1.0f / xor32_sum(l_run);
