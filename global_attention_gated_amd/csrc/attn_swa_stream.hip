@@ -176,35 +176,35 @@ __global__ void __launch_bounds__(256, 2) __attribute__((amdgpu_num_vgpr(256))) 
     }
   };
 
-  // ---- q rows of a step -> QS, straight from HBM: wave w loads the 32 rows of its own head kvh*4 + w
-  // (positions i0 .. i0+31, clamped into the sequence; rows past the end are computed but not stored), so
-  // only the wave itself reads them and no barrier is needed.  Lane l of instruction k fills row
-  // 32w + 4k + l/16, chunk position l%16.
-  auto load_q = [&](int i0) {
+  // ---- q rows and gate rows of a step -> QS / GO, straight from HBM (buffer loads with LDS as the destination,
+  // 64 lanes x 16 B per instruction).  Wave w loads the 32 rows of its own head kvh*4 + w: lane l of instruction
+  // k fills row 32w + 4k + l/16 (position i0 + 4k + l/16), chunk position l%16, which holds the row's chunk
+  // (l%16) ^ (row%16).  Rows 0..15 and 16..31 of the step go through two descriptors whose ranges end with the
+  // sequence (rows past it read as zero; their outputs are computed but not stored), so the per-lane byte
+  // offsets are the same for both halves and for every step: 4 registers for the whole kernel.
+  uint32_t qg_off[4];
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const int row = 32 * wave + 4 * k + (lane >> 4);
-      const int c = (lane & 15) ^ (row & 15);
-      const int i = min(i0 + (row & 31), a.S - 1);
-      const uint16_t* src = qb + (int64_t)i * rowHq + (int64_t)wave * kHeadDim + 8 * c;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(QS + (32 * wave + 4 * k) * 256), 16, 0, 0);
-    }
+  for (int k = 0; k < 4; k++) {
+    const int rr = 4 * k + (lane >> 4);                   // position within the half step, 0..15
+    const int c = (lane & 15) ^ rr;
+    qg_off[k] = (uint32_t)(((int64_t)rr * rowHq + wave * kHeadDim + 8 * c) * 2);
+  }
+  auto half_rows = [&](const uint16_t* base, int p0) {    // positions p0 .. p0+15, clipped to the sequence
+    const int nvalid = min(kStep / 2, a.S - p0);
+    const int bytes = nvalid > 0 ? (int)(((int64_t)(nvalid - 1) * rowHq + kGroup * kHeadDim) * 2) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)min(p0, a.S - 1) * rowHq), (short)0, bytes,
+                                             0x00020000);
   };
-  // ---- gate tile of a step -> GO, straight from HBM (global_load_lds: 64 lanes x 16 B per instruction,
-  // lane l of instruction k of wave w fills row 4(8w + k) + l/16, chunk position l%16)
-  auto load_gate = [&](int i0) {
+  auto load_rows = [&](const uint16_t* base, unsigned char* dst, int i0) {
+    const __amdgpu_buffer_rsrc_t r0 = half_rows(base, i0), r1 = half_rows(base, i0 + kStep / 2);
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const int row = 4 * (8 * wave + k) + (lane >> 4);
-      const int cp = lane & 15;
-      const int c = cp ^ (row & 15);                       // swizzled: position cp holds chunk c
-      const int i = min(i0 + (row & 31), a.S - 1);
-      const uint16_t* src = gb + (int64_t)i * rowHq + (int64_t)(row >> 5) * kHeadDim + 8 * c;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(GO + (8 * wave + k) * 1024), 16, 0, 0);
-    }
+    for (int k = 0; k < 8; k++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k < 4 ? r0 : r1,
+                                               (__attribute__((address_space(3))) void*)(dst + (32 * wave + 4 * k) * 256),
+                                               16, (int)qg_off[k & 3], 0, 0, 0);
   };
+  auto load_q = [&](int i0) { load_rows(qb, QS, i0); };
+  auto load_gate = [&](int i0) { load_rows(gb, GO, i0); };
 
   // ---- the norm weights and RoPE frequencies, once, into LDS (global loads issued later would wait behind
   // the streaming loads: the vector-memory counter retires in order)
