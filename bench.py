@@ -99,14 +99,22 @@ def run_prefill(zg, steps, warmup, S=16384, B=1):
     for _ in range(warmup):
         prefill_step(zg, layers, ws)
     sync()
-    zg.kernel_timer_enable(True)
+    # Timed steps: only the roofline kernel (the global layer's attention) records events, so the step time
+    # carries the cost of 10 events per step, not of 74.  The other kernels' durations come from a short pass
+    # after the timed steps, with every kernel timed.
+    zg.kernel_timer_enable(True, only="attn_global")
     sync()
     t0 = time.perf_counter()
     for _ in range(steps):
         prefill_step(zg, layers, ws)
     sync()
     t1 = time.perf_counter()
-    kt = {n: zg.kernel_timer_read(n) for n in ("attn_global", "attn_swa", "kv_prologue")}
+    kt = {"attn_global": zg.kernel_timer_read("attn_global")}
+    zg.kernel_timer_enable(True)
+    for _ in range(min(steps, 3)):
+        prefill_step(zg, layers, ws)
+    sync()
+    kt.update({n: zg.kernel_timer_read(n) for n in ("attn_swa", "kv_prologue")})
     zg.kernel_timer_enable(False)
     ms = (t1 - t0) * 1e3 / steps
     pairs_global = S * (S + 1) // 2
@@ -134,6 +142,8 @@ def run_prefill(zg, steps, warmup, S=16384, B=1):
                          "traffic": stored_traffic("attn_swa"),
                          "tflops": flop_swa / (s_avg / 1e3) / 1e12},
             "kv_prologue": {"avg_ms": p_ms / max(p_n, 1), "launches": p_n},
+            "timing": "attn_global: HIP events over the timed steps; attn_swa, kv_prologue: HIP events over a "
+                      "pass of up to 3 steps right after them",
         },
         "roofline": {"bound": "mfma", "achieved": flop_global / (g_avg / 1e3) / 1e12, "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flop_global / (g_avg / 1e3) / 1e12 / MFMA_PEAK_TFLOPS,

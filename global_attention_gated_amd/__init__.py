@@ -82,6 +82,7 @@ _lib.global_prefill_backward.argtypes = [_vp] * 13 + [_i32] * 6 + [_f64, _f32, _
 _lib.zg_last_error.restype = ctypes.c_char_p
 _lib.zg_kernel_timer_enable.argtypes = [_i32]
 _lib.zg_kernel_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_f64), ctypes.POINTER(_i64)]
+_lib.zg_kernel_timer_only.argtypes = [ctypes.c_char_p]
 
 EXPORTED = ["kv_cache_alloc", "kv_cache_free", "kv_cache_footprint_bytes", "kv_cache_layer_view", "kv_cache_length",
             "kv_cache_set_length", "prefill_workspace_bytes", "swa_prefill", "global_prefill", "hybrid_decode_step",
@@ -90,7 +91,7 @@ EXPORTED = ["kv_cache_alloc", "kv_cache_free", "kv_cache_footprint_bytes", "kv_c
             "fp8_layer_alloc", "fp8_layer_free", "fp8_layer_scales", "fp8_layer_workspace_bytes", "gated_swa_layer_fp8",
             "global_layer_fp8", "swa_prefill_train", "global_prefill_train", "backward_workspace_bytes",
             "swa_prefill_backward", "global_prefill_backward", "zg_last_error", "zg_kernel_timer_enable",
-            "zg_kernel_timer_read"]
+            "zg_kernel_timer_read", "zg_kernel_timer_only"]
 
 
 class ZgError(RuntimeError):
@@ -497,7 +498,9 @@ def hybrid_decode_step(q, k, v, gate, q_norm_w, k_norm_w, positions, cache: KVCa
 
 
 # ------------------------------------------------------------------------------------------- timer
-def kernel_timer_enable(on: bool = True):
+def kernel_timer_enable(on: bool = True, only: str = None):
+    """Enable (and reset) or disable the kernel timer; `only` restricts it to one kernel family."""
+    _check(_lib.zg_kernel_timer_only((only or "").encode()))
     _check(_lib.zg_kernel_timer_enable(1 if on else 0))
 
 

@@ -53,6 +53,7 @@ struct TimerEntry {
 };
 std::mutex g_timer_mu;
 bool g_timer_on = false;
+std::string g_timer_only;   // when not empty, only this kernel family is timed
 std::vector<TimerEntry> g_timer_log;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_timer_pool;
 
@@ -63,6 +64,7 @@ struct ScopedTimer {
   ScopedTimer(const char* name, hipStream_t s) : st(s) {
     std::lock_guard<std::mutex> lk(g_timer_mu);
     if (!g_timer_on) return;
+    if (!g_timer_only.empty() && g_timer_only != name) return;
     if (g_timer_pool.empty()) {
       hipEvent_t a, b;
       if (hipEventCreate(&a) != hipSuccess) return;
@@ -1112,6 +1114,12 @@ extern "C" int zg_kernel_timer_enable(int32_t on) {
   for (auto& t : g_timer_log) g_timer_pool.push_back({t.start, t.stop});
   g_timer_log.clear();
   g_timer_on = on != 0;
+  return ZG_OK;
+}
+
+extern "C" int zg_kernel_timer_only(const char* name) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_timer_only = name ? name : "";
   return ZG_OK;
 }
 

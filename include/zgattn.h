@@ -285,6 +285,9 @@ const char* zg_last_error(void);
  * since the last reset.  Enabling resets the counters. */
 int zg_kernel_timer_enable(int32_t on);
 int zg_kernel_timer_read(const char* name, double* total_ms, int64_t* launches);
+/* Restrict the kernel timer to one kernel family (`name` as above), so that a timed run pays for the events of
+ * that family only; NULL or "" times every family again.  Takes effect for launches made after the call. */
+int zg_kernel_timer_only(const char* name);
 
 #ifdef __cplusplus
 }
