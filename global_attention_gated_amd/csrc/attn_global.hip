@@ -243,11 +243,14 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
           if (key > qpos) sacc[kb][j] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // row max: two chains of three-input maxima (v_max3), one per 32-key half
+    float mx0 = sacc[0][0], mx1 = sacc[1][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) mx = fmaxf(mx, fmaxf(sacc[kb][j], sacc[kb][j + 1]));
+    for (int j = 1; j < 15; j += 2) {
+      mx0 = fmaxf(fmaxf(mx0, sacc[0][j]), sacc[0][j + 1]);
+      mx1 = fmaxf(fmaxf(mx1, sacc[1][j]), sacc[1][j + 1]);
+    }
+    float mx = fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15]));
     mx = xor32_max(mx);
     // mx is the tile's max relative to m.  m is raised only when the scores exceed it by more than 2^8 (exact:
     // the m used is carried along; every p stays <= 256), or set on the query's first visible key.
