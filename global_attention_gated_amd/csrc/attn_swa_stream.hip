@@ -330,6 +330,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     const float inv_l = 1.0f / l_run;
+    // training: the log-sum-exp of the query's scores (natural log; scores in log2 units are s log2(e))
+    if (a.lse && g == 0 && i < p_end)
+      a.lse[((int64_t)b * a.Hq + kvh * kGroup + head) * a.S + i] = (mx + __log2f(l_run)) * 0.6931471805599453f;
 
     // ---- epilogue.  acc_o[db][e] is dim d = 16db + 4g + e of this lane's query row.
     // This wave's gate rows have landed in GO: they were issued before the next key/value tile (2 loads) and

@@ -122,6 +122,7 @@ struct SwaStreamArgs {
   float q_scale;         // log2(e) / sqrt(D)
   int32_t n_units;       // B * Hkv
   int32_t run;           // positions per work-group
+  float* lse;            // [B][Hq][S] natural log of each softmax denominator (training), or null
   double inv_freq_rev[64];
 };
 

@@ -345,7 +345,7 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rot_pairs = R / 2;
   if (lse && cache) return fail(ZG_EINVAL, "%s: the training forward takes no cache", fn);
-  if (gated && !cache && G == 4 && window <= 128 && !lse) {
+  if (gated && !cache && G == 4 && window <= 128) {
     // streaming SWA kernel: k_hat computed in its tile loader, no workspace pass
     SwaStreamArgs sa{};
     sa.q = static_cast<const uint16_t*>(q);
@@ -362,6 +362,7 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
     sa.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
     sa.n_units = B * Hkv;
     sa.run = swa_stream_run_length(S, sa.n_units);
+    sa.lse = lse;
     fill_inv_freq(sa.inv_freq_rev, rot_pairs, R, base);
     ScopedTimer tm("attn_swa", st);
     hipError_t e = launch_swa_stream(sa, st);
