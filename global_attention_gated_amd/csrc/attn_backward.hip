@@ -32,12 +32,10 @@ namespace zg {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16v8;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kT = 32;          // query / key tile of the MFMA kernels
 constexpr int kG = 4;           // GQA group (query heads per KV head), the one shape the host accepts
-constexpr int kRowS = 136;      // LDS row stride (halves) of [32][128] tiles: 16-byte pad
-constexpr int kTrS = 36;        // LDS row stride (halves) of [128][32] transposed tiles: 72 B, so 16 lanes'
-                                // 8-byte reads at consecutive rows cover all 128 bytes of the banks once
 constexpr int kPrepTok = 64;    // tokens per prep work-group
 constexpr int kPrepTS = 72;     // LDS row stride (halves) of the prep transpose tiles [128][64]
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima (no wait)
@@ -57,14 +55,48 @@ __device__ __forceinline__ bf16v8 c8_to_bf16(const floatx16& c, int j0) {
                               pack_bf16(c[j0 + 6], c[j0 + 7])));
 }
 
-// A-operand fragment of a transposed [128][kTrS] tile for k-step t: row `row`, the 8 columns
-// 16t + 4hi + {0..3} and 16t + 8 + 4hi + {0..3} (the order in which an MFMA C block holds its rows, so the
-// fragment pairs with a B operand built from C registers 8t..8t+7).
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS tile images, filled by buffer loads whose destination is LDS (16 bytes per lane at consecutive addresses;
+// the lanes pick their source chunks so the images come out XOR-swizzled, and reads of one chunk by 16 lanes of 16
+// consecutive rows hit all 64 banks once):
+//   row-major [32 rows][128] (q_hat', dA, k_hat, v): 16-byte chunk c of row r at position c ^ (r % 16)
+//   transposed [128 rows][32] (q_hat^T, dA^T, k_hat^T): chunk c (8 columns) of row r at position c ^ ((r / 4) % 4)
+// The transposed workspace tensors hold, within each group of 16 tokens, the quads of 4 tokens in the order
+// 0, 2, 1, 3 (the prep writes them so): the 8 columns 16t + 4hi + {0..3} and 16t + 8 + 4hi + {0..3}, the order in
+// which an MFMA C block holds its rows, are then the stored columns 16t + 8hi .. +7, one chunk.
+__device__ __forceinline__ int rm_off(int row, int chunk) { return row * kHeadDim + 8 * (chunk ^ (row & 15)); }
+__device__ __forceinline__ int tr_off(int row, int chunk) { return row * kT + 8 * (chunk ^ ((row >> 2) & 3)); }
+
+// Tile reads go through vector types, not the uint4 / float4 structs: a struct copy carries no type-based alias
+// information, and without it the compiler makes each LDS read wait for every tile load in flight (the next
+// tile's included), which would leave nothing of the prefetch.
+__device__ __forceinline__ half8 ld_h8(const uint16_t* p) { return *reinterpret_cast<const half8*>(p); }
+__device__ __forceinline__ bf16v8 ld_b8(const uint16_t* p) { return *reinterpret_cast<const bf16v8*>(p); }
+
+// A-operand fragment of a transposed tile for k-step t: row `row`, columns 16t + 4hi + {0..3}, 16t + 8 + 4hi +
+// {0..3} (pairs with a B operand built from C registers 8t..8t+7)
 __device__ __forceinline__ bf16v8 tr_frag(const uint16_t* tile, int row, int t, int hi) {
-  const uint16_t* p = tile + row * kTrS + 16 * t + 4 * hi;
-  const uint2 lo = *reinterpret_cast<const uint2*>(p);
-  const uint2 hh = *reinterpret_cast<const uint2*>(p + 8);
-  return as_bf16v8(make_uint4(lo.x, lo.y, hh.x, hh.y));
+  return ld_b8(tile + tr_off(row, 2 * t + hi));
+}
+
+// Byte offsets of a lane's 16-byte sources when wave w copies the 1 KB blocks 2w, 2w+1 of an 8 KB tile:
+// row-major (block j = rows 4j..4j+3; source rows `stride` bytes apart) and transposed (block j = rows 16j..16j+15).
+__device__ __forceinline__ uint32_t rm_src(int wave, int jj, int lane, uint32_t stride) {
+  const int row = 4 * (2 * wave + jj) + (lane >> 4);
+  return (uint32_t)row * stride + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+}
+__device__ __forceinline__ uint32_t tr_src(int wave, int jj, int lane, uint32_t stride) {
+  const int row = 16 * (2 * wave + jj) + (lane >> 2);
+  return (uint32_t)row * stride + 16u * (uint32_t)((lane & 3) ^ ((row >> 2) & 3));
+}
+__device__ __forceinline__ void dma_tile(const __amdgpu_buffer_rsrc_t& r, uint16_t* tile, int wave, const uint32_t (&off)[2]) {
+#pragma unroll
+  for (int jj = 0; jj < 2; jj++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + (2 * wave + jj) * 512), 16, (int)off[jj], 0, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // ------------------------------------------------------------------------------------------ prep
@@ -144,10 +176,12 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
     }
     const uint16_t* p1 = reinterpret_cast<const uint16_t*>(&t1);
     const uint16_t* p2 = reinterpret_cast<const uint16_t*>(&t2);
+    const int qd = (row >> 2) & 3;   // transposed column: quads of 4 tokens in the order 0, 2, 1, 3 per 16
+    const int col = (row & ~15) | (4 * (qd == 1 ? 2 : qd == 2 ? 1 : qd)) | (row & 3);
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      T1[(8 * c + e) * kPrepTS + row] = p1[e];
-      if (qmode) T2[(8 * c + e) * kPrepTS + row] = p2[e];
+      T1[(8 * c + e) * kPrepTS + col] = p1[e];
+      if (qmode) T2[(8 * c + e) * kPrepTS + col] = p2[e];
     }
   }
   __syncthreads();
@@ -249,19 +283,13 @@ __device__ __forceinline__ void norm_rope_bwd_rows(const floatx16 (&acc)[4], con
   red[d0 + 1] = dy[1];
 }
 
-// 8-byte halves of a 16-byte chunk into a transposed tile row (its rows are 8- but not 16-byte aligned)
-__device__ __forceinline__ void st_tr(uint16_t* dst, const uint4& v) {
-  reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
-  reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
-}
-
 // One query tile of the key-centric kernels.  The dV kernel needs q_hat' (scores) and dA^T; the dK kernel
 // q_hat' (scores), dA (dP) and q_hat^T.
 template <bool DK>
 struct KvStage {
-  uint16_t qs[kT * kRowS];              // q_hat' fp16 [32 queries][128]
-  uint16_t xs[DK ? kT * kRowS : 8];     // dK: dA bf16 [32][128]
-  uint16_t xts[kHeadDim * kTrS];        // dV: dA^T, dK: q_hat^T, bf16 [128][32]
+  uint16_t qs[kT * kHeadDim];           // q_hat' fp16 [32 queries][128], row-major image
+  uint16_t xs[DK ? kT * kHeadDim : 8];  // dK: dA bf16 [32][128], row-major image
+  uint16_t xts[kHeadDim * kT];          // dV: dA^T, dK: q_hat^T, bf16 [128][32], transposed image
   float lse2[kT];
   float dl[kT];
 };
@@ -274,7 +302,8 @@ template <bool DK>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_kv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) KvStage<DK> st[2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS destinations of the tile loads
   const int n_units = a.B * a.Hkv;
   const int unit = blockIdx.x % n_units, kb = blockIdx.x / n_units;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
@@ -314,44 +343,36 @@ bwd_kv_kernel(BwdArgs a) {
   const int n_it = ntiles * kG;
   const int wq_end = swa ? min(a.S, j0 + 31 + a.window) : a.S;   // this wave's visible queries [j0, wq_end)
 
-  // staging: 2 x 16-byte chunks per tile per thread, plus lse / Delta.  Named registers, not an array: an array
-  // captured by the lambdas is left in memory (LDS or scratch) by the compiler, which makes every prefetch
-  // synchronous.
-  uint4 pq0, pq1, pt0, pt1, px0, px1;
+  // staging: the tiles go from the workspace straight into LDS (2 x 16 bytes per lane and tile); lse / Delta
+  // through a register
   float pf = 0.f;
-  const int r0 = tid >> 4, r1 = (tid + 256) >> 4, cc = tid & 15;   // row-major chunks (rows r0, r1; chunk cc)
-  const int d0 = tid >> 2, d1 = (tid + 256) >> 2, pt = tid & 3;    // transposed chunks (dims d0, d1; part pt)
+  // lanes 0..31 fetch lse, 32..63 (dK) Delta.  The pointer is picked by arithmetic: a select of the two arguments
+  // becomes a load of the pointer from the argument block at a per-lane offset, and its wait in the loop would also
+  // wait for the tile loads.
+  const float* pf_src = reinterpret_cast<const float*>(
+      reinterpret_cast<uintptr_t>(a.lse2) +
+      (tid >= 32 ? reinterpret_cast<uintptr_t>(a.delta) - reinterpret_cast<uintptr_t>(a.lse2) : (uintptr_t)0));
+  const uint32_t rm_o[2] = {rm_src(wave, 0, lane, kHeadDim * 2), rm_src(wave, 1, lane, kHeadDim * 2)};
+  const uint32_t tr_o[2] = {tr_src(wave, 0, lane, (uint32_t)a.Sp * 2), tr_src(wave, 1, lane, (uint32_t)a.Sp * 2)};
   // Tiles are walked from the last one down, the group's heads inside each tile: every work-group of a
   // (sequence, KV head) starts at the same last tile and advances at the same pace, so the work-groups running
   // together on an XCD read the same tiles at about the same time and share them through its L2.
   auto tile_q0 = [&](int it) { return (qt1 - 1 - it / kG) * kT; };
-  auto load_stage = [&](int it) {
+  // issue the loads of tile `it` into buffer buf (the tiles lie wholly inside the workspace: q0 + 32 <= Sp)
+  auto load_stage = [&](int it, int buf) {
     const int hq = kvh * kG + it % kG;
     const int q0 = tile_q0(it);
     const int64_t bh = (int64_t)b * a.Hq + hq;
-    const uint16_t* qrow = a.qh16 + (bh * a.Sp + q0) * kHeadDim + 8 * cc;
-    pq0 = *reinterpret_cast<const uint4*>(qrow + r0 * kHeadDim);
-    pq1 = *reinterpret_cast<const uint4*>(qrow + r1 * kHeadDim);
-    const uint16_t* trow = (DK ? a.qt : a.dat) + (bh * kHeadDim) * a.Sp + q0 + 8 * pt;
-    pt0 = *reinterpret_cast<const uint4*>(trow + (int64_t)d0 * a.Sp);
-    pt1 = *reinterpret_cast<const uint4*>(trow + (int64_t)d1 * a.Sp);
-    if constexpr (DK) {
-      const uint16_t* xrow = a.da + (bh * a.Sp + q0) * kHeadDim + 8 * cc;
-      px0 = *reinterpret_cast<const uint4*>(xrow + r0 * kHeadDim);
-      px1 = *reinterpret_cast<const uint4*>(xrow + r1 * kHeadDim);
-    }
-    if (tid < (DK ? 64 : 32)) pf = (tid < 32 ? a.lse2 : a.delta)[bh * a.Sp + q0 + (tid & 31)];
+    KvStage<DK>& s = st[buf];
+    dma_tile(rsrc(a.qh16 + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2), s.qs, wave, rm_o);
+    dma_tile(rsrc((DK ? a.qt : a.dat) + bh * kHeadDim * a.Sp + q0, (uint32_t)(kHeadDim * a.Sp - q0) * 2), s.xts, wave,
+             tr_o);
+    if constexpr (DK) dma_tile(rsrc(a.da + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2), s.xs, wave, rm_o);
+    if (tid < (DK ? 64 : 32)) pf = pf_src[bh * a.Sp + q0 + (tid & 31)];
   };
+  // the small arrays, once their loads are in; the tile loads before them retire with them (in order)
   auto store_stage = [&](int buf) {
     KvStage<DK>& s = st[buf];
-    *reinterpret_cast<uint4*>(&s.qs[r0 * kRowS + 8 * cc]) = pq0;
-    *reinterpret_cast<uint4*>(&s.qs[r1 * kRowS + 8 * cc]) = pq1;
-    st_tr(&s.xts[d0 * kTrS + 8 * pt], pt0);
-    st_tr(&s.xts[d1 * kTrS + 8 * pt], pt1);
-    if constexpr (DK) {
-      *reinterpret_cast<uint4*>(&s.xs[r0 * kRowS + 8 * cc]) = px0;
-      *reinterpret_cast<uint4*>(&s.xs[r1 * kRowS + 8 * cc]) = px1;
-    }
     if (tid < 32) s.lse2[tid] = pf;
     else if (DK && tid < 64) s.dl[tid - 32] = pf;
   };
@@ -365,20 +386,19 @@ bwd_kv_kernel(BwdArgs a) {
     floatx16 sacc, dpacc;
 #pragma unroll
     for (int jq = 0; jq < 4; jq++) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&s.lse2[8 * jq + 4 * hi]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s.lse2[8 * jq + 4 * hi]);
       sacc[4 * jq] = -l4.x; sacc[4 * jq + 1] = -l4.y; sacc[4 * jq + 2] = -l4.z; sacc[4 * jq + 3] = -l4.w;
       if constexpr (DK) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&s.dl[8 * jq + 4 * hi]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s.dl[8 * jq + 4 * hi]);
         dpacc[4 * jq] = -d4.x; dpacc[4 * jq + 1] = -d4.y; dpacc[4 * jq + 2] = -d4.z; dpacc[4 * jq + 3] = -d4.w;
       }
     }
     if constexpr (DK) {
 #pragma unroll
       for (int t = 0; t < 8; t++) {
-        const uint4 qa = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 8 * hi]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(qa), as_half8(kf[t]), sacc, 0, 0, 0);
-        const uint4 da = *reinterpret_cast<const uint4*>(&s.xs[l32 * kRowS + 16 * t + 8 * hi]);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16v8(da), as_bf16v8(vf[t]), dpacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]), as_half8(kf[t]), sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_b8(&s.xs[rm_off(l32, 2 * t + hi)]), as_bf16v8(vf[t]), dpacc, 0,
+                                                        0, 0);
       }
     } else {
       // two independent chains (even and odd k-steps) so consecutive MFMAs do not wait on each other
@@ -387,10 +407,10 @@ bwd_kv_kernel(BwdArgs a) {
       for (int j = 0; j < 16; j++) s2[j] = 0.f;
 #pragma unroll
       for (int t = 0; t < 8; t += 2) {
-        const uint4 qa = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 8 * hi]);
-        const uint4 qb = *reinterpret_cast<const uint4*>(&s.qs[l32 * kRowS + 16 * t + 16 + 8 * hi]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(qa), as_half8(kf[t]), sacc, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(qb), as_half8(kf[t + 1]), s2, 0, 0, 0);
+        const half8 qa = ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]);
+        const half8 qb = ld_h8(&s.qs[rm_off(l32, 2 * t + 2 + hi)]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, as_half8(kf[t]), sacc, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qb, as_half8(kf[t + 1]), s2, 0, 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < 16; j++) sacc[j] += s2[j];
@@ -423,27 +443,36 @@ bwd_kv_kernel(BwdArgs a) {
   };
 
   if (n_it > 0) {
-    load_stage(0);
+    load_stage(0, 0);
     store_stage(0);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the tile loads write LDS without the compiler waiting for them
   __syncthreads();
-  for (int it = 0; it < n_it; it++) {
-    const int buf = it & 1;
+  // Two steps per pass, so that each step's buffer is a constant (with a computed buffer index the compiler waits
+  // for the next tile's loads before the compute's first LDS read).
+  auto step = [&](int it, int buf) {
     const bool more = it + 1 < n_it;
-    if (more) load_stage(it + 1);
+    if (more) load_stage(it + 1, buf ^ 1);
     compute(buf, it);
-    // Keep the stores of the prefetched tile after the compute: they go to the other buffer, so the compiler
-    // would otherwise move them (and the waits for their loads) up against the loads, which makes the prefetch
-    // synchronous.
+    // Keep the stores of the prefetched small arrays after the compute: they go to the other buffer, so the
+    // compiler would otherwise move them (and the wait for their loads) up against the loads, which makes the
+    // prefetch synchronous.
     asm volatile("" ::: "memory");
     if (more) store_stage(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+  };
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, 0);
+    if (it + 1 < n_it) step(it + 1, 1);
   }
 
   // outputs: C layout reg j of block db is dim 32db + 8(j/4) + 4hi + j%4 of this lane's key
   if constexpr (DK) {
     // dk: back through RoPE and the key RMSNorm here; the work-group's 128 keys' share of dw_k into its partial
-    __shared__ float red[4][kHeadDim];
+    // the weight-gradient sums in the tile buffers (free after the loop's last barrier): a second LDS array would
+    // give the tile reads alias scopes that make them wait for the tile loads in flight
+    float (*red)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&st[0]);
     const int64_t row = ((int64_t)b * a.S + key) * a.Hkv + kvh;
     const bool valid = key < a.S;
     norm_rope_bwd_rows(acc, valid ? a.k + row * kHeadDim : nullptr, a.kw, valid ? a.dk + row * kHeadDim : nullptr,
@@ -466,14 +495,15 @@ bwd_kv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------------------------ dQ
 struct QStage {
-  uint16_t ks[kT * kRowS];         // k_hat fp16 [32 keys][128]
-  uint16_t vs[kT * kRowS];         // v bf16 [32][128]
-  uint16_t kts[kHeadDim * kTrS];   // k_hat^T bf16 [128][32]
+  uint16_t ks[kT * kHeadDim];      // k_hat fp16 [32 keys][128], row-major image
+  uint16_t vs[kT * kHeadDim];      // v bf16 [32][128], row-major image
+  uint16_t kts[kHeadDim * kT];     // k_hat^T bf16 [128][32], transposed image
 };
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_q_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) QStage st[2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS destinations of the tile loads
   const int n_units = a.B * a.Hkv;
   const int n_qt = (a.S + kT - 1) / kT;
   const int unit = blockIdx.x % n_units, rank = blockIdx.x / n_units;
@@ -510,36 +540,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int kt0 = k_beg / kT, kt1 = (k_end + kT - 1) / kT;
   const int n_it = kt1 - kt0;
 
-  // staging in named registers (see bwd_kv_kernel): 2 x 16-byte chunks per tile per thread; wave-uniform bases
-  // plus 32-bit lane offsets
-  uint4 pk0, pk1, pv0, pv1, pt0, pt1;
-  const int r0 = tid >> 4, r1 = (tid + 256) >> 4, cc = tid & 15;
-  const int d0 = tid >> 2, d1 = (tid + 256) >> 2, pt = tid & 3;
-  const uint16_t* kbase = a.kh16 + (int64_t)unit * a.Sp * kHeadDim;
-  const uint16_t* tbase = a.kt + (int64_t)unit * kHeadDim * a.Sp;
-  const uint16_t* vbase = a.v + ((int64_t)b * a.S * a.Hkv + kvh) * kHeadDim;
-  const int ok0 = r0 * kHeadDim + 8 * cc, ok1 = r1 * kHeadDim + 8 * cc;
-  const int ot0 = d0 * a.Sp + 8 * pt, ot1 = d1 * a.Sp + 8 * pt;
-  const int vrow = a.Hkv * kHeadDim;
-  auto load_stage = [&](int it) {
+  // staging: the tiles go from the workspace (k_hat, k_hat^T) and the input (v) straight into LDS, 2 x 16 bytes
+  // per lane and tile.  v rows are Hkv * 128 elements apart; the descriptor ends after the sequence's last row, so
+  // the rows of a tile past it read zeros (their keys are masked).
+  const uint32_t vstride = (uint32_t)a.Hkv * kHeadDim * 2;
+  const uint32_t rm_o[2] = {rm_src(wave, 0, lane, kHeadDim * 2), rm_src(wave, 1, lane, kHeadDim * 2)};
+  const uint32_t rv_o[2] = {rm_src(wave, 0, lane, vstride), rm_src(wave, 1, lane, vstride)};
+  const uint32_t tr_o[2] = {tr_src(wave, 0, lane, (uint32_t)a.Sp * 2), tr_src(wave, 1, lane, (uint32_t)a.Sp * 2)};
+  auto load_stage = [&](int it, int buf) {
     const int k0 = (kt0 + it) * kT;
-    const uint16_t* kb = kbase + k0 * kHeadDim;
-    pk0 = *reinterpret_cast<const uint4*>(kb + ok0);
-    pk1 = *reinterpret_cast<const uint4*>(kb + ok1);
-    pv0 = *reinterpret_cast<const uint4*>(vbase + (int64_t)min(k0 + r0, a.S - 1) * vrow + 8 * cc);
-    pv1 = *reinterpret_cast<const uint4*>(vbase + (int64_t)min(k0 + r1, a.S - 1) * vrow + 8 * cc);
-    const uint16_t* tb = tbase + k0;
-    pt0 = *reinterpret_cast<const uint4*>(tb + ot0);
-    pt1 = *reinterpret_cast<const uint4*>(tb + ot1);
-  };
-  auto store_stage = [&](int buf) {
     QStage& s = st[buf];
-    *reinterpret_cast<uint4*>(&s.ks[r0 * kRowS + 8 * cc]) = pk0;
-    *reinterpret_cast<uint4*>(&s.ks[r1 * kRowS + 8 * cc]) = pk1;
-    *reinterpret_cast<uint4*>(&s.vs[r0 * kRowS + 8 * cc]) = pv0;
-    *reinterpret_cast<uint4*>(&s.vs[r1 * kRowS + 8 * cc]) = pv1;
-    st_tr(&s.kts[d0 * kTrS + 8 * pt], pt0);
-    st_tr(&s.kts[d1 * kTrS + 8 * pt], pt1);
+    dma_tile(rsrc(a.kh16 + ((int64_t)unit * a.Sp + k0) * kHeadDim, kT * kHeadDim * 2), s.ks, wave, rm_o);
+    dma_tile(rsrc(a.v + (((int64_t)b * a.S + k0) * a.Hkv + kvh) * kHeadDim,
+                  (uint32_t)(a.S - 1 - k0) * vstride + kHeadDim * 2),
+             s.vs, wave, rv_o);
+    dma_tile(rsrc(a.kt + (int64_t)unit * kHeadDim * a.Sp + k0, (uint32_t)(kHeadDim * a.Sp - k0) * 2), s.kts, wave,
+             tr_o);
   };
   auto compute = [&](int buf, int it) {
     const int k0 = (kt0 + it) * kT;
@@ -554,10 +570,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 #pragma unroll
     for (int t = 0; t < 8; t++) {
-      const uint4 ka = *reinterpret_cast<const uint4*>(&s.ks[l32 * kRowS + 16 * t + 8 * hi]);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(ka), as_half8(qf[t]), sacc, 0, 0, 0);
-      const uint4 va = *reinterpret_cast<const uint4*>(&s.vs[l32 * kRowS + 16 * t + 8 * hi]);
-      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16v8(va), as_bf16v8(daf[t]), dpacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld_h8(&s.ks[rm_off(l32, 2 * t + hi)]), as_half8(qf[t]), sacc, 0, 0, 0);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_b8(&s.vs[rm_off(l32, 2 * t + hi)]), as_bf16v8(daf[t]), dpacc, 0, 0,
+                                                      0);
     }
     // the mask only where the diagonal, the window edge or the sequence end cuts the tile (wave-uniform test)
     const bool inside = k0 + 31 <= i0 && i0 + 31 < a.S && (!swa || i0 + 31 - k0 < a.window);
@@ -581,26 +596,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  if (n_it > 0) {
-    load_stage(0);
-    store_stage(0);
-  }
+  if (n_it > 0) load_stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the tile loads write LDS without the compiler waiting for them
   __syncthreads();
-  for (int it = 0; it < n_it; it++) {
-    const int buf = it & 1;
-    const bool more = it + 1 < n_it;
-    if (more) load_stage(it + 1);
+  auto step = [&](int it, int buf) {   // two per pass, constant buffers (as in bwd_kv_kernel)
+    if (it + 1 < n_it) load_stage(it + 1, buf ^ 1);
     compute(buf, it);
-    // Keep the stores of the prefetched tile after the compute: they go to the other buffer, so the compiler
-    // would otherwise move them (and the waits for their loads) up against the loads, which makes the prefetch
-    // synchronous.
-    asm volatile("" ::: "memory");
-    if (more) store_stage(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+  };
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, 0);
+    if (it + 1 < n_it) step(it + 1, 1);
   }
 
   // dq: back through RoPE and the query RMSNorm here; the work-group's 4 x 32 rows' share of dw_q into its partial
-  __shared__ float red[4][kHeadDim];
+  float (*red)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&st[0]);   // in the tile buffers, as in bwd_kv_kernel
   const int64_t row = ((int64_t)b * a.S + qi) * a.Hq + hq;
   const bool valid = qi < a.S;
   norm_rope_bwd_rows(dq, valid ? a.q + row * kHeadDim : nullptr, a.qw, valid ? a.dq + row * kHeadDim : nullptr, qi, a,
