@@ -212,6 +212,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     }
   }
   load_rows(qb, QS, p_start, true);
+  // w_q for this lane's 32 dims (chunks 4t + g), once
+  float wq[4][8];
+#pragma unroll
+  for (int t = 0; t < 4; t++) unpack8(*reinterpret_cast<const uint4*>(Wn + 8 * (4 * t + g)), wq[t]);
 
   // MFMA operand offsets within a tile (bytes): K row 16kh + l16, chunk 4t + g (t = 0..3); V^T row 16db + l16,
   // chunk g (stored keys 8g..8g+7)
@@ -243,16 +247,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
       }
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
-      const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps);
+      const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps) * a.q_scale;
 #pragma unroll
       for (int t = 0; t < 4; t++) {
-        float w[8];
-        unpack8(*reinterpret_cast<const uint4*>(Wn + 8 * (4 * t + g)), w);
 #pragma unroll
-        for (int e = 0; e < 8; e++) f[t][e] = f[t][e] * inv * w[e];
+        for (int e = 0; e < 8; e++) f[t][e] = f[t][e] * inv * wq[t][e];
         rope8(f[t], 8 * (4 * t + g), min(i, a.S - 1), a.rot_pairs, Fr);
 #pragma unroll
-        for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)(f[t][e] * a.q_scale);
+        for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)f[t][e];
       }
     }
     // this step's gate rows, the next key/value tile and the next step's q rows (into QS: this wave has consumed
@@ -352,7 +354,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
       float o[4];
 #pragma unroll
       for (int e = 0; e < 4; e++)   // sigmoid(g) = 1 / (1 + e^-g): v_exp and v_rcp, exact at g = +-inf
-        o[e] = acc_o[db][e] * inv_l * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[e]));
+        o[e] = acc_o[db][e] * __builtin_amdgcn_rcpf(__builtin_fmaf(l_run, __expf(-gv[e]), l_run));
       *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
     }
     lds_barrier();

@@ -90,7 +90,7 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 // take their argument in revolutions.
 __device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq_rev, float& c, float& s) {
   double r = (double)pos * inv_freq_rev;
-  r -= floor(r);
+  r = __builtin_amdgcn_fract(r);
   const float rf = (float)r;
   s = __builtin_amdgcn_sinf(rf);
   c = __builtin_amdgcn_cosf(rf);
