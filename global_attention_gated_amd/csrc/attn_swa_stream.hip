@@ -216,6 +216,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   float wq[4][8];
 #pragma unroll
   for (int t = 0; t < 4; t++) unpack8(*reinterpret_cast<const uint4*>(Wn + 8 * (4 * t + g)), wq[t]);
+  // RoPE of the lane's query rows in chunks 4t + g, t = 0, 1 (pairs 4(4t + g) + m: every pair below 32), carried
+  // along the steps: the lane's position advances by one step's 32 positions, so each pair's (cos, sin) advances
+  // by a fixed rotation.  Pairs at or past rot_pairs stay at (1, 0).  Rows past the sequence end follow the same
+  // progression; their outputs are not stored.
+  float rc[2][4], rs[2][4], dc[2][4], dsn[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; t++)
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const int pi = 4 * (4 * t + g) + m;
+      rc[t][m] = 1.0f; rs[t][m] = 0.0f; dc[t][m] = 1.0f; dsn[t][m] = 0.0f;
+      if (pi < a.rot_pairs) {
+        rope_cs((int64_t)p_start + 16 * half + l16, Fr[pi], rc[t][m], rs[t][m]);
+        rope_cs(kStep, Fr[pi], dc[t][m], dsn[t][m]);
+      }
+    }
 
   // MFMA operand offsets within a tile (bytes): K row 16kh + l16, chunk 4t + g (t = 0..3); V^T row 16db + l16,
   // chunk g (stored keys 8g..8g+7)
@@ -252,7 +268,19 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
       for (int t = 0; t < 4; t++) {
 #pragma unroll
         for (int e = 0; e < 8; e++) f[t][e] = f[t][e] * inv * wq[t][e];
-        rope8(f[t], 8 * (4 * t + g), min(i, a.S - 1), a.rot_pairs, Fr);
+        if (t < 2) {
+#pragma unroll
+          for (int m = 0; m < 4; m++) {
+            const float x0 = f[t][2 * m], x1 = f[t][2 * m + 1];
+            f[t][2 * m] = x0 * rc[t][m] - x1 * rs[t][m];
+            f[t][2 * m + 1] = x0 * rs[t][m] + x1 * rc[t][m];
+            const float c1 = rc[t][m] * dc[t][m] - rs[t][m] * dsn[t][m];
+            rs[t][m] = rs[t][m] * dc[t][m] + rc[t][m] * dsn[t][m];
+            rc[t][m] = c1;
+          }
+        } else {
+          rope8(f[t], 8 * (4 * t + g), min(i, a.S - 1), a.rot_pairs, Fr);
+        }
 #pragma unroll
         for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)f[t][e];
       }
