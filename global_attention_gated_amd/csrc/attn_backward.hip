@@ -113,8 +113,28 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
   float wf[8];
   unpack8(*reinterpret_cast<const uint4*>((qmode ? a.qw : a.kw) + 8 * c), wf);
   const bool gated = a.gate != nullptr;
+  constexpr int kPasses = kPrepTok / 16;
 
-  for (int pass = 0; pass < kPrepTok / 16; pass++) {
+  // every input chunk of the thread's 4 rows first (16 loads in flight per thread in q mode), then the math
+  uint4 xin[kPasses], din[kPasses], oin[kPasses], gin[kPasses];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; pass++) {
+    const int s = s0 + pass * 16 + rg;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    xin[pass] = din[pass] = oin[pass] = gin[pass] = z;
+    if (s < a.S) {
+      const int64_t irow = (((int64_t)b * a.S + s) * H + h) * kHeadDim + 8 * c;   // [B][S][H][D] input row
+      xin[pass] = *reinterpret_cast<const uint4*>((qmode ? a.q : a.k) + irow);
+      if (qmode) {
+        din[pass] = *reinterpret_cast<const uint4*>(a.dout + irow);
+        oin[pass] = *reinterpret_cast<const uint4*>(a.out + irow);
+        if (gated) gin[pass] = *reinterpret_cast<const uint4*>(a.gate + irow);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int pass = 0; pass < kPasses; pass++) {
     const int row = pass * 16 + rg;
     const int s = s0 + row;
     const int64_t wrow = ((int64_t)bh * a.Sp + s) * kHeadDim + 8 * c;   // [b][h][Sp][D] workspace row
@@ -122,7 +142,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
     if (s < a.S) {
       const int64_t irow = (((int64_t)b * a.S + s) * H + h) * kHeadDim + 8 * c;   // [B][S][H][D] input row
       float f[8];
-      unpack8(*reinterpret_cast<const uint4*>((qmode ? a.q : a.k) + irow), f);
+      unpack8(xin[pass], f);
       norm_rope8_g16_w(f, wf, c, s, a.eps, a.rot_pairs, a.inv_freq_rev);
       if (qmode) {
         float fs[8];
@@ -132,13 +152,13 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
                                                               pack_f16(fs[4], fs[5]), pack_f16(fs[6], fs[7]));
         t1 = pack8(f);
         float d[8], o[8], g[8];
-        unpack8(*reinterpret_cast<const uint4*>(a.dout + irow), d);
-        unpack8(*reinterpret_cast<const uint4*>(a.out + irow), o);
+        unpack8(din[pass], d);
+        unpack8(oin[pass], o);
         float delta = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e++) delta += d[e] * o[e];
         if (gated) {
-          unpack8(*reinterpret_cast<const uint4*>(a.gate + irow), g);
+          unpack8(gin[pass], g);
           float dg[8];
 #pragma unroll
           for (int e = 0; e < 8; e++) {
