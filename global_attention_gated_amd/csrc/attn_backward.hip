@@ -25,6 +25,9 @@
 //   epilogues        the dK and dQ kernels take their rows back through RoPE (its transpose) and RMSNorm in their
 //                    epilogues, write bf16 dk / dq and a per-work-group partial of dw_k / dw_q, which
 //                    bwd_dw_reduce_kernel sums in a fixed order.
+// The three MFMA kernels copy their tiles from the workspace straight into LDS (buffer loads with LDS as the
+// destination, one tile ahead, XOR-swizzled images); the prep writes the transposed tensors in the column order
+// those images need.
 #include "common.h"
 #include "launch.h"
 
