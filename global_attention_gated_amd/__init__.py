@@ -121,6 +121,19 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def _shapes(fn, want, device=None):
+    """Check every tensor of ``want`` ({name: (tensor or None, expected shape tuple)}) against its expected shape
+    and, when ``device`` is given, that it lives on that device, before anything reaches the library (whose kernels
+    index raw pointers with the sizes taken from q or the cache).  Raises ValueError naming the first mismatch."""
+    for name, (t, shape) in want.items():
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if device is not None and t.device != device:
+            raise ValueError(f"{fn}: {name} is on {t.device}, expected {device}")
+
+
 # ------------------------------------------------------------------------------------------- cache
 def _desc(n_layers, global_layers, batch, n_kv_heads, head_dim, window, max_tokens):
     gl = (_i32 * max(1, len(global_layers)))(*global_layers)
@@ -207,11 +220,24 @@ def workspace_bytes(B, S, Hkv, D=128) -> int:
     return int(_lib.prefill_workspace_bytes(B, S, Hkv, D))
 
 
-def _prefill(gated, q, k, v, gate, q_norm_w, k_norm_w, out, window, rotary_dims, rope_base, eps, pos0, cache, layer,
-             workspace):
-    _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _bf16(gate, "gate"), _bf16(q_norm_w, "q_norm_w"), _bf16(k_norm_w, "k_norm_w")
+def _qkv_shapes(fn, q, k, v, gate, q_norm_w, k_norm_w, out):
+    """(B, S, Hq, Hkv, D) from q and k, after checking every tensor of a layer call against them."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError(f"{fn}: q and k must be [B, S, H, D]")
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
+    _shapes(fn, {"k": (k, (B, S, Hkv, D)), "v": (v, (B, S, Hkv, D)), "gate": (gate, (B, S, Hq, D)),
+                 "q_norm_w": (q_norm_w, (D,)), "k_norm_w": (k_norm_w, (D,)), "out": (out, (B, S, Hq, D))}, q.device)
+    return B, S, Hq, Hkv, D
+
+
+def _prefill(gated, q, k, v, gate, q_norm_w, k_norm_w, out, window, rotary_dims, rope_base, eps, pos0, cache, layer,
+             workspace):
+    fn = "swa_prefill" if gated else "global_prefill"
+    if gated and gate is None:
+        raise ValueError(f"{fn}: gate is required")
+    B, S, Hq, Hkv, D = _qkv_shapes(fn, q, k, v, gate, q_norm_w, k_norm_w, out)
+    _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _bf16(gate, "gate"), _bf16(q_norm_w, "q_norm_w"), _bf16(k_norm_w, "k_norm_w")
     if out is None:
         out = torch.empty_like(q)
     _bf16(out, "out")
@@ -258,10 +284,11 @@ def prefill_train(q, k, v, gate, q_norm_w, k_norm_w, *, window=128, rotary_dims=
                   out=None, lse=None, workspace=None):
     """Training forward (swa_prefill_train, or global_prefill_train when gate is None): returns (out, lse), out
     [B,S,Hq,D] bf16 and lse [B,Hq,S] fp32 (natural log of each softmax denominator)."""
+    fn = "swa_prefill_train" if gate is not None else "global_prefill_train"
+    B, S, Hq, Hkv, D = _qkv_shapes(fn, q, k, v, gate, q_norm_w, k_norm_w, out)
+    _shapes(fn, {"lse": (lse, (B, Hq, S))}, q.device)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
         _bf16(t, n)
-    B, S, Hq, D = q.shape
-    Hkv = k.shape[2]
     out = torch.empty_like(q) if out is None else _bf16(out, "out")
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if lse is None else _f32cuda(lse, "lse")
     if workspace is None:
@@ -287,13 +314,23 @@ def prefill_backward(q, k, v, gate, q_norm_w, k_norm_w, out, lse, dout, *, windo
                      eps=1e-6, grads=None, workspace=None):
     """Backward (swa_prefill_backward, or global_prefill_backward when gate is None): returns a dict with dq, dk,
     dv (bf16, shaped as q/k/v), dgate (bf16, None for a global layer) and dq_norm_w, dk_norm_w ([D] fp32)."""
+    fn = "swa_prefill_backward" if gate is not None else "global_prefill_backward"
+    B, S, Hq, Hkv, D = _qkv_shapes(fn, q, k, v, gate, q_norm_w, k_norm_w, out)
+    g = grads or {}
+    _shapes(fn, {"lse": (lse, (B, Hq, S)), "dout": (dout, (B, S, Hq, D)), "dq": (g.get("dq"), (B, S, Hq, D)),
+                 "dk": (g.get("dk"), (B, S, Hkv, D)), "dv": (g.get("dv"), (B, S, Hkv, D)),
+                 "dgate": (g.get("dgate") if gate is not None else None, (B, S, Hq, D)),
+                 "dq_norm_w": (g.get("dq_norm_w"), (D,)), "dk_norm_w": (g.get("dk_norm_w"), (D,))}, q.device)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"),
                  (out, "out"), (dout, "dout")):
         _bf16(t, n)
     _f32cuda(lse, "lse")
-    B, S, Hq, D = q.shape
-    Hkv = k.shape[2]
-    g = grads or {}
+    for n in ("dq", "dk", "dv", "dgate"):
+        if g.get(n) is not None:
+            _bf16(g[n], n)
+    for n in ("dq_norm_w", "dk_norm_w"):
+        if g.get(n) is not None:
+            _f32cuda(g[n], n)
     dq = g.get("dq", torch.empty_like(q))
     dk = g.get("dk", torch.empty_like(k))
     dv = g.get("dv", torch.empty_like(v))
@@ -320,10 +357,13 @@ def prefill_backward(q, k, v, gate, q_norm_w, k_norm_w, out, lse, dout, *, windo
 # ------------------------------------------------------------------------------------------- projections, layers
 def linear_bf16(x, w, y=None):
     """y = x W^T: x [..., K], w [N, K] (bf16); returns y [..., N]."""
-    _bf16(x, "x"), _bf16(w, "w")
+    if w.dim() != 2:
+        raise ValueError("linear_bf16: w must be [N, K]")
     N, K = w.shape
-    if x.shape[-1] != K:
-        raise ValueError(f"x has {x.shape[-1]} features, w expects {K}")
+    if x.dim() < 1 or x.shape[-1] != K:
+        raise ValueError(f"linear_bf16: x has {tuple(x.shape)[-1:]} features, w expects {K}")
+    _shapes("linear_bf16", {"w": (w, (N, K)), "y": (y, (*x.shape[:-1], N))}, x.device)
+    _bf16(x, "x"), _bf16(w, "w")
     T = x.numel() // K
     if y is None:
         y = torch.empty((*x.shape[:-1], N), dtype=torch.bfloat16, device=x.device)
@@ -349,6 +389,9 @@ class Fp8Linear:
         return float(out[0]), float(out[1])
 
     def __call__(self, x, w, y=None):
+        if x.dim() < 1 or x.shape[-1] != self.K:
+            raise ValueError(f"linear_fp8_delayed: x has {tuple(x.shape)[-1:]} features, the state expects {self.K}")
+        _shapes("linear_fp8_delayed", {"w": (w, (self.N, self.K)), "y": (y, (*x.shape[:-1], self.N))}, x.device)
         _bf16(x, "x"), _bf16(w, "w")
         T = x.numel() // self.K
         if y is None:
@@ -419,11 +462,19 @@ def fp8_layer_workspace_bytes(B, S, d_model, Hq, Hkv, D=128) -> int:
 
 def _layer(gated, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, window, rotary_dims, rope_base, eps,
            pos0, cache, layer, workspace, fp8=None):
+    fn = ("gated_swa_layer" if gated else "global_layer") + ("_fp8" if fp8 is not None else "")
+    if h.dim() != 3 or q_norm_w.dim() != 1:
+        raise ValueError(f"{fn}: h must be [B, S, d_model] and q_norm_w [D]")
+    B, S, d_model = h.shape
+    D = q_norm_w.shape[0]
+    if gated and w_g is None:
+        raise ValueError(f"{fn}: w_g is required")
+    _shapes(fn, {"w_q": (w_q, (Hq * D, d_model)), "w_k": (w_k, (Hkv * D, d_model)), "w_v": (w_v, (Hkv * D, d_model)),
+                 "w_g": (w_g, (Hq * D, d_model)), "w_o": (w_o, (d_model, Hq * D)), "k_norm_w": (k_norm_w, (D,)),
+                 "y": (y, (B, S, d_model))}, h.device)
     for t, n in ((h, "h"), (w_q, "w_q"), (w_k, "w_k"), (w_v, "w_v"), (w_g, "w_g"), (w_o, "w_o"), (q_norm_w, "q_norm_w"),
                  (k_norm_w, "k_norm_w")):
         _bf16(t, n)
-    B, S, d_model = h.shape
-    D = q_norm_w.shape[0]
     if y is None:
         y = torch.empty_like(h)
     _bf16(y, "y")
@@ -483,15 +534,26 @@ def global_layer_fp8(h, w_q, w_k, w_v, w_o, q_norm_w, k_norm_w, y=None, *, fp8: 
 def hybrid_decode_step(q, k, v, gate, q_norm_w, k_norm_w, positions, cache: KVCache, out=None, *, rotary_dims=42,
                        rope_base=1e7, eps=1e-6):
     """q/gate [L,B,Hq,D], k/v [L,B,Hkv,D], weights [L,D] (bf16), positions: B ints; returns out [L,B,Hq,D]."""
+    fn = "hybrid_decode_step"
+    if q.dim() != 4:
+        raise ValueError(f"{fn}: q must be [L, B, Hq, D]")
+    L, B, Hq, D = q.shape
+    if (L, B, D) != (cache.n_layers, cache.batch, cache.head_dim):
+        raise ValueError(f"{fn}: q has shape {tuple(q.shape)}, the cache needs [{cache.n_layers}, {cache.batch}, Hq, "
+                         f"{cache.head_dim}]")
+    Hkv = cache.n_kv_heads
+    _shapes(fn, {"k": (k, (L, B, Hkv, D)), "v": (v, (L, B, Hkv, D)), "gate": (gate, (L, B, Hq, D)),
+                 "q_norm_w": (q_norm_w, (L, D)), "k_norm_w": (k_norm_w, (L, D)), "out": (out, (L, B, Hq, D))},
+            q.device)
+    positions = [int(p) for p in positions]
+    if len(positions) != B:
+        raise ValueError(f"{fn}: {len(positions)} positions for a batch of {B}")
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
         _bf16(t, n)
-    L, B, Hq, D = q.shape
-    if (L, B, D) != (cache.n_layers, cache.batch, cache.head_dim) or tuple(k.shape) != (L, B, cache.n_kv_heads, D):
-        raise ValueError("tensor shapes do not match the cache")
     if out is None:
         out = torch.empty_like(q)
     _bf16(out, "out")
-    pos = (_i64 * B)(*[int(p) for p in positions])
+    pos = (_i64 * B)(*positions)
     _check(_lib.hybrid_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out),
                                    pos, Hq, rotary_dims, rope_base, eps, cache.handle, _stream()))
     return out

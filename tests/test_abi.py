@@ -181,3 +181,100 @@ def test_training_forward_needs_lse(zg):
     p = 16
     rc = zg._lib.swa_prefill_train(p, p, p, p, p, p, p, None, 1, 4, 4, 1, 128, 128, 42, 1e4, 1e-6, 256, 1 << 30, None)
     assert rc == zg.ZG_EINVAL and b"null lse" in zg._lib.zg_last_error()
+
+
+# ------------------------------------------------------------------------------------------ binding shape checks
+# The binding checks every tensor's full shape against q (or the cache) before anything reaches the library; on the
+# host these checks run on CPU tensors, which the later device check would refuse anyway.
+def _bt(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _layer_tensors(B=1, S=8, Hq=4, Hkv=1, D=128):
+    return dict(q=_bt(B, S, Hq, D), k=_bt(B, S, Hkv, D), v=_bt(B, S, Hkv, D), gate=_bt(B, S, Hq, D),
+                q_norm_w=_bt(D), k_norm_w=_bt(D))
+
+
+@pytest.mark.parametrize("name,bad", [("k", (1, 7, 1, 128)), ("v", (1, 7, 1, 128)), ("gate", (1, 8, 4, 64)),
+                                      ("q_norm_w", (2, 128)), ("k_norm_w", (64,)), ("out", (1, 8, 4, 127))])
+def test_binding_rejects_mis_shaped_prefill_tensors(zg, name, bad):
+    t = _layer_tensors()
+    t[name] = _bt(*bad)
+    with pytest.raises(ValueError, match=name):
+        zg.swa_prefill(t["q"], t["k"], t["v"], t["gate"], t["q_norm_w"], t["k_norm_w"], t.get("out"))
+    if name != "gate":
+        with pytest.raises(ValueError, match=name):
+            zg.global_prefill(t["q"], t["k"], t["v"], t["q_norm_w"], t["k_norm_w"], t.get("out"))
+    with pytest.raises(ValueError, match=name):
+        zg.prefill_train(t["q"], t["k"], t["v"], t["gate"], t["q_norm_w"], t["k_norm_w"], out=t.get("out"))
+
+
+def test_binding_well_shaped_host_tensors_reach_the_device_check(zg):
+    t = _layer_tensors()
+    with pytest.raises(TypeError, match="CUDA"):
+        zg.swa_prefill(t["q"], t["k"], t["v"], t["gate"], t["q_norm_w"], t["k_norm_w"])
+    with pytest.raises(ValueError, match="gate is required"):
+        zg.swa_prefill(t["q"], t["k"], t["v"], None, t["q_norm_w"], t["k_norm_w"])
+
+
+def test_binding_rejects_mis_shaped_backward_tensors(zg):
+    import torch
+    t = _layer_tensors()
+    out, dout = _bt(1, 8, 4, 128), _bt(1, 8, 4, 128)
+    lse = torch.zeros((1, 4, 8), dtype=torch.float32)
+    args = (t["q"], t["k"], t["v"], t["gate"], t["q_norm_w"], t["k_norm_w"], out)
+    with pytest.raises(ValueError, match="lse"):
+        zg.prefill_backward(*args, torch.zeros((1, 8, 4), dtype=torch.float32), dout)
+    with pytest.raises(ValueError, match="dout"):
+        zg.prefill_backward(*args, lse, _bt(1, 8, 4, 64))
+    with pytest.raises(ValueError, match="dk"):
+        zg.prefill_backward(*args, lse, dout, grads={"dk": _bt(1, 8, 4, 128)})
+    with pytest.raises(ValueError, match="dq_norm_w"):
+        zg.prefill_backward(*args, lse, dout, grads={"dq_norm_w": torch.zeros(64, dtype=torch.float32)})
+
+
+def test_binding_rejects_decode_tensors_that_do_not_match_the_cache(zg):
+    import types
+    cache = types.SimpleNamespace(n_layers=3, batch=2, head_dim=128, n_kv_heads=2, handle=None)
+    L, B, Hq, Hkv, D = 3, 2, 8, 2, 128
+    ok = dict(q=_bt(L, B, Hq, D), k=_bt(L, B, Hkv, D), v=_bt(L, B, Hkv, D), gate=_bt(L, B, Hq, D),
+              q_norm_w=_bt(L, D), k_norm_w=_bt(L, D))
+
+    def call(**over):
+        a = dict(ok, **over)
+        return zg.hybrid_decode_step(a["q"], a["k"], a["v"], a["gate"], a["q_norm_w"], a["k_norm_w"],
+                                     a.get("positions", [5, 5]), cache, out=a.get("out"))
+    with pytest.raises(ValueError, match="q has shape"):
+        call(q=_bt(L, 3, Hq, D))
+    # the per-layer norm weights are [L, D] in decode (a [D] vector would be read past its end)
+    with pytest.raises(ValueError, match="q_norm_w"):
+        call(q_norm_w=_bt(D))
+    with pytest.raises(ValueError, match="k has shape"):
+        call(k=_bt(L, B, 1, D))
+    with pytest.raises(ValueError, match="gate"):
+        call(gate=_bt(L, B, Hq + 1, D))
+    with pytest.raises(ValueError, match="out"):
+        call(out=_bt(L, B, Hq, 64))
+    with pytest.raises(ValueError, match="positions"):
+        call(positions=[5])
+    with pytest.raises(TypeError, match="CUDA"):
+        call()
+
+
+def test_binding_rejects_mis_shaped_layer_tensors(zg):
+    B, S, dm, Hq, Hkv, D = 1, 4, 256, 4, 1, 128
+    h = _bt(B, S, dm)
+    w = dict(w_q=_bt(Hq * D, dm), w_k=_bt(Hkv * D, dm), w_v=_bt(Hkv * D, dm), w_g=_bt(Hq * D, dm),
+             w_o=_bt(dm, Hq * D))
+    nw = _bt(D)
+    for name, bad in (("w_q", (Hq * D, dm + 8)), ("w_k", (Hq * D, dm)), ("w_o", (Hq * D, dm)), ("w_g", (dm, dm))):
+        a = dict(w, **{name: _bt(*bad)})
+        with pytest.raises(ValueError, match=name):
+            zg.gated_swa_layer(h, a["w_q"], a["w_k"], a["w_v"], a["w_g"], a["w_o"], nw, nw, Hq=Hq, Hkv=Hkv)
+    with pytest.raises(ValueError, match="y"):
+        zg.global_layer(h, w["w_q"], w["w_k"], w["w_v"], w["w_o"], nw, nw, _bt(B, S, dm + 1), Hq=Hq, Hkv=Hkv)
+    with pytest.raises(ValueError, match="y has shape"):
+        zg.linear_bf16(_bt(3, 256), _bt(128, 256), _bt(3, 64))
+    with pytest.raises(ValueError, match="features"):
+        zg.linear_bf16(_bt(3, 255), _bt(128, 256))

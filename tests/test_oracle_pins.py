@@ -248,17 +248,86 @@ def test_prefill_keys_are_read_in_bf16_cache_form():
         np.testing.assert_allclose(o[0, :, h], oracle.attend(qh[:, h], pos, kb, v[0, :, 0], pos, None), rtol=1e-12, atol=1e-13)
 
 
+def _bf16_exact(a):
+    """Round float64 data to bf16 values (torch's conversion) and return them as float64 (exact inputs)."""
+    return torch.from_numpy(np.asarray(a, dtype=np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _torch_bits(x):
+    """bf16 bit patterns of float64 data through torch's own conversion (not the oracle's rounding)."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _khat_independent(k, w, eps, R, base):
+    """k_hat of raw rows k [B,S,H,D] at positions 0..S-1 without the oracle: torch's rms_norm in float64, then
+    RoFormer's complex form of the rotation."""
+    B, S, H, D = k.shape
+    y = torch.nn.functional.rms_norm(torch.from_numpy(k), (D,), torch.from_numpy(np.asarray(w, dtype=np.float64)),
+                                     eps).numpy()
+    return _rope_complex(y, np.arange(S)[None, :, None], R, base)
+
+
+def _image_problem(seed, B, S, Hq, Hkv, D):
+    r = np.random.default_rng(seed)
+    q = _bf16_exact(r.standard_normal((B, S, Hq, D)))
+    k = _bf16_exact(r.standard_normal((B, S, Hkv, D)))
+    v = _bf16_exact(r.standard_normal((B, S, Hkv, D)))
+    g = _bf16_exact(r.standard_normal((B, S, Hq, D)))
+    w = _bf16_exact(1 + 0.1 * r.standard_normal(D))
+    return q, k, v, g, w
+
+
 def test_ring_image_holds_last_window_positions_by_slot():
-    L, B, S, Hq, Hkv, D, W = 1, 2, 300, 2, 1, 8, 128
-    q, k, v, g, wq, wk = _small_problem(3, L, B, S, Hq, Hkv, D)
-    cache = oracle.OracleCache(L, [], B, Hkv, D, W)
-    oracle.prefill_layer(q[0], k[0], v[0], g[0], wq[0], wk[0], window=W, rotary_dims=4, base=1e4, eps=1e-6,
-                         cache=cache, layer=1)
+    """The SWA ring (jaehun.me, "Why the KV Cache Shrinks by 6.4x": only the last W keys are kept): slot s of
+    sequence b, KV head h holds position p = the one of the last W with p mod W = s, its k_hat rounded to bf16 and
+    its v bits unchanged; k_hat comes from torch's rms_norm and the complex form of RoPE, not from the oracle.
+    Two sequences and two KV heads with different data catch a swapped (b, h); prefill in chunks catches an
+    off-by-one slot."""
+    B, S, Hq, Hkv, D, W, R, eps, base = 2, 300, 4, 2, 16, 128, 6, 1e-6, 1e4
+    q, k, v, g, w = _image_problem(3, B, S, Hq, Hkv, D)
+    cache = oracle.OracleCache(1, [], B, Hkv, D, W)
+    for c0, c1 in ((0, 90), (90, 91), (91, 300)):
+        oracle.prefill_layer(q[:, c0:c1], k[:, c0:c1], v[:, c0:c1], g[:, c0:c1], w, w, window=W, rotary_dims=R,
+                             base=base, eps=eps, pos0=c0, cache=cache, layer=1)
     K, V, P = cache.ring_image(1)
-    for s in range(W):
-        p = P[0, s]
-        assert p % W == s and S - W <= p < S
-        np.testing.assert_array_equal(V[0, 0, s], oracle.round_bf16(v[0, 0, p, 0]))
+    kref = _torch_bits(_khat_independent(k, w, eps, R, base))
+    vbits = _torch_bits(v)
+    for b in range(B):
+        assert sorted(P[b]) == list(range(S - W, S))
+        for s in range(W):
+            p = P[b, s]
+            assert p % W == s
+            for h in range(Hkv):
+                np.testing.assert_array_equal(V[b, h, s], vbits[b, p, h])
+                np.testing.assert_array_equal(K[b, h, s], kref[b, p, h])
+    # fewer positions than slots: the others stay empty (position -1, zero bits)
+    short = oracle.OracleCache(1, [], B, Hkv, D, W)
+    oracle.prefill_layer(q[:, :5], k[:, :5], v[:, :5], g[:, :5], w, w, window=W, rotary_dims=R, base=base, eps=eps,
+                         cache=short, layer=1)
+    K, V, P = short.ring_image(1)
+    assert np.all(P[:, :5] == np.arange(5)) and np.all(P[:, 5:] == -1)
+    assert not K[:, :, 5:].any() and not V[:, :, 5:].any()
+    np.testing.assert_array_equal(K[:, :, :5], kref[:, :5].transpose(0, 2, 1, 3))
+
+
+def test_global_image_holds_every_position_by_row():
+    """A global layer's cache keeps every position: row p of sequence b, KV head h holds k_hat at position p
+    (rounded to bf16) and v unchanged, whether the rows were written by one prefill or by chunks (jaehun.me, "Why
+    the KV Cache Shrinks by 6.4x": K and V of every earlier token, 2 bytes per element).  k_hat comes from torch's
+    rms_norm and the complex form of RoPE, not from the oracle."""
+    B, S, Hq, Hkv, D, R, eps, base = 2, 70, 4, 2, 16, 6, 1e-6, 1e7
+    q, k, v, _, w = _image_problem(4, B, S, Hq, Hkv, D)
+    kref = _torch_bits(_khat_independent(k, w, eps, R, base)).transpose(0, 2, 1, 3)   # [B][Hkv][S][D]
+    vref = _torch_bits(v).transpose(0, 2, 1, 3)
+    for chunks in (((0, S),), ((0, 1), (1, 33), (33, 70))):
+        cache = oracle.OracleCache(2, [2], B, Hkv, D, 16)
+        for c0, c1 in chunks:
+            oracle.prefill_layer(q[:, c0:c1], k[:, c0:c1], v[:, c0:c1], None, w, w, window=None, rotary_dims=R,
+                                 base=base, eps=eps, pos0=c0, cache=cache, layer=2)
+        K, V = cache.global_image(2)
+        assert K.shape == (B, Hkv, S, D)
+        np.testing.assert_array_equal(K, kref)
+        np.testing.assert_array_equal(V, vref)
 
 
 # ----------------------------------------------------------------------------- pages' closed forms
