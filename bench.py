@@ -487,6 +487,85 @@ def run_backward(zg, steps=5, warmup=2, S=16384, seed=1008):
     return res
 
 
+# ------------------------------------------------------------------------------------------ chunked prefill
+def run_chunked(zg, S_total=262144, C=16384, seed=1005, passes=1):
+    """Long-context chunked prefill: one sequence of S_total tokens in C-token chunks through the 32-layer schedule
+    against a KV cache (RoPE base 1e7).  Each chunk's 32 layer inputs are generated before its timed layer calls;
+    the time is the sum over chunks of HIP-event times around the 32 calls of a chunk.  The global layers' tile
+    kernel is timed on its own too (kernel timer), for its roofline line."""
+    import torch
+    import synth
+    cache = zg.KVCache(n_layers=N_LAYERS, global_layers=GLOBAL_LAYERS, batch=1, n_kv_heads=HKV, head_dim=D, window=W,
+                       max_tokens=S_total)
+    ws = torch.empty(zg.workspace_bytes(1, C, HKV, D, pos0=S_total - C), dtype=torch.uint8, device="cuda")
+    w = {}
+    for l in range(1, N_LAYERS + 1):
+        for name, tid in (("wq", synth.TENSOR_WQ), ("wk", synth.TENSOR_WK)):
+            w[(l, name)] = torch.from_numpy(synth.norm_weight_bf16(seed, l, tid, D).view("int16")).cuda().view(torch.bfloat16)
+    out = torch.empty((1, C, HQ, D), dtype=torch.bfloat16, device="cuda")
+    total_ms, chunk_ms = 0.0, []
+    glob_ms, glob_n, glob_flop = 0.0, 0, 0
+    for p in range(passes):
+        if p:
+            for l in range(1, N_LAYERS + 1):
+                cache.set_length(l, 0, 0)
+        for c in range(S_total // C):
+            pos0 = c * C
+            t = []
+            for l in range(1, N_LAYERS + 1):
+                glob = l in GLOBAL_LAYERS
+                d = {}
+                for name, tid, H in (("q", synth.TENSOR_Q, HQ), ("k", synth.TENSOR_K, HKV), ("v", synth.TENSOR_V, HKV)) + \
+                        (() if glob else (("gate", synth.TENSOR_GATE, HQ),)):
+                    d[name] = synth.normal_bf16_device(seed, l, tid, (1, C, H, D), index_offset=pos0 * H * D)
+                t.append(d)
+            sync()
+            zg.kernel_timer_enable(True, only="attn_global")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for l in range(1, N_LAYERS + 1):
+                d = t[l - 1]
+                if l in GLOBAL_LAYERS:
+                    zg.global_prefill(d["q"], d["k"], d["v"], w[(l, "wq")], w[(l, "wk")], out, rotary_dims=R,
+                                      rope_base=1e7, eps=1e-6, pos0=pos0, cache=cache, layer=l, workspace=ws)
+                else:
+                    zg.swa_prefill(d["q"], d["k"], d["v"], d["gate"], w[(l, "wq")], w[(l, "wk")], out, window=W,
+                                   rotary_dims=R, rope_base=1e7, eps=1e-6, pos0=pos0, cache=cache, layer=l,
+                                   workspace=ws)
+            e1.record()
+            sync()
+            ms = e0.elapsed_time(e1)
+            gms, gn = zg.kernel_timer_read("attn_global")
+            zg.kernel_timer_enable(False)
+            if p == passes - 1:
+                chunk_ms.append(ms)
+                total_ms += ms
+                glob_ms += gms
+                glob_n += gn
+                glob_flop += 5 * 4 * D * HQ * (C * pos0 + C * (C + 1) // 2)
+            log(f"chunked: pass {p} chunk {c} at {pos0}: {ms:.1f} ms (global kernels {gms:.1f} ms)")
+            del t
+    fp = zg.footprint_bytes(S_total)
+    fp_all = zg.footprint_bytes(S_total, global_layers=range(1, N_LAYERS + 1))
+    res = {
+        "ms_total": total_ms,
+        "tokens_per_s": S_total / (total_ms / 1e3),
+        "chunk_ms": chunk_ms,
+        "global_kernel": {"ms_total": glob_ms, "launches": glob_n, "algorithmic_tflop": glob_flop / 1e12,
+                          "tflops": glob_flop / (glob_ms / 1e3) / 1e12},
+        "roofline": {"bound": "mfma", "achieved": glob_flop / (glob_ms / 1e3) / 1e12, "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": glob_flop / (glob_ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "attn_tile_kernel<global> over all 16 chunks of the 5 global layers"},
+        "kv_cache_bytes": {"hybrid": fp, "all_global": fp_all, "hybrid_gib": fp / 2**30, "all_global_gib": fp_all / 2**30,
+                           "device_bytes": cache.device_bytes},
+    }
+    cache.close()
+    del ws
+    import torch as _t
+    _t.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------------------------------ CPU baseline
 def cpu_baseline(S=16384, n_rows=8192, seed=1003):
     """The fp64 oracle on a sample of the prefill workload: n_rows random positions, all 32 query heads, in
@@ -513,19 +592,26 @@ def cpu_baseline(S=16384, n_rows=8192, seed=1003):
         t1 = time.perf_counter()
         qhat = oracle.qk_prologue(q, rows[:, None], wq, 1e-6, R, 1e4)
         vf = oracle.bf16_to_f64(v)
-        for h in range(HQ):
-            kh = h // (HQ // HKV)
-            if glob:
-                lo = 0
-            else:
-                lo = max(0, int(rows.min()) - W + 1)
+        G = HQ // HKV
+        if glob:
             hi = int(rows.max()) + 1
-            oracle.attend(qhat[:, h], rows, khat[lo:hi, kh], vf[lo:hi, kh], pos[lo:hi], None if glob else W,
-                          None if gate is None else gate[:, h])
+            for h in range(HQ):
+                oracle.attend(qhat[:, h], rows, khat[:hi, h // G], vf[:hi, h // G], pos[:hi], None)
+        else:
+            # blocks of 32 consecutive sampled rows, each block over the keys its rows' windows span (about 190
+            # for 32 rows of a 2-in-4 sample), the G heads of a KV head at once
+            for i0 in range(0, n_rows, 32):
+                rb = rows[i0:i0 + 32]
+                lo, hi = max(0, int(rb[0]) - W + 1), int(rb[-1]) + 1
+                for kh in range(HKV):
+                    hs = slice(kh * G, (kh + 1) * G)
+                    oracle.attend(qhat[i0:i0 + 32, hs].reshape(-1, D), np.repeat(rb, G), khat[lo:hi, kh],
+                                  vf[lo:hi, kh], pos[lo:hi], W, gate[i0:i0 + 32, hs].reshape(-1, D))
         t2 = time.perf_counter()
         per_layer["global" if glob else "swa"] = ((t2 - t1) / n_rows, (t1 - t0) / S)
     per_tok = 27 * sum(per_layer["swa"]) + 5 * sum(per_layer["global"])
-    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": oracle.num_threads(), "host_cores": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"{n_rows} random positions x 32 heads of layer 1 (gated SWA) and layer 6 (global) of the "
                       f"1x16384 schedule, plus each layer's key prologue over all {S} positions; scaled to one "
                       f"token through 27 SWA + 5 global layers",
@@ -550,6 +636,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="instead of the benchmark: time the training forward and backward of one gated-SWA and one "
                          "global layer at 1 x 16384 tokens (one JSON line)")
+    ap.add_argument("--chunked", action="store_true",
+                    help="instead of the benchmark: prefill one 262,144-token sequence in 16,384-token chunks through "
+                         "the 32-layer schedule against the KV cache (one JSON line)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="also copy a GIB-sized device tensor 3 times (a plain copy kernel of known traffic, for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -571,6 +660,21 @@ def main():
         log(f"copy calibration: 3 elementwise copies of {n * 4} bytes (read {n * 4} B + write {n * 4} B each)")
         del src, dst
         torch.cuda.empty_cache()
+    if args.chunked:
+        res = run_chunked(zg)
+        log(f"chunked: {res['ms_total']:.1f} ms, {res['tokens_per_s']:.0f} tokens/s, global tile kernel "
+            f"{res['global_kernel']['tflops']:.0f} TFLOP/s")
+        print(json.dumps({
+            "metric": "long-context chunked prefill tokens/s + % of MFMA roofline (global layers)",
+            "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "data": "synthetic",
+            "higher_is_better": True, "dtype": "fp16", "ms_per_step": res["ms_total"],
+            "config": {"workload": "one 262,144-token sequence prefilled in 16,384-token chunks, 32-layer schedule "
+                                   "(27 gated SWA + 5 global) against the KV cache", "batch": 1, "seq_len": 262144,
+                       "chunk": 16384, "layers": N_LAYERS, "global_layers": list(GLOBAL_LAYERS), "q_heads": HQ,
+                       "kv_heads": HKV, "head_dim": D, "window": W, "rotary_dims": R, "rope_base": 1e7, "seed": 1005},
+            "roofline": res["roofline"], "chunked": res,
+        }), flush=True)
+        return
     if args.backward:
         res = run_backward(zg, steps=args.steps, warmup=args.warmup)
         print(json.dumps({

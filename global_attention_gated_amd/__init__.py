@@ -51,6 +51,8 @@ _lib.kv_cache_length.argtypes = [_vp, _i32, _i32, ctypes.POINTER(_i64)]
 _lib.kv_cache_set_length.argtypes = [_vp, _i32, _i32, _i64]
 _lib.prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
 _lib.prefill_workspace_bytes.restype = _u64
+_lib.prefill_workspace_bytes_at.argtypes = [_i32, _i32, _i32, _i32, _i64, _i32]
+_lib.prefill_workspace_bytes_at.restype = _u64
 _lib.swa_prefill.argtypes = [_vp] * 7 + [_i32] * 7 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
 _lib.global_prefill.argtypes = [_vp] * 6 + [_i32] * 6 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
 _lib.hybrid_decode_step.argtypes = [_vp] * 7 + [ctypes.POINTER(_i64), _i32, _i32, _f64, _f32, _vp, _vp]
@@ -85,7 +87,7 @@ _lib.zg_kernel_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_f64), cty
 _lib.zg_kernel_timer_only.argtypes = [ctypes.c_char_p]
 
 EXPORTED = ["kv_cache_alloc", "kv_cache_free", "kv_cache_footprint_bytes", "kv_cache_layer_view", "kv_cache_length",
-            "kv_cache_set_length", "prefill_workspace_bytes", "swa_prefill", "global_prefill", "hybrid_decode_step",
+            "kv_cache_set_length", "prefill_workspace_bytes", "prefill_workspace_bytes_at", "swa_prefill", "global_prefill", "hybrid_decode_step",
             "linear_bf16", "layer_workspace_bytes", "gated_swa_layer", "global_layer", "fp8_linear_alloc",
             "fp8_linear_free", "fp8_linear_scales", "fp8_linear_workspace_bytes", "linear_fp8_delayed",
             "fp8_layer_alloc", "fp8_layer_free", "fp8_layer_scales", "fp8_layer_workspace_bytes", "gated_swa_layer_fp8",
@@ -216,8 +218,9 @@ def _hip_memcpy_d2h(dst, src, n):
 
 
 # ------------------------------------------------------------------------------------------- prefill
-def workspace_bytes(B, S, Hkv, D=128) -> int:
-    return int(_lib.prefill_workspace_bytes(B, S, Hkv, D))
+def workspace_bytes(B, S, Hkv, D=128, *, pos0=0, window=0) -> int:
+    """prefill_workspace_bytes_at: the workspace a prefill of S tokens at pos0 needs (window 0: a global layer)."""
+    return int(_lib.prefill_workspace_bytes_at(B, S, Hkv, D, pos0, window))
 
 
 def _qkv_shapes(fn, q, k, v, gate, q_norm_w, k_norm_w, out):
@@ -241,9 +244,9 @@ def _prefill(gated, q, k, v, gate, q_norm_w, k_norm_w, out, window, rotary_dims,
     if out is None:
         out = torch.empty_like(q)
     _bf16(out, "out")
-    need_ws = gated or cache is None
-    if workspace is None and need_ws:
-        workspace = torch.empty(max(16, workspace_bytes(B, S, Hkv, D)), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = workspace_bytes(B, S, Hkv, D, pos0=pos0 if cache is not None else 0, window=window if gated else 0)
+        workspace = torch.empty(max(16, need), dtype=torch.uint8, device=q.device)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ch = None if cache is None else cache.handle
@@ -481,6 +484,8 @@ def _layer(gated, h, w_q, w_k, w_v, w_g, w_o, q_norm_w, k_norm_w, y, Hq, Hkv, wi
     if workspace is None:
         need = (layer_workspace_bytes(B, S, Hq, Hkv, D) if fp8 is None
                 else fp8_layer_workspace_bytes(B, S, d_model, Hq, Hkv, D))
+        if cache is not None:   # the attention's part (the tail) also stages the cached positions
+            need += workspace_bytes(B, S, Hkv, D, pos0=pos0, window=window if gated else 0) - workspace_bytes(B, S, Hkv, D)
         workspace = torch.empty(max(16, need), dtype=torch.uint8, device=h.device)
     ws_n = workspace.numel() * workspace.element_size()
     ch = None if cache is None else cache.handle

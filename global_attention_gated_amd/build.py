@@ -28,7 +28,7 @@ DEVICE_FLAGS = ["-fno-honor-nans"]
 # registers and put every MFMA accumulator in AGPRs; its softmax reads the score accumulators with VALU
 # instructions, so its MFMAs are kept in VGPR form.
 SOURCE_FLAGS = {"attn_swa_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
-SOURCES = ["attn_prefill.hip", "attn_global.hip", "attn_swa_stream.hip", "attn_backward.hip", "decode.hip", "fp8.hip", "linear.cpp",
+SOURCES = ["attn_tile.hip", "attn_swa_stream.hip", "attn_backward.hip", "decode.hip", "fp8.hip", "linear.cpp",
            "zgattn_api.cpp"]
 
 

@@ -1,22 +1,28 @@
-// Global causal prefill of the ZGCM-1 attention core for gfx950 (CDNA4, wave64, MFMA): the layer without a
-// cache (one-shot prefill and the training forward).
+// Tile-path prefill of the ZGCM-1 attention core for gfx950 (CDNA4, wave64, MFMA): every prefill that the streaming
+// gated-SWA kernel does not take -- global layers (one-shot, chunked against the KV cache, the training forward),
+// gated-SWA chunks that continue a cached sequence, and gated layers of other GQA groups or windows above 128.
 //
-//   kv_tiles_kernel     k_hat = RoPE(RMSNorm(k) w_k), rounded to bf16 (the KV-cache value) and held as fp16, and
-//                       v^T as fp16, written once per layer in the layout that the attention kernel copies into
-//                       LDS unchanged.
-//   attn_global_kernel  flash-style causal attention of 128 query rows (G heads x P positions of one KV head) per
-//                       work-group against 64-key tiles.  Each tile goes from the workspace straight into LDS
-//                       (buffer loads with LDS as the destination: no registers, no LDS write instructions), 16 KB
-//                       of keys and 16 KB of transposed values, double-buffered.  A direct load writes 16 bytes
-//                       per lane at consecutive LDS addresses; the lanes choose their source chunks so that the LDS
-//                       rows come out XOR-swizzled, which keeps the MFMA operand reads free of bank conflicts
-//                       without padding.
+//   kv_stage_kernel    writes the keys and values a call attends to, once, as fp16 tiles in the layout that the
+//                      attention kernel copies into LDS unchanged: k_hat = RoPE(RMSNorm(k) w_k) of the chunk's own
+//                      tokens (rounded to bf16, the KV-cache value; a global layer with a cache also stores it and v
+//                      in the cache rows of those positions), the earlier positions read back from the cache (the
+//                      global layer's rows or the gated layer's ring), and v^T.
+//   attn_tile_kernel   flash-style attention of 128 query rows (G heads x P positions of one KV head) per work-group
+//                      against 64-key tiles: causal (global layer) or within the window W (gated layer, whose
+//                      epilogue multiplies by sigmoid(gate)).  Each tile goes from the workspace straight into LDS
+//                      (buffer loads with LDS as the destination: no registers, no LDS write instructions), 16 KB of
+//                      keys and 16 KB of transposed values, double-buffered.  A direct load writes 16 bytes per lane
+//                      at consecutive LDS addresses; the lanes choose their source chunks so that the LDS rows come
+//                      out XOR-swizzled, which keeps the MFMA operand reads free of bank conflicts without padding.
+//   ring_write_kernel  after a gated chunk with a cache, its last min(S, W) keys and values go to ring slot p mod W.
 //
-// Method (ZGCM-1 paper summaries: onedev.kr "How it works"): per (token, head) q_hat = RoPE(RMSNorm(q) w_q), k_hat
-// likewise; the global output is softmax_{j <= i}(q_hat k_hat_j / sqrt(D)) v_j.
+// Method (ZGCM-1 paper summaries: onedev.kr "How it works"; jaehun.me "How Gated SWA Behaves"): per (token, head)
+// q_hat = RoPE(RMSNorm(q) w_q), k_hat likewise; the global output is softmax_{j <= i}(q_hat k_hat_j / sqrt(D)) v_j,
+// the gated output softmax_{i-W < j <= i}(...) v_j (.) sigmoid(g).  Positions are absolute: a chunk's queries at
+// pos0 .. pos0+S-1 see the cached keys of earlier positions.
 //
-// Precision as the other prefill kernels: k_hat and v are bf16 values held exactly in fp16, q_hat and P are
-// rounded once to fp16, the MFMAs accumulate in fp32, and the online softmax runs in fp32.
+// Precision: k_hat and v are bf16 values held exactly in fp16 (saturating at +-65504), q_hat and P are rounded
+// once to fp16, the MFMAs accumulate in fp32, and the online softmax runs in fp32.
 #include "common.h"
 #include "launch.h"
 
@@ -32,28 +38,43 @@ constexpr int kWaitVm0 = (7 << 4) | (15 << 8);   // s_waitcnt vmcnt(0), other co
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// ------------------------------------------------------------------------------------------------ prologue
-// One work-group per (sequence, KV head, 64-key tile).
-__global__ void __launch_bounds__(256) kv_tiles_kernel(KvTilesArgs a) {
+// ------------------------------------------------------------------------------------------------ staging
+// One work-group per (sequence, KV head, 64-row tile).  Staged row r holds position kbase + r: from the chunk's
+// input (pos0 <= p < pos0 + S), from the cache (p < pos0), zero past the chunk (padding of the last tile).
+__global__ void __launch_bounds__(256) kv_stage_kernel(StageArgs a) {
   const int tid = threadIdx.x;
-  const int n_tiles = a.S_pad / kBN;
+  const int n_tiles = a.S_kpad / kBN;
   const int unit = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
   const int b = unit / a.Hkv, h = unit % a.Hkv;
-  const int kt = tile * kBN;
-  const int64_t row_b = (int64_t)b * a.S;   // input row of (b, s, h): (row_b + s) * Hkv + h
-  // k_hat: a 16-lane group per key row (rows g, g + 16, g + 32, g + 48), 8 dims per lane; padding rows are zero
+  const int64_t row_b = (int64_t)b * a.S;                                      // input row (b, s, h): (row_b + s) * Hkv + h
+  const int64_t cbase = ((int64_t)b * a.Hkv + h) * a.slots * kHeadDim;        // cache rows of (b, h)
+  const int p0 = a.kbase + tile * kBN;                                          // position of the tile's row 0
+  const int pend = a.pos0 + a.S;
+  auto cache_row = [&](int p) -> int64_t {   // element offset of position p's row in the cache (ring: slot p mod W)
+    const int64_t slot = a.ring ? (int64_t)(p % a.slots) : (int64_t)p;
+    return cbase + slot * kHeadDim;
+  };
+  // k_hat: a 16-lane group per key row (rows g, g + 16, g + 32, g + 48), 8 dims per lane.  Every lane runs the
+  // norm on a chunk row (clamped), so the group's exchanges never meet inactive lanes; the row's source selects.
   {
     const int c = tid & 15, g = tid >> 4;
-    uint16_t* dst = a.kt + ((int64_t)unit * a.S_pad + kt) * kHeadDim + 8 * c;
+    uint16_t* dst = a.kt + ((int64_t)unit * a.S_kpad + (int64_t)tile * kBN) * kHeadDim + 8 * c;
 #pragma unroll
     for (int rr = 0; rr < 4; rr++) {
-      const int r = g + 16 * rr, s = kt + r;
-      const int sc = s < a.S ? s : a.S - 1;
+      const int r = g + 16 * rr, p = p0 + r;
+      const int sc = min(max(p - a.pos0, 0), a.S - 1);
       float f[8];
       unpack8(*reinterpret_cast<const uint4*>(a.k + ((row_b + sc) * a.Hkv + h) * kHeadDim + 8 * c), f);
-      norm_rope8_g16(f, a.kw, c, sc, a.eps, a.rot_pairs, a.inv_freq_rev);
-      const uint4 w = s < a.S ? bf16x8_to_f16x8(pack8(f)) : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(dst + (int64_t)r * kHeadDim) = w;
+      norm_rope8_g16(f, a.kw, c, a.pos0 + sc, a.eps, a.rot_pairs, a.inv_freq_rev);
+      uint4 kb = pack8(f);   // the KV-cache value of k_hat (bf16, nearest-even)
+      if (p >= a.pos0 && p < pend) {
+        if (a.dk) *reinterpret_cast<uint4*>(a.dk + cache_row(p) + 8 * c) = kb;
+      } else if (p < a.pos0) {
+        kb = *reinterpret_cast<const uint4*>(a.ck + cache_row(p) + 8 * c);
+      } else {
+        kb = make_uint4(0u, 0u, 0u, 0u);
+      }
+      *reinterpret_cast<uint4*>(dst + (int64_t)r * kHeadDim) = bf16x8_to_f16x8(kb);
     }
   }
   // v^T: thread (vq, vd) turns keys 4vq..4vq+3 x dims 8vd..8vd+7 into 8 dim rows of 4 keys (v_perm pairs the
@@ -63,22 +84,27 @@ __global__ void __launch_bounds__(256) kv_tiles_kernel(KvTilesArgs a) {
     uint32_t w[4][4];
 #pragma unroll
     for (int rr = 0; rr < 4; rr++) {
-      const int s = kt + 4 * vq + rr;
+      const int p = p0 + 4 * vq + rr;
       uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (s < a.S)
-        x = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.v + ((row_b + s) * a.Hkv + h) * kHeadDim + 8 * vd));
+      if (p >= a.pos0 && p < pend) {
+        x = *reinterpret_cast<const uint4*>(a.v + ((row_b + (p - a.pos0)) * a.Hkv + h) * kHeadDim + 8 * vd);
+        if (a.dv) *reinterpret_cast<uint4*>(a.dv + cache_row(p) + 8 * vd) = x;
+      } else if (p < a.pos0) {
+        x = *reinterpret_cast<const uint4*>(a.cv + cache_row(p) + 8 * vd);
+      }
+      x = bf16x8_to_f16x8(x);
       w[rr][0] = x.x; w[rr][1] = x.y; w[rr][2] = x.z; w[rr][3] = x.w;
     }
     const int qin = vq & 3;
     const int col = 16 * (vq >> 2) + 4 * (qin == 1 ? 2 : qin == 2 ? 1 : qin);
-    uint16_t* dst = a.vt + ((int64_t)unit * kHeadDim + 8 * vd) * a.S_pad + kt + col;
+    uint16_t* dst = a.vt + ((int64_t)unit * kHeadDim + 8 * vd) * a.S_kpad + (int64_t)tile * kBN + col;
 #pragma unroll
     for (int e = 0; e < 8; e++) {
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
       uint2 o;
       o.x = __builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel);
       o.y = __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel);
-      *reinterpret_cast<uint2*>(dst + (int64_t)e * a.S_pad) = o;
+      *reinterpret_cast<uint2*>(dst + (int64_t)e * a.S_kpad) = o;
     }
   }
 }
@@ -93,7 +119,8 @@ __global__ void __launch_bounds__(256) kv_tiles_kernel(KvTilesArgs a) {
 //   V^T [128 dims][64 keys]: chunk c (8 stored keys) of dim row r sits at chunk position c ^ ((r / 2) mod 8)
 // The MFMA A-operand reads take one chunk from each of 16 consecutive rows per LDS cycle group; the swizzles
 // spread those 16 chunks over all 64 banks.
-__global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
+template <bool GATED>
+__global__ void __launch_bounds__(256, 2) attn_tile_kernel(TileAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[kSmemBytes / 2];
   uint16_t* const Ks = smem;                     // [2] K tiles
   uint16_t* const Vt = smem + 2 * kTileHalves;   // [2] V^T tiles
@@ -105,7 +132,7 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
 
   // Block order: consecutive block ids walk the (b, kv head) units first, so with B*Hkv a multiple of 8 every
   // block of one unit lands on the same XCD (blocks go round-robin over the 8 XCDs) and its keys and values stay
-  // in that XCD's L2; the longest query tiles go first.
+  // in that XCD's L2; a causal layer's longest query tiles go first.
   const int unit = blockIdx.x % a.n_units;
   const int qt = a.n_qtiles - 1 - (int)(blockIdx.x / a.n_units);
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
@@ -113,23 +140,29 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
 
   const int r = wave * 32 + l32;
   const int hq = kvh * a.G + r / a.P;
-  const int i = i0 + r % a.P;
+  const int i = i0 + r % a.P;                     // row within the chunk
   const bool qvalid = i < a.S;
-  const int qpos = qvalid ? i : a.S - 1;
+  const int ic = qvalid ? i : a.S - 1;
+  const int qpos = a.pos0 + ic;                   // absolute position
 
-  // wave-uniform position range of this wave's rows (clamped to the sequence)
+  // wave-uniform absolute position range of this wave's rows (clamped to the chunk)
   int pl_lo, pl_hi;
   if (a.P >= 32) { pl_lo = (wave * 32) % a.P; pl_hi = pl_lo + 31; } else { pl_lo = 0; pl_hi = a.P - 1; }
-  const int wlo = min(i0 + pl_lo, a.S - 1);
-  const int whi = min(i0 + pl_hi, a.S - 1);
-  const int khi = min(i0 + a.P, a.S);             // keys 0 .. khi-1 are visible to some row of the work-group
-  const int n_tiles = (khi + kBN - 1) / kBN;
+  const int wlo = a.pos0 + min(i0 + pl_lo, a.S - 1);
+  const int whi = a.pos0 + min(i0 + pl_hi, a.S - 1);
+  // staged tiles the work-group visits: keys from the oldest any row sees to the newest (its last position)
+  const int khi = a.pos0 + min(i0 + a.P, a.S);    // exclusive
+  const int klo = GATED ? max(a.kbase, a.pos0 + i0 - a.window + 1) : a.kbase;
+  const int t_lo = (klo - a.kbase) / kBN;
+  const int t_hi = (khi - a.kbase + kBN - 1) / kBN;
+  // visible iff 0 <= qpos - key < lim (one unsigned compare)
+  const unsigned lim = GATED ? (unsigned)a.window : 0x7fffffffu;
 
   // ---- Q prologue: load, RMSNorm * w_q, partial RoPE, scale by log2(e)/sqrt(D), round to fp16.
   // MFMA B operand (Q^T, K = d): lane holds q_hat[query l32][16t + 8hi .. +8] for k-step t.
   half8 qf[8];
   {
-    const uint16_t* qrow = a.q + (((int64_t)b * a.S + qpos) * a.Hq + hq) * kHeadDim;
+    const uint16_t* qrow = a.q + (((int64_t)b * a.S + ic) * a.Hq + hq) * kHeadDim;
     float f[8][8];
     float ss = 0.f;
 #pragma unroll
@@ -169,11 +202,11 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
   // ---- direct loads: wave w copies the 1 KB LDS blocks 4w..4w+3 of the K tile (key rows 4j..4j+3 each) and of
   // the V^T tile (dim rows 8j..8j+7 each).  Byte offsets within the planes, constant over the tiles; the tile
   // moves the scalar offset.  Every tile lies inside the padded planes, so no load is out of range.
-  const uint32_t plane_bytes = (uint32_t)a.S_pad * kHeadDim * 2;
+  const uint32_t plane_bytes = (uint32_t)a.S_kpad * kHeadDim * 2;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.kt + (int64_t)unit * a.S_pad * kHeadDim), (short)0, (int)plane_bytes, 0x00020000);
+      (void*)(a.kt + (int64_t)unit * a.S_kpad * kHeadDim), (short)0, (int)plane_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.vt + (int64_t)unit * kHeadDim * a.S_pad), (short)0, (int)plane_bytes, 0x00020000);
+      (void*)(a.vt + (int64_t)unit * kHeadDim * a.S_kpad), (short)0, (int)plane_bytes, 0x00020000);
   uint32_t koff[4], voff[4];
 #pragma unroll
   for (int jj = 0; jj < 4; jj++) {
@@ -181,7 +214,7 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
     const int kr = 4 * j + (lane >> 4);            // key row that this lane's 16 bytes fill
     koff[jj] = (uint32_t)kr * (kHeadDim * 2) + 16u * (uint32_t)((lane & 15) ^ (kr & 15));
     const int vr = 8 * j + (lane >> 3);            // dim row
-    voff[jj] = (uint32_t)vr * (uint32_t)a.S_pad * 2u + 16u * (uint32_t)((lane & 7) ^ ((vr >> 1) & 7));
+    voff[jj] = (uint32_t)vr * (uint32_t)a.S_kpad * 2u + 16u * (uint32_t)((lane & 7) ^ ((vr >> 1) & 7));
   }
   auto issue_tile = [&](int t, int buf) {
     const uint32_t ks = (uint32_t)t * kBN * kHeadDim * 2, vs = (uint32_t)t * kBN * 2;
@@ -205,8 +238,9 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
 
   const half2 ones = {(_Float16)1.0f, (_Float16)1.0f};
   auto compute = [&](int buf, int t) {
-    const int kt = t * kBN;
-    if (kt > whi) return;   // beyond every query of the wave
+    const int kt = a.kbase + t * kBN;              // absolute position of the tile's first key
+    if (kt > whi) return;                          // after every query of the wave
+    if (GATED && kt + kBN - 1 < wlo - a.window + 1) return;   // before every query's window
     const uint16_t* kb_ = Ks + buf * kTileHalves;
     const uint16_t* vb_ = Vt + buf * kTileHalves;
     // S^T = K Q^T for the two 32-key halves; the two accumulator chains are interleaved so consecutive MFMAs are
@@ -234,13 +268,14 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; db++)
           op[8 * kb + 4 * h2 + db] = *reinterpret_cast<const half8*>(vb_ + db * 32 * kBN + vfo[2 * kb + h2]);
-    if (kt + kBN - 1 > wlo) {   // the diagonal cuts this tile for some row of the wave
+    // the diagonal (or, for a gated layer, the window's far edge) cuts this tile for some row of the wave
+    if (kt + kBN - 1 > wlo || (GATED && kt < whi - a.window + 1)) {
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
         for (int j = 0; j < 16; j++) {
           const int key = kt + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-          if (key > qpos) sacc[kb][j] = -INFINITY;
+          if ((unsigned)(qpos - key) >= lim) sacc[kb][j] = -INFINITY;
         }
     }
     // row max: two chains of three-input maxima (v_max3), one per 32-key half
@@ -302,22 +337,23 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
   // last use), compute this one, then wait for this wave's copies and meet the other waves, after which the next
   // tile is complete in LDS.  The loop runs two steps per pass so each step's buffer is a constant.
   auto step = [&](int t, int buf) {
-    if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1);
+    if (t + 1 < t_hi) issue_tile(t + 1, buf ^ 1);
     compute(buf, t);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   };
-  issue_tile(0, 0);
+  issue_tile(t_lo, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t_lo; t < t_hi; t += 2) {
     step(t, 0);
-    if (t + 1 < n_tiles) step(t + 1, 1);
+    if (t + 1 < t_hi) step(t + 1, 1);
   }
 
   // ---- epilogue: normalise, stage the 128 rows through LDS as fp32 (the tile buffers are free after the loop's
-  // last barrier), then each thread rounds 8 consecutive dims of a row to bf16 and 16 consecutive lanes store a
-  // whole 256-byte row.  O^T lane layout: acc_o[db][j] is d = 32db + 8(j/4) + 4hi + j%4 of query row r.
+  // last barrier), then each thread rounds 8 consecutive dims of a row to bf16 (a gated layer after multiplying by
+  // sigmoid(gate)) and 16 consecutive lanes store a whole 256-byte row.  O^T lane layout: acc_o[db][j] is
+  // d = 32db + 8(j/4) + 4hi + j%4 of query row r.
   l_run = xor32_sum(l_run);
   const float inv_l = 1.0f / l_run;
   // training: the log-sum-exp of the query's scores (natural log; scores in log2 units are s log2(e))
@@ -346,27 +382,78 @@ __global__ void __launch_bounds__(256, 2) attn_global_kernel(GlobalArgs a) {
       const int64_t goff = (((int64_t)b * a.S + ipos) * a.Hq + kvh * a.G + orow / a.P) * kHeadDim + 8 * oc;
       const float4 o0 = *reinterpret_cast<const float4*>(&Os[orow * kOsStride + 8 * oc]);
       const float4 o1 = *reinterpret_cast<const float4*>(&Os[orow * kOsStride + 8 * oc + 4]);
-      const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+      float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+      if (GATED) {
+        // sigmoid(g) = 1 / (1 + 2^(-g log2 e)): exactly 1 at g = +inf and 0 at g = -inf
+        float gv[8];
+        unpack8(*reinterpret_cast<const uint4*>(a.gate + goff), gv);
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          o[e] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[e] * kLog2e));
+      }
       *reinterpret_cast<uint4*>(a.out + goff) = pack8(o);
     }
   }
 }
 
+// ------------------------------------------------------------------------------------------------ ring write
+// After a gated chunk with a cache: k_hat (recomputed from k, bit-identical to the staging's) and raw v of the
+// chunk's last n rows go to ring slot (position mod W).  One 16-lane group per row.
+__global__ void __launch_bounds__(256) ring_write_kernel(RingWriteArgs a) {
+  const int c = threadIdx.x & 15;
+  const int64_t n_rows = (int64_t)a.B * a.Hkv * a.n;
+  const int64_t row_raw = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool valid = row_raw < n_rows;
+  const int64_t row = valid ? row_raw : n_rows - 1;
+  const int j = (int)(row % a.n);
+  const int h = (int)((row / a.n) % a.Hkv);
+  const int64_t b = row / ((int64_t)a.n * a.Hkv);
+  const int64_t s = a.S - a.n + j;
+  const int64_t src = ((b * a.S + s) * a.Hkv + h) * kHeadDim + 8 * c;
+  float f[8];
+  unpack8(*reinterpret_cast<const uint4*>(a.k + src), f);
+  norm_rope8_g16(f, a.kw, c, a.pos0 + s, a.eps, a.rot_pairs, a.inv_freq_rev);
+  if (valid) {
+    const int64_t slot = (a.pos0 + s) % a.W;
+    const int64_t dst = ((b * a.Hkv + h) * a.W + slot) * kHeadDim + 8 * c;
+    *reinterpret_cast<uint4*>(a.kring + dst) = pack8(f);
+    *reinterpret_cast<uint4*>(a.vring + dst) = *reinterpret_cast<const uint4*>(a.v + src);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_kv_tiles(const KvTilesArgs& a, hipStream_t st) {
-  if (a.S < 1 || a.S_pad % kBN || a.S_pad < a.S || a.S_pad - a.S >= kBN) return hipErrorInvalidValue;
-  const int64_t blocks = (int64_t)a.B * a.Hkv * (a.S_pad / kBN);
-  hipLaunchKernelGGL(kv_tiles_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+hipError_t launch_kv_stage(const StageArgs& a, hipStream_t st) {
+  // the staged rows cover kbase .. pos0+S-1 in whole tiles; the prefix (< pos0) needs a cache to read
+  const int64_t staged = (int64_t)a.pos0 + a.S - a.kbase;
+  if (a.S < 1 || a.S_kpad % kBN || a.kbase < 0 || a.kbase > a.pos0 || staged > a.S_kpad || a.S_kpad - staged >= kBN ||
+      (a.kbase < a.pos0 && (!a.ck || !a.cv || a.slots < 1)) || (a.ring && a.pos0 - a.kbase >= a.slots))
+    return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)a.B * a.Hkv * (a.S_kpad / kBN);
+  hipLaunchKernelGGL(kv_stage_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_global(const GlobalArgs& a, hipStream_t st) {
-  if (a.S < 1 || a.S_pad % kBN || a.S_pad < a.S || a.G * a.P != 128 || a.n_units != a.B * a.Hkv ||
-      a.n_qtiles != (a.S + a.P - 1) / a.P)
+hipError_t launch_attn_tile(const TileAttnArgs& a, bool gated, hipStream_t st) {
+  // every key the work-groups visit must be staged: from kbase (no later than the first visible key of the
+  // chunk's first query) to the chunk's last position
+  const int64_t staged = (int64_t)a.pos0 + a.S - a.kbase;
+  const int64_t first_key = gated ? std::max<int64_t>(0, (int64_t)a.pos0 - a.window + 1) : 0;
+  if (a.S < 1 || a.S_kpad % kBN || a.kbase < 0 || a.kbase > first_key || staged > a.S_kpad || a.G * a.P != 128 ||
+      a.n_units != a.B * a.Hkv || a.n_qtiles != (a.S + a.P - 1) / a.P || (gated && (a.window < 1 || !a.gate)))
     return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)a.n_units * a.n_qtiles;
-  hipLaunchKernelGGL(attn_global_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  if (gated)
+    hipLaunchKernelGGL(attn_tile_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_tile_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_write(const RingWriteArgs& a, hipStream_t st) {
+  if (a.n < 1 || a.n > a.S || a.n > a.W) return hipErrorInvalidValue;
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.n;
+  hipLaunchKernelGGL(ring_write_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -36,14 +36,26 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// 8 bf16 -> 8 fp16.  Exact for magnitudes in [2^-14, 65504]; below 2^-14 the fp16 subnormal keeps an
-// absolute error under 2^-25.  The attention operands (normalised keys, values ~N(0,1)) stay in range.
+// fp16's largest finite magnitude.
+constexpr float kF16Max = 65504.0f;
+
+// Round two fp32 to fp16 after clamping them to +-65504 (v_med3 then v_cvt_pk_f16_f32): values beyond fp16's range
+// saturate instead of becoming infinite.
+__device__ __forceinline__ uint32_t pack_f16_sat(float a, float b) {
+  return pack_f16(__builtin_amdgcn_fmed3f(a, -kF16Max, kF16Max), __builtin_amdgcn_fmed3f(b, -kF16Max, kF16Max));
+}
+
+// 8 bf16 -> 8 fp16, saturating.  Exact for magnitudes in [2^-14, 65504]; below 2^-14 the fp16 subnormal keeps an
+// absolute error under 2^-25; above 65504 the value becomes +-65504.  Keys (k_hat = RMSNorm * w_k, so |k_hat_d| <=
+// sqrt(128) |w_k,d|) and values enter the fp16 MFMAs through this conversion.  Saturation keeps an out-of-range
+// value finite, so a masked key's zero weight never meets an infinity (0 * inf would turn every output of the
+// MFMA's column into NaN, earlier queries of the tile included).
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& w) {
   uint4 r;
-  r.x = pack_f16(bf16lo(w.x), bf16hi(w.x));
-  r.y = pack_f16(bf16lo(w.y), bf16hi(w.y));
-  r.z = pack_f16(bf16lo(w.z), bf16hi(w.z));
-  r.w = pack_f16(bf16lo(w.w), bf16hi(w.w));
+  r.x = pack_f16_sat(bf16lo(w.x), bf16hi(w.x));
+  r.y = pack_f16_sat(bf16lo(w.y), bf16hi(w.y));
+  r.z = pack_f16_sat(bf16lo(w.z), bf16hi(w.z));
+  r.w = pack_f16_sat(bf16lo(w.w), bf16hi(w.w));
   return r;
 }
 

@@ -10,27 +10,8 @@ constexpr int kMaxLayers = 64;
 constexpr int kMaxDecodeBatch = 128;
 constexpr int kDecodeChunk = 8192;   // keys per split-K work-group of a global decode layer
 
-// k_hat = RoPE(RMSNorm(k) * w) for a chunk of S tokens, rounded to bf16 (the KV-cache format) and
-// written to a destination with strides, either as those bf16 bits (KV cache) or converted exactly to
-// fp16 (workspace read by the fp16 MFMAs); v optionally copied alongside (bf16, or converted to fp16).
-// Rows are (b, s, h) of k [B][S][Hkv][D].
-struct KvPrologueArgs {
-  const uint16_t* k;
-  const uint16_t* v;         // nullable: copy v rows to vdst when set
-  const uint16_t* kw;        // [D]
-  uint16_t* kdst;
-  uint16_t* vdst;
-  int64_t d_sb, d_sh, d_st;  // destination element strides for (b, h, s), same for kdst and vdst
-  int32_t dst_f16;           // 1: write fp16 (workspace), 0: write bf16 (KV cache)
-  int32_t B, S, Hkv;
-  int64_t pos0;
-  int32_t rot_pairs;
-  float eps;
-  double inv_freq_rev[64];
-};
-
-// After an SWA chunk: k_hat (recomputed from k, bit-identical to the prologue's) and raw v of the chunk's
-// last n rows go to ring slot (position mod W).
+// After a gated chunk with a cache: k_hat (recomputed from k, bit-identical to the staging's) and raw v of the
+// chunk's last n rows go to ring slot (position mod W).
 struct RingWriteArgs {
   const uint16_t* k;         // input k [B][S][Hkv][D]
   const uint16_t* v;         // input v [B][S][Hkv][D]
@@ -44,59 +25,46 @@ struct RingWriteArgs {
   double inv_freq_rev[64];
 };
 
-struct PrefillArgs {
-  const uint16_t* q;     // [B][S][Hq][D]
-  const uint16_t* gate;  // [B][S][Hq][D], null for global layers
-  const uint16_t* qw;    // [D]
-  uint16_t* out;         // [B][S][Hq][D]
-  // key/value source A holds positions >= a_pos0: row(b,h,pos) = base + b*sb + h*sh + (pos-a_pos0)*st
-  const uint16_t* kA;        // fp16 bits (workspace) unless ka_bf16
-  const uint16_t* vA;        // fp16 bits (workspace) unless va_bf16
-  int32_t ka_bf16, va_bf16;  // source A element format; ring rows are always bf16
-  int64_t kA_sb, kA_sh, kA_st;
-  int64_t vA_sb, vA_sh, vA_st;
-  int64_t a_pos0;
-  // ring source for positions < a_pos0 (SWA chunked prefill): row = base + b*R_sb + h*R_sh + (pos mod W)*D
-  const uint16_t* kR;
-  const uint16_t* vR;
-  int64_t R_sb, R_sh;
-  int32_t B, S, Hq, Hkv, G, P;  // G = Hq/Hkv, P = 128/G query positions per work-group
-  int64_t pos0;
-  int32_t window;               // 0 for a global layer
-  int32_t rot_pairs;
-  float eps;
-  float q_scale;                // log2(e) / sqrt(D)
-  int32_t n_units;              // B * Hkv
-  int32_t n_qtiles;             // ceil(S / P)
-  float* lse;                   // [B][Hq][S] natural log of each softmax denominator (training), or null
-  double inv_freq_rev[64];
-};
-
-// Global causal prefill without a cache.  The tile prologue writes the keys and values once, in the layout the
-// attention kernel copies into LDS with direct (buffer-to-LDS) loads:
-//   kt: k_hat fp16 [B][Hkv][S_pad][D]
-//   vt: v^T fp16 [B][Hkv][D][S_pad], inside each group of 16 keys the quads of 4 keys in the order 0, 2, 1, 3
-// S_pad = S rounded up to a whole 64-key tile; the padding keys are zero in both.
-struct KvTilesArgs {
-  const uint16_t* k;   // [B][S][Hkv][D] bf16
-  const uint16_t* v;   // [B][S][Hkv][D] bf16
-  const uint16_t* kw;  // [D]
+// Staging of the keys and values a tile-path call attends to, positions kbase .. pos0+S-1 (kbase <= pos0), in the
+// layout the attention kernel copies into LDS with direct (buffer-to-LDS) loads:
+//   kt: k_hat fp16 [B][Hkv][S_kpad][D]
+//   vt: v^T fp16 [B][Hkv][D][S_kpad], inside each group of 16 keys the quads of 4 keys in the order 0, 2, 1, 3
+// Staged row r is position kbase + r; S_kpad = the staged count rounded up to a whole 64-key tile, the padding
+// rows zero.  Positions >= pos0 come from the chunk's k (k_hat computed here) and v; earlier ones from the cache
+// (ck/cv, bf16 [B][Hkv][slots][D]: row p of a global layer, or ring slot p mod slots).  With dk/dv set, the chunk's
+// k_hat and v are also stored in those cache rows (a global layer with a cache).
+struct StageArgs {
+  const uint16_t* k;     // [B][S][Hkv][D] bf16, the chunk
+  const uint16_t* v;
+  const uint16_t* kw;    // [D]
+  const uint16_t* ck;    // cache K / V of the layer, or null when kbase == pos0
+  const uint16_t* cv;
+  uint16_t* dk;          // cache K / V rows for the chunk's positions, or null
+  uint16_t* dv;
+  int64_t slots;         // rows per (b, head) of the cache arrays
+  int32_t ring;          // 1: slot = position mod slots
   uint16_t* kt;
   uint16_t* vt;
-  int32_t B, S, S_pad, Hkv;
+  int32_t pos0, kbase;
+  int32_t B, S, S_kpad, Hkv;
   int32_t rot_pairs;
   float eps;
   double inv_freq_rev[64];
 };
 
-struct GlobalArgs {
+// Tile-path attention over the staged keys (see StageArgs): queries at pos0 .. pos0+S-1; causal when gate is null
+// (global layer), else within the window and multiplied by sigmoid(gate).
+struct TileAttnArgs {
   const uint16_t* q;    // [B][S][Hq][D]
+  const uint16_t* gate; // [B][S][Hq][D], null for a global layer
   const uint16_t* qw;   // [D]
   uint16_t* out;        // [B][S][Hq][D]
   float* lse;           // [B][Hq][S] or null
-  const uint16_t* kt;   // tile workspace, layouts as above
+  const uint16_t* kt;   // staged tiles
   const uint16_t* vt;
-  int32_t B, S, S_pad, Hq, Hkv, G, P;  // P = 128 / G query positions per work-group
+  int32_t pos0, kbase;
+  int32_t B, S, S_kpad, Hq, Hkv, G, P;  // P = 128 / G query positions per work-group
+  int32_t window;       // gated layers
   int32_t rot_pairs;
   float eps;
   float q_scale;        // log2(e) / sqrt(D)
@@ -214,11 +182,9 @@ struct DecodeArgs {
   int64_t pos[kMaxDecodeBatch];
 };
 
-hipError_t launch_kv_prologue(const KvPrologueArgs& a, hipStream_t st);
 hipError_t launch_ring_write(const RingWriteArgs& a, hipStream_t st);
-hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st);
-hipError_t launch_kv_tiles(const KvTilesArgs& a, hipStream_t st);
-hipError_t launch_attn_global(const GlobalArgs& a, hipStream_t st);
+hipError_t launch_kv_stage(const StageArgs& a, hipStream_t st);
+hipError_t launch_attn_tile(const TileAttnArgs& a, bool gated, hipStream_t st);
 hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st);
 int32_t fp8_quantize_blocks(int64_t n);   // work-groups launch_fp8_quantize uses for n values
 hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const float* scale, float* partial,

@@ -2,6 +2,7 @@
 // enqueued on the caller's stream by the kernels in attn_prefill.hip and decode.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -274,10 +275,29 @@ extern "C" int kv_cache_set_length(zg_kv_cache* c, int32_t layer, int32_t b, int
   return ZG_OK;
 }
 
+namespace {
+// Keys a tile-path call stages: positions kbase .. pos0+S-1, kbase = the oldest position the chunk's first query
+// sees (0 for a global layer), in whole 64-key tiles.
+struct StagePlan {
+  int64_t kbase, staged, s_kpad;
+};
+StagePlan stage_plan(int64_t pos0, int64_t S, int64_t window) {
+  const int64_t kbase = window > 0 ? std::max<int64_t>(0, pos0 - window + 1) : 0;
+  const int64_t staged = pos0 + S - kbase;
+  return {kbase, staged, (staged + 63) / 64 * 64};
+}
+}  // namespace
+
+extern "C" uint64_t prefill_workspace_bytes_at(int32_t B, int32_t S, int32_t Hkv, int32_t D, int64_t pos0,
+                                               int32_t window) {
+  if (B < 0 || S < 0 || Hkv < 0 || D < 0 || pos0 < 0 || window < 0) return 0;
+  if (S == 0) return 0;
+  const StagePlan pl = stage_plan(pos0, S, window);
+  return 2ull * (uint64_t)B * (uint64_t)pl.s_kpad * (uint64_t)Hkv * (uint64_t)D * 2ull;
+}
+
 extern "C" uint64_t prefill_workspace_bytes(int32_t B, int32_t S, int32_t Hkv, int32_t D) {
-  if (B < 0 || S < 0 || Hkv < 0 || D < 0) return 0;
-  const uint64_t s_pad = ((uint64_t)S + 63) / 64 * 64;   // whole 64-key tiles
-  return 2ull * (uint64_t)B * s_pad * (uint64_t)Hkv * (uint64_t)D * 2ull;
+  return prefill_workspace_bytes_at(B, S, Hkv, D, 0, 0);
 }
 
 // ---------------------------------------------------------------------------------- prefill
@@ -327,14 +347,12 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(qw) || !aligned16(kw) || !aligned16(out) ||
       (gated && !aligned16(gate)))
     return fail(ZG_EINVAL, "%s: tensors must be 16-byte aligned", fn);
-  const bool need_ws = gated || !cache;
-  if (need_ws) {
-    if (!ws) return fail(ZG_EINVAL, "%s: workspace required", fn);
-    if (!aligned16(ws)) return fail(ZG_EINVAL, "%s: workspace must be 16-byte aligned", fn);
-    if (ws_bytes < prefill_workspace_bytes(B, S, Hkv, D))
-      return fail(ZG_ERANGE, "%s: workspace of %llu bytes < %llu needed", fn, (unsigned long long)ws_bytes,
-                  (unsigned long long)prefill_workspace_bytes(B, S, Hkv, D));
-  }
+  if (!ws) return fail(ZG_EINVAL, "%s: workspace required", fn);
+  if (!aligned16(ws)) return fail(ZG_EINVAL, "%s: workspace must be 16-byte aligned", fn);
+  const uint64_t ws_need = prefill_workspace_bytes_at(B, S, Hkv, D, cache ? pos0 : 0, gated ? window : 0);
+  if (ws_bytes < ws_need)
+    return fail(ZG_ERANGE, "%s: workspace of %llu bytes < %llu needed", fn, (unsigned long long)ws_bytes,
+                (unsigned long long)ws_need);
   if (cache) {
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess || cur != cache->device)
@@ -369,125 +387,58 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     return ZG_OK;
   }
+  // tile path: stage the keys the chunk sees (its own, and with a cache the earlier positions from the cache) as
+  // fp16 tiles in the workspace, then the tile kernel
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
-  const int64_t D64 = kHeadDim;
-  if (!gated && !cache) {
-    // global layer without a cache: k_hat and v^T into the tile workspace, then the direct-load kernel
-    const int32_t S_pad = (S + 63) / 64 * 64;
-    KvTilesArgs ta{};
-    ta.k = k16;
-    ta.v = v16;
-    ta.kw = static_cast<const uint16_t*>(kw);
-    ta.kt = static_cast<uint16_t*>(ws);
-    ta.vt = ta.kt + (int64_t)B * Hkv * S_pad * D64;
-    ta.B = B; ta.S = S; ta.S_pad = S_pad; ta.Hkv = Hkv; ta.rot_pairs = rot_pairs; ta.eps = eps;
-    fill_inv_freq(ta.inv_freq_rev, rot_pairs, R, base);
-    {
-      ScopedTimer tm("kv_prologue", st);
-      hipError_t e = launch_kv_tiles(ta, st);
-      if (e != hipSuccess) return hip_fail(e, "kv_tiles launch");
-    }
-    GlobalArgs ga{};
-    ga.q = static_cast<const uint16_t*>(q);
-    ga.qw = static_cast<const uint16_t*>(qw);
-    ga.out = static_cast<uint16_t*>(out);
-    ga.lse = lse;
-    ga.kt = ta.kt; ga.vt = ta.vt;
-    ga.B = B; ga.S = S; ga.S_pad = S_pad; ga.Hq = Hq; ga.Hkv = Hkv; ga.G = G; ga.P = 128 / G;
-    ga.rot_pairs = rot_pairs;
-    ga.eps = eps;
-    ga.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
-    ga.n_units = B * Hkv;
-    ga.n_qtiles = (S + ga.P - 1) / ga.P;
-    std::memcpy(ga.inv_freq_rev, ta.inv_freq_rev, sizeof ga.inv_freq_rev);
-    ScopedTimer tm("attn_global", st);
-    hipError_t e = launch_attn_global(ga, st);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
-    return ZG_OK;
-  }
   const LayerDesc* ld = cache ? &cache->layers[layer - 1] : nullptr;
-
-  // 1. k_hat of the chunk, rounded to the bf16 cache format: into the cache (global layer with a cache,
-  //    with v) or, as exact fp16, into the workspace [B][Hkv][S][D] (a global layer without a cache also
-  //    puts v there, as fp16, right after the keys)
-  uint16_t* ws16 = static_cast<uint16_t*>(ws);
-  const int64_t ws_half = (int64_t)B * Hkv * S * D64;
-  KvPrologueArgs pa{};
-  pa.k = k16;
-  pa.kw = static_cast<const uint16_t*>(kw);
-  pa.B = B; pa.S = S; pa.Hkv = Hkv; pa.pos0 = pos0; pa.rot_pairs = rot_pairs; pa.eps = eps;
-  fill_inv_freq(pa.inv_freq_rev, rot_pairs, R, base);
-  if (!gated && cache) {
-    pa.v = v16;
-    pa.kdst = ld->k + pos0 * D64;
-    pa.vdst = ld->v + pos0 * D64;
-    pa.d_sb = (int64_t)Hkv * ld->slots * D64; pa.d_sh = ld->slots * D64; pa.d_st = D64;
-    pa.dst_f16 = 0;
-  } else {
-    pa.v = gated ? nullptr : v16;
-    pa.kdst = ws16;
-    pa.vdst = gated ? nullptr : ws16 + ws_half;
-    pa.d_sb = (int64_t)Hkv * S * D64; pa.d_sh = (int64_t)S * D64; pa.d_st = D64;
-    pa.dst_f16 = 1;
+  const StagePlan pl = stage_plan(cache ? pos0 : 0, S, gated ? window : 0);
+  StageArgs sa{};
+  sa.k = k16;
+  sa.v = v16;
+  sa.kw = static_cast<const uint16_t*>(kw);
+  if (cache) {
+    sa.slots = ld->slots;
+    sa.ring = gated ? 1 : 0;
+    if (pl.kbase < pos0) { sa.ck = ld->k; sa.cv = ld->v; }
+    if (!gated) { sa.dk = ld->k; sa.dv = ld->v; }   // the chunk's rows of a global layer's cache
   }
+  sa.kt = static_cast<uint16_t*>(ws);
+  sa.vt = sa.kt + (int64_t)B * Hkv * pl.s_kpad * kHeadDim;
+  sa.pos0 = (int32_t)(cache ? pos0 : 0);
+  sa.kbase = (int32_t)pl.kbase;
+  sa.B = B; sa.S = S; sa.S_kpad = (int32_t)pl.s_kpad; sa.Hkv = Hkv;
+  sa.rot_pairs = rot_pairs;
+  sa.eps = eps;
+  fill_inv_freq(sa.inv_freq_rev, rot_pairs, R, base);
   {
     ScopedTimer tm("kv_prologue", st);
-    hipError_t e = launch_kv_prologue(pa, st);
-    if (e != hipSuccess) return hip_fail(e, "kv_prologue launch");
+    hipError_t e = launch_kv_stage(sa, st);
+    if (e != hipSuccess) return hip_fail(e, "key staging launch");
   }
-
-  // 2. attention
-  PrefillArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.gate = gated ? static_cast<const uint16_t*>(gate) : nullptr;
-  a.qw = static_cast<const uint16_t*>(qw);
-  a.out = static_cast<uint16_t*>(out);
-  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.P = 128 / G;
-  a.pos0 = pos0;
-  a.window = gated ? window : 0;
-  a.rot_pairs = rot_pairs;
-  a.eps = eps;
-  a.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
-  a.n_units = B * Hkv;
-  a.n_qtiles = (S + a.P - 1) / a.P;
-  a.lse = lse;
-  std::memcpy(a.inv_freq_rev, pa.inv_freq_rev, sizeof a.inv_freq_rev);
-  if (!gated && cache) {          // every key from the cache (bf16), absolute positions
-    a.kA = ld->k; a.vA = ld->v;
-    a.ka_bf16 = a.va_bf16 = 1;
-    a.kA_sb = a.vA_sb = (int64_t)Hkv * ld->slots * D64;
-    a.kA_sh = a.vA_sh = ld->slots * D64;
-    a.kA_st = a.vA_st = D64;
-    a.a_pos0 = 0;
-  } else if (!gated) {            // keys and values from the workspace (fp16)
-    a.kA = ws16; a.vA = ws16 + ws_half;
-    a.ka_bf16 = a.va_bf16 = 0;
-    a.kA_sb = a.vA_sb = (int64_t)Hkv * S * D64;
-    a.kA_sh = a.vA_sh = (int64_t)S * D64;
-    a.kA_st = a.vA_st = D64;
-    a.a_pos0 = 0;
-  } else {                        // SWA: chunk keys from the workspace, values from the input, older from the ring
-    a.kA = ws16;
-    a.ka_bf16 = 0;
-    a.kA_sb = (int64_t)Hkv * S * D64; a.kA_sh = (int64_t)S * D64; a.kA_st = D64;
-    a.vA = v16;
-    a.va_bf16 = 1;
-    a.vA_sb = (int64_t)S * Hkv * D64; a.vA_sh = D64; a.vA_st = (int64_t)Hkv * D64;
-    a.a_pos0 = pos0;
-    if (cache) {
-      a.kR = ld->k; a.vR = ld->v;
-      a.R_sb = (int64_t)Hkv * window * D64; a.R_sh = (int64_t)window * D64;
-    }
-  }
+  TileAttnArgs ta{};
+  ta.q = static_cast<const uint16_t*>(q);
+  ta.gate = gated ? static_cast<const uint16_t*>(gate) : nullptr;
+  ta.qw = static_cast<const uint16_t*>(qw);
+  ta.out = static_cast<uint16_t*>(out);
+  ta.lse = lse;
+  ta.kt = sa.kt; ta.vt = sa.vt;
+  ta.pos0 = sa.pos0; ta.kbase = sa.kbase;
+  ta.B = B; ta.S = S; ta.S_kpad = sa.S_kpad; ta.Hq = Hq; ta.Hkv = Hkv; ta.G = G; ta.P = 128 / G;
+  ta.window = gated ? window : 0;
+  ta.rot_pairs = rot_pairs;
+  ta.eps = eps;
+  ta.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
+  ta.n_units = B * Hkv;
+  ta.n_qtiles = (S + ta.P - 1) / ta.P;
+  std::memcpy(ta.inv_freq_rev, sa.inv_freq_rev, sizeof ta.inv_freq_rev);
   {
     ScopedTimer tm(gated ? "attn_swa" : "attn_global", st);
-    hipError_t e = launch_attn_prefill(a, st);
+    hipError_t e = launch_attn_tile(ta, gated, st);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
   }
-
-  // 3. SWA with a cache: the chunk's last min(S, W) positions go to the ring (after the attention has
-  //    read the ring's previous contents)
+  // a gated layer with a cache: the chunk's last min(S, W) positions go to the ring (the staging has read the
+  // ring's earlier contents)
   if (gated && cache) {
     RingWriteArgs ra{};
     ra.k = k16;
@@ -496,7 +447,7 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
     ra.kring = ld->k; ra.vring = ld->v;
     ra.B = B; ra.S = S; ra.Hkv = Hkv; ra.W = window; ra.n = S < window ? S : window; ra.pos0 = pos0;
     ra.rot_pairs = rot_pairs; ra.eps = eps;
-    std::memcpy(ra.inv_freq_rev, pa.inv_freq_rev, sizeof ra.inv_freq_rev);
+    std::memcpy(ra.inv_freq_rev, sa.inv_freq_rev, sizeof ra.inv_freq_rev);
     hipError_t e = launch_ring_write(ra, st);
     if (e != hipSuccess) return hip_fail(e, "ring write launch");
   }
@@ -786,21 +737,24 @@ int layer_common(bool gated, const void* h, const void* w_q, const void* w_k, co
       (gated && !aligned16(w_g)))
     return fail(ZG_EINVAL, "%s: tensors must be 16-byte aligned", fn);
   if (!ws || !aligned16(ws)) return fail(ZG_EINVAL, "%s: a 16-byte aligned workspace is required", fn);
-  const uint64_t need = f8 ? fp8_layer_workspace_bytes(B, S, d_model, Hq, Hkv, D) : layer_workspace_bytes(B, S, Hq, Hkv, D);
+  // layout: the activations q [T][Hq*D], k, v [T][Hkv*D], g, o [T][Hq*D]; (FP8) the E4M3 codes of h, o, W_q, W_k,
+  // W_v, W_g and W_o; then the attention's workspace, which takes the rest (with a cache at pos0 > 0 the attention
+  // stages the earlier positions too, so it needs more than without)
+  const uint64_t act = layer_activation_bytes(B, S, Hq, Hkv, D);
+  const uint64_t codes = f8 ? fp8_layer_workspace_bytes(B, S, d_model, Hq, Hkv, D) - layer_workspace_bytes(B, S, Hq, Hkv, D) : 0;
+  const uint64_t attn_need = prefill_workspace_bytes_at(B, S, Hkv, D, cache ? pos0 : 0, gated ? window : 0);
+  const uint64_t need = act + codes + attn_need;
   if (ws_bytes < need)
     return fail(ZG_ERANGE, "%s: workspace of %llu bytes < %llu needed", fn, (unsigned long long)ws_bytes,
                 (unsigned long long)need);
-  // carve the activations: q [T][Hq*D], k, v [T][Hkv*D], g, o [T][Hq*D], then the attention workspace, then
-  // (FP8) the E4M3 codes of h, o, W_q, W_k, W_v, W_g and W_o
   const int64_t T = (int64_t)B * S;
   uint16_t* q = static_cast<uint16_t*>(ws);
   uint16_t* k = q + T * Hq * D;
   uint16_t* v = k + T * Hkv * D;
   uint16_t* g = v + T * Hkv * D;
   uint16_t* o = g + T * Hq * D;
-  const uint64_t act = layer_activation_bytes(B, S, Hq, Hkv, D);
-  void* aws = static_cast<unsigned char*>(ws) + act;
-  const uint64_t aws_bytes = layer_workspace_bytes(B, S, Hq, Hkv, D) - act;
+  void* aws = static_cast<unsigned char*>(ws) + act + codes;
+  const uint64_t aws_bytes = ws_bytes - act - codes;
   // the attention's arguments first, so a bad one enqueues nothing
   int rc = prefill_common(gated, q, k, v, gated ? g : nullptr, qw, kw, o, B, S, Hq, Hkv, D, window, R, base, eps, pos0,
                           cache, layer, aws, aws_bytes, stream, /*validate_only=*/true);
@@ -818,7 +772,7 @@ int layer_common(bool gated, const void* h, const void* w_q, const void* w_k, co
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t dm = d_model, qd = (int64_t)Hq * D, kd = (int64_t)Hkv * D;
-  uint8_t* hc = static_cast<uint8_t*>(ws) + layer_workspace_bytes(B, S, Hq, Hkv, D);
+  uint8_t* hc = static_cast<uint8_t*>(ws) + act;
   uint8_t* oc = hc + align256(T * dm);
   uint8_t* wc[kF8LayerTensors] = {};
   wc[kF8Wq] = oc + align256(T * qd);

@@ -28,6 +28,12 @@
  *     keeps no reference to them after the enqueued work completes.  The KV cache is library-owned.
  *   - Calls that share a KV cache or a workspace must be ordered on one stream (or synchronised by
  *     the caller); the library does not lock.
+ *   - Value range.  Inside the prefill MFMAs, k_hat and v are held in fp16 (exact for bf16 values of magnitude
+ *     2^-14 .. 65504): a value beyond +-65504 is clamped to +-65504 (never infinite), so results are exact for
+ *     |v| <= 65504 and a larger value only changes the outputs of the queries that attend to it (as if it were
+ *     +-65504), never those of other queries.  |k_hat_d| <= sqrt(D) |w_k,d| by the RMSNorm, so keys stay in range
+ *     for |w_k| <= 5790; q_hat * log2(e)/sqrt(D) for |w_q| <= 45000.  Decode and the backward read v in bf16 and
+ *     are exact over bf16's whole range.  NaN inputs are outside the contract.
  */
 #ifndef ZGATTN_H
 #define ZGATTN_H
@@ -98,10 +104,13 @@ int kv_cache_length(const zg_kv_cache* cache, int32_t layer, int32_t b, int64_t*
  * for a global layer, len > max_tokens. */
 int kv_cache_set_length(zg_kv_cache* cache, int32_t layer, int32_t b, int64_t len);
 
-/* Device workspace bytes that swa_prefill / global_prefill need for a chunk of S tokens:
- * 2 * B*Hkv*S_pad*D 16-bit elements, S_pad = S rounded up to a multiple of 64 (the chunk's normalised, rotated
- * keys and, for a global layer without a cache, its transposed values, staged as fp16 for the MFMAs in whole
- * 64-key tiles). */
+/* Device workspace bytes that swa_prefill / global_prefill need for a chunk of S tokens at absolute positions
+ * pos0 .. pos0+S-1 (pos0 > 0 only with a cache).  The call stages the keys its queries see, positions kbase ..
+ * pos0+S-1 (kbase = 0 for a global layer, max(0, pos0 - window + 1) for a gated one: window 0 means global), as
+ * fp16 k_hat and transposed v in whole 64-key tiles: 2 * B*Hkv*K_pad*D 16-bit elements, K_pad = pos0+S-kbase
+ * rounded up to a multiple of 64.  0 when S == 0 or an argument is negative. */
+uint64_t prefill_workspace_bytes_at(int32_t B, int32_t S, int32_t Hkv, int32_t D, int64_t pos0, int32_t window);
+/* The same for a call without a cache (pos0 = 0): prefill_workspace_bytes_at(B, S, Hkv, D, 0, 0). */
 uint64_t prefill_workspace_bytes(int32_t B, int32_t S, int32_t Hkv, int32_t D);
 
 /* Gated sliding-window attention layer, prefill of S new tokens per sequence at absolute positions
@@ -112,7 +121,9 @@ uint64_t prefill_workspace_bytes(int32_t B, int32_t S, int32_t Hkv, int32_t D);
  *   cache (nullable): with a cache, keys at positions pos0-W+1 .. pos0-1 are read from layer `layer`'s
  *     ring, whose length must equal pos0, and the chunk's last min(S, W) positions are written into
  *     the ring (length becomes pos0+S).  Without a cache pos0 must be 0.
- *   workspace: device buffer of at least prefill_workspace_bytes(B, S, Hkv, D) bytes, 16-byte aligned.
+ *   workspace: device buffer of at least prefill_workspace_bytes_at(B, S, Hkv, D, pos0 (0 without a cache), window)
+ *     bytes, 16-byte aligned (the streaming kernel of the common case, GQA group 4, W <= 128 and no cache, does not
+ *     touch it).
  * S == 0 or B == 0 is a no-op.  Errors: EINVAL, EUNSUPPORTED, ERANGE, EHIP. */
 int swa_prefill(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
                 const void* k_norm_w, void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
@@ -123,14 +134,19 @@ int swa_prefill(const void* q, const void* k, const void* v, const void* gate, c
  * whole context without the gate).  Arguments as swa_prefill without gate and window.
  *   cache (nullable): with a cache, layer `layer` must be a global layer of the cache whose length
  *     equals pos0 (positions 0..pos0-1 are read from it: chunked prefill), pos0+S <= max_tokens, and the
- *     chunk's k_hat and v are written at rows pos0 .. pos0+S-1 first.  Without a cache pos0 must be 0.
- *   workspace: as swa_prefill (unused, may be NULL, when a cache is given). */
+ *     chunk's k_hat and v are written at rows pos0 .. pos0+S-1.  Without a cache pos0 must be 0.
+ *   workspace: at least prefill_workspace_bytes_at(B, S, Hkv, D, pos0 (0 without a cache), 0) bytes: with a cache
+ *     every earlier position is staged, so the workspace grows with the context (1 GiB at 262,144 positions for
+ *     B = 1, Hkv = 8). */
 int global_prefill(const void* q, const void* k, const void* v, const void* q_norm_w, const void* k_norm_w,
                    void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t rotary_dims,
                    double rope_base, float eps, int64_t pos0, zg_kv_cache* cache, int32_t layer,
                    void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* One decode step of every layer of the cache: each sequence b adds one token at absolute position
+/* One decode step of every layer of the cache (onedev.kr "How it works": the 5:1 hybrid of gated-SWA and global
+ * layers; jaehun.me "Why the KV Cache Shrinks by 6.4x": an SWA layer keeps only the last W keys, a global layer
+ * every key, so decoding reads a W-slot ring per SWA layer and the whole cache per global layer).
+ * Each sequence b adds one token at absolute position
  * positions[b] (HOST array [B]; must equal the cache length of every layer for that sequence).
  *   q, gate, out: [L][B][Hq][D]; k, v: [L][B][Hkv][D]; q_norm_w, k_norm_w: [L][D]   (device bf16)
  *   with L = the cache's n_layers, B = its batch.  gate rows of global layers are ignored.
@@ -219,8 +235,11 @@ uint64_t fp8_linear_workspace_bytes(int64_t T, int32_t K, int32_t N);
 int linear_fp8_delayed(const void* x, const void* w, void* y, int64_t T, int32_t K, int32_t N, zg_fp8_linear* state,
                        void* workspace, uint64_t workspace_bytes, void* stream);
 
-/* Workspace bytes for gated_swa_layer / global_layer on B x S tokens: the bf16 activations q, g, o [T][Hq*D] and
- * k, v [T][Hkv*D] (T = B*S), 256-byte aligned, followed by prefill_workspace_bytes(B, S, Hkv, D). */
+/* Workspace bytes for gated_swa_layer / global_layer on B x S tokens without a cache: the bf16 activations q, g, o
+ * [T][Hq*D] and k, v [T][Hkv*D] (T = B*S), 256-byte aligned, followed by the attention's workspace, which takes the
+ * rest of the buffer: prefill_workspace_bytes(B, S, Hkv, D) here; with a cache at pos0 > 0, pass
+ * layer_workspace_bytes - prefill_workspace_bytes(B, S, Hkv, D) + prefill_workspace_bytes_at(B, S, Hkv, D, pos0,
+ * window) bytes (window 0 for a global layer). */
 uint64_t layer_workspace_bytes(int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D);
 
 /* A gated-SWA attention layer from the hidden state: q = h W_q^T, k = h W_k^T, v = h W_v^T, g = h W_g^T, then
@@ -257,8 +276,9 @@ int fp8_layer_alloc(int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D, int32_t
 int fp8_layer_free(zg_fp8_layer* state);
 /* The seven scales the next call will use (HOST float[7], tensor order above); synchronises the device. */
 int fp8_layer_scales(const zg_fp8_layer* state, float* scales_out);
-/* Workspace bytes of the FP8 layers: layer_workspace_bytes(B, S, Hq, Hkv, D), then the E4M3 codes of h [T][d_model],
- * o [T][Hq*D], W_q, W_k, W_v, W_g and W_o, each starting on a 256-byte boundary. */
+/* Workspace bytes of the FP8 layers without a cache: the activations of layer_workspace_bytes, then the E4M3 codes of
+ * h [T][d_model], o [T][Hq*D], W_q, W_k, W_v, W_g and W_o, each starting on a 256-byte boundary, then the attention's
+ * workspace, the rest of the buffer (with a cache, sized as for gated_swa_layer / global_layer). */
 uint64_t fp8_layer_workspace_bytes(int32_t B, int32_t S, int32_t d_model, int32_t Hq, int32_t Hkv, int32_t D);
 /* gated_swa_layer / global_layer with every projection on E4M3 operands under the layer state `fp8` (shapes must
  * match the state's).  Calls that share a state must be ordered on one stream.  B*S == 0 is a no-op (the state

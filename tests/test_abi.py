@@ -51,6 +51,19 @@ def test_workspace_bytes(zg):
     # whole 64-key tiles
     assert zg.workspace_bytes(2, 100, 8) == 2 * 2 * 128 * 8 * 128 * 2
     assert zg.workspace_bytes(1, 1, 1) == 2 * 64 * 128 * 2
+    assert zg.workspace_bytes(1, 0, 8) == 0
+
+
+def test_workspace_bytes_with_a_cache(zg):
+    """A chunk at pos0 stages the keys its queries see: every earlier position for a global layer (window 0), the
+    W - 1 before pos0 for a gated one, in whole 64-key tiles."""
+    per_key = 2 * 8 * 128 * 2            # k_hat and v^T, fp16, 8 KV heads
+    assert zg.workspace_bytes(1, 16384, 8, pos0=245760) == 262144 * per_key
+    assert zg.workspace_bytes(1, 100, 8, pos0=1000) == 1152 * per_key              # 1100 keys -> 18 tiles
+    assert zg.workspace_bytes(1, 100, 8, pos0=1000, window=128) == 256 * per_key    # 227 keys -> 4 tiles
+    assert zg.workspace_bytes(1, 100, 8, pos0=50, window=128) == 192 * per_key      # keys 0..149
+    assert zg.workspace_bytes(2, 100, 8, pos0=0, window=128) == 2 * zg.workspace_bytes(1, 100, 8)
+    assert zg._lib.prefill_workspace_bytes_at(1, 10, 8, 128, -1, 0) == 0
 
 
 def _swa(zg, **over):

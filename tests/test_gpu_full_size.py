@@ -228,7 +228,9 @@ def test_chunked_prefill_262144_in_16384_chunks(zg):
     bounds = [c * C + d for c in range(1, S_total // C) for d in (-128, -127, -1, 0, 1, 127)]
     pos = sample_positions(S_total, rng, 16, extra=bounds)
     checked = {1: {}, 6: {}, 32: {}}
-    ws = torch.empty(zg.workspace_bytes(1, C, Hkv, D), dtype=torch.uint8, device="cuda")
+    # the largest workspaces a chunk needs: a gated chunk stages W-1 earlier keys, the last global chunk every key
+    ws = torch.empty(zg.workspace_bytes(1, C, Hkv, D, pos0=C, window=W), dtype=torch.uint8, device="cuda")
+    gws = torch.empty(zg.workspace_bytes(1, C, Hkv, D, pos0=S_total - C), dtype=torch.uint8, device="cuda")
     for layer in range(1, L + 1):
         gated = layer not in GLOBAL_LAYERS
         for c in range(S_total // C):
@@ -238,7 +240,7 @@ def test_chunked_prefill_262144_in_16384_chunks(zg):
                                      rope_base=base, eps=1e-6, pos0=c * C, cache=cache, layer=layer, workspace=ws)
             else:
                 out = zg.global_prefill(t["q"], t["k"], t["v"], t["wq"], t["wk"], rotary_dims=R, rope_base=base,
-                                        eps=1e-6, pos0=c * C, cache=cache, layer=layer)
+                                        eps=1e-6, pos0=c * C, cache=cache, layer=layer, workspace=gws)
             if layer in checked:
                 rows = [p - c * C for p in pos if c * C <= p < (c + 1) * C]
                 if rows:

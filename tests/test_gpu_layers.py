@@ -102,11 +102,11 @@ def _e4m3_step(a):
 
 
 def _fp8_layer_codes(ws, B, S, gated):
-    """The E4M3 codes the layer leaves in its workspace (layout of fp8_layer_workspace_bytes)."""
+    """The E4M3 codes the layer leaves in its workspace (after the activations; the attention's part is last)."""
     import global_attention_gated_amd as zgm
     a = lambda n: (n + 255) // 256 * 256
     T, qd, kd = B * S, HQ * D, HKV * D
-    off = zgm.layer_workspace_bytes(B, S, HQ, HKV, D)
+    off = zgm.layer_workspace_bytes(B, S, HQ, HKV, D) - zgm.workspace_bytes(B, S, HKV, D)   # right after the activations
     mem = ws.cpu().numpy()
     out = {}
     for name, n, shape in (("h", T * D_MODEL, (T, D_MODEL)), ("o", T * qd, (T, qd)), ("w_q", qd * D_MODEL, (qd, D_MODEL)),

@@ -116,6 +116,9 @@ def test_prefill_running_max_jumps(zg, gated):
 
 
 def test_gate_infinities(zg):
+    """sigma(+inf) = 1 exactly: a gated layer whose window covers the whole context is the global layer, bit for bit
+    (both run on the tile kernel: same staging, same tiles, same masks; the gated epilogue multiplies by exactly 1);
+    sigma(-inf) = 0 exactly (jaehun.me, "How Gated SWA Behaves": global layers skip the gate)."""
     import torch
     L = Layer(77, 1, 1, 300, 8, 2)
     plus = torch.full_like(L.dgate, float("inf"))
@@ -123,14 +126,47 @@ def test_gate_infinities(zg):
     o_plus = zg.swa_prefill(L.dq, L.dk, L.dv, plus, L.dwq, L.dwk, window=1 << 20, rotary_dims=42, rope_base=1e4, eps=1e-6)
     o_glob = zg.global_prefill(L.dq, L.dk, L.dv, L.dwq, L.dwk, rotary_dims=42, rope_base=1e4, eps=1e-6)
     o_minus = zg.swa_prefill(L.dq, L.dk, L.dv, minus, L.dwq, L.dwk, window=128, rotary_dims=42, rope_base=1e4, eps=1e-6)
-    # sigma(+inf) = 1 exactly: the gated layer with a window covering the sequence is the global layer.  The
-    # two kernels round the softmax differently (the global one folds -m into the score accumulators), so
-    # both are held to the oracle's global layer and to each other at the parity bar.
     ref = oracle_prefill(L, False, None, 42, 1e4, 1e-6)
-    compare(to_host_f64(o_plus), ref, "swa, gate +inf, window >= S")
     compare(to_host_f64(o_glob), ref, "global")
-    compare(to_host_f64(o_plus), to_host_f64(o_glob), "swa with gate +inf against global")
+    np.testing.assert_array_equal(to_host_bits(o_plus), to_host_bits(o_glob))
     assert np.all(to_host_f64(o_minus) == 0.0)
+
+
+def test_gate_plus_infinity_with_a_cache_is_the_global_layer_bit_for_bit(zg):
+    """The same invariant on chunks against a KV cache: a 2-layer cache (layer 1 gated with a window longer than the
+    sequence, layer 2 global), chunks of 70, 1 and 129 positions; with gate = +inf every chunk's output of layer 1
+    equals layer 2's bit for bit, and both match the oracle's global layer."""
+    import torch
+    B, Hq, Hkv, R, base, eps, S_total = 2, 8, 2, 42, 1e7, 1e-6, 200
+    W = 4096
+    cache = zg.KVCache(n_layers=2, global_layers=[2], batch=B, n_kv_heads=Hkv, window=W, max_tokens=256)
+    pos0 = 0
+    for S in (70, 1, 129):
+        L = Layer(41, 0, B, S, Hq, Hkv, gated=True, pos0=pos0, S_total=S_total)
+        full = Layer(41, 0, B, pos0 + S, Hq, Hkv, gated=False, S_total=S_total, device=None)
+        plus = torch.full_like(L.dgate, float("inf"))
+        o_g = zg.swa_prefill(L.dq, L.dk, L.dv, plus, L.dwq, L.dwk, window=W, rotary_dims=R, rope_base=base, eps=eps,
+                             pos0=pos0, cache=cache, layer=1)
+        o_c = zg.global_prefill(L.dq, L.dk, L.dv, L.dwq, L.dwk, rotary_dims=R, rope_base=base, eps=eps, pos0=pos0,
+                                cache=cache, layer=2)
+        np.testing.assert_array_equal(to_host_bits(o_g), to_host_bits(o_c))
+        ref = oracle_prefill(full, False, None, R, base, eps)[:, pos0:]
+        compare(to_host_f64(o_c), ref, f"global chunk at {pos0}")
+        pos0 += S
+    cache.close()
+
+
+def test_cached_first_chunk_is_the_cacheless_layer_bit_for_bit(zg):
+    """A chunk at position 0 against an empty cache runs the same staging and tile kernel as a call without a cache,
+    so the outputs agree bit for bit (global layer, and a gated layer the tile kernel takes: window above 128)."""
+    B, Hq, Hkv, S, R = 1, 16, 2, 333, 42
+    cache = zg.KVCache(n_layers=2, global_layers=[2], batch=B, n_kv_heads=Hkv, window=200, max_tokens=512)
+    for layer, gated in ((1, True), (2, False)):
+        L = Layer(12, layer, B, S, Hq, Hkv, gated=gated)
+        a = gpu_prefill(zg, L, gated, 200, R, 1e4, 1e-6)
+        c = gpu_prefill(zg, L, gated, 200, R, 1e4, 1e-6, pos0=0, cache=cache, layer=layer)
+        np.testing.assert_array_equal(to_host_bits(a), to_host_bits(c))
+    cache.close()
 
 
 def test_empty_inputs_are_noops(zg):
@@ -242,4 +278,81 @@ def test_decode_from_empty_cache_equals_prefill(zg):
                                                 rotary_dims=R, rope_base=base, eps=eps))
         for li in range(Lh):
             compare(got[li], refs[li][:, t], f"decode t={t} layer {li + 1}")
+    cache.close()
+
+
+# ------------------------------------------------------------------------------------------ value range
+@pytest.mark.parametrize("gated", [True, False])
+def test_values_beyond_fp16_range_stay_finite_and_causal(zg, gated):
+    """k_hat and v enter the prefill MFMAs as fp16 (include/zgattn.h, "Value range"): a value beyond +-65504
+    saturates.  One key at position j carries |v| = 1e5 (and -2e5): the queries before j (which must not see it,
+    also those sharing its 32- and 64-key tiles) match the oracle exactly as without it, and the queries that see it
+    match the oracle with that value clamped to +-65504.  Streaming kernel (gated) and tile kernel (global)."""
+    B, S, Hq, Hkv, W = 1, 700, 4, 1, 128
+    L = Layer(808, 4, B, S, Hq, Hkv, gated=gated)
+    j = 333                                   # inside a 64-key tile and a 32-key ring tile, not at their start
+    v = synth.bf16_bits_to_f64(L.v).copy()
+    v[0, j, 0, :64] = 1.0e5
+    v[0, j, 0, 64:] = -2.0e5
+    L.v = synth.f64_to_bf16_bits(v)
+    L.dv = to_dev(L.v)
+    got = to_host_f64(gpu_prefill(zg, L, gated, W, 42, 1e4, 1e-6))
+    assert np.all(np.isfinite(got))
+    clamped = Layer(808, 4, B, S, Hq, Hkv, gated=gated, device=None)
+    clamped.v = synth.f64_to_bf16_bits(np.clip(v, -65504.0, 65504.0))
+    ref = oracle_prefill(clamped, gated, W, 42, 1e4, 1e-6)
+    compare(got[:, :j], ref[:, :j], "queries before the out-of-range key")
+    see = slice(j, min(S, j + W)) if gated else slice(j, S)
+    # the clamped value is exact in bf16 and fp16; errors scale with |v| ~ 6.5e4 where the output is dominated by it
+    err = np.abs(got[:, see] - ref[:, see]) / np.maximum(1.0, np.abs(ref[:, see]))
+    assert err.max() < 1e-2, err.max()
+    if gated:
+        compare(got[:, j + W:], ref[:, j + W:], "queries past the window of the out-of-range key")
+
+
+# ------------------------------------------------------------------------------------------ error paths
+def test_cache_beyond_device_memory_is_enomem(zg):
+    """kv_cache_alloc of more than the GPU holds: ENOMEM, nothing allocated, and the device stays usable."""
+    import torch
+    with pytest.raises(zg.ZgError) as e:
+        zg.KVCache(n_layers=32, global_layers=[6, 12, 18, 24, 30], batch=64, n_kv_heads=8, max_tokens=1 << 22)
+    assert e.value.status == zg.ZG_ENOMEM
+    x = torch.ones(4, device="cuda")
+    assert float(x.sum()) == 4.0
+
+
+def test_decode_positions_out_of_range_are_erange(zg):
+    """hybrid_decode_step refuses a position that differs from the cache length, or that reaches the capacity, with
+    ERANGE before anything is enqueued (the cache lengths stay as they were)."""
+    L, B, Hq, Hkv = 2, 2, 8, 2
+    cache = zg.KVCache(n_layers=L, global_layers=[2], batch=B, n_kv_heads=Hkv, window=16, max_tokens=8)
+    q, k, v, g = _decode_inputs(3, L, B, Hq, Hkv, 0)
+    w = np.stack([synth.norm_weight_bf16(3, l, synth.TENSOR_WQ, 128) for l in range(L)])
+    args = (to_dev(q), to_dev(k), to_dev(v), to_dev(g), to_dev(w), to_dev(w))
+    for positions in ([1, 0], [0, 5], [-1, 0]):           # the caches hold 0 positions
+        with pytest.raises(zg.ZgError) as e:
+            zg.hybrid_decode_step(*args, positions, cache)
+        assert e.value.status == zg.ZG_ERANGE
+    for l in (1, 2):
+        for b in range(B):
+            cache.set_length(l, b, 8)
+    with pytest.raises(zg.ZgError) as e:                  # position 8 = max_tokens: no row left in the global cache
+        zg.hybrid_decode_step(*args, [8, 8], cache)
+    assert e.value.status == zg.ZG_ERANGE and b"capacity" in zg._lib.zg_last_error()
+    assert all(cache.length(l, b) == 8 for l in (1, 2) for b in range(B))
+    cache.close()
+
+
+def test_prefill_workspace_too_small_for_the_cached_context_is_erange(zg):
+    """A global chunk at pos0 stages every earlier key: a workspace sized for the chunk alone is refused."""
+    import torch
+    B, Hq, Hkv, S = 1, 4, 1, 64
+    cache = zg.KVCache(n_layers=1, global_layers=[1], batch=B, n_kv_heads=Hkv, max_tokens=256)
+    L0 = Layer(5, 0, B, S, Hq, Hkv, gated=False)
+    gpu_prefill(zg, L0, False, None, 42, 1e4, 1e-6, cache=cache, layer=1)
+    small = torch.empty(zg.workspace_bytes(B, S, Hkv), dtype=torch.uint8, device="cuda")
+    with pytest.raises(zg.ZgError) as e:
+        gpu_prefill(zg, L0, False, None, 42, 1e4, 1e-6, pos0=S, cache=cache, layer=1, workspace=small)
+    assert e.value.status == zg.ZG_ERANGE
+    assert cache.length(1, 0) == S
     cache.close()
