@@ -55,6 +55,8 @@ _lib.prefill_workspace_bytes_at.argtypes = [_i32, _i32, _i32, _i32, _i64, _i32]
 _lib.prefill_workspace_bytes_at.restype = _u64
 _lib.swa_prefill.argtypes = [_vp] * 7 + [_i32] * 7 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
 _lib.global_prefill.argtypes = [_vp] * 6 + [_i32] * 6 + [_f64, _f32, _i64, _vp, _i32, _vp, _u64, _vp]
+_lib.global_prefill_noalloc.argtypes = [_vp] * 6 + [_i32] * 6 + [_f64, _f32, _i64, _vp, _i32, _vp]
+_lib.global_prefill_noalloc_max_bytes.restype = _u64
 _lib.hybrid_decode_step.argtypes = [_vp] * 7 + [ctypes.POINTER(_i64), _i32, _i32, _f64, _f32, _vp, _vp]
 _lib.linear_bf16.argtypes = [_vp, _vp, _vp, _i64, _i32, _i32, _vp]
 _lib.layer_workspace_bytes.argtypes = [_i32] * 5
@@ -87,7 +89,8 @@ _lib.zg_kernel_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_f64), cty
 _lib.zg_kernel_timer_only.argtypes = [ctypes.c_char_p]
 
 EXPORTED = ["kv_cache_alloc", "kv_cache_free", "kv_cache_footprint_bytes", "kv_cache_layer_view", "kv_cache_length",
-            "kv_cache_set_length", "prefill_workspace_bytes", "prefill_workspace_bytes_at", "swa_prefill", "global_prefill", "hybrid_decode_step",
+            "kv_cache_set_length", "prefill_workspace_bytes", "prefill_workspace_bytes_at", "swa_prefill", "global_prefill", "global_prefill_noalloc",
+            "global_prefill_noalloc_max_bytes", "hybrid_decode_step",
             "linear_bf16", "layer_workspace_bytes", "gated_swa_layer", "global_layer", "fp8_linear_alloc",
             "fp8_linear_free", "fp8_linear_scales", "fp8_linear_workspace_bytes", "linear_fp8_delayed",
             "fp8_layer_alloc", "fp8_layer_free", "fp8_layer_scales", "fp8_layer_workspace_bytes", "gated_swa_layer_fp8",
@@ -274,6 +277,22 @@ def global_prefill(q, k, v, q_norm_w, k_norm_w, out=None, *, rotary_dims=42, rop
     """Ungated global causal layer: q [B,S,Hq,D], k/v [B,S,Hkv,D], weights [D] (bf16); returns out."""
     return _prefill(False, q, k, v, None, q_norm_w, k_norm_w, out, 0, rotary_dims, rope_base, eps, pos0, cache,
                     layer, workspace)
+
+
+def global_prefill_noalloc(q, k, v, q_norm_w, k_norm_w, out, *, rotary_dims=42, rope_base=1e4, eps=1e-6, pos0=0,
+                           cache: KVCache | None = None, layer=0):
+    """global_prefill staging its keys in the library's per-GPU scratch array (no workspace, no allocation): out must
+    be given.  At most global_prefill_noalloc_max_bytes() of staged keys."""
+    fn = "global_prefill_noalloc"
+    if out is None:
+        raise ValueError(f"{fn}: out is required (the call allocates nothing)")
+    B, S, Hq, Hkv, D = _qkv_shapes(fn, q, k, v, None, q_norm_w, k_norm_w, out)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"), (out, "out")):
+        _bf16(t, n)
+    ch = None if cache is None else cache.handle
+    _check(_lib.global_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), B, S, Hq,
+                                       Hkv, D, rotary_dims, rope_base, eps, pos0, ch, layer, _stream()))
+    return out
 
 
 # ------------------------------------------------------------------------------------------- training

@@ -475,6 +475,59 @@ extern "C" int global_prefill(const void* q, const void* k, const void* v, const
                         eps, pos0, cache, layer, workspace, workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------------- allocation-free global prefill
+// The staging workspace of global_prefill_noalloc: one array per GPU, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: kernels get the device address that hipGetSymbolAddress
+// returns for the current device (kept in g_scratch_dev), never the array's name.
+namespace {
+constexpr uint64_t kScratchBytes = 64ull << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The device address of this device's scratch array (looked up once per device, with that device current).
+int scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(ZG_EUNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(ZG_EHIP, "%s: hipGetSymbolAddress of the scratch array: %s", fn, hipGetErrorString(e));
+    }
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return ZG_OK;
+}
+}  // namespace
+
+extern "C" uint64_t global_prefill_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int global_prefill_noalloc(const void* q, const void* k, const void* v, const void* q_norm_w,
+                                      const void* k_norm_w, void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv,
+                                      int32_t D, int32_t rotary_dims, double rope_base, float eps, int64_t pos0,
+                                      zg_kv_cache* cache, int32_t layer, void* stream) {
+  const char* fn = "global_prefill_noalloc";
+  if (B < 0 || S < 0 || Hkv < 0 || D < 0 || pos0 < 0) return fail(ZG_EINVAL, "%s: negative size or position", fn);
+  const uint64_t need = prefill_workspace_bytes_at(B, S, Hkv, D, cache ? pos0 : 0, 0);
+  if (need > kScratchBytes)
+    return fail(ZG_ERANGE, "%s: the call stages %llu bytes of keys, more than the %llu-byte scratch array", fn,
+                (unsigned long long)need, (unsigned long long)kScratchBytes);
+  void* ws = nullptr;
+  if (B > 0 && S > 0) {
+    const int rc = scratch_address(fn, &ws);
+    if (rc) return rc;
+  }
+  return prefill_common(false, q, k, v, nullptr, q_norm_w, k_norm_w, out, B, S, Hq, Hkv, D, 0, rotary_dims, rope_base,
+                        eps, pos0, cache, layer, ws, kScratchBytes, stream, false, nullptr, fn);
+}
+
 // ---------------------------------------------------------------------------------- training: forward + backward
 extern "C" int swa_prefill_train(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
                                  const void* k_norm_w, void* out, float* lse, int32_t B, int32_t S, int32_t Hq,

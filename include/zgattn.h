@@ -159,6 +159,18 @@ int hybrid_decode_step(const void* q, const void* k, const void* v, const void* 
                        const void* k_norm_w, void* out, const int64_t* positions, int32_t Hq,
                        int32_t rotary_dims, double rope_base, float eps, zg_kv_cache* cache, void* stream);
 
+/* ---- For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): global_prefill without a workspace argument.  The keys are staged in a scratch array that the library
+ * holds on each GPU it runs on (global_prefill_noalloc_max_bytes() = 64 MiB per GPU, until the process ends; enough
+ * for 8 KV heads x 16,384 positions); the call allocates nothing.  A call whose staging needs more
+ * (prefill_workspace_bytes_at(B, S, Hkv, D, pos0, 0) above the maximum) returns ERANGE.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (different streams, or other threads) race: order them
+ * on one stream.  Arguments and other errors as global_prefill. */
+uint64_t global_prefill_noalloc_max_bytes(void);
+int global_prefill_noalloc(const void* q, const void* k, const void* v, const void* q_norm_w, const void* k_norm_w,
+                           void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t rotary_dims,
+                           double rope_base, float eps, int64_t pos0, zg_kv_cache* cache, int32_t layer, void* stream);
+
 /* ---- Training: forward with log-sum-exp, and the backward of an attention layer (no cache, positions 0..S-1).
  * The forward is swa_prefill / global_prefill that also writes, per (sequence, query head, position), the natural
  * log of its softmax denominator: lse_i = log sum_j exp(s_ij), s_ij = q_hat_i . k_hat_j / sqrt(D) over the visible
