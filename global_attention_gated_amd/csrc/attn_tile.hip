@@ -23,6 +23,8 @@
 //
 // Precision: k_hat and v are bf16 values held exactly in fp16 (saturating at +-65504), q_hat and P are rounded
 // once to fp16, the MFMAs accumulate in fp32, and the online softmax runs in fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -421,6 +423,366 @@ __global__ void __launch_bounds__(256) ring_write_kernel(RingWriteArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------ ping-pong
+// The same attention with 8 waves per work-group in two groups of 4 (one wave of each group per SIMD), 256 query
+// rows = G heads x 2P positions, whose phases alternate: while one group runs its MFMA phase M(m) (P V^T of tile m-1,
+// then S^T = K Q^T of tile m) the other runs its softmax phase V (max, exponentials, row sums of its last scores) on
+// the VALU, so a SIMD's matrix unit is fed by one wave while the other wave's vector work runs beside it.  Every phase
+// ends with one work-group barrier; group 1 runs one phase behind group 0, and each group's straight-line sequence
+// meets the same 2n + 2 barriers (n tiles).
+//
+// LDS: keys and transposed values in separate double buffers (K[2], V^T[2], 16 KB each).  At phase 2m every wave
+// issues its eighth of K(m+1) and of V(m) (their buffers' previous tiles, K(m-1) and V(m-2), were last read in phase
+// 2m-1) and waits for them at the end of phase 2m+1; M(m) reads K(m) and V(m-1).  The loop runs two tiles per pass,
+// so every buffer is a compile-time constant and each operand fragment's LDS address is one of 12 per-lane registers
+// plus an immediate offset.  Fragments stream through an 8-deep window of registers ahead of their MFMAs.
+constexpr int kPPRows = 256;
+constexpr int kPPSmemBytes = kPPRows * kOsStride * 4;   // 135,168 B: the epilogue staging; the tiles use 64 KB of it
+static_assert(4 * kTileHalves * 2 <= kPPSmemBytes, "tile buffers exceed the LDS block");
+
+template <bool GATED>
+__global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kPPSmemBytes / 2];
+  // K buffer j at smem + j * kTileHalves, V^T buffer j at smem + (2 + j) * kTileHalves
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  const int unit = blockIdx.x % a.n_units;
+  const int qt = a.n_qtiles - 1 - (int)(blockIdx.x / a.n_units);
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int P2 = 2 * a.P;                         // positions per work-group
+  const int i0 = qt * P2;
+
+  const int r = wave * 32 + l32;
+  const int hq = kvh * a.G + r / P2;
+  const int i = i0 + r % P2;
+  const bool qvalid = i < a.S;
+  const int ic = qvalid ? i : a.S - 1;
+  const int qpos = a.pos0 + ic;
+
+  int pl_lo, pl_hi;
+  if (P2 >= 32) { pl_lo = (wave * 32) % P2; pl_hi = pl_lo + 31; } else { pl_lo = 0; pl_hi = P2 - 1; }
+  const int wlo = a.pos0 + min(i0 + pl_lo, a.S - 1);
+  const int whi = a.pos0 + min(i0 + pl_hi, a.S - 1);
+  const int khi = a.pos0 + min(i0 + P2, a.S);
+  const int klo = GATED ? max(a.kbase, a.pos0 + i0 - a.window + 1) : a.kbase;
+  const int t_lo = (klo - a.kbase) / kBN;
+  const int n_tiles = (khi - a.kbase + kBN - 1) / kBN - t_lo;
+  const unsigned lim = GATED ? (unsigned)a.window : 0x7fffffffu;
+
+  // ---- Q prologue (as attn_tile_kernel)
+  half8 qf[8];
+  {
+    const uint16_t* qrow = a.q + (((int64_t)b * a.S + ic) * a.Hq + hq) * kHeadDim;
+    float f[8][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      unpack8(*reinterpret_cast<const uint4*>(qrow + 16 * t + 8 * hi), f[t]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) ss += f[t][e] * f[t][e];
+    }
+    ss = xor32_sum(ss);
+    const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps);
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      float w[8];
+      unpack8(*reinterpret_cast<const uint4*>(a.qw + 16 * t + 8 * hi), w);
+#pragma unroll
+      for (int e = 0; e < 8; e++) f[t][e] = f[t][e] * inv * w[e];
+      rope8(f[t], 16 * t + 8 * hi, qpos, a.rot_pairs, a.inv_freq_rev);
+#pragma unroll
+      for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)(f[t][e] * a.q_scale);
+    }
+  }
+
+  floatx16 acc_o[4];
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) acc_o[db][j] = 0.f;
+  // running max (log2 units, kept negated in a whole accumulator block that starts each score chain) and sum
+  float m_run = 0.f, l_run = 0.f;
+  bool m_set = false;
+  floatx16 negm;
+#pragma unroll
+  for (int j = 0; j < 16; j++) negm[j] = 0.f;
+  floatx16 sacc[2];
+  half8 pf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) sacc[kb][j] = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; h2++) pf[kb][h2] = (half8){};
+
+  // ---- direct loads: wave w copies the 1 KB LDS blocks 2w, 2w+1 of a K tile (key rows 4j..4j+3 each) and of a V^T
+  // tile (dim rows 8j..8j+7 each), with the swizzles of attn_tile_kernel
+  const uint32_t plane_bytes = (uint32_t)a.S_kpad * kHeadDim * 2;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.kt + (int64_t)unit * a.S_kpad * kHeadDim), (short)0, (int)plane_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.vt + (int64_t)unit * kHeadDim * a.S_kpad), (short)0, (int)plane_bytes, 0x00020000);
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int jj = 0; jj < 2; jj++) {
+    const int j = 2 * wave + jj;
+    const int kr = 4 * j + (lane >> 4);
+    koff[jj] = (uint32_t)kr * (kHeadDim * 2) + 16u * (uint32_t)((lane & 15) ^ (kr & 15));
+    const int vr = 8 * j + (lane >> 3);
+    voff[jj] = (uint32_t)vr * (uint32_t)a.S_kpad * 2u + 16u * (uint32_t)((lane & 7) ^ ((vr >> 1) & 7));
+  }
+  auto issue_k = [&](int n, int buf) {   // K of tile t_lo + n into K buffer buf
+    uint16_t* dst = smem + buf * kTileHalves;
+    const uint32_t ks = (uint32_t)(t_lo + n) * kBN * kHeadDim * 2;
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + (2 * wave + jj) * 512), 16, (int)koff[jj],
+                                               (int)ks, 0, 0);
+  };
+  auto issue_v = [&](int n, int buf) {   // V^T of tile t_lo + n into V buffer buf
+    uint16_t* dst = smem + (2 + buf) * kTileHalves;
+    const uint32_t vs = (uint32_t)(t_lo + n) * kBN * 2;
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + (2 * wave + jj) * 512), 16, (int)voff[jj],
+                                               (int)vs, 0, 0);
+  };
+
+  // operand fragment addresses within a tile: V^T row 32db + l32, chunk 4kb + 2h2 + hi (fp16 elements, per lane);
+  // K row 32hf + l32, chunk 2t8 + hi at chunk position (2t8 + hi) ^ (l32 mod 16), whose byte offset
+  // l32 * 256 + 16 * ((2t8 + hi) ^ (l32 mod 16)) is kx ^ (32 t8) with kx the t8 = 0 offset (bits 5..7 hold t8 ^ ...)
+  int vfo[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) vfo[c] = l32 * kBN + 8 * ((2 * c + hi) ^ ((l32 >> 1) & 7));
+  const uint32_t kx = (uint32_t)l32 * (kHeadDim * 2) + 16u * (uint32_t)(hi ^ (l32 & 15));
+
+  auto live = [&](int n) {   // this wave's queries see a key of tile n (relative index)
+    const int kt = a.kbase + (t_lo + n) * kBN;
+    if (kt > whi) return false;
+    if (GATED && kt + kBN - 1 < wlo - a.window + 1) return false;
+    return true;
+  };
+
+  // MFMA phase: P V^T of the previous tile (V buffer VB), then S^T = K Q^T of this one (K buffer KB), both always
+  // (P is zero where the previous tile showed this wave nothing; scores past the last tile are never used)
+  auto mfma_phase = [&](auto KBc, auto VBc) {
+    constexpr int KB = decltype(KBc)::value, VB = decltype(VBc)::value;
+    auto frag = [&](int f) -> half8 {
+      if (f < 16) {
+        const int kb = f >> 3, h2 = (f >> 2) & 1, db = f & 3;
+        return *reinterpret_cast<const half8*>(smem + (2 + VB) * kTileHalves + db * 32 * kBN + vfo[2 * kb + h2]);
+      }
+      const int g = f - 16, t8 = g >> 1, hf = g & 1;
+      const uint32_t kb_bytes = kx ^ (32u * (uint32_t)t8);
+      return *reinterpret_cast<const half8*>(reinterpret_cast<const unsigned char*>(smem) +
+                                             (KB * kTileHalves + hf * 32 * kHeadDim) * 2 + kb_bytes);
+    };
+    half8 win[8];
+#pragma unroll
+    for (int f = 0; f < 8; f++) win[f] = frag(f);
+#pragma unroll
+    for (int f = 0; f < 32; f++) {
+      const half8 op = win[f & 7];
+      if (f + 8 < 32) win[(f + 8) & 7] = frag(f + 8);
+      if (f < 16) {
+        const int kb = f >> 3, h2 = (f >> 2) & 1, db = f & 3;
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op, pf[kb][h2], acc_o[db], 0, 0, 0);
+      } else {
+        const int g = f - 16, t8 = g >> 1, hf = g & 1;
+        sacc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op, qf[t8], t8 == 0 ? negm : sacc[hf], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // softmax phase of tile m: scores (relative to -m) -> P (fp16) and the row statistics
+  auto softmax_phase = [&](int m) {
+    if (m >= n_tiles || !live(m)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) pf[kb][h2] = (half8){};
+      return;
+    }
+    const int kt = a.kbase + (t_lo + m) * kBN;
+    if (kt + kBN - 1 > wlo || (GATED && kt < whi - a.window + 1)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int key = kt + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
+          if ((unsigned)(qpos - key) >= lim) sacc[kb][j] = -INFINITY;
+        }
+    }
+    float mx0 = sacc[0][0], mx1 = sacc[1][0];
+#pragma unroll
+    for (int j = 1; j < 15; j += 2) {
+      mx0 = fmaxf(fmaxf(mx0, sacc[0][j]), sacc[0][j + 1]);
+      mx1 = fmaxf(fmaxf(mx1, sacc[1][j]), sacc[1][j + 1]);
+    }
+    float mx = fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15]));
+    mx = xor32_max(mx);
+    const bool need = m_set ? mx > 8.0f : mx > -INFINITY;
+    if (__any(need)) {
+      const float sh = need ? mx : 0.0f;
+      const float alpha = m_set ? __builtin_amdgcn_exp2f(-sh) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) acc_o[db][j] *= alpha;
+      m_run += sh;
+      m_set = m_set || need;
+#pragma unroll
+      for (int j = 0; j < 16; j++) negm[j] = -m_run;
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int j = 0; j < 16; j++) sacc[kb][j] -= sh;
+    }
+    // P = exp2(s - m) rounded to fp16; the row sum adds the fp32 values (v_add, which runs beside the other wave's
+    // MFMAs, unlike v_dot2)
+    float ls[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; h2++) {
+        uint32_t wp[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int j = 8 * h2 + 2 * e;
+          const float e0 = __builtin_amdgcn_exp2f(sacc[kb][j]), e1 = __builtin_amdgcn_exp2f(sacc[kb][j + 1]);
+          wp[e] = pack_f16(e0, e1);
+          ls[e & 1] += e0 + e1;
+        }
+        pf[kb][h2] = __builtin_bit_cast(half8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
+      }
+    l_run += ls[0] + ls[1];
+  };
+
+  // ---- prologue: K(0) in LDS for everyone; V buffer 1, which M(0) multiplies by its zero P, is cleared (LDS starts
+  // with arbitrary bits, and 0 * inf would be NaN)
+  issue_k(0, 0);
+  {
+    uint4* v1 = reinterpret_cast<uint4*>(smem + 3 * kTileHalves);
+    v1[tid] = make_uint4(0u, 0u, 0u, 0u);
+    v1[tid + 512] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  const int n = n_tiles;
+  // a phase boundary: this wave's LDS reads are done (lgkmcnt 0), then the work-group barrier; the memory clobber
+  // keeps the compiler from moving LDS accesses across it, the scheduling barriers keep every instruction of a phase
+  // inside it.  (__syncthreads() would also wait for the tile loads in flight.)
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_tiles = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  };
+  // the loads of phase 2m: K(m+1) into K buffer (m+1) mod 2, V(m) into V buffer m mod 2
+  auto issue = [&](int m, auto PARc) {
+    constexpr int PAR = decltype(PARc)::value;   // m mod 2
+    if (m + 1 < n) issue_k(m + 1, PAR ^ 1);
+    if (m < n) issue_v(m, PAR);
+  };
+  // ---- phases.  Group 0 runs M(0) V(0) M(1) V(1) ... M(np), group 1 the same one phase later, np = n rounded up to
+  // even (an odd n gets one empty tile: no loads, zero P).  M(m) uses K buffer m mod 2 and V buffer (m-1) mod 2.  Each
+  // group meets 2 np + 2 barriers.
+  const int np = (n + 1) & ~1;
+  if (group == 0) {
+    for (int m = 0; m < np; m += 2) {
+      issue(m, C0{});
+      mfma_phase(C0{}, C1{});
+      barrier();
+      softmax_phase(m);
+      wait_tiles();
+      barrier();
+      issue(m + 1, C1{});
+      mfma_phase(C1{}, C0{});
+      barrier();
+      softmax_phase(m + 1);
+      wait_tiles();
+      barrier();
+    }
+    mfma_phase(C0{}, C1{});
+    barrier();
+    barrier();
+  } else {
+    issue(0, C0{});
+    barrier();
+    for (int m = 0; m < np; m += 2) {
+      mfma_phase(C0{}, C1{});
+      wait_tiles();
+      barrier();
+      issue(m + 1, C1{});
+      softmax_phase(m);
+      barrier();
+      mfma_phase(C1{}, C0{});
+      wait_tiles();
+      barrier();
+      issue(m + 2, C0{});
+      softmax_phase(m + 1);
+      barrier();
+    }
+    mfma_phase(C0{}, C1{});
+    barrier();
+  }
+
+  // ---- epilogue (as attn_tile_kernel, 256 rows)
+  l_run = xor32_sum(l_run);
+  const float inv_l = 1.0f / l_run;
+  if (a.lse && hi == 0 && qvalid)
+    a.lse[((int64_t)b * a.Hq + hq) * a.S + i] = (m_run + __log2f(l_run)) * 0.6931471805599453f;
+  float* Os = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int db = 0; db < 4; db++)
+#pragma unroll
+    for (int jq = 0; jq < 4; jq++) {
+      const int d = db * 32 + 8 * jq + 4 * hi;
+      float4 o;
+      o.x = acc_o[db][4 * jq] * inv_l;
+      o.y = acc_o[db][4 * jq + 1] * inv_l;
+      o.z = acc_o[db][4 * jq + 2] * inv_l;
+      o.w = acc_o[db][4 * jq + 3] * inv_l;
+      *reinterpret_cast<float4*>(&Os[r * kOsStride + d]) = o;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const int c = tid + 512 * k;
+    const int orow = c >> 4, oc = c & 15;
+    const int ipos = i0 + orow % P2;
+    if (ipos < a.S) {
+      const int64_t goff = (((int64_t)b * a.S + ipos) * a.Hq + kvh * a.G + orow / P2) * kHeadDim + 8 * oc;
+      const float4 o0 = *reinterpret_cast<const float4*>(&Os[orow * kOsStride + 8 * oc]);
+      const float4 o1 = *reinterpret_cast<const float4*>(&Os[orow * kOsStride + 8 * oc + 4]);
+      float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+      if (GATED) {
+        float gv[8];
+        unpack8(*reinterpret_cast<const uint4*>(a.gate + goff), gv);
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          o[e] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[e] * kLog2e));
+      }
+      *reinterpret_cast<uint4*>(a.out + goff) = pack8(o);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t st) {
@@ -447,6 +809,21 @@ hipError_t launch_attn_tile(const TileAttnArgs& a, bool gated, hipStream_t st) {
     hipLaunchKernelGGL(attn_tile_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(attn_tile_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_pp(const TileAttnArgs& a, bool gated, hipStream_t st) {
+  // a.P is half the work-group's positions here: 256 query rows = G heads x 2P positions
+  const int64_t staged = (int64_t)a.pos0 + a.S - a.kbase;
+  const int64_t first_key = gated ? std::max<int64_t>(0, (int64_t)a.pos0 - a.window + 1) : 0;
+  if (a.S < 1 || a.S_kpad % kBN || a.kbase < 0 || a.kbase > first_key || staged > a.S_kpad || a.G * a.P != 128 ||
+      a.n_units != a.B * a.Hkv || a.n_qtiles != (a.S + 2 * a.P - 1) / (2 * a.P) || (gated && (a.window < 1 || !a.gate)))
+    return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)a.n_units * a.n_qtiles;
+  if (gated)
+    hipLaunchKernelGGL(attn_pp_kernel<true>, dim3((unsigned)blocks), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_pp_kernel<false>, dim3((unsigned)blocks), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

@@ -185,6 +185,7 @@ struct DecodeArgs {
 hipError_t launch_ring_write(const RingWriteArgs& a, hipStream_t st);
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t st);
 hipError_t launch_attn_tile(const TileAttnArgs& a, bool gated, hipStream_t st);
+hipError_t launch_attn_pp(const TileAttnArgs& a, bool gated, hipStream_t st);
 hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st);
 int32_t fp8_quantize_blocks(int64_t n);   // work-groups launch_fp8_quantize uses for n values
 hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const float* scale, float* partial,

@@ -276,6 +276,9 @@ extern "C" int kv_cache_set_length(zg_kv_cache* c, int32_t layer, int32_t b, int
 }
 
 namespace {
+// The tile path's attention kernel: the ping-pong kernel (8 waves, 256 query rows per work-group) or the 4-wave one.
+constexpr bool kPingPongTile = true;
+
 // Keys a tile-path call stages: positions kbase .. pos0+S-1, kbase = the oldest position the chunk's first query
 // sees (0 for a global layer), in whole 64-key tiles.
 struct StagePlan {
@@ -430,11 +433,17 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   ta.eps = eps;
   ta.q_scale = (float)(1.4426950408889634 / std::sqrt((double)D));
   ta.n_units = B * Hkv;
-  ta.n_qtiles = (S + ta.P - 1) / ta.P;
   std::memcpy(ta.inv_freq_rev, sa.inv_freq_rev, sizeof ta.inv_freq_rev);
   {
     ScopedTimer tm(gated ? "attn_swa" : "attn_global", st);
-    hipError_t e = launch_attn_tile(ta, gated, st);
+    hipError_t e;
+    if (kPingPongTile) {   // 256 query rows per work-group in two alternating wave groups
+      ta.n_qtiles = (S + 2 * ta.P - 1) / (2 * ta.P);
+      e = launch_attn_pp(ta, gated, st);
+    } else {
+      ta.n_qtiles = (S + ta.P - 1) / ta.P;
+      e = launch_attn_tile(ta, gated, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "attention launch");
   }
   // a gated layer with a cache: the chunk's last min(S, W) positions go to the ring (the staging has read the
