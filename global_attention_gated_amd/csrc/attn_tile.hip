@@ -431,19 +431,20 @@ __global__ void __launch_bounds__(256) ring_write_kernel(RingWriteArgs a) {
 // ends with one work-group barrier; group 1 runs one phase behind group 0, and each group's straight-line sequence
 // meets the same 2n + 2 barriers (n tiles).
 //
-// LDS: keys and transposed values in separate double buffers (K[2], V^T[2], 16 KB each).  At phase 2m every wave
-// issues its eighth of K(m+1) and of V(m) (their buffers' previous tiles, K(m-1) and V(m-2), were last read in phase
-// 2m-1) and waits for them at the end of phase 2m+1; M(m) reads K(m) and V(m-1).  The loop runs two tiles per pass,
-// so every buffer is a compile-time constant and each operand fragment's LDS address is one of 12 per-lane registers
-// plus an immediate offset.  Fragments stream through an 8-deep window of registers ahead of their MFMAs.
+// LDS: keys and transposed values in separate triple buffers (K[3], V^T[3], 16 KB each), loaded two phases ahead: at
+// phase 2m every wave issues its eighth of K(m+2) and of V(m+1) (their buffers' previous tiles, K(m-1) and V(m-2),
+// were last read in phase 2m-1) and waits for them at the end of phase 2m+1.  M(m) reads K(m) and V(m-1), which are
+// in LDS from the end of phase 2m-1 on, so the softmax phase before it ends by reading M(m)'s first four operand
+// fragments into registers: the MFMA phase starts without waiting for LDS.  The loop runs three tiles per pass, so
+// every buffer is a compile-time constant and each fragment's LDS address is a per-lane register plus an immediate.
 constexpr int kPPRows = 256;
-constexpr int kPPSmemBytes = kPPRows * kOsStride * 4;   // 135,168 B: the epilogue staging; the tiles use 64 KB of it
-static_assert(4 * kTileHalves * 2 <= kPPSmemBytes, "tile buffers exceed the LDS block");
+constexpr int kPPSmemBytes = kPPRows * kOsStride * 4;   // 135,168 B: the epilogue staging; the tiles use 96 KB of it
+static_assert(6 * kTileHalves * 2 <= kPPSmemBytes, "tile buffers exceed the LDS block");
 
 template <bool GATED>
 __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[kPPSmemBytes / 2];
-  // K buffer j at smem + j * kTileHalves, V^T buffer j at smem + (2 + j) * kTileHalves
+  // K buffer j at smem + j * kTileHalves, V^T buffer j at smem + (3 + j) * kTileHalves
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -547,7 +548,7 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
                                                (int)ks, 0, 0);
   };
   auto issue_v = [&](int n, int buf) {   // V^T of tile t_lo + n into V buffer buf
-    uint16_t* dst = smem + (2 + buf) * kTileHalves;
+    uint16_t* dst = smem + (3 + buf) * kTileHalves;
     const uint32_t vs = (uint32_t)(t_lo + n) * kBN * 2;
 #pragma unroll
     for (int jj = 0; jj < 2; jj++)
@@ -558,9 +559,10 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
   // operand fragment addresses within a tile: V^T row 32db + l32, chunk 4kb + 2h2 + hi (fp16 elements, per lane);
   // K row 32hf + l32, chunk 2t8 + hi at chunk position (2t8 + hi) ^ (l32 mod 16), whose byte offset
   // l32 * 256 + 16 * ((2t8 + hi) ^ (l32 mod 16)) is kx ^ (32 t8) with kx the t8 = 0 offset (bits 5..7 hold t8 ^ ...)
+  // (vfo includes the V^T region's base, 3 tiles in, so every fragment's immediate offset stays below 64 KB)
   int vfo[4];
 #pragma unroll
-  for (int c = 0; c < 4; c++) vfo[c] = l32 * kBN + 8 * ((2 * c + hi) ^ ((l32 >> 1) & 7));
+  for (int c = 0; c < 4; c++) vfo[c] = 3 * kTileHalves + l32 * kBN + 8 * ((2 * c + hi) ^ ((l32 >> 1) & 7));
   const uint32_t kx = (uint32_t)l32 * (kHeadDim * 2) + 16u * (uint32_t)(hi ^ (l32 & 15));
 
   auto live = [&](int n) {   // this wave's queries see a key of tile n (relative index)
@@ -570,27 +572,35 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
     return true;
   };
 
-  // MFMA phase: P V^T of the previous tile (V buffer VB), then S^T = K Q^T of this one (K buffer KB), both always
-  // (P is zero where the previous tile showed this wave nothing; scores past the last tile are never used)
-  auto mfma_phase = [&](auto KBc, auto VBc) {
+  // operand fragment f of an MFMA phase with K buffer KB and V buffer VB: 0..15 V^T (kb = f/8, h2 = (f/4)%2, db =
+  // f%4), 16..31 K (t8 = (f-16)/2, half (f-16)%2)
+  auto frag = [&](auto KBc, auto VBc, int f) -> half8 {
     constexpr int KB = decltype(KBc)::value, VB = decltype(VBc)::value;
-    auto frag = [&](int f) -> half8 {
-      if (f < 16) {
-        const int kb = f >> 3, h2 = (f >> 2) & 1, db = f & 3;
-        return *reinterpret_cast<const half8*>(smem + (2 + VB) * kTileHalves + db * 32 * kBN + vfo[2 * kb + h2]);
-      }
-      const int g = f - 16, t8 = g >> 1, hf = g & 1;
-      const uint32_t kb_bytes = kx ^ (32u * (uint32_t)t8);
-      return *reinterpret_cast<const half8*>(reinterpret_cast<const unsigned char*>(smem) +
-                                             (KB * kTileHalves + hf * 32 * kHeadDim) * 2 + kb_bytes);
-    };
-    half8 win[8];
+    if (f < 16) {
+      const int kb = f >> 3, h2 = (f >> 2) & 1, db = f & 3;
+      return *reinterpret_cast<const half8*>(smem + VB * kTileHalves + db * 32 * kBN + vfo[2 * kb + h2]);
+    }
+    const int g = f - 16, t8 = g >> 1, hf = g & 1;
+    const uint32_t kb_bytes = kx ^ (32u * (uint32_t)t8);
+    return *reinterpret_cast<const half8*>(reinterpret_cast<const unsigned char*>(smem) +
+                                           (KB * kTileHalves + hf * 32 * kHeadDim) * 2 + kb_bytes);
+  };
+  // the first four fragments of the next MFMA phase, read ahead of it
+  half8 win[8];
+  auto prefetch = [&](auto KBc, auto VBc) {
 #pragma unroll
-    for (int f = 0; f < 8; f++) win[f] = frag(f);
+    for (int f = 0; f < 4; f++) win[f] = frag(KBc, VBc, f);
+  };
+  // MFMA phase: P V^T of the previous tile (V buffer VB), then S^T = K Q^T of this one (K buffer KB), both always
+  // (P is zero where the previous tile showed this wave nothing; scores past the last tile are never used).  The
+  // window holds the first four fragments on entry and takes the next four at once.
+  auto mfma_phase = [&](auto KBc, auto VBc) {
+#pragma unroll
+    for (int f = 4; f < 8; f++) win[f] = frag(KBc, VBc, f);
 #pragma unroll
     for (int f = 0; f < 32; f++) {
       const half8 op = win[f & 7];
-      if (f + 8 < 32) win[(f + 8) & 7] = frag(f + 8);
+      if (f + 8 < 32) win[(f + 8) & 7] = frag(KBc, VBc, f + 8);
       if (f < 16) {
         const int kb = f >> 3, h2 = (f >> 2) & 1, db = f & 3;
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op, pf[kb][h2], acc_o[db], 0, 0, 0);
@@ -602,7 +612,9 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
     }
   };
 
-  // softmax phase of tile m: scores (relative to -m) -> P (fp16) and the row statistics
+  // softmax phase of tile m: scores (relative to -m) -> P (fp16) and the row statistics.  The exponentials come
+  // first; their sum exceeds 256 whenever a score exceeds m + 8, and only then (or before m is set) the tile's max
+  // is taken, m raised and the exponentials redone.
   auto softmax_phase = [&](int m) {
     if (m >= n_tiles || !live(m)) {
 #pragma unroll
@@ -621,65 +633,75 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
           if ((unsigned)(qpos - key) >= lim) sacc[kb][j] = -INFINITY;
         }
     }
-    float mx0 = sacc[0][0], mx1 = sacc[1][0];
-#pragma unroll
-    for (int j = 1; j < 15; j += 2) {
-      mx0 = fmaxf(fmaxf(mx0, sacc[0][j]), sacc[0][j + 1]);
-      mx1 = fmaxf(fmaxf(mx1, sacc[1][j]), sacc[1][j + 1]);
-    }
-    float mx = fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15]));
-    mx = xor32_max(mx);
-    const bool need = m_set ? mx > 8.0f : mx > -INFINITY;
-    if (__any(need)) {
-      const float sh = need ? mx : 0.0f;
-      const float alpha = m_set ? __builtin_amdgcn_exp2f(-sh) : 1.0f;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; db++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) acc_o[db][j] *= alpha;
-      m_run += sh;
-      m_set = m_set || need;
-#pragma unroll
-      for (int j = 0; j < 16; j++) negm[j] = -m_run;
+    auto exps = [&]() {
+      float ls[2] = {0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-        for (int j = 0; j < 16; j++) sacc[kb][j] -= sh;
-    }
-    // P = exp2(s - m) rounded to fp16; the row sum adds the fp32 values (v_add, which runs beside the other wave's
-    // MFMAs, unlike v_dot2)
-    float ls[2] = {0.f, 0.f};
+        for (int h2 = 0; h2 < 2; h2++) {
+          uint32_t wp[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; h2++) {
-        uint32_t wp[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int j = 8 * h2 + 2 * e;
-          const float e0 = __builtin_amdgcn_exp2f(sacc[kb][j]), e1 = __builtin_amdgcn_exp2f(sacc[kb][j + 1]);
-          wp[e] = pack_f16(e0, e1);
-          ls[e & 1] += e0 + e1;
+          for (int e = 0; e < 4; e++) {
+            const int j = 8 * h2 + 2 * e;
+            const float e0 = __builtin_amdgcn_exp2f(sacc[kb][j]), e1 = __builtin_amdgcn_exp2f(sacc[kb][j + 1]);
+            wp[e] = pack_f16(e0, e1);
+            ls[e & 1] += e0 + e1;
+          }
+          pf[kb][h2] = __builtin_bit_cast(half8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
         }
-        pf[kb][h2] = __builtin_bit_cast(half8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
+      return xor32_sum(ls[0] + ls[1]);
+    };
+    float lt = exps();
+    if (__any(!m_set || !(lt <= 256.0f))) {
+      float mx0 = sacc[0][0], mx1 = sacc[1][0];
+#pragma unroll
+      for (int j = 1; j < 15; j += 2) {
+        mx0 = fmaxf(fmaxf(mx0, sacc[0][j]), sacc[0][j + 1]);
+        mx1 = fmaxf(fmaxf(mx1, sacc[1][j]), sacc[1][j + 1]);
       }
-    l_run += ls[0] + ls[1];
+      float mx = fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15]));
+      mx = xor32_max(mx);
+      const bool need = m_set ? mx > 8.0f : mx > -INFINITY;
+      if (__any(need)) {
+        const float sh = need ? mx : 0.0f;
+        const float alpha = m_set ? __builtin_amdgcn_exp2f(-sh) : 1.0f;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; db++)
+#pragma unroll
+          for (int j = 0; j < 16; j++) acc_o[db][j] *= alpha;
+        m_run += sh;
+        m_set = m_set || need;
+#pragma unroll
+        for (int j = 0; j < 16; j++) negm[j] = -m_run;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+          for (int j = 0; j < 16; j++) sacc[kb][j] -= sh;
+        lt = exps();
+      }
+    }
+    // lt is the sum over both lane halves; each half adds half of it back in the epilogue's final exchange
+    l_run += 0.5f * lt;
   };
 
-  // ---- prologue: K(0) in LDS for everyone; V buffer 1, which M(0) multiplies by its zero P, is cleared (LDS starts
-  // with arbitrary bits, and 0 * inf would be NaN)
+  // ---- prologue: K(0), K(1) and V(0) in LDS for everyone; V buffers 1 and 2 cleared (LDS starts with arbitrary
+  // bits: M(0) multiplies V buffer 2 by its zero P, and a buffer no tile reaches is multiplied by zero P too, where
+  // 0 * inf would be NaN)
   issue_k(0, 0);
+  if (1 < n_tiles) issue_k(1, 1);
+  issue_v(0, 0);
   {
-    uint4* v1 = reinterpret_cast<uint4*>(smem + 3 * kTileHalves);
-    v1[tid] = make_uint4(0u, 0u, 0u, 0u);
-    v1[tid + 512] = make_uint4(0u, 0u, 0u, 0u);
+    uint4* v12 = reinterpret_cast<uint4*>(smem + 4 * kTileHalves);
+#pragma unroll
+    for (int x = 0; x < 4; x++) v12[tid + 512 * x] = make_uint4(0u, 0u, 0u, 0u);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
 
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
   const int n = n_tiles;
   // a phase boundary: this wave's LDS reads are done (lgkmcnt 0), then the work-group barrier; the memory clobber
   // keeps the compiler from moving LDS accesses across it, the scheduling barriers keep every instruction of a phase
@@ -693,52 +715,84 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
   };
-  // the loads of phase 2m: K(m+1) into K buffer (m+1) mod 2, V(m) into V buffer m mod 2
-  auto issue = [&](int m, auto PARc) {
-    constexpr int PAR = decltype(PARc)::value;   // m mod 2
-    if (m + 1 < n) issue_k(m + 1, PAR ^ 1);
-    if (m < n) issue_v(m, PAR);
+  // the loads of phase 2m: K(m+2) into K buffer (m+2) mod 3, V(m+1) into V buffer (m+1) mod 3
+  auto issue = [&](int m, auto K2c, auto V1c) {
+    if (m + 2 < n) issue_k(m + 2, decltype(K2c)::value);
+    if (m + 1 < n) issue_v(m + 1, decltype(V1c)::value);
   };
-  // ---- phases.  Group 0 runs M(0) V(0) M(1) V(1) ... M(np), group 1 the same one phase later, np = n rounded up to
-  // even (an odd n gets one empty tile: no loads, zero P).  M(m) uses K buffer m mod 2 and V buffer (m-1) mod 2.  Each
-  // group meets 2 np + 2 barriers.
-  const int np = (n + 1) & ~1;
+  // ---- phases.  Group 0 runs M(0) V(0) M(1) V(1) ... M(np), group 1 the same one phase later, np = the smallest
+  // count >= n with np mod 3 = 1 (up to two empty tiles: no loads, zero P).  M(m) uses K buffer m mod 3 and V buffer
+  // (m-1) mod 3; V(m) ends by reading M(m+1)'s first fragments.  Each group meets 2 np + 2 barriers.
+  const int np = n + (4 - n % 3) % 3;
+  prefetch(C0{}, C2{});
   if (group == 0) {
-    for (int m = 0; m < np; m += 2) {
-      issue(m, C0{});
-      mfma_phase(C0{}, C1{});
-      barrier();
-      softmax_phase(m);
-      wait_tiles();
-      barrier();
-      issue(m + 1, C1{});
+    issue(0, C2{}, C1{});
+    mfma_phase(C0{}, C2{});
+    barrier();
+    softmax_phase(0);
+    prefetch(C1{}, C0{});
+    wait_tiles();
+    barrier();
+    for (int m = 1; m < np; m += 3) {
+      issue(m, C0{}, C2{});
       mfma_phase(C1{}, C0{});
       barrier();
+      softmax_phase(m);
+      prefetch(C2{}, C1{});
+      wait_tiles();
+      barrier();
+      issue(m + 1, C1{}, C0{});
+      mfma_phase(C2{}, C1{});
+      barrier();
       softmax_phase(m + 1);
+      prefetch(C0{}, C2{});
+      wait_tiles();
+      barrier();
+      issue(m + 2, C2{}, C1{});
+      mfma_phase(C0{}, C2{});
+      barrier();
+      softmax_phase(m + 2);
+      prefetch(C1{}, C0{});
       wait_tiles();
       barrier();
     }
-    mfma_phase(C0{}, C1{});
+    mfma_phase(C1{}, C0{});
     barrier();
     barrier();
   } else {
-    issue(0, C0{});
+    issue(0, C2{}, C1{});
     barrier();
-    for (int m = 0; m < np; m += 2) {
-      mfma_phase(C0{}, C1{});
-      wait_tiles();
-      barrier();
-      issue(m + 1, C1{});
-      softmax_phase(m);
-      barrier();
+    mfma_phase(C0{}, C2{});
+    wait_tiles();
+    barrier();
+    issue(1, C0{}, C2{});
+    softmax_phase(0);
+    prefetch(C1{}, C0{});
+    barrier();
+    for (int m = 1; m < np; m += 3) {
       mfma_phase(C1{}, C0{});
       wait_tiles();
       barrier();
-      issue(m + 2, C0{});
+      issue(m + 1, C1{}, C0{});
+      softmax_phase(m);
+      prefetch(C2{}, C1{});
+      barrier();
+      mfma_phase(C2{}, C1{});
+      wait_tiles();
+      barrier();
+      issue(m + 2, C2{}, C1{});
       softmax_phase(m + 1);
+      prefetch(C0{}, C2{});
+      barrier();
+      mfma_phase(C0{}, C2{});
+      wait_tiles();
+      barrier();
+      issue(m + 3, C0{}, C2{});
+      softmax_phase(m + 2);
+      prefetch(C1{}, C0{});
       barrier();
     }
-    mfma_phase(C0{}, C1{});
+    mfma_phase(C1{}, C0{});
     barrier();
   }
 
