@@ -3,15 +3,17 @@
 inputs.
 
 Bar of the backward, per gradient X against the exact X_ref (elementwise, then the mean):
-    |err| <= 2 |D_X| + 2^-7 |X_ref| + 0.1 R_X,        mean |err| <= 2 mean |D_X| + 0.005 R_X
+    |err| <= 2 |D_X| + 2^-7 |X_ref| + R_X / 16,        mean |err| <= 2 mean |D_X| + 0.005 R_X
 with R_X = rms(X_ref) (dv's rms where X_ref is identically zero: one visible key), and D_X the change in the
 exact gradient when Delta_i = dout_i . out_i is formed from the bf16 output, as this backward (the standard
 flash-attention form) must: out is handed over in bf16, 2^-9 relative per element.  The other terms: the bf16
 rounding of every result (2^-9 |X|, 2^-7 leaves margin), and the bf16 operands of the gradient products (dA, P,
 dS, q_hat: 2^-9 each, fp32 accumulation), whose errors scale with the summed terms rather than with the result:
 ds_ij = p_ij (dp_ij - Delta_i) subtracts two values of size ~sqrt(D) |dout| |v| to get a much smaller one.
-Measured: max 0.3-2.1 of (2|D_X| + 2^-7|X_ref| + 0.01 R_X), mean 0.1-0.3% of R_X.  A missed tile, wrong mask,
-head or scale errs by ~R_X on whole rows.
+Measured (small cases and 1 x 16384): the largest element error is 0.055 R_X (a 16K gated layer's dq), 0.78 of this
+bound; at 0.03 R_X it would be 1.46.  These errors come from the bf16 gradient products (dA = dout sigmoid(g) in
+bf16 enters dp, whose difference with Delta is small), not from a missed term: a missed tile, wrong mask, head or
+scale errs by ~R_X on whole rows.  Mean 0.1-0.3% of R_X.
 """
 import numpy as np
 import pytest
@@ -53,7 +55,7 @@ def _check(g, ref, ref16, gated, tag):
         dlt = np.abs(r16 - r)
         rms = float(np.sqrt(np.mean(r ** 2)))
         R = rms if rms > 0.01 * rms_dv else rms_dv
-        bound = 2 * dlt + 2.0 ** -7 * np.abs(r) + 0.1 * R
+        bound = 2 * dlt + 2.0 ** -7 * np.abs(r) + R / 16
         print(f"{tag} {gn}: max_abs {err.max():.3e} mean_abs {err.mean():.3e} R {R:.3e} "
               f"max err/bound {np.max(err / bound):.3f} mean/R {err.mean() / R:.2e}")
         assert np.all(err <= bound), f"{tag} {gn}: max err/bound {np.max(err / bound):.3f}"

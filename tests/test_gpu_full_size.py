@@ -265,7 +265,7 @@ def test_chunked_prefill_262144_in_16384_chunks(zg):
 def test_backward_1x16384_sampled(zg, gated):
     """Training forward and backward at 1 x 16384, 32 query / 8 KV heads (the backward benchmark's launch
     configuration): sampled query rows (dq, dgate) and key rows (dk, dv) of one KV head's group against the
-    row-sampled oracle, to the bar of test_gpu_backward (2 |D_X| + 2^-7 |X_ref| + 0.1 R_X; mean 2 mean|D_X| + 0.005 R_X)."""
+    row-sampled oracle, to the bar of test_gpu_backward (2 |D_X| + 2^-7 |X_ref| + R_X / 16; mean 2 mean|D_X| + 0.005 R_X)."""
     import torch
     seed, layer, S, Hq, Hkv, kvh = 1009, 2 if gated else 6, 16384, 32, 8, 5
     G = Hq // Hkv
@@ -303,7 +303,7 @@ def test_backward_1x16384_sampled(zg, gated):
         err = np.abs(x - r)
         rms = float(np.sqrt(np.mean(r ** 2)))
         R = rms if rms > 0.01 * rms_dv else rms_dv
-        bound = 2 * d + 2.0 ** -7 * np.abs(r) + 0.1 * R
+        bound = 2 * d + 2.0 ** -7 * np.abs(r) + R / 16
         print(f"backward 16K {'swa' if gated else 'global'} {n}: max_abs {err.max():.3e} mean_abs {err.mean():.3e} "
               f"R {R:.3e} max err/bound {np.max(err / bound):.3f}")
         assert np.all(np.isfinite(x)), n
