@@ -218,8 +218,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   for (int t = 0; t < 4; t++) unpack8(*reinterpret_cast<const uint4*>(Wn + 8 * (4 * t + g)), wq[t]);
   // RoPE of the lane's query rows in chunks 4t + g, t = 0, 1 (pairs 4(4t + g) + m: every pair below 32), carried
   // along the steps: the lane's position advances by one step's 32 positions, so each pair's (cos, sin) advances
-  // by a fixed rotation.  Pairs at or past rot_pairs stay at (1, 0).  Rows past the sequence end follow the same
-  // progression; their outputs are not stored.
+  // by a fixed rotation (re-seeded from the exact angle every 16 steps).  Pairs at or past rot_pairs stay at (1, 0).
+  // Rows past the sequence end follow the same progression; their outputs are not stored.
   float rc[2][4], rs[2][4], dc[2][4], dsn[2][4];
 #pragma unroll
   for (int t = 0; t < 2; t++)
@@ -246,6 +246,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     if (c == 0) ZG_WAIT_VM(0);
     else ZG_WAIT_VM(4);
     lds_barrier();                 // the previous step's ring store is visible and its GO reads are done
+    // the carried RoPE rotation is re-seeded from the exact angle every 16 steps, so its rounding cannot build up
+    // over a long run (a run of 8192 positions has 256 steps)
+    if (c > 0 && (c & 15) == 0) {
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+          const int pi = 4 * (4 * t + g) + m;
+          if (pi < a.rot_pairs) rope_cs((int64_t)i, Fr[pi], rc[t][m], rs[t][m]);
+        }
+    }
 
     // ---- q_hat of this step: RMSNorm * w_q, partial RoPE, scale by log2(e)/sqrt(D), round to fp16
     // (MFMA B operand of k-step t: lane holds q_hat[query l16][8(4t + g) .. +8])
