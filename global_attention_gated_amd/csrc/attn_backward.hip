@@ -16,10 +16,11 @@
 //   bwd_prep_kernel  per 64-token block of one head: q_hat (fp16, pre-scaled by log2(e)/sqrt(D), the forward's
 //                    score operand) and q_hat^T (bf16); dA and dA^T (bf16), Delta, lse in log2 units, dgate;
 //                    for the KV heads k_hat (fp16) and k_hat^T (bf16).  Transposes go through LDS.
-//   bwd_kv_kernel    key-centric, in two launches (dV, then dK): a work-group owns 128 keys of one (sequence, KV
-//                    head), one wave per 32 keys, and walks the query tiles that see them for each head of the
-//                    group; dV^T = dA^T P or dK_hat^T = Q_hat^T dS accumulates in registers (MFMA 32x32x16, scores
-//                    in fp16 as the forward, gradient products in bf16 for their range).
+//   bwd_kv_kernel    key-centric, in two launches (dV, then dK): a work-group owns a block of 128 keys of one
+//                    (sequence, KV head) (causal: two blocks, one from each end of the sequence), one wave per 32
+//                    keys, and walks the query tiles that see them for each head of the group; dV^T = dA^T P or
+//                    dK_hat^T = Q_hat^T dS accumulates in registers (MFMA 32x32x16, scores in fp16 as the forward,
+//                    gradient products in bf16 for their range).
 //   bwd_q_kernel     query-centric: a work-group owns 32 positions of the 4 heads of a group (one wave each) and
 //                    walks the key tiles they see: dQ_hat^T = K_hat^T dS^T.
 //   epilogues        the dK and dQ kernels take their rows back through RoPE (its transpose) and RMSNorm in their
@@ -28,6 +29,8 @@
 // The three MFMA kernels copy their tiles from the workspace straight into LDS (buffer loads with LDS as the
 // destination, one tile ahead, XOR-swizzled images); the prep writes the transposed tensors in the column order
 // those images need.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -328,191 +331,208 @@ bwd_kv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS destinations of the tile loads
   const int n_units = a.B * a.Hkv;
-  const int unit = blockIdx.x % n_units, kb = blockIdx.x / n_units;
+  const int unit = blockIdx.x % n_units, slot = blockIdx.x / n_units;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
   const bool swa = a.window > 0;
-  const int jb0 = kb * 128;              // the work-group's keys jb0 .. jb0+127
-  const int j0 = jb0 + 32 * wave;        // this wave's keys j0 .. j0+31
-  const int key = j0 + l32;              // this lane's key (MFMA column)
+  // Causal layers: a work-group takes two key blocks, nkb-1-slot (the fewest query tiles) and then slot (the
+  // most), so that every work-group has the same work and a (sequence, KV head)'s work-groups all run at once.
+  // The first block walks its tiles from the last down, the second from its first up: at any time the
+  // work-groups of a KV head in their first block read one tile and those in their second block another, so the
+  // work-groups on an XCD share every tile they read through its L2.  Windowed layers: one block each, walked
+  // from the last tile down.
+  const int nkb = (a.S + 127) / 128;
+  // one block: kb, walked upward (UP) or downward; inlined once per direction
+  auto run = [&](const int kb, auto up_c) {
+    constexpr bool up = decltype(up_c)::value;
+    const int jb0 = kb * 128;              // the work-group's keys jb0 .. jb0+127
+    const int j0 = jb0 + 32 * wave;        // this wave's keys j0 .. j0+31
+    const int key = j0 + l32;              // this lane's key (MFMA column)
 
-  // this lane's key row: k_hat fp16 (score operand) and, for dK, v bf16 (dP operand); K-steps of 16 dims
-  uint4 kf[8], vf[DK ? 8 : 1];
-  {
-    const uint16_t* kr = a.kh16 + ((int64_t)unit * a.Sp + key) * kHeadDim + 8 * hi;
+    // this lane's key row: k_hat fp16 (score operand) and, for dK, v bf16 (dP operand); K-steps of 16 dims
+    uint4 kf[8], vf[DK ? 8 : 1];
+    {
+      const uint16_t* kr = a.kh16 + ((int64_t)unit * a.Sp + key) * kHeadDim + 8 * hi;
 #pragma unroll
-    for (int t = 0; t < 8; t++) kf[t] = *reinterpret_cast<const uint4*>(kr + 16 * t);
-    if constexpr (DK) {
-      const int kc = min(key, a.S - 1);
-      const uint16_t* vr = a.v + (((int64_t)b * a.S + kc) * a.Hkv + kvh) * kHeadDim + 8 * hi;
-#pragma unroll
-      for (int t = 0; t < 8; t++) vf[t] = *reinterpret_cast<const uint4*>(vr + 16 * t);
-    }
-  }
-  // The key rows feed the MFMAs straight from these loads.  Retire them here: otherwise the compiler, unable to
-  // prove them complete across the loop's back edge, waits for every load in flight (the next tile's prefetch
-  // included; the vector-memory counter retires in order) in front of each MFMA that reads them.
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  floatx16 acc[4];
-#pragma unroll
-  for (int db = 0; db < 4; db++)
-#pragma unroll
-    for (int j = 0; j < 16; j++) acc[db][j] = 0.f;
-
-  // query tiles that see some key of the work-group, per head
-  const int jb_last = min(jb0 + 127, a.S - 1);
-  const int q_end = swa ? min(a.S, jb_last + a.window) : a.S;   // exclusive
-  const int qt0 = jb0 / kT, qt1 = (q_end + kT - 1) / kT;
-  const int ntiles = max(qt1 - qt0, 0);
-  const int n_it = ntiles * kG;
-  const int wq_end = swa ? min(a.S, j0 + 31 + a.window) : a.S;   // this wave's visible queries [j0, wq_end)
-
-  // staging: the tiles go from the workspace straight into LDS (2 x 16 bytes per lane and tile); lse / Delta
-  // through a register
-  float pf = 0.f;
-  // lanes 0..31 fetch lse, 32..63 (dK) Delta.  The pointer is picked by arithmetic: a select of the two arguments
-  // becomes a load of the pointer from the argument block at a per-lane offset, and its wait in the loop would also
-  // wait for the tile loads.
-  const float* pf_src = reinterpret_cast<const float*>(
-      reinterpret_cast<uintptr_t>(a.lse2) +
-      (tid >= 32 ? reinterpret_cast<uintptr_t>(a.delta) - reinterpret_cast<uintptr_t>(a.lse2) : (uintptr_t)0));
-  const uint32_t rm_o[2] = {rm_src(wave, 0, lane, kHeadDim * 2), rm_src(wave, 1, lane, kHeadDim * 2)};
-  const uint32_t tr_o[2] = {tr_src(wave, 0, lane, (uint32_t)a.Sp * 2), tr_src(wave, 1, lane, (uint32_t)a.Sp * 2)};
-  // Tiles are walked from the last one down, the group's heads inside each tile: every work-group of a
-  // (sequence, KV head) starts at the same last tile and advances at the same pace, so the work-groups running
-  // together on an XCD read the same tiles at about the same time and share them through its L2.
-  auto tile_q0 = [&](int it) { return (qt1 - 1 - it / kG) * kT; };
-  // issue the loads of tile `it` into buffer buf (the tiles lie wholly inside the workspace: q0 + 32 <= Sp)
-  auto load_stage = [&](int it, int buf) {
-    const int hq = kvh * kG + it % kG;
-    const int q0 = tile_q0(it);
-    const int64_t bh = (int64_t)b * a.Hq + hq;
-    KvStage<DK>& s = st[buf];
-    dma_tile(rsrc(a.qh16 + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2), s.qs, wave, rm_o);
-    dma_tile(rsrc((DK ? a.qt : a.dat) + bh * kHeadDim * a.Sp + q0, (uint32_t)(kHeadDim * a.Sp - q0) * 2), s.xts, wave,
-             tr_o);
-    if constexpr (DK) dma_tile(rsrc(a.da + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2), s.xs, wave, rm_o);
-    if (tid < (DK ? 64 : 32)) pf = pf_src[bh * a.Sp + q0 + (tid & 31)];
-  };
-  // the small arrays, once their loads are in; the tile loads before them retire with them (in order)
-  auto store_stage = [&](int buf) {
-    KvStage<DK>& s = st[buf];
-    if (tid < 32) s.lse2[tid] = pf;
-    else if (DK && tid < 64) s.dl[tid - 32] = pf;
-  };
-
-  auto compute = [&](int buf, int it) {
-    const int q0 = tile_q0(it);
-    if (q0 + kT <= j0 || q0 >= wq_end) return;            // no query of the tile sees this wave's keys
-    const KvStage<DK>& s = st[buf];
-    // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key.  The accumulators start from
-    // -lse (scores) and -Delta (dP), so the MFMAs return s - lse and dP - Delta.
-    floatx16 sacc, dpacc;
-#pragma unroll
-    for (int jq = 0; jq < 4; jq++) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s.lse2[8 * jq + 4 * hi]);
-      sacc[4 * jq] = -l4.x; sacc[4 * jq + 1] = -l4.y; sacc[4 * jq + 2] = -l4.z; sacc[4 * jq + 3] = -l4.w;
+      for (int t = 0; t < 8; t++) kf[t] = *reinterpret_cast<const uint4*>(kr + 16 * t);
       if constexpr (DK) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s.dl[8 * jq + 4 * hi]);
-        dpacc[4 * jq] = -d4.x; dpacc[4 * jq + 1] = -d4.y; dpacc[4 * jq + 2] = -d4.z; dpacc[4 * jq + 3] = -d4.w;
+        const int kc = min(key, a.S - 1);
+        const uint16_t* vr = a.v + (((int64_t)b * a.S + kc) * a.Hkv + kvh) * kHeadDim + 8 * hi;
+#pragma unroll
+        for (int t = 0; t < 8; t++) vf[t] = *reinterpret_cast<const uint4*>(vr + 16 * t);
       }
     }
-    if constexpr (DK) {
-#pragma unroll
-      for (int t = 0; t < 8; t++) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]), as_half8(kf[t]), sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_b8(&s.xs[rm_off(l32, 2 * t + hi)]), as_bf16v8(vf[t]), dpacc, 0,
-                                                        0, 0);
-      }
-    } else {
-      // two independent chains (even and odd k-steps) so consecutive MFMAs do not wait on each other
-      floatx16 s2;
-#pragma unroll
-      for (int j = 0; j < 16; j++) s2[j] = 0.f;
-#pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        const half8 qa = ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]);
-        const half8 qb = ld_h8(&s.qs[rm_off(l32, 2 * t + 2 + hi)]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, as_half8(kf[t]), sacc, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qb, as_half8(kf[t + 1]), s2, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; j++) sacc[j] += s2[j];
-    }
-    // P (dV) or dS = P (dP - Delta) (dK) replaces S; the mask only where the diagonal, the window edge or the
-    // sequence end cuts the tile (wave-uniform test)
-    const bool inside = q0 >= j0 + 31 && q0 + 31 < a.S && (!swa || q0 + 31 - j0 < a.window) && j0 + 31 < a.S;
-    if (inside) {
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const float pj = __builtin_amdgcn_exp2f(sacc[j]);
-        sacc[j] = DK ? pj * dpacc[j] : pj;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const int qi = q0 + 8 * (j >> 2) + 4 * hi + (j & 3);
-        const bool vis = qi < a.S && key <= qi && (!swa || qi - key < a.window);
-        const float pj = vis ? __builtin_amdgcn_exp2f(sacc[j]) : 0.f;
-        sacc[j] = DK ? pj * dpacc[j] : pj;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-      const bf16v8 xb = c8_to_bf16(sacc, 8 * t);
-#pragma unroll
-      for (int db = 0; db < 4; db++)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.xts, 32 * db + l32, t, hi), xb, acc[db], 0, 0, 0);
-    }
-  };
-
-  if (n_it > 0) {
-    load_stage(0, 0);
-    store_stage(0);
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the tile loads write LDS without the compiler waiting for them
-  __syncthreads();
-  // Two steps per pass, so that each step's buffer is a constant (with a computed buffer index the compiler waits
-  // for the next tile's loads before the compute's first LDS read).
-  auto step = [&](int it, int buf) {
-    const bool more = it + 1 < n_it;
-    if (more) load_stage(it + 1, buf ^ 1);
-    compute(buf, it);
-    // Keep the stores of the prefetched small arrays after the compute: they go to the other buffer, so the
-    // compiler would otherwise move them (and the wait for their loads) up against the loads, which makes the
-    // prefetch synchronous.
-    asm volatile("" ::: "memory");
-    if (more) store_stage(buf ^ 1);
+    // The key rows feed the MFMAs straight from these loads.  Retire them here: otherwise the compiler, unable to
+    // prove them complete across the loop's back edge, waits for every load in flight (the next tile's prefetch
+    // included; the vector-memory counter retires in order) in front of each MFMA that reads them.
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-  };
-  for (int it = 0; it < n_it; it += 2) {
-    step(it, 0);
-    if (it + 1 < n_it) step(it + 1, 1);
-  }
-
-  // outputs: C layout reg j of block db is dim 32db + 8(j/4) + 4hi + j%4 of this lane's key
-  if constexpr (DK) {
-    // dk: back through RoPE and the key RMSNorm here; the work-group's 128 keys' share of dw_k into its partial
-    // the weight-gradient sums in the tile buffers (free after the loop's last barrier): a second LDS array would
-    // give the tile reads alias scopes that make them wait for the tile loads in flight
-    float (*red)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&st[0]);
-    const int64_t row = ((int64_t)b * a.S + key) * a.Hkv + kvh;
-    const bool valid = key < a.S;
-    norm_rope_bwd_rows(acc, valid ? a.k + row * kHeadDim : nullptr, a.kw, valid ? a.dk + row * kHeadDim : nullptr,
-                       key, a, hi, l32, red[wave]);
-    __syncthreads();
-    if (tid < kHeadDim)
-      a.dw_part[((int64_t)a.n_qblk + blockIdx.x) * kHeadDim + tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-  } else if (key < a.S) {
-    uint16_t* dvr = a.dv + (((int64_t)b * a.S + key) * a.Hkv + kvh) * kHeadDim;
+    floatx16 acc[4];
 #pragma unroll
     for (int db = 0; db < 4; db++)
 #pragma unroll
+      for (int j = 0; j < 16; j++) acc[db][j] = 0.f;
+
+    // query tiles that see some key of the work-group, per head
+    const int jb_last = min(jb0 + 127, a.S - 1);
+    const int q_end = swa ? min(a.S, jb_last + a.window) : a.S;   // exclusive
+    const int qt0 = jb0 / kT, qt1 = (q_end + kT - 1) / kT;
+    const int ntiles = max(qt1 - qt0, 0);
+    const int n_it = ntiles * kG;
+    const int wq_end = swa ? min(a.S, j0 + 31 + a.window) : a.S;   // this wave's visible queries [j0, wq_end)
+
+    // staging: the tiles go from the workspace straight into LDS (2 x 16 bytes per lane and tile); lse / Delta
+    // through a register
+    float pf = 0.f;
+    // lanes 0..31 fetch lse, 32..63 (dK) Delta.  The pointer is picked by arithmetic: a select of the two arguments
+    // becomes a load of the pointer from the argument block at a per-lane offset, and its wait in the loop would also
+    // wait for the tile loads.
+    const float* pf_src = reinterpret_cast<const float*>(
+        reinterpret_cast<uintptr_t>(a.lse2) +
+        (tid >= 32 ? reinterpret_cast<uintptr_t>(a.delta) - reinterpret_cast<uintptr_t>(a.lse2) : (uintptr_t)0));
+    const uint32_t rm_o[2] = {rm_src(wave, 0, lane, kHeadDim * 2), rm_src(wave, 1, lane, kHeadDim * 2)};
+    const uint32_t tr_o[2] = {tr_src(wave, 0, lane, (uint32_t)a.Sp * 2), tr_src(wave, 1, lane, (uint32_t)a.Sp * 2)};
+    // the group's heads inside each tile
+    auto tile_q0 = [&](int it) { return (up ? qt0 + it / kG : qt1 - 1 - it / kG) * kT; };
+    // issue the loads of tile `it` into buffer buf (the tiles lie wholly inside the workspace: q0 + 32 <= Sp)
+    auto load_stage = [&](int it, int buf) {
+      const int hq = kvh * kG + it % kG;
+      const int q0 = tile_q0(it);
+      const int64_t bh = (int64_t)b * a.Hq + hq;
+      KvStage<DK>& s = st[buf];
+      dma_tile(rsrc(a.qh16 + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2), s.qs, wave, rm_o);
+      dma_tile(rsrc((DK ? a.qt : a.dat) + bh * kHeadDim * a.Sp + q0, (uint32_t)(kHeadDim * a.Sp - q0) * 2), s.xts, wave,
+               tr_o);
+      if constexpr (DK) dma_tile(rsrc(a.da + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2), s.xs, wave, rm_o);
+      if (tid < (DK ? 64 : 32)) pf = pf_src[bh * a.Sp + q0 + (tid & 31)];
+    };
+    // the small arrays, once their loads are in; the tile loads before them retire with them (in order)
+    auto store_stage = [&](int buf) {
+      KvStage<DK>& s = st[buf];
+      if (tid < 32) s.lse2[tid] = pf;
+      else if (DK && tid < 64) s.dl[tid - 32] = pf;
+    };
+
+    auto compute = [&](int buf, int it) {
+      const int q0 = tile_q0(it);
+      if (q0 + kT <= j0 || q0 >= wq_end) return;            // no query of the tile sees this wave's keys
+      const KvStage<DK>& s = st[buf];
+      // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key.  The accumulators start from
+      // -lse (scores) and -Delta (dP), so the MFMAs return s - lse and dP - Delta.
+      floatx16 sacc, dpacc;
+#pragma unroll
       for (int jq = 0; jq < 4; jq++) {
-        const int d = 32 * db + 8 * jq + 4 * hi;
-        *reinterpret_cast<uint2*>(dvr + d) = make_uint2(pack_bf16(acc[db][4 * jq], acc[db][4 * jq + 1]),
-                                                        pack_bf16(acc[db][4 * jq + 2], acc[db][4 * jq + 3]));
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s.lse2[8 * jq + 4 * hi]);
+        sacc[4 * jq] = -l4.x; sacc[4 * jq + 1] = -l4.y; sacc[4 * jq + 2] = -l4.z; sacc[4 * jq + 3] = -l4.w;
+        if constexpr (DK) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s.dl[8 * jq + 4 * hi]);
+          dpacc[4 * jq] = -d4.x; dpacc[4 * jq + 1] = -d4.y; dpacc[4 * jq + 2] = -d4.z; dpacc[4 * jq + 3] = -d4.w;
+        }
       }
+      if constexpr (DK) {
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]), as_half8(kf[t]), sacc, 0, 0, 0);
+          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_b8(&s.xs[rm_off(l32, 2 * t + hi)]), as_bf16v8(vf[t]), dpacc, 0,
+                                                          0, 0);
+        }
+      } else {
+        // two independent chains (even and odd k-steps) so consecutive MFMAs do not wait on each other
+        floatx16 s2;
+#pragma unroll
+        for (int j = 0; j < 16; j++) s2[j] = 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          const half8 qa = ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]);
+          const half8 qb = ld_h8(&s.qs[rm_off(l32, 2 * t + 2 + hi)]);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, as_half8(kf[t]), sacc, 0, 0, 0);
+          s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qb, as_half8(kf[t + 1]), s2, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; j++) sacc[j] += s2[j];
+      }
+      // P (dV) or dS = P (dP - Delta) (dK) replaces S; the mask only where the diagonal, the window edge or the
+      // sequence end cuts the tile (wave-uniform test)
+      const bool inside = q0 >= j0 + 31 && q0 + 31 < a.S && (!swa || q0 + 31 - j0 < a.window) && j0 + 31 < a.S;
+      if (inside) {
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const float pj = __builtin_amdgcn_exp2f(sacc[j]);
+          sacc[j] = DK ? pj * dpacc[j] : pj;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int qi = q0 + 8 * (j >> 2) + 4 * hi + (j & 3);
+          const bool vis = qi < a.S && key <= qi && (!swa || qi - key < a.window);
+          const float pj = vis ? __builtin_amdgcn_exp2f(sacc[j]) : 0.f;
+          sacc[j] = DK ? pj * dpacc[j] : pj;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const bf16v8 xb = c8_to_bf16(sacc, 8 * t);
+#pragma unroll
+        for (int db = 0; db < 4; db++)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.xts, 32 * db + l32, t, hi), xb, acc[db], 0, 0, 0);
+      }
+    };
+
+    if (n_it > 0) {
+      load_stage(0, 0);
+      store_stage(0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the tile loads write LDS without the compiler waiting for them
+    __syncthreads();
+    // Two steps per pass, so that each step's buffer is a constant (with a computed buffer index the compiler waits
+    // for the next tile's loads before the compute's first LDS read).
+    auto step = [&](int it, int buf) {
+      const bool more = it + 1 < n_it;
+      if (more) load_stage(it + 1, buf ^ 1);
+      compute(buf, it);
+      // Keep the stores of the prefetched small arrays after the compute: they go to the other buffer, so the
+      // compiler would otherwise move them (and the wait for their loads) up against the loads, which makes the
+      // prefetch synchronous.
+      asm volatile("" ::: "memory");
+      if (more) store_stage(buf ^ 1);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+    };
+    for (int it = 0; it < n_it; it += 2) {
+      step(it, 0);
+      if (it + 1 < n_it) step(it + 1, 1);
+    }
+
+    // outputs: C layout reg j of block db is dim 32db + 8(j/4) + 4hi + j%4 of this lane's key
+    if constexpr (DK) {
+      // dk: back through RoPE and the key RMSNorm here; the work-group's 128 keys' share of dw_k into its partial
+      // the weight-gradient sums in the tile buffers (free after the loop's last barrier): a second LDS array would
+      // give the tile reads alias scopes that make them wait for the tile loads in flight
+      float (*red)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&st[0]);
+      const int64_t row = ((int64_t)b * a.S + key) * a.Hkv + kvh;
+      const bool valid = key < a.S;
+      norm_rope_bwd_rows(acc, valid ? a.k + row * kHeadDim : nullptr, a.kw, valid ? a.dk + row * kHeadDim : nullptr,
+                         key, a, hi, l32, red[wave]);
+      __syncthreads();
+      if (tid < kHeadDim)
+        a.dw_part[((int64_t)a.n_qblk + (int64_t)kb * n_units + unit) * kHeadDim + tid] =
+            red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    } else if (key < a.S) {
+      uint16_t* dvr = a.dv + (((int64_t)b * a.S + key) * a.Hkv + kvh) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int jq = 0; jq < 4; jq++) {
+          const int d = 32 * db + 8 * jq + 4 * hi;
+          *reinterpret_cast<uint2*>(dvr + d) = make_uint2(pack_bf16(acc[db][4 * jq], acc[db][4 * jq + 1]),
+                                                          pack_bf16(acc[db][4 * jq + 2], acc[db][4 * jq + 3]));
+        }
+    }
+  };
+  if (swa || 2 * slot + 1 == nkb) {
+    run(swa ? slot : nkb - 1 - slot, std::false_type{});
+  } else {
+    run(nkb - 1 - slot, std::false_type{});
+    __syncthreads();   // the second block's first tile loads go to the buffer the weight-gradient sums were read from
+    run(slot, std::true_type{});
   }
 }
 
@@ -697,7 +717,9 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.B * a.Hkv * ((a.S + 127) / 128));
+  // causal layers pair the key blocks (two per work-group, the middle one alone when their count is odd)
+  const int nkb = (a.S + 127) / 128;
+  const dim3 grid(a.B * a.Hkv * (a.window > 0 ? nkb : (nkb + 1) / 2));
   hipLaunchKernelGGL(bwd_kv_kernel<false>, grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
