@@ -114,7 +114,7 @@ def run_prefill(zg, steps, warmup, S=16384, B=1):
     for _ in range(min(steps, 3)):
         prefill_step(zg, layers, ws)
     sync()
-    kt.update({n: zg.kernel_timer_read(n) for n in ("attn_swa", "kv_prologue")})
+    kt.update({n: zg.kernel_timer_read(n) for n in ("attn_swa", "kv_stage")})
     zg.kernel_timer_enable(False)
     ms = (t1 - t0) * 1e3 / steps
     pairs_global = S * (S + 1) // 2
@@ -122,10 +122,11 @@ def run_prefill(zg, steps, warmup, S=16384, B=1):
     pairs_swa = sum(min(i + 1, W) for i in range(S))
     flop_swa = 4 * D * HQ * B * pairs_swa
     bytes_swa = B * S * (3 * HQ * D * 2 + 2 * HKV * D * 2)             # q, gate, out + k, v (bf16)
+    bytes_stage = B * S * HKV * D * 2 * 4                              # k, v in (bf16); k_hat, v^T out (fp16)
     total_flop = 5 * flop_global + 27 * flop_swa
     g_ms, g_n = kt["attn_global"]
     s_ms, s_n = kt["attn_swa"]
-    p_ms, p_n = kt["kv_prologue"]
+    p_ms, p_n = kt["kv_stage"]
     g_avg = g_ms / max(g_n, 1)
     s_avg = s_ms / max(s_n, 1)
     res = {
@@ -141,14 +142,16 @@ def run_prefill(zg, steps, warmup, S=16384, B=1):
                          "hbm_frac": bytes_swa / (s_avg / 1e3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": stored_traffic("attn_swa"),
                          "tflops": flop_swa / (s_avg / 1e3) / 1e12},
-            "kv_prologue": {"avg_ms": p_ms / max(p_n, 1), "launches": p_n},
-            "timing": "attn_global: HIP events over the timed steps; attn_swa, kv_prologue: HIP events over a "
+            "kv_stage": {"avg_ms": p_ms / max(p_n, 1), "launches": p_n,
+                         "algorithmic_bytes_per_launch": bytes_stage,
+                         "gbs": bytes_stage / (p_ms / max(p_n, 1) / 1e3) / 1e9 if p_n else None},
+            "timing": "attn_global: HIP events over the timed steps; attn_swa, kv_stage: HIP events over a "
                       "pass of up to 3 steps right after them",
         },
         "roofline": {"bound": "mfma", "achieved": flop_global / (g_avg / 1e3) / 1e12, "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flop_global / (g_avg / 1e3) / 1e12 / MFMA_PEAK_TFLOPS,
                      "traffic": stored_traffic("attn_global"),
-                     "kernel": "attn_global_kernel (one global layer per launch)"},
+                     "kernel": "attn_pp_kernel<false> (one global layer per launch)"},
     }
     del layers, ws
     import torch
@@ -555,7 +558,7 @@ def run_chunked(zg, S_total=262144, C=16384, seed=1005, passes=1):
                           "tflops": glob_flop / (glob_ms / 1e3) / 1e12},
         "roofline": {"bound": "mfma", "achieved": glob_flop / (glob_ms / 1e3) / 1e12, "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": glob_flop / (glob_ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "attn_tile_kernel<global> over all 16 chunks of the 5 global layers"},
+                     "kernel": "attn_pp_kernel<false> over all 16 chunks of the 5 global layers"},
         "kv_cache_bytes": {"hybrid": fp, "all_global": fp_all, "hybrid_gib": fp / 2**30, "all_global_gib": fp_all / 2**30,
                            "device_bytes": cache.device_bytes},
     }

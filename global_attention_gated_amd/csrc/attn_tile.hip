@@ -7,13 +7,13 @@
 //                      tokens (rounded to bf16, the KV-cache value; a global layer with a cache also stores it and v
 //                      in the cache rows of those positions), the earlier positions read back from the cache (the
 //                      global layer's rows or the gated layer's ring), and v^T.
-//   attn_tile_kernel   flash-style attention of 128 query rows (G heads x P positions of one KV head) per work-group
-//                      against 64-key tiles: causal (global layer) or within the window W (gated layer, whose
-//                      epilogue multiplies by sigmoid(gate)).  Each tile goes from the workspace straight into LDS
-//                      (buffer loads with LDS as the destination: no registers, no LDS write instructions), 16 KB of
-//                      keys and 16 KB of transposed values, double-buffered.  A direct load writes 16 bytes per lane
-//                      at consecutive LDS addresses; the lanes choose their source chunks so that the LDS rows come
-//                      out XOR-swizzled, which keeps the MFMA operand reads free of bank conflicts without padding.
+//   attn_pp_kernel     flash-style attention of 256 query rows (G heads x 2P positions of one KV head) per
+//                      work-group against 64-key tiles: causal (global layer) or within the window W (gated layer,
+//                      whose epilogue multiplies by sigmoid(gate)).  Each tile goes from the workspace straight into
+//                      LDS (buffer loads with LDS as the destination: no registers, no LDS write instructions), 16 KB
+//                      of keys and 16 KB of transposed values.  A direct load writes 16 bytes per lane at
+//                      consecutive LDS addresses; the lanes choose their source chunks so that the LDS rows come out
+//                      XOR-swizzled, which keeps the MFMA operand reads free of bank conflicts without padding.
 //   ring_write_kernel  after a gated chunk with a cache, its last min(S, W) keys and values go to ring slot p mod W.
 //
 // Method (ZGCM-1 paper summaries: onedev.kr "How it works"; jaehun.me "How Gated SWA Behaves"): per (token, head)
@@ -34,8 +34,6 @@ namespace {
 constexpr int kBN = 64;                          // keys per tile
 constexpr int kTileHalves = kBN * kHeadDim;      // 8192 fp16 = 16 KB: one K tile, or one V^T tile
 constexpr int kOsStride = 132;                   // floats per output row staged in LDS (epilogue): 128 + 4 pad
-constexpr int kSmemBytes = 128 * kOsStride * 4;  // 67,584 B: the epilogue staging; the tile loop uses 64 KB of it
-static_assert(4 * kTileHalves * 2 <= kSmemBytes, "tile buffers exceed the LDS block");
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);   // s_waitcnt vmcnt(0), other counters not waited for
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -111,293 +109,6 @@ __global__ void __launch_bounds__(256) kv_stage_kernel(StageArgs a) {
   }
 }
 
-// ------------------------------------------------------------------------------------------------ attention
-// Work-group: 256 threads = 4 waves; 128 query rows = G heads x P positions of one KV head; wave w owns rows
-// 32w..32w+31 (row r -> head r / P, position i0 + r % P).  S^T = K Q^T puts one query per lane column, so the
-// softmax statistics of a query live in lanes l and l + 32 only.
-//
-// LDS tile images (fp16, dense):
-//   K   [64 keys][128 dims]: 16-byte chunk c (dims 8c..8c+7) of key row r sits at chunk position c ^ (r mod 16)
-//   V^T [128 dims][64 keys]: chunk c (8 stored keys) of dim row r sits at chunk position c ^ ((r / 2) mod 8)
-// The MFMA A-operand reads take one chunk from each of 16 consecutive rows per LDS cycle group; the swizzles
-// spread those 16 chunks over all 64 banks.
-template <bool GATED>
-__global__ void __launch_bounds__(256, 2) attn_tile_kernel(TileAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kSmemBytes / 2];
-  uint16_t* const Ks = smem;                     // [2] K tiles
-  uint16_t* const Vt = smem + 2 * kTileHalves;   // [2] V^T tiles
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-
-  // Block order: consecutive block ids walk the (b, kv head) units first, so with B*Hkv a multiple of 8 every
-  // block of one unit lands on the same XCD (blocks go round-robin over the 8 XCDs) and its keys and values stay
-  // in that XCD's L2; a causal layer's longest query tiles go first.
-  const int unit = blockIdx.x % a.n_units;
-  const int qt = a.n_qtiles - 1 - (int)(blockIdx.x / a.n_units);
-  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
-  const int i0 = qt * a.P;
-
-  const int r = wave * 32 + l32;
-  const int hq = kvh * a.G + r / a.P;
-  const int i = i0 + r % a.P;                     // row within the chunk
-  const bool qvalid = i < a.S;
-  const int ic = qvalid ? i : a.S - 1;
-  const int qpos = a.pos0 + ic;                   // absolute position
-
-  // wave-uniform absolute position range of this wave's rows (clamped to the chunk)
-  int pl_lo, pl_hi;
-  if (a.P >= 32) { pl_lo = (wave * 32) % a.P; pl_hi = pl_lo + 31; } else { pl_lo = 0; pl_hi = a.P - 1; }
-  const int wlo = a.pos0 + min(i0 + pl_lo, a.S - 1);
-  const int whi = a.pos0 + min(i0 + pl_hi, a.S - 1);
-  // staged tiles the work-group visits: keys from the oldest any row sees to the newest (its last position)
-  const int khi = a.pos0 + min(i0 + a.P, a.S);    // exclusive
-  const int klo = GATED ? max(a.kbase, a.pos0 + i0 - a.window + 1) : a.kbase;
-  const int t_lo = (klo - a.kbase) / kBN;
-  const int t_hi = (khi - a.kbase + kBN - 1) / kBN;
-  // visible iff 0 <= qpos - key < lim (one unsigned compare)
-  const unsigned lim = GATED ? (unsigned)a.window : 0x7fffffffu;
-
-  // ---- Q prologue: load, RMSNorm * w_q, partial RoPE, scale by log2(e)/sqrt(D), round to fp16.
-  // MFMA B operand (Q^T, K = d): lane holds q_hat[query l32][16t + 8hi .. +8] for k-step t.
-  half8 qf[8];
-  {
-    const uint16_t* qrow = a.q + (((int64_t)b * a.S + ic) * a.Hq + hq) * kHeadDim;
-    float f[8][8];
-    float ss = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; t++) {
-      unpack8(*reinterpret_cast<const uint4*>(qrow + 16 * t + 8 * hi), f[t]);
-#pragma unroll
-      for (int e = 0; e < 8; e++) ss += f[t][e] * f[t][e];
-    }
-    ss = xor32_sum(ss);
-    const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps);
-#pragma unroll
-    for (int t = 0; t < 8; t++) {
-      float w[8];
-      unpack8(*reinterpret_cast<const uint4*>(a.qw + 16 * t + 8 * hi), w);
-#pragma unroll
-      for (int e = 0; e < 8; e++) f[t][e] = f[t][e] * inv * w[e];
-      rope8(f[t], 16 * t + 8 * hi, qpos, a.rot_pairs, a.inv_freq_rev);
-#pragma unroll
-      for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)(f[t][e] * a.q_scale);
-    }
-  }
-
-  floatx16 acc_o[4];
-#pragma unroll
-  for (int db = 0; db < 4; db++)
-#pragma unroll
-    for (int j = 0; j < 16; j++) acc_o[db][j] = 0.f;
-  // Running max m (log2 units) and sum l of this lane's query.  -m fills a whole accumulator block and starts
-  // each score chain, so the MFMAs yield s - m directly.  m is set by the first tile that shows the query a
-  // visible key (m_set) and raised lazily after that.
-  float m_run = 0.f, l_run = 0.f;
-  bool m_set = false;
-  floatx16 negm;
-#pragma unroll
-  for (int j = 0; j < 16; j++) negm[j] = 0.f;
-
-  // ---- direct loads: wave w copies the 1 KB LDS blocks 4w..4w+3 of the K tile (key rows 4j..4j+3 each) and of
-  // the V^T tile (dim rows 8j..8j+7 each).  Byte offsets within the planes, constant over the tiles; the tile
-  // moves the scalar offset.  Every tile lies inside the padded planes, so no load is out of range.
-  const uint32_t plane_bytes = (uint32_t)a.S_kpad * kHeadDim * 2;
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.kt + (int64_t)unit * a.S_kpad * kHeadDim), (short)0, (int)plane_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.vt + (int64_t)unit * kHeadDim * a.S_kpad), (short)0, (int)plane_bytes, 0x00020000);
-  uint32_t koff[4], voff[4];
-#pragma unroll
-  for (int jj = 0; jj < 4; jj++) {
-    const int j = 4 * wave + jj;
-    const int kr = 4 * j + (lane >> 4);            // key row that this lane's 16 bytes fill
-    koff[jj] = (uint32_t)kr * (kHeadDim * 2) + 16u * (uint32_t)((lane & 15) ^ (kr & 15));
-    const int vr = 8 * j + (lane >> 3);            // dim row
-    voff[jj] = (uint32_t)vr * (uint32_t)a.S_kpad * 2u + 16u * (uint32_t)((lane & 7) ^ ((vr >> 1) & 7));
-  }
-  auto issue_tile = [&](int t, int buf) {
-    const uint32_t ks = (uint32_t)t * kBN * kHeadDim * 2, vs = (uint32_t)t * kBN * 2;
-#pragma unroll
-    for (int jj = 0; jj < 4; jj++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(Ks + buf * kTileHalves + (4 * wave + jj) * 512), 16,
-                                               (int)koff[jj], (int)ks, 0, 0);
-#pragma unroll
-    for (int jj = 0; jj < 4; jj++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(Vt + buf * kTileHalves + (4 * wave + jj) * 512), 16,
-                                               (int)voff[jj], (int)vs, 0, 0);
-  };
-
-  // MFMA A-operand reads (fp16 element offsets within a tile): K row 32kb + l32, chunk 2t8 + hi; V^T row
-  // 32db + l32, chunk 4kb + 2h2 + hi (the 8 stored keys that P's C registers 8h2..8h2+7 of block kb hold).
-  int kfo[8], vfo[4];
-#pragma unroll
-  for (int t8 = 0; t8 < 8; t8++) kfo[t8] = l32 * kHeadDim + 8 * ((2 * t8 + hi) ^ (l32 & 15));
-#pragma unroll
-  for (int c = 0; c < 4; c++) vfo[c] = l32 * kBN + 8 * ((2 * c + hi) ^ ((l32 >> 1) & 7));
-
-  const half2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-  auto compute = [&](int buf, int t) {
-    const int kt = a.kbase + t * kBN;              // absolute position of the tile's first key
-    if (kt > whi) return;                          // after every query of the wave
-    if (GATED && kt + kBN - 1 < wlo - a.window + 1) return;   // before every query's window
-    const uint16_t* kb_ = Ks + buf * kTileHalves;
-    const uint16_t* vb_ = Vt + buf * kTileHalves;
-    // S^T = K Q^T for the two 32-key halves; the two accumulator chains are interleaved so consecutive MFMAs are
-    // independent, and both start from -m.  All 16 K fragments are read first (the scheduler would otherwise put
-    // each read right before its MFMA and expose the LDS latency), and the same registers then take the 16 V^T
-    // fragments of the PV product, read while the softmax runs.
-    half8 op[16];
-#pragma unroll
-    for (int t8 = 0; t8 < 8; t8++) {
-      op[2 * t8] = *reinterpret_cast<const half8*>(kb_ + kfo[t8]);
-      op[2 * t8 + 1] = *reinterpret_cast<const half8*>(kb_ + 32 * kHeadDim + kfo[t8]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    floatx16 sacc[2];
-#pragma unroll
-    for (int t8 = 0; t8 < 8; t8++) {
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[2 * t8], qf[t8], t8 == 0 ? negm : sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[2 * t8 + 1], qf[t8], t8 == 0 ? negm : sacc[1], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; h2++)
-#pragma unroll
-        for (int db = 0; db < 4; db++)
-          op[8 * kb + 4 * h2 + db] = *reinterpret_cast<const half8*>(vb_ + db * 32 * kBN + vfo[2 * kb + h2]);
-    // the diagonal (or, for a gated layer, the window's far edge) cuts this tile for some row of the wave
-    if (kt + kBN - 1 > wlo || (GATED && kt < whi - a.window + 1)) {
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-          const int key = kt + kb * 32 + 8 * (j >> 2) + 4 * hi + (j & 3);
-          if ((unsigned)(qpos - key) >= lim) sacc[kb][j] = -INFINITY;
-        }
-    }
-    // row max: two chains of three-input maxima (v_max3), one per 32-key half
-    float mx0 = sacc[0][0], mx1 = sacc[1][0];
-#pragma unroll
-    for (int j = 1; j < 15; j += 2) {
-      mx0 = fmaxf(fmaxf(mx0, sacc[0][j]), sacc[0][j + 1]);
-      mx1 = fmaxf(fmaxf(mx1, sacc[1][j]), sacc[1][j + 1]);
-    }
-    float mx = fmaxf(fmaxf(mx0, sacc[0][15]), fmaxf(mx1, sacc[1][15]));
-    mx = xor32_max(mx);
-    // mx is the tile's max relative to m.  m is raised only when the scores exceed it by more than 2^8 (exact:
-    // the m used is carried along; every p stays <= 256), or set on the query's first visible key.
-    const bool need = m_set ? mx > 8.0f : mx > -INFINITY;
-    if (__any(need)) {
-      const float sh = need ? mx : 0.0f;
-      const float alpha = m_set ? __builtin_amdgcn_exp2f(-sh) : 1.0f;   // l and acc are still 0 before
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; db++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) acc_o[db][j] *= alpha;
-      m_run += sh;
-      m_set = m_set || need;
-#pragma unroll
-      for (int j = 0; j < 16; j++) negm[j] = -m_run;
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int j = 0; j < 16; j++) sacc[kb][j] -= sh;
-    }
-    // P = exp2(s - m) rounded to fp16; the row sum adds the same rounded values (v_dot2 with ones), so numerator
-    // and denominator use identical weights.
-    half8 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; h2++) {
-        uint32_t wp[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int j = 8 * h2 + 2 * e;
-          wp[e] = pack_f16(__builtin_amdgcn_exp2f(sacc[kb][j]), __builtin_amdgcn_exp2f(sacc[kb][j + 1]));
-          l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2, wp[e]), ones, l_run, false);
-        }
-        pf[kb][h2] = __builtin_bit_cast(half8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
-      }
-    // O^T += V^T P^T: four independent accumulators (32-dim blocks) per k-step
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; h2++)
-#pragma unroll
-        for (int db = 0; db < 4; db++)
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[8 * kb + 4 * h2 + db], pf[kb][h2], acc_o[db], 0, 0, 0);
-  };
-
-  // One step: start the next tile's copy into the other buffer (free: every wave passed the barrier after its
-  // last use), compute this one, then wait for this wave's copies and meet the other waves, after which the next
-  // tile is complete in LDS.  The loop runs two steps per pass so each step's buffer is a constant.
-  auto step = [&](int t, int buf) {
-    if (t + 1 < t_hi) issue_tile(t + 1, buf ^ 1);
-    compute(buf, t);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-  };
-  issue_tile(t_lo, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-  for (int t = t_lo; t < t_hi; t += 2) {
-    step(t, 0);
-    if (t + 1 < t_hi) step(t + 1, 1);
-  }
-
-  // ---- epilogue: normalise, stage the 128 rows through LDS as fp32 (the tile buffers are free after the loop's
-  // last barrier), then each thread rounds 8 consecutive dims of a row to bf16 (a gated layer after multiplying by
-  // sigmoid(gate)) and 16 consecutive lanes store a whole 256-byte row.  O^T lane layout: acc_o[db][j] is
-  // d = 32db + 8(j/4) + 4hi + j%4 of query row r.
-  l_run = xor32_sum(l_run);
-  const float inv_l = 1.0f / l_run;
-  // training: the log-sum-exp of the query's scores (natural log; scores in log2 units are s log2(e))
-  if (a.lse && hi == 0 && qvalid)
-    a.lse[((int64_t)b * a.Hq + hq) * a.S + i] = (m_run + __log2f(l_run)) * 0.6931471805599453f;
-  float* Os = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int db = 0; db < 4; db++)
-#pragma unroll
-    for (int jq = 0; jq < 4; jq++) {
-      const int d = db * 32 + 8 * jq + 4 * hi;
-      float4 o;
-      o.x = acc_o[db][4 * jq] * inv_l;
-      o.y = acc_o[db][4 * jq + 1] * inv_l;
-      o.z = acc_o[db][4 * jq + 2] * inv_l;
-      o.w = acc_o[db][4 * jq + 3] * inv_l;
-      *reinterpret_cast<float4*>(&Os[r * kOsStride + d]) = o;
-    }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 8; k++) {
-    const int c = tid + 256 * k;
-    const int orow = c >> 4, oc = c & 15;
-    const int ipos = i0 + orow % a.P;
-    if (ipos < a.S) {
-      const int64_t goff = (((int64_t)b * a.S + ipos) * a.Hq + kvh * a.G + orow / a.P) * kHeadDim + 8 * oc;
-      const float4 o0 = *reinterpret_cast<const float4*>(&Os[orow * kOsStride + 8 * oc]);
-      const float4 o1 = *reinterpret_cast<const float4*>(&Os[orow * kOsStride + 8 * oc + 4]);
-      float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-      if (GATED) {
-        // sigmoid(g) = 1 / (1 + 2^(-g log2 e)): exactly 1 at g = +inf and 0 at g = -inf
-        float gv[8];
-        unpack8(*reinterpret_cast<const uint4*>(a.gate + goff), gv);
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-          o[e] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv[e] * kLog2e));
-      }
-      *reinterpret_cast<uint4*>(a.out + goff) = pack8(o);
-    }
-  }
-}
-
 // ------------------------------------------------------------------------------------------------ ring write
 // After a gated chunk with a cache: k_hat (recomputed from k, bit-identical to the staging's) and raw v of the
 // chunk's last n rows go to ring slot (position mod W).  One 16-lane group per row.
@@ -423,9 +134,18 @@ __global__ void __launch_bounds__(256) ring_write_kernel(RingWriteArgs a) {
   }
 }
 
-// ------------------------------------------------------------------------------------------------ ping-pong
-// The same attention with 8 waves per work-group in two groups of 4 (one wave of each group per SIMD), 256 query
-// rows = G heads x 2P positions, whose phases alternate: while one group runs its MFMA phase M(m) (P V^T of tile m-1,
+// ------------------------------------------------------------------------------------------------ attention
+// Rows: wave w owns query rows 32w..32w+31 of the work-group's 256 (row r -> head r / 2P, position i0 + r % 2P).
+// S^T = K Q^T puts one query per lane column (MFMA 32x32x16, keys as the A rows), so the softmax statistics of a
+// query live in lanes l and l + 32 only, and O^T = V^T P^T keeps the output in the same layout.
+//
+// LDS tile images (fp16, dense):
+//   K   [64 keys][128 dims]: 16-byte chunk c (dims 8c..8c+7) of key row r sits at chunk position c ^ (r mod 16)
+//   V^T [128 dims][64 keys]: chunk c (8 stored keys) of dim row r sits at chunk position c ^ ((r / 2) mod 8)
+// The MFMA A-operand reads take one chunk from each of 16 consecutive rows per LDS cycle group; the swizzles
+// spread those 16 chunks over all 64 banks.
+//
+// Ping-pong: the 8 waves form two groups of 4 (one wave of each group per SIMD) whose phases alternate: while one group runs its MFMA phase M(m) (P V^T of tile m-1,
 // then S^T = K Q^T of tile m) the other runs its softmax phase V (max, exponentials, row sums of its last scores) on
 // the VALU, so a SIMD's matrix unit is fed by one wave while the other wave's vector work runs beside it.  Every phase
 // ends with one work-group barrier; group 1 runs one phase behind group 0, and each group's straight-line sequence
@@ -475,7 +195,8 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
   const int n_tiles = (khi - a.kbase + kBN - 1) / kBN - t_lo;
   const unsigned lim = GATED ? (unsigned)a.window : 0x7fffffffu;
 
-  // ---- Q prologue (as attn_tile_kernel)
+  // ---- Q prologue: q_hat = RoPE(RMSNorm(q) w_q), scaled by log2(e)/sqrt(D), fp16; lane (l32, hi) holds dims
+  // 16t + 8hi .. +7 of its row for k-step t
   half8 qf[8];
   {
     const uint16_t* qrow = a.q + (((int64_t)b * a.S + ic) * a.Hq + hq) * kHeadDim;
@@ -524,7 +245,7 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
     for (int h2 = 0; h2 < 2; h2++) pf[kb][h2] = (half8){};
 
   // ---- direct loads: wave w copies the 1 KB LDS blocks 2w, 2w+1 of a K tile (key rows 4j..4j+3 each) and of a V^T
-  // tile (dim rows 8j..8j+7 each), with the swizzles of attn_tile_kernel
+  // tile (dim rows 8j..8j+7 each), in the swizzled images above
   const uint32_t plane_bytes = (uint32_t)a.S_kpad * kHeadDim * 2;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.kt + (int64_t)unit * a.S_kpad * kHeadDim), (short)0, (int)plane_bytes, 0x00020000);
@@ -796,7 +517,8 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
     barrier();
   }
 
-  // ---- epilogue (as attn_tile_kernel, 256 rows)
+  // ---- epilogue: O / l staged in LDS as fp32 rows, then 16 lanes per 256-byte bf16 output row (times sigmoid(g)
+  // for a gated layer)
   l_run = xor32_sum(l_run);
   const float inv_l = 1.0f / l_run;
   if (a.lse && hi == 0 && qvalid)
@@ -847,22 +569,6 @@ hipError_t launch_kv_stage(const StageArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)a.B * a.Hkv * (a.S_kpad / kBN);
   hipLaunchKernelGGL(kv_stage_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_tile(const TileAttnArgs& a, bool gated, hipStream_t st) {
-  // every key the work-groups visit must be staged: from kbase (no later than the first visible key of the
-  // chunk's first query) to the chunk's last position
-  const int64_t staged = (int64_t)a.pos0 + a.S - a.kbase;
-  const int64_t first_key = gated ? std::max<int64_t>(0, (int64_t)a.pos0 - a.window + 1) : 0;
-  if (a.S < 1 || a.S_kpad % kBN || a.kbase < 0 || a.kbase > first_key || staged > a.S_kpad || a.G * a.P != 128 ||
-      a.n_units != a.B * a.Hkv || a.n_qtiles != (a.S + a.P - 1) / a.P || (gated && (a.window < 1 || !a.gate)))
-    return hipErrorInvalidValue;
-  const int64_t blocks = (int64_t)a.n_units * a.n_qtiles;
-  if (gated)
-    hipLaunchKernelGGL(attn_tile_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_tile_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

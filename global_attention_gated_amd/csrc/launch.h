@@ -63,13 +63,13 @@ struct TileAttnArgs {
   const uint16_t* kt;   // staged tiles
   const uint16_t* vt;
   int32_t pos0, kbase;
-  int32_t B, S, S_kpad, Hq, Hkv, G, P;  // P = 128 / G query positions per work-group
+  int32_t B, S, S_kpad, Hq, Hkv, G, P;  // P = 128 / G: query positions per wave group (a work-group has two)
   int32_t window;       // gated layers
   int32_t rot_pairs;
   float eps;
   float q_scale;        // log2(e) / sqrt(D)
   int32_t n_units;      // B * Hkv
-  int32_t n_qtiles;     // ceil(S / P)
+  int32_t n_qtiles;     // ceil(S / 2P): work-groups per (sequence, KV head)
   double inv_freq_rev[64];
 };
 
@@ -184,7 +184,6 @@ struct DecodeArgs {
 
 hipError_t launch_ring_write(const RingWriteArgs& a, hipStream_t st);
 hipError_t launch_kv_stage(const StageArgs& a, hipStream_t st);
-hipError_t launch_attn_tile(const TileAttnArgs& a, bool gated, hipStream_t st);
 hipError_t launch_attn_pp(const TileAttnArgs& a, bool gated, hipStream_t st);
 hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st);
 int32_t fp8_quantize_blocks(int64_t n);   // work-groups launch_fp8_quantize uses for n values

@@ -276,9 +276,6 @@ extern "C" int kv_cache_set_length(zg_kv_cache* c, int32_t layer, int32_t b, int
 }
 
 namespace {
-// The tile path's attention kernel: the ping-pong kernel (8 waves, 256 query rows per work-group) or the 4-wave one.
-constexpr bool kPingPongTile = true;
-
 // Keys a tile-path call stages: positions kbase .. pos0+S-1, kbase = the oldest position the chunk's first query
 // sees (0 for a global layer), in whole 64-key tiles.
 struct StagePlan {
@@ -415,7 +412,7 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   sa.eps = eps;
   fill_inv_freq(sa.inv_freq_rev, rot_pairs, R, base);
   {
-    ScopedTimer tm("kv_prologue", st);
+    ScopedTimer tm("kv_stage", st);
     hipError_t e = launch_kv_stage(sa, st);
     if (e != hipSuccess) return hip_fail(e, "key staging launch");
   }
@@ -436,14 +433,8 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   std::memcpy(ta.inv_freq_rev, sa.inv_freq_rev, sizeof ta.inv_freq_rev);
   {
     ScopedTimer tm(gated ? "attn_swa" : "attn_global", st);
-    hipError_t e;
-    if (kPingPongTile) {   // 256 query rows per work-group in two alternating wave groups
-      ta.n_qtiles = (S + 2 * ta.P - 1) / (2 * ta.P);
-      e = launch_attn_pp(ta, gated, st);
-    } else {
-      ta.n_qtiles = (S + ta.P - 1) / ta.P;
-      e = launch_attn_tile(ta, gated, st);
-    }
+    ta.n_qtiles = (S + 2 * ta.P - 1) / (2 * ta.P);   // 256 query rows = G heads x 2P positions per work-group
+    hipError_t e = launch_attn_pp(ta, gated, st);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
   }
   // a gated layer with a cache: the chunk's last min(S, W) positions go to the ring (the staging has read the

@@ -312,7 +312,7 @@ const char* zg_last_error(void);
 /* Kernel timer: while enabled, every launch of the main attention kernels records a pair of HIP
  * events on the launch stream.  zg_kernel_timer_read synchronises on the recorded events and returns,
  * for the kernel family `name` ("attn_swa", "attn_global", "decode_global", "decode_swa",
- * "kv_prologue", "decode_merge", "decode_append", "linear", "fp8_quantize", "bwd_prep", "bwd_kv", "bwd_q"),
+ * "kv_stage", "decode_merge", "decode_append", "linear", "fp8_quantize", "bwd_prep", "bwd_kv", "bwd_q"),
  * the summed device time in ms and the launch count
  * since the last reset.  Enabling resets the counters. */
 int zg_kernel_timer_enable(int32_t on);
