@@ -133,9 +133,22 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecodeArgs a, int32_t 
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(ld.k + plane * kHeadDim), (short)0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(ld.v + plane * kHeadDim), (short)0, nbytes, 0x00020000);
 
-  constexpr int U = 4;   // rows in flight per group
+  constexpr int U = 2;   // rows per group and block
+  // software pipeline: the next block's rows are loaded while this block computes
+  uint4 kw[U], vw[U];
+  auto load_block = [&](int64_t rb, uint4 (&kd)[U], uint4 (&vd)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      // rows past r1 fall outside the descriptor and read as zero (masked below)
+      const int off = (int)((rb + 16 * u - r0) * kHeadDim + 8 * c) * 2;
+      kd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      vd[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+  };
+  load_block(r0 + g, kw, vw);
   for (int64_t rb = r0 + g; rb < r1; rb += 16 * U) {
-    uint4 kw[U], vw[U];
+    uint4 kn[U], vn[U];
+    load_block(rb + 16 * U, kn, vn);
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -146,10 +159,6 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecodeArgs a, int32_t 
         const int64_t back = ((p - row) % a.W + a.W) % a.W;
         ok[u] = p - back >= 0;
       }
-      // rows past r1 fall outside the descriptor and read as zero (masked below)
-      const int off = (int)((row - r0) * kHeadDim + 8 * c) * 2;
-      kw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vw[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
     // scores of the U rows, then one running-max check for the block (lazy: the max is raised only when a
     // score exceeds it by more than 2^8, which keeps p <= 256 and the result exact)
@@ -193,6 +202,8 @@ __global__ void __launch_bounds__(256) decode_attn_kernel(DecodeArgs a, int32_t 
         for (int e = 0; e < 8; e++) acc[hh][e] += pr * vf[e];
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; u++) { kw[u] = kn[u]; vw[u] = vn[u]; }
   }
 
   // merge the 16 groups
