@@ -200,10 +200,12 @@ def _cache_check(zg, cache, ocache, layer, glob):
     return float(np.mean(kd != 0))
 
 
-def test_chunked_prefill_with_cache_matches_oracle(zg):
-    """A 2-layer cache (layer 1 gated SWA with window 128, layer 2 global), 2 sequences of 400 tokens in
-    chunks of 150, 40 and 210: every chunk's output against the oracle, then the cache images."""
-    B, Hq, Hkv, R, base, eps, W = 2, 8, 2, 42, 1e7, 1e-6, 128
+@pytest.mark.parametrize("W", [128, 16, 200])
+def test_chunked_prefill_with_cache_matches_oracle(zg, W):
+    """A 2-layer cache (layer 1 gated SWA with window W, layer 2 global), 2 sequences of 400 tokens in chunks of
+    150, 40 and 210 (a chunk shorter than the window, chunk starts off the 32- and 64-key tile grid): every chunk's
+    output against the oracle, then the cache images."""
+    B, Hq, Hkv, R, base, eps = 2, 8, 2, 42, 1e7, 1e-6
     cache = zg.KVCache(n_layers=2, global_layers=[2], batch=B, n_kv_heads=Hkv, window=W, max_tokens=512)
     ocache = oracle.OracleCache(2, [2], B, Hkv, 128, W)
     S_total = 400
