@@ -427,28 +427,55 @@ bwd_kv_kernel(BwdArgs a) {
           dpacc[4 * jq] = -d4.x; dpacc[4 * jq + 1] = -d4.y; dpacc[4 * jq + 2] = -d4.z; dpacc[4 * jq + 3] = -d4.w;
         }
       }
+      // the LDS operands are read two k-steps ahead of the MFMAs that use them (the scheduling barriers keep that
+      // order: left alone, the compiler reads each operand right before its MFMA and waits for it there)
       if constexpr (DK) {
+        half8 qwin[2];
+        bf16v8 xwin[2];
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+          qwin[t] = ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]);
+          xwin[t] = ld_b8(&s.xs[rm_off(l32, 2 * t + hi)]);
+        }
 #pragma unroll
         for (int t = 0; t < 8; t++) {
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]), as_half8(kf[t]), sacc, 0, 0, 0);
-          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_b8(&s.xs[rm_off(l32, 2 * t + hi)]), as_bf16v8(vf[t]), dpacc, 0,
-                                                          0, 0);
+          const half8 qa = qwin[t & 1];
+          const bf16v8 xa = xwin[t & 1];
+          if (t + 2 < 8) {
+            qwin[t & 1] = ld_h8(&s.qs[rm_off(l32, 2 * (t + 2) + hi)]);
+            xwin[t & 1] = ld_b8(&s.xs[rm_off(l32, 2 * (t + 2) + hi)]);
+          }
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, as_half8(kf[t]), sacc, 0, 0, 0);
+          dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, as_bf16v8(vf[t]), dpacc, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
         // two independent chains (even and odd k-steps) so consecutive MFMAs do not wait on each other
         floatx16 s2;
 #pragma unroll
         for (int j = 0; j < 16; j++) s2[j] = 0.f;
+        half8 qwin[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) qwin[t] = ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]);
 #pragma unroll
         for (int t = 0; t < 8; t += 2) {
-          const half8 qa = ld_h8(&s.qs[rm_off(l32, 2 * t + hi)]);
-          const half8 qb = ld_h8(&s.qs[rm_off(l32, 2 * t + 2 + hi)]);
+          const half8 qa = qwin[t & 3], qb = qwin[(t + 1) & 3];
+          if (t + 4 < 8) {
+            qwin[t & 3] = ld_h8(&s.qs[rm_off(l32, 2 * (t + 4) + hi)]);
+            qwin[(t + 1) & 3] = ld_h8(&s.qs[rm_off(l32, 2 * (t + 5) + hi)]);
+          }
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, as_half8(kf[t]), sacc, 0, 0, 0);
           s2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(qb, as_half8(kf[t + 1]), s2, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int j = 0; j < 16; j++) sacc[j] += s2[j];
       }
+      // the first four operands of the dV / dK products, read while the exponentials run
+      constexpr int TW = DK ? 2 : 4;
+      bf16v8 twin[TW];
+#pragma unroll
+      for (int f = 0; f < TW; f++) twin[f] = tr_frag(s.xts, 32 * (f & 3) + l32, f >> 2, hi);
       // P (dV) or dS = P (dP - Delta) (dK) replaces S; the mask only where the diagonal, the window edge or the
       // sequence end cuts the tile (wave-uniform test)
       const bool inside = q0 >= j0 + 31 && q0 + 31 < a.S && (!swa || q0 + 31 - j0 < a.window) && j0 + 31 < a.S;
@@ -467,12 +494,13 @@ bwd_kv_kernel(BwdArgs a) {
           sacc[j] = DK ? pj * dpacc[j] : pj;
         }
       }
+      const bf16v8 xb[2] = {c8_to_bf16(sacc, 0), c8_to_bf16(sacc, 8)};
 #pragma unroll
-      for (int t = 0; t < 2; t++) {
-        const bf16v8 xb = c8_to_bf16(sacc, 8 * t);
-#pragma unroll
-        for (int db = 0; db < 4; db++)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.xts, 32 * db + l32, t, hi), xb, acc[db], 0, 0, 0);
+      for (int f = 0; f < 8; f++) {   // f = 4t + db
+        const bf16v8 ta = twin[f % TW];
+        if (f + TW < 8) twin[f % TW] = tr_frag(s.xts, 32 * ((f + TW) & 3) + l32, (f + TW) >> 2, hi);
+        acc[f & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, xb[f >> 2], acc[f & 3], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -611,12 +639,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       sacc[j] = -lse2;
       dpacc[j] = -dl;
     }
+    // the LDS operands are read two k-steps ahead of the MFMAs that use them (the scheduling barriers keep that
+    // order: left alone, the compiler reads each operand right before its MFMA and waits for it there)
+    half8 kwin[2];
+    bf16v8 vwin[2];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      kwin[t] = ld_h8(&s.ks[rm_off(l32, 2 * t + hi)]);
+      vwin[t] = ld_b8(&s.vs[rm_off(l32, 2 * t + hi)]);
+    }
 #pragma unroll
     for (int t = 0; t < 8; t++) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ld_h8(&s.ks[rm_off(l32, 2 * t + hi)]), as_half8(qf[t]), sacc, 0, 0, 0);
-      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_b8(&s.vs[rm_off(l32, 2 * t + hi)]), as_bf16v8(daf[t]), dpacc, 0, 0,
-                                                      0);
+      const half8 ka = kwin[t & 1];
+      const bf16v8 va = vwin[t & 1];
+      if (t + 2 < 8) {
+        kwin[t & 1] = ld_h8(&s.ks[rm_off(l32, 2 * (t + 2) + hi)]);
+        vwin[t & 1] = ld_b8(&s.vs[rm_off(l32, 2 * (t + 2) + hi)]);
+      }
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, as_half8(qf[t]), sacc, 0, 0, 0);
+      dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, as_bf16v8(daf[t]), dpacc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first four k_hat^T operands of the dQ products, read while the exponentials run
+    bf16v8 twin[4];
+#pragma unroll
+    for (int f = 0; f < 4; f++) twin[f] = tr_frag(s.kts, 32 * (f & 3) + l32, f >> 2, hi);
     // the mask only where the diagonal, the window edge or the sequence end cuts the tile (wave-uniform test)
     const bool inside = k0 + 31 <= i0 && i0 + 31 < a.S && (!swa || i0 + 31 - k0 < a.window);
     if (inside) {
@@ -630,12 +677,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
         sacc[j] = vis ? __builtin_amdgcn_exp2f(sacc[j]) * dpacc[j] : 0.f;
       }
     }
+    const bf16v8 sb[2] = {c8_to_bf16(sacc, 0), c8_to_bf16(sacc, 8)};
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-      const bf16v8 sb = c8_to_bf16(sacc, 8 * t);
-#pragma unroll
-      for (int db = 0; db < 4; db++)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(s.kts, 32 * db + l32, t, hi), sb, dq[db], 0, 0, 0);
+    for (int f = 0; f < 8; f++) {   // f = 4t + db
+      const bf16v8 ta = twin[f & 3];
+      if (f + 4 < 8) twin[f & 3] = tr_frag(s.kts, 32 * ((f + 4) & 3) + l32, (f + 4) >> 2, hi);
+      dq[f & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, sb[f >> 2], dq[f & 3], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
