@@ -316,13 +316,23 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     floatx4 sacc[kBlocks];
 #pragma unroll
     for (int kb = 0; kb < kBlocks; kb++) sacc[kb] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    // score MFMA f = kBlocks t + kb takes its K fragment from a window read 4 MFMAs ahead (the scheduling barriers
+    // keep that order: left alone, the compiler reads each fragment right before its MFMA and waits for it there)
+    constexpr int kWinS = 4;
+    auto kfrag = [&](int f) {
+      const int t = f / kBlocks, kb = f % kBlocks;
+      return *reinterpret_cast<const half8*>(Ks + slot_k[kb >> 1] + k_off(0, 16 * (kb & 1) + l16, 4 * t + g));
+    };
+    half8 kwin[kWinS];
 #pragma unroll
-    for (int t = 0; t < 4; t++)
+    for (int f = 0; f < kWinS; f++) kwin[f] = kfrag(f);
 #pragma unroll
-      for (int kb = 0; kb < kBlocks; kb++) {
-        const half8 kf = *reinterpret_cast<const half8*>(Ks + slot_k[kb >> 1] + k_off(0, 16 * (kb & 1) + l16, 4 * t + g));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[t], sacc[kb], 0, 0, 0);
-      }
+    for (int f = 0; f < 4 * kBlocks; f++) {
+      const half8 kf = kwin[f % kWinS];
+      if (f + kWinS < 4 * kBlocks) kwin[f % kWinS] = kfrag(f + kWinS);
+      sacc[f % kBlocks] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[f / kBlocks], sacc[f % kBlocks], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // mask: key visible iff 0 <= i - key < min(W, i + 1) (one unsigned compare); blocks wholly inside every
     // window of the wave's 16 queries skip it.  C layout: lane (l16, g) holds keys 4g .. 4g+3 of the block.
     {
