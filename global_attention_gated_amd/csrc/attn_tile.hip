@@ -355,7 +355,7 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
         }
     }
     auto exps = [&]() {
-      float ls[2] = {0.f, 0.f};
+      half2 hs[2] = {half2{}, half2{}};
 #pragma unroll
       for (int kb = 0; kb < 2; kb++)
 #pragma unroll
@@ -364,13 +364,13 @@ __global__ void __launch_bounds__(512, 1) attn_pp_kernel(TileAttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             const int j = 8 * h2 + 2 * e;
-            const float e0 = __builtin_amdgcn_exp2f(sacc[kb][j]), e1 = __builtin_amdgcn_exp2f(sacc[kb][j + 1]);
-            wp[e] = pack_f16(e0, e1);
-            ls[e & 1] += e0 + e1;
+            wp[e] = pack_f16(__builtin_amdgcn_exp2f(sacc[kb][j]), __builtin_amdgcn_exp2f(sacc[kb][j + 1]));
+            hs[e & 1] = hs[e & 1] + __builtin_bit_cast(half2, wp[e]);   // packed fp16 sums of the rounded P
           }
           pf[kb][h2] = __builtin_bit_cast(half8, make_uint4(wp[0], wp[1], wp[2], wp[3]));
         }
-      return xor32_sum(ls[0] + ls[1]);
+      const half2 h = hs[0] + hs[1];
+      return xor32_sum((float)h.x + (float)h.y);
     };
     float lt = exps();
     if (__any(!m_set || !(lt <= 256.0f))) {
