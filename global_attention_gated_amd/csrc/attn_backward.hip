@@ -53,9 +53,6 @@ __device__ __forceinline__ bf16v8 as_bf16v8(const uint4& w) { return __builtin_b
 __device__ __forceinline__ half8 as_half8(const uint4& w) { return __builtin_bit_cast(half8, w); }
 
 // 8 fp32 of an MFMA C block (regs j0..j0+7) -> bf16 operand fragment
-__device__ __forceinline__ bf16v8 c8_to_bf16(const float* c) {
-  return as_bf16v8(make_uint4(pack_bf16(c[0], c[1]), pack_bf16(c[2], c[3]), pack_bf16(c[4], c[5]), pack_bf16(c[6], c[7])));
-}
 __device__ __forceinline__ bf16v8 c8_to_bf16(const floatx16& c, int j0) {
   return as_bf16v8(make_uint4(pack_bf16(c[j0], c[j0 + 1]), pack_bf16(c[j0 + 2], c[j0 + 3]), pack_bf16(c[j0 + 4], c[j0 + 5]),
                               pack_bf16(c[j0 + 6], c[j0 + 7])));
