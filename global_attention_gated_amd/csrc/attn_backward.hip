@@ -83,6 +83,18 @@ __device__ __forceinline__ bf16v8 tr_frag(const uint16_t* tile, int row, int t, 
   return ld_b8(tile + tr_off(row, 2 * t + hi));
 }
 
+// LDS reads at a byte address (the LDS offset of an array plus a per-lane byte offset)
+typedef __attribute__((address_space(3))) const unsigned char lds_byte;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ half8 lds_h8(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) half8*>((lds_byte*)(uintptr_t)addr);
+}
+__device__ __forceinline__ bf16v8 lds_b8(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16v8*>((lds_byte*)(uintptr_t)addr);
+}
+
 // Byte offsets of a lane's 16-byte sources when wave w copies the 1 KB blocks 2w, 2w+1 of an 8 KB tile:
 // row-major (block j = rows 4j..4j+3; source rows `stride` bytes apart) and transposed (block j = rows 16j..16j+15).
 __device__ __forceinline__ uint32_t rm_src(int wave, int jj, int lane, uint32_t stride) {
@@ -561,6 +573,241 @@ bwd_kv_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------ dK and dV together
+// Causal (global) layers: one kernel forms S and dP once per (key block, query tile) and accumulates both dV^T +=
+// dA^T P and dK_hat^T += q_hat^T dS (four products per tile instead of five in the two kernels above, and one set of
+// exponentials).  A work-group of 8 waves owns 256 keys (one wave per 32), so that its two gradient accumulators
+// fit two waves per SIMD: the wave's k_hat rows stay in registers (score operand) and the block's 256 v rows sit
+// in LDS as a row-major image (dP operand), read like the query tiles.
+constexpr int kKvfKeys = 256;   // keys per work-group
+struct KvfStage {
+  uint16_t qs[kT * kHeadDim];    // q_hat' fp16 [32 queries][128], row-major image
+  uint16_t xs[kT * kHeadDim];    // dA bf16 [32][128], row-major image
+  uint16_t dat[kHeadDim * kT];   // dA^T bf16 [128][32], transposed image
+  uint16_t qts[kHeadDim * kT];   // q_hat^T bf16 [128][32], transposed image
+  float lse2[kT];
+  float dl[kT];
+};
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_kvf_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t vimg[kKvfKeys * kHeadDim];   // v bf16 [256 keys][128], row-major
+  __shared__ __attribute__((aligned(16))) KvfStage st[2];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..7, wave-uniform: LDS destinations of the loads
+  const int n_units = a.B * a.Hkv;
+  const int unit = blockIdx.x % n_units, slot = blockIdx.x / n_units;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  // key blocks paired as in bwd_kv_kernel: nkb-1-slot walked down, then slot walked up (equal work per work-group)
+  const int nkb = (a.S + kKvfKeys - 1) / kKvfKeys;
+  // source offsets of this wave's 1 KB blocks: block w of each staged tile (row-major rows 4w..4w+3 are
+  // rm_src(w/2, w%2); transposed rows 16w..16w+15 tr_src(w/2, w%2))
+  const uint32_t rm_o = rm_src(wave >> 1, wave & 1, lane, kHeadDim * 2);
+  const uint32_t tr_o = tr_src(wave >> 1, wave & 1, lane, (uint32_t)a.Sp * 2);
+  auto run = [&](const int kb, auto up_c) {
+    constexpr bool up = decltype(up_c)::value;
+    const int jb0 = kb * kKvfKeys;          // the work-group's keys jb0 .. jb0+255
+    const int j0 = jb0 + 32 * wave;         // this wave's keys j0 .. j0+31
+    const int key = j0 + l32;               // this lane's key (MFMA column)
+
+    // the block's v rows -> LDS image (row r: chunk c at position c ^ (r % 16)); rows past the sequence read as zero
+    {
+      const uint32_t vstride = (uint32_t)a.Hkv * kHeadDim * 2;
+      // (wave-uniform; readfirstlane keeps the descriptor in scalar registers, which the min / max would not)
+      const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kKvfKeys, a.S - jb0)));
+      const uint32_t vbytes = rows > 0 ? (uint32_t)(rows - 1) * vstride + kHeadDim * 2 : 0u;
+      const __amdgpu_buffer_rsrc_t rv =
+          rsrc(a.v + (((int64_t)b * a.S + min(jb0, a.S - 1)) * a.Hkv + kvh) * kHeadDim, vbytes);
+#pragma unroll
+      for (int jj = 0; jj < 8; jj++) {
+        const int blk = 8 * wave + jj, row = 4 * blk + (lane >> 4);
+        const uint32_t off = (uint32_t)row * vstride + 16u * (uint32_t)((lane & 15) ^ (row & 15));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vimg + blk * 512), 16, (int)off, 0, 0, 0);
+      }
+    }
+    // this lane's k_hat row (fp16, the score operand), K-steps of 16 dims; rows past the workspace clamp to its last
+    // row (their scores are masked)
+    uint4 kf[8];
+    {
+      const uint16_t* kr = a.kh16 + ((int64_t)unit * a.Sp + min(key, a.Sp - 1)) * kHeadDim + 8 * hi;
+#pragma unroll
+      for (int t = 0; t < 8; t++) kf[t] = *reinterpret_cast<const uint4*>(kr + 16 * t);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // retire the preloads (see bwd_kv_kernel)
+    floatx16 accv[4], acck[4];
+#pragma unroll
+    for (int db = 0; db < 4; db++)
+#pragma unroll
+      for (int j = 0; j < 16; j++) accv[db][j] = acck[db][j] = 0.f;
+
+    const int qt0 = jb0 / kT, qt1 = (a.S + kT - 1) / kT;
+    const int n_it = max(qt1 - qt0, 0) * kG;
+    float pf = 0.f;
+    const float* pf_src = reinterpret_cast<const float*>(
+        reinterpret_cast<uintptr_t>(a.lse2) +
+        (tid >= 32 ? reinterpret_cast<uintptr_t>(a.delta) - reinterpret_cast<uintptr_t>(a.lse2) : (uintptr_t)0));
+    auto tile_q0 = [&](int it) { return (up ? qt0 + it / kG : qt1 - 1 - it / kG) * kT; };
+    auto load_stage = [&](int it, int buf) {
+      const int hq = kvh * kG + it % kG;
+      const int q0 = tile_q0(it);
+      const int64_t bh = (int64_t)b * a.Hq + hq;
+      KvfStage& sg = st[buf];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(a.qh16 + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2),
+                                               (lds_void*)(sg.qs + wave * 512), 16, (int)rm_o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(a.da + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2),
+                                               (lds_void*)(sg.xs + wave * 512), 16, (int)rm_o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(a.dat + bh * kHeadDim * a.Sp + q0, (uint32_t)(kHeadDim * a.Sp - q0) * 2),
+                                               (lds_void*)(sg.dat + wave * 512), 16, (int)tr_o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(a.qt + bh * kHeadDim * a.Sp + q0, (uint32_t)(kHeadDim * a.Sp - q0) * 2),
+                                               (lds_void*)(sg.qts + wave * 512), 16, (int)tr_o, 0, 0, 0);
+      if (tid < 64) pf = pf_src[bh * a.Sp + q0 + (tid & 31)];
+    };
+    auto store_stage = [&](int buf) {
+      KvfStage& sg = st[buf];
+      if (tid < 32) sg.lse2[tid] = pf;
+      else if (tid < 64) sg.dl[tid - 32] = pf;
+    };
+    // Fragment addresses.  Row-major images: chunk 2t + hi of row r sits at byte r * 256 + 16 ((2t + hi) ^ (r % 16)),
+    // which is (r * 256 + 16 (hi ^ (r % 16))) ^ 32t; the q / dA tiles read row l32, the v image row 32 wave + l32
+    // (the same XOR pattern, 8 KB further per wave).  Transposed images: chunk 2t + hi of row 32db + l32 sits at
+    // db * 2048 + ((l32 * 64 + 16 (hi ^ ((l32 / 4) % 4))) ^ 32t).  One XOR per read from three per-lane bases.
+    const uint32_t rm_b = (uint32_t)l32 * 256u + 16u * (uint32_t)(hi ^ (l32 & 15));
+    const uint32_t tr_b = (uint32_t)l32 * 64u + 16u * (uint32_t)(hi ^ ((l32 >> 2) & 3));
+    const uint32_t v_b = rm_b + (uint32_t)wave * 8192u;
+
+    auto compute = [&](int buf, int it) {
+      const int q0 = tile_q0(it);
+      if (q0 + kT <= j0) return;   // every query of the tile is before this wave's keys
+      const KvfStage& sg = st[buf];
+      // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key; the accumulators start from
+      // -lse and -Delta, so the MFMAs return s - lse and dP - Delta
+      floatx16 sacc, dpacc;
+#pragma unroll
+      for (int jq = 0; jq < 4; jq++) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sg.lse2[8 * jq + 4 * hi]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sg.dl[8 * jq + 4 * hi]);
+        sacc[4 * jq] = -l4.x; sacc[4 * jq + 1] = -l4.y; sacc[4 * jq + 2] = -l4.z; sacc[4 * jq + 3] = -l4.w;
+        dpacc[4 * jq] = -d4.x; dpacc[4 * jq + 1] = -d4.y; dpacc[4 * jq + 2] = -d4.z; dpacc[4 * jq + 3] = -d4.w;
+      }
+      // per-lane bases made opaque here, so the compiler derives each address inside the tile (one XOR) instead of
+      // holding every fragment's address in a register across the loop
+      uint32_t rb = rm_b, tb = tr_b, vbb = v_b;
+      asm volatile("" : "+v"(rb), "+v"(tb), "+v"(vbb));
+      const uint32_t qs_a = lds_addr(sg.qs), xs_a = lds_addr(sg.xs), v_a = lds_addr(vimg);
+      const uint32_t dat_a = lds_addr(sg.dat), qts_a = lds_addr(sg.qts);
+      // LDS operands two k-steps ahead of their MFMAs (scheduling barriers keep the order)
+      half8 qwin[2];
+      bf16v8 xwin[2], vwin[2];
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        qwin[t] = lds_h8(qs_a + (rb ^ (32u * t)));
+        xwin[t] = lds_b8(xs_a + (rb ^ (32u * t)));
+        vwin[t] = lds_b8(v_a + (vbb ^ (32u * t)));
+      }
+#pragma unroll
+      for (int t = 0; t < 8; t++) {
+        const half8 qa = qwin[t & 1];
+        const bf16v8 xa = xwin[t & 1], vb = vwin[t & 1];
+        if (t + 2 < 8) {
+          qwin[t & 1] = lds_h8(qs_a + (rb ^ (32u * (t + 2))));
+          xwin[t & 1] = lds_b8(xs_a + (rb ^ (32u * (t + 2))));
+          vwin[t & 1] = lds_b8(v_a + (vbb ^ (32u * (t + 2))));
+        }
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, as_half8(kf[t]), sacc, 0, 0, 0);
+        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, vb, dpacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the first two operands of the dV product, read while the exponentials run
+      // transposed-image operand f (f % 8 = 4t + db): dA^T for f < 8, q_hat^T after
+      auto tfrag = [&](int f) {
+        return lds_b8((f < 8 ? dat_a : qts_a) + 2048u * (uint32_t)(f & 3) + (tb ^ (32u * (uint32_t)((f >> 2) & 1))));
+      };
+      bf16v8 twin[2];
+#pragma unroll
+      for (int f = 0; f < 2; f++) twin[f] = tfrag(f);
+      // P = exp2(s - lse), masked only where the diagonal or the sequence end cuts the tile (wave-uniform test)
+      const bool inside = q0 >= j0 + 31 && q0 + 31 < a.S && j0 + 31 < a.S;
+      if (inside) {
+#pragma unroll
+        for (int j = 0; j < 16; j++) sacc[j] = __builtin_amdgcn_exp2f(sacc[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          const int qi = q0 + 8 * (j >> 2) + 4 * hi + (j & 3);
+          sacc[j] = (qi < a.S && key <= qi) ? __builtin_amdgcn_exp2f(sacc[j]) : 0.f;
+        }
+      }
+      const bf16v8 pb[2] = {c8_to_bf16(sacc, 0), c8_to_bf16(sacc, 8)};
+#pragma unroll
+      for (int j = 0; j < 16; j++) sacc[j] *= dpacc[j];   // dS = P (dP - Delta)
+      const bf16v8 sb[2] = {c8_to_bf16(sacc, 0), c8_to_bf16(sacc, 8)};
+      // dV^T += dA^T P (f = 0..7), then dK_hat^T += q_hat^T dS (f = 8..15); f % 8 = 4t + db
+#pragma unroll
+      for (int f = 0; f < 16; f++) {
+        const bf16v8 ta = twin[f & 1];
+        const int n = f + 2;
+        if (n < 16) twin[f & 1] = tfrag(n);
+        if (f < 8) accv[f & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, pb[f >> 2], accv[f & 3], 0, 0, 0);
+        else acck[f & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta, sb[(f >> 2) & 1], acck[f & 3], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    if (n_it > 0) {
+      load_stage(0, 0);
+      store_stage(0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the v image and the first tiles, loaded into LDS without compiler waits
+    __syncthreads();
+    auto step = [&](int it, int buf) {
+      const bool more = it + 1 < n_it;
+      if (more) load_stage(it + 1, buf ^ 1);
+      compute(buf, it);
+      asm volatile("" ::: "memory");   // keep the small arrays' stores after the compute (see bwd_kv_kernel)
+      if (more) store_stage(buf ^ 1);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+    };
+    for (int it = 0; it < n_it; it += 2) {
+      step(it, 0);
+      if (it + 1 < n_it) step(it + 1, 1);
+    }
+
+    // outputs: C layout reg j of block db is dim 32db + 8(j/4) + 4hi + j%4 of this lane's key
+    if (key < a.S) {
+      uint16_t* dvr = a.dv + (((int64_t)b * a.S + key) * a.Hkv + kvh) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; db++)
+#pragma unroll
+        for (int jq = 0; jq < 4; jq++) {
+          const int d = 32 * db + 8 * jq + 4 * hi;
+          *reinterpret_cast<uint2*>(dvr + d) = make_uint2(pack_bf16(accv[db][4 * jq], accv[db][4 * jq + 1]),
+                                                          pack_bf16(accv[db][4 * jq + 2], accv[db][4 * jq + 3]));
+        }
+    }
+    // dk back through RoPE and the key RMSNorm; the block's share of dw_k into its partial (sums in the tile buffers,
+    // free after the loop's last barrier)
+    float (*red)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&st[0]);
+    const int64_t row = ((int64_t)b * a.S + key) * a.Hkv + kvh;
+    const bool valid = key < a.S;
+    norm_rope_bwd_rows(acck, valid ? a.k + row * kHeadDim : nullptr, a.kw, valid ? a.dk + row * kHeadDim : nullptr,
+                       key, a, hi, l32, red[wave]);
+    __syncthreads();
+    if (tid < kHeadDim) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; w++) sum += red[w][tid];
+      a.dw_part[((int64_t)a.n_qblk + (int64_t)kb * n_units + unit) * kHeadDim + tid] = sum;
+    }
+  };
+  if (2 * slot + 1 == nkb) {
+    run(slot, std::false_type{});
+  } else {
+    run(nkb - 1 - slot, std::false_type{});
+    __syncthreads();   // the second block's loads go to the v image and the buffers the weight-gradient sums used
+    run(slot, std::true_type{});
+  }
+}
+
 // ------------------------------------------------------------------------------------------ dQ
 struct QStage {
   uint16_t ks[kT * kHeadDim];      // k_hat fp16 [32 keys][128], row-major image
@@ -761,10 +1008,17 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+int bwd_k_blocks(int32_t S, int32_t window) { return window > 0 ? (S + 127) / 128 : (S + kKvfKeys - 1) / kKvfKeys; }
+
 hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st) {
-  // causal layers pair the key blocks (two per work-group, the middle one alone when their count is odd)
-  const int nkb = (a.S + 127) / 128;
-  const dim3 grid(a.B * a.Hkv * (a.window > 0 ? nkb : (nkb + 1) / 2));
+  // causal layers: dK and dV in one kernel, key blocks paired (two per work-group, the middle one alone when their
+  // count is odd)
+  if (a.window == 0) {
+    const int nkb = bwd_k_blocks(a.S, 0);
+    hipLaunchKernelGGL(bwd_kvf_kernel, dim3(a.B * a.Hkv * ((nkb + 1) / 2)), dim3(512), 0, st, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(a.B * a.Hkv * bwd_k_blocks(a.S, a.window));
   hipLaunchKernelGGL(bwd_kv_kernel<false>, grid, dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

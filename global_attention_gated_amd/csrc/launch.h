@@ -141,7 +141,7 @@ struct BwdArgs {
   uint16_t* kt;           // [B][Hkv][D][Sp] bf16 k_hat transposed
   float* dw_part;         // [n_qblk + n_kblk][D]: per-work-group partials of dw_q (dQ kernel), then of dw_k (dK)
   int32_t n_qblk;         // work-groups of the dQ kernel: B * Hkv * ceil(S / 32)
-  int32_t n_kblk;         // work-groups of the dK kernel: B * Hkv * ceil(S / 128)
+  int32_t n_kblk;         // key blocks of the dK kernels: B * Hkv * bwd_k_blocks(S, window)
   int32_t B, S, Sp, Hq, Hkv, G;
   int32_t window;         // 0 for a global layer
   int32_t rot_pairs;
@@ -192,6 +192,8 @@ hipError_t launch_fp8_quantize(const uint16_t* x, uint8_t* q, int64_t n, const f
 hipError_t launch_bwd_dw_zero(float* dqw, float* dkw, hipStream_t st);   // D = 128 floats each
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_kv(const BwdArgs& a, hipStream_t st);
+// key blocks (dw_k partials per (sequence, KV head)) of the key-centric backward: 256 keys (causal) or 128 (window)
+int bwd_k_blocks(int32_t S, int32_t window);
 hipError_t launch_bwd_q(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_dw_reduce(const BwdArgs& a, hipStream_t st);
 hipError_t launch_fp8_finalize(const Fp8State& s, int32_t idx, const Fp8Blocks& nb, hipStream_t st);

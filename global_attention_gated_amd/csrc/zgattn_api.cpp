@@ -631,7 +631,7 @@ int backward_common(bool gated, const void* q, const void* k, const void* v, con
   a.kt = reinterpret_cast<uint16_t*>(w + L.kt);
   a.dw_part = reinterpret_cast<float*>(w + L.dw_part);
   a.n_qblk = B * Hkv * ((S + 31) / 32);
-  a.n_kblk = B * Hkv * ((S + 127) / 128);
+  a.n_kblk = B * Hkv * bwd_k_blocks(S, gated ? window : 0);
   a.B = B; a.S = S; a.Sp = (S + 127) / 128 * 128; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.window = gated ? window : 0;
   a.rot_pairs = R / 2;

@@ -66,7 +66,9 @@ def _check(g, ref, ref16, gated, tag):
 CASES = [(True, 1, 300, 8, 2, 128), (False, 1, 257, 8, 2, 0), (True, 2, 129, 4, 1, 16), (True, 1, 33, 4, 1, 128),
          (False, 1, 1, 4, 1, 0), (True, 1, 1, 4, 1, 128),
          # window 1 (no score gradient), a window wider than the tile ring, 3 sequences x 4 KV heads, ragged ends
-         (True, 1, 97, 4, 1, 1), (True, 1, 400, 4, 1, 256), (True, 3, 70, 16, 4, 32), (False, 3, 161, 16, 4, 0)]
+         (True, 1, 97, 4, 1, 1), (True, 1, 400, 4, 1, 256), (True, 3, 70, 16, 4, 32), (False, 3, 161, 16, 4, 0),
+         # causal: three 256-key blocks (a pair and the middle one alone), the last one past the sequence's end
+         (False, 2, 600, 8, 2, 0)]
 
 
 @pytest.mark.parametrize("gated,B,S,Hq,Hkv,W", CASES)
