@@ -95,6 +95,30 @@ __device__ __forceinline__ bf16v8 lds_b8(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) bf16v8*>((lds_byte*)(uintptr_t)addr);
 }
 
+// A load of 16 bytes per lane from a buffer into LDS at m0 + 16 * lane, written out so that the compiler does not
+// track it.  Its wait-count pass cannot always tell these writes (into one stage buffer) from the compute's LDS reads
+// (of the other), and then waits for each prefetch right after issuing it.  The kernel that uses it orders these
+// loads itself: s_waitcnt vmcnt(0) and a barrier before any read of their data.  The compiler's own vector-memory
+// waits stay correct (loads complete in order; an untracked younger load only makes them wait longer).
+// desc: buffer descriptor; lds: byte address in LDS; both wave-uniform.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t buf_desc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)) & 0xffffu;
+  const uint32_t n = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
+  return (u32x4_t){lo, hi, n, 0x00020000u};
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved, and declared clobbered: nothing here keeps it
+__device__ __forceinline__ void dma16(const u32x4_t& desc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(desc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Byte offsets of a lane's 16-byte sources when wave w copies the 1 KB blocks 2w, 2w+1 of an 8 KB tile:
 // row-major (block j = rows 4j..4j+3; source rows `stride` bytes apart) and transposed (block j = rows 16j..16j+15).
 __device__ __forceinline__ uint32_t rm_src(int wave, int jj, int lane, uint32_t stride) {
@@ -615,13 +639,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       // (wave-uniform; readfirstlane keeps the descriptor in scalar registers, which the min / max would not)
       const int rows = __builtin_amdgcn_readfirstlane(max(0, min(kKvfKeys, a.S - jb0)));
       const uint32_t vbytes = rows > 0 ? (uint32_t)(rows - 1) * vstride + kHeadDim * 2 : 0u;
-      const __amdgpu_buffer_rsrc_t rv =
-          rsrc(a.v + (((int64_t)b * a.S + min(jb0, a.S - 1)) * a.Hkv + kvh) * kHeadDim, vbytes);
+      const u32x4_t rv = buf_desc(a.v + (((int64_t)b * a.S + min(jb0, a.S - 1)) * a.Hkv + kvh) * kHeadDim, vbytes);
 #pragma unroll
       for (int jj = 0; jj < 8; jj++) {
         const int blk = 8 * wave + jj, row = 4 * blk + (lane >> 4);
         const uint32_t off = (uint32_t)row * vstride + 16u * (uint32_t)((lane & 15) ^ (row & 15));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vimg + blk * 512), 16, (int)off, 0, 0, 0);
+        dma16(rv, lds_addr(vimg + blk * 512), off);
       }
     }
     // this lane's k_hat row (fp16, the score operand), K-steps of 16 dims; rows past the workspace clamp to its last
@@ -651,14 +674,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int q0 = tile_q0(it);
       const int64_t bh = (int64_t)b * a.Hq + hq;
       KvfStage& sg = st[buf];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(a.qh16 + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2),
-                                               (lds_void*)(sg.qs + wave * 512), 16, (int)rm_o, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(a.da + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2),
-                                               (lds_void*)(sg.xs + wave * 512), 16, (int)rm_o, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(a.dat + bh * kHeadDim * a.Sp + q0, (uint32_t)(kHeadDim * a.Sp - q0) * 2),
-                                               (lds_void*)(sg.dat + wave * 512), 16, (int)tr_o, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(a.qt + bh * kHeadDim * a.Sp + q0, (uint32_t)(kHeadDim * a.Sp - q0) * 2),
-                                               (lds_void*)(sg.qts + wave * 512), 16, (int)tr_o, 0, 0, 0);
+      dma16(buf_desc(a.qh16 + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2), lds_addr(sg.qs + wave * 512), rm_o);
+      dma16(buf_desc(a.da + (bh * a.Sp + q0) * kHeadDim, kT * kHeadDim * 2), lds_addr(sg.xs + wave * 512), rm_o);
+      dma16(buf_desc(a.dat + bh * kHeadDim * a.Sp + q0, (uint32_t)(kHeadDim * a.Sp - q0) * 2), lds_addr(sg.dat + wave * 512),
+            tr_o);
+      dma16(buf_desc(a.qt + bh * kHeadDim * a.Sp + q0, (uint32_t)(kHeadDim * a.Sp - q0) * 2), lds_addr(sg.qts + wave * 512),
+            tr_o);
       if (tid < 64) pf = pf_src[bh * a.Sp + q0 + (tid & 31)];
     };
     auto store_stage = [&](int buf) {
@@ -694,23 +715,21 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       asm volatile("" : "+v"(rb), "+v"(tb), "+v"(vbb));
       const uint32_t qs_a = lds_addr(sg.qs), xs_a = lds_addr(sg.xs), v_a = lds_addr(vimg);
       const uint32_t dat_a = lds_addr(sg.dat), qts_a = lds_addr(sg.qts);
-      // LDS operands two k-steps ahead of their MFMAs (scheduling barriers keep the order)
-      half8 qwin[2];
-      bf16v8 xwin[2], vwin[2];
-#pragma unroll
-      for (int t = 0; t < 2; t++) {
-        qwin[t] = lds_h8(qs_a + (rb ^ (32u * t)));
-        xwin[t] = lds_b8(xs_a + (rb ^ (32u * t)));
-        vwin[t] = lds_b8(v_a + (vbb ^ (32u * t)));
-      }
+      // LDS operands one k-step ahead of their MFMAs (scheduling barriers keep the order; two ahead would not fit
+      // the registers without spill reloads in the loop, whose waits would also wait for the prefetch)
+      half8 qwin;
+      bf16v8 xwin, vwin;
+      qwin = lds_h8(qs_a + rb);
+      xwin = lds_b8(xs_a + rb);
+      vwin = lds_b8(v_a + vbb);
 #pragma unroll
       for (int t = 0; t < 8; t++) {
-        const half8 qa = qwin[t & 1];
-        const bf16v8 xa = xwin[t & 1], vb = vwin[t & 1];
-        if (t + 2 < 8) {
-          qwin[t & 1] = lds_h8(qs_a + (rb ^ (32u * (t + 2))));
-          xwin[t & 1] = lds_b8(xs_a + (rb ^ (32u * (t + 2))));
-          vwin[t & 1] = lds_b8(v_a + (vbb ^ (32u * (t + 2))));
+        const half8 qa = qwin;
+        const bf16v8 xa = xwin, vb = vwin;
+        if (t + 1 < 8) {
+          qwin = lds_h8(qs_a + (rb ^ (32u * (t + 1))));
+          xwin = lds_b8(xs_a + (rb ^ (32u * (t + 1))));
+          vwin = lds_b8(v_a + (vbb ^ (32u * (t + 1))));
         }
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa, as_half8(kf[t]), sacc, 0, 0, 0);
         dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, vb, dpacc, 0, 0, 0);
