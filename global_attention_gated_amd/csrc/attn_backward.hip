@@ -214,8 +214,8 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
         delta += __shfl_xor(delta, 2);
         delta += __shfl_xor(delta, 1);
         if (c == 0) {
-          a.delta[(int64_t)bh * a.Sp + s] = delta;
-          a.lse2[(int64_t)bh * a.Sp + s] = a.lse[(int64_t)bh * a.S + s] * kLog2e;
+          a.ndelta[(int64_t)bh * a.Sp + s] = -delta;
+          a.nlse2[(int64_t)bh * a.Sp + s] = -(a.lse[(int64_t)bh * a.S + s] * kLog2e);
         }
       } else {
         t1 = pack8(f);                                            // k_hat in its bf16 cache form
@@ -226,8 +226,8 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
         *reinterpret_cast<uint4*>(a.qh16 + wrow) = t1;
         *reinterpret_cast<uint4*>(a.da + wrow) = t2;
         if (c == 0) {
-          a.delta[(int64_t)bh * a.Sp + s] = 0.f;
-          a.lse2[(int64_t)bh * a.Sp + s] = INFINITY;
+          a.ndelta[(int64_t)bh * a.Sp + s] = 0.f;
+          a.nlse2[(int64_t)bh * a.Sp + s] = -INFINITY;
         }
       } else {
         *reinterpret_cast<uint4*>(a.kh16 + wrow) = t1;
@@ -349,8 +349,8 @@ struct KvStage {
   uint16_t qs[kT * kHeadDim];           // q_hat' fp16 [32 queries][128], row-major image
   uint16_t xs[DK ? kT * kHeadDim : 8];  // dK: dA bf16 [32][128], row-major image
   uint16_t xts[kHeadDim * kT];          // dV: dA^T, dK: q_hat^T, bf16 [128][32], transposed image
-  float lse2[kT];
-  float dl[kT];
+  float nlse2[kT];   // -lse * log2(e) of the tile's queries
+  float ndl[kT];     // -Delta
 };
 
 // Key-centric: a work-group owns 128 keys of one (sequence, KV head), one wave per 32 keys, and walks the query
@@ -419,8 +419,8 @@ bwd_kv_kernel(BwdArgs a) {
     // becomes a load of the pointer from the argument block at a per-lane offset, and its wait in the loop would also
     // wait for the tile loads.
     const float* pf_src = reinterpret_cast<const float*>(
-        reinterpret_cast<uintptr_t>(a.lse2) +
-        (tid >= 32 ? reinterpret_cast<uintptr_t>(a.delta) - reinterpret_cast<uintptr_t>(a.lse2) : (uintptr_t)0));
+        reinterpret_cast<uintptr_t>(a.nlse2) +
+        (tid >= 32 ? reinterpret_cast<uintptr_t>(a.ndelta) - reinterpret_cast<uintptr_t>(a.nlse2) : (uintptr_t)0));
     const uint32_t rm_o[2] = {rm_src(wave, 0, lane, kHeadDim * 2), rm_src(wave, 1, lane, kHeadDim * 2)};
     const uint32_t tr_o[2] = {tr_src(wave, 0, lane, (uint32_t)a.Sp * 2), tr_src(wave, 1, lane, (uint32_t)a.Sp * 2)};
     // the group's heads inside each tile
@@ -440,8 +440,8 @@ bwd_kv_kernel(BwdArgs a) {
     // the small arrays, once their loads are in; the tile loads before them retire with them (in order)
     auto store_stage = [&](int buf) {
       KvStage<DK>& s = st[buf];
-      if (tid < 32) s.lse2[tid] = pf;
-      else if (DK && tid < 64) s.dl[tid - 32] = pf;
+      if (tid < 32) s.nlse2[tid] = pf;
+      else if (DK && tid < 64) s.ndl[tid - 32] = pf;
     };
 
     auto compute = [&](int buf, int it) {
@@ -449,15 +449,15 @@ bwd_kv_kernel(BwdArgs a) {
       if (q0 + kT <= j0 || q0 >= wq_end) return;            // no query of the tile sees this wave's keys
       const KvStage<DK>& s = st[buf];
       // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key.  The accumulators start from
-      // -lse (scores) and -Delta (dP), so the MFMAs return s - lse and dP - Delta.
+      // -lse (scores) and -Delta (dP), stored negated, so the MFMAs return s - lse and dP - Delta.
       floatx16 sacc, dpacc;
 #pragma unroll
       for (int jq = 0; jq < 4; jq++) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s.lse2[8 * jq + 4 * hi]);
-        sacc[4 * jq] = -l4.x; sacc[4 * jq + 1] = -l4.y; sacc[4 * jq + 2] = -l4.z; sacc[4 * jq + 3] = -l4.w;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s.nlse2[8 * jq + 4 * hi]);
+        sacc[4 * jq] = l4.x; sacc[4 * jq + 1] = l4.y; sacc[4 * jq + 2] = l4.z; sacc[4 * jq + 3] = l4.w;
         if constexpr (DK) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s.dl[8 * jq + 4 * hi]);
-          dpacc[4 * jq] = -d4.x; dpacc[4 * jq + 1] = -d4.y; dpacc[4 * jq + 2] = -d4.z; dpacc[4 * jq + 3] = -d4.w;
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s.ndl[8 * jq + 4 * hi]);
+          dpacc[4 * jq] = d4.x; dpacc[4 * jq + 1] = d4.y; dpacc[4 * jq + 2] = d4.z; dpacc[4 * jq + 3] = d4.w;
         }
       }
       // the LDS operands are read two k-steps ahead of the MFMAs that use them (the scheduling barriers keep that
@@ -609,8 +609,8 @@ struct KvfStage {
   uint16_t xs[kT * kHeadDim];    // dA bf16 [32][128], row-major image
   uint16_t dat[kHeadDim * kT];   // dA^T bf16 [128][32], transposed image
   uint16_t qts[kHeadDim * kT];   // q_hat^T bf16 [128][32], transposed image
-  float lse2[kT];
-  float dl[kT];
+  float nlse2[kT];   // -lse * log2(e) of the tile's queries
+  float ndl[kT];     // -Delta
 };
 
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) bwd_kvf_kernel(BwdArgs a) {
@@ -666,8 +666,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int n_it = max(qt1 - qt0, 0) * kG;
     float pf = 0.f;
     const float* pf_src = reinterpret_cast<const float*>(
-        reinterpret_cast<uintptr_t>(a.lse2) +
-        (tid >= 32 ? reinterpret_cast<uintptr_t>(a.delta) - reinterpret_cast<uintptr_t>(a.lse2) : (uintptr_t)0));
+        reinterpret_cast<uintptr_t>(a.nlse2) +
+        (tid >= 32 ? reinterpret_cast<uintptr_t>(a.ndelta) - reinterpret_cast<uintptr_t>(a.nlse2) : (uintptr_t)0));
     auto tile_q0 = [&](int it) { return (up ? qt0 + it / kG : qt1 - 1 - it / kG) * kT; };
     auto load_stage = [&](int it, int buf) {
       const int hq = kvh * kG + it % kG;
@@ -684,8 +684,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
     auto store_stage = [&](int buf) {
       KvfStage& sg = st[buf];
-      if (tid < 32) sg.lse2[tid] = pf;
-      else if (tid < 64) sg.dl[tid - 32] = pf;
+      if (tid < 32) sg.nlse2[tid] = pf;
+      else if (tid < 64) sg.ndl[tid - 32] = pf;
     };
     // Fragment addresses.  Row-major images: chunk 2t + hi of row r sits at byte r * 256 + 16 ((2t + hi) ^ (r % 16)),
     // which is (r * 256 + 16 (hi ^ (r % 16))) ^ 32t; the q / dA tiles read row l32, the v image row 32 wave + l32
@@ -700,14 +700,14 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (q0 + kT <= j0) return;   // every query of the tile is before this wave's keys
       const KvfStage& sg = st[buf];
       // C layout: reg j is query q0 + 8(j/4) + 4hi + j%4, column = this lane's key; the accumulators start from
-      // -lse and -Delta, so the MFMAs return s - lse and dP - Delta
+      // -lse and -Delta (stored negated), so the MFMAs return s - lse and dP - Delta
       floatx16 sacc, dpacc;
 #pragma unroll
       for (int jq = 0; jq < 4; jq++) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sg.lse2[8 * jq + 4 * hi]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sg.dl[8 * jq + 4 * hi]);
-        sacc[4 * jq] = -l4.x; sacc[4 * jq + 1] = -l4.y; sacc[4 * jq + 2] = -l4.z; sacc[4 * jq + 3] = -l4.w;
-        dpacc[4 * jq] = -d4.x; dpacc[4 * jq + 1] = -d4.y; dpacc[4 * jq + 2] = -d4.z; dpacc[4 * jq + 3] = -d4.w;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sg.nlse2[8 * jq + 4 * hi]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sg.ndl[8 * jq + 4 * hi]);
+        sacc[4 * jq] = l4.x; sacc[4 * jq + 1] = l4.y; sacc[4 * jq + 2] = l4.z; sacc[4 * jq + 3] = l4.w;
+        dpacc[4 * jq] = d4.x; dpacc[4 * jq + 1] = d4.y; dpacc[4 * jq + 2] = d4.z; dpacc[4 * jq + 3] = d4.w;
       }
       // per-lane bases made opaque here, so the compiler derives each address inside the tile (one XOR) instead of
       // holding every fragment's address in a register across the loop
@@ -859,8 +859,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       daf[t] = *reinterpret_cast<const uint4*>(dr + 16 * t);
     }
   }
-  const float lse2 = a.lse2[bh * a.Sp + qi];
-  const float dl = a.delta[bh * a.Sp + qi];
+  const float nlse2 = a.nlse2[bh * a.Sp + qi];
+  const float ndl = a.ndelta[bh * a.Sp + qi];
   // retire the preloads (see bwd_kv_kernel)
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   floatx16 dq[4];
@@ -899,8 +899,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     floatx16 sacc, dpacc;
 #pragma unroll
     for (int j = 0; j < 16; j++) {
-      sacc[j] = -lse2;
-      dpacc[j] = -dl;
+      sacc[j] = nlse2;
+      dpacc[j] = ndl;
     }
     // the LDS operands are read two k-steps ahead of the MFMAs that use them (the scheduling barriers keep that
     // order: left alone, the compiler reads each operand right before its MFMA and waits for it there)

@@ -113,7 +113,7 @@ struct Fp8Blocks {
 };
 
 // Backward of an attention layer (training), no cache, positions 0..S-1.  Sp = S rounded up to 128; the
-// workspace arrays are zero past S (and lse2 +inf), so tiles may run over the end.
+// workspace arrays are zero past S (and nlse2 -inf), so tiles may run over the end.
 struct BwdArgs {
   const uint16_t* q;      // [B][S][Hq][D] bf16
   const uint16_t* k;      // [B][S][Hkv][D]
@@ -135,8 +135,8 @@ struct BwdArgs {
   uint16_t* qt;           // [B][Hq][D][Sp] bf16 q_hat transposed
   uint16_t* da;           // [B][Hq][Sp][D] bf16 dA
   uint16_t* dat;          // [B][Hq][D][Sp] bf16 dA transposed
-  float* lse2;            // [B][Hq][Sp] lse * log2(e)
-  float* delta;           // [B][Hq][Sp] dout . out
+  float* nlse2;           // [B][Hq][Sp] -lse * log2(e) (negated: the score accumulators start from it)
+  float* ndelta;          // [B][Hq][Sp] -(dout . out) (negated: the dP accumulators start from it)
   uint16_t* kh16;         // [B][Hkv][Sp][D] fp16 k_hat (bf16 values)
   uint16_t* kt;           // [B][Hkv][D][Sp] bf16 k_hat transposed
   float* dw_part;         // [n_qblk + n_kblk][D]: per-work-group partials of dw_q (dQ kernel), then of dw_k (dK)

@@ -625,8 +625,8 @@ int backward_common(bool gated, const void* q, const void* k, const void* v, con
   a.qt = reinterpret_cast<uint16_t*>(w + L.qt);
   a.da = reinterpret_cast<uint16_t*>(w + L.da);
   a.dat = reinterpret_cast<uint16_t*>(w + L.dat);
-  a.lse2 = reinterpret_cast<float*>(w + L.lse2);
-  a.delta = reinterpret_cast<float*>(w + L.delta);
+  a.nlse2 = reinterpret_cast<float*>(w + L.lse2);
+  a.ndelta = reinterpret_cast<float*>(w + L.delta);
   a.kh16 = reinterpret_cast<uint16_t*>(w + L.kh16);
   a.kt = reinterpret_cast<uint16_t*>(w + L.kt);
   a.dw_part = reinterpret_cast<float*>(w + L.dw_part);
