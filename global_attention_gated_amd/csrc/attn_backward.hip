@@ -43,7 +43,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kT = 32;          // query / key tile of the MFMA kernels
 constexpr int kG = 4;           // GQA group (query heads per KV head), the one shape the host accepts
 constexpr int kPrepTok = 64;    // tokens per prep work-group
-constexpr int kPrepTS = 72;     // LDS row stride (halves) of the prep transpose tiles [128][64]
+constexpr int kPrepTS = 64;     // LDS row (halves) of the prep transpose tiles [128 dims][64 tokens]
+// Element (dim d, token column col) of a prep transpose tile: 16-byte chunk col / 8 of row d sits at chunk position
+// (col / 8) ^ (d / 8 % 8).  The writes of one instruction (dims 8c + e of 16 lanes c, one token) then fall in 8
+// different chunk positions instead of one bank pair (rows 8 apart are 1 KB apart), and a chunk still reads as one
+// 16-byte load.
+__device__ __forceinline__ int prep_off(int d, int col) {
+  return d * kPrepTS + ((((col >> 3) ^ (d >> 3)) & 7) << 3) + (col & 7);
+}
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima (no wait)
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
 
@@ -239,8 +246,8 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
     const int col = (row & ~15) | (4 * (qd == 1 ? 2 : qd == 2 ? 1 : qd)) | (row & 3);
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-      T1[(8 * c + e) * kPrepTS + col] = p1[e];
-      if (qmode) T2[(8 * c + e) * kPrepTS + col] = p2[e];
+      T1[prep_off(8 * c + e, col)] = p1[e];
+      if (qmode) T2[prep_off(8 * c + e, col)] = p2[e];
     }
   }
   __syncthreads();
@@ -251,10 +258,10 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < 4; k++) {
     *reinterpret_cast<uint4*>(dst1 + trow + 8 * k) =
-        *reinterpret_cast<const uint4*>(&T1[d * kPrepTS + 32 * half + 8 * k]);
+        *reinterpret_cast<const uint4*>(&T1[prep_off(d, 32 * half + 8 * k)]);
     if (qmode)
       *reinterpret_cast<uint4*>(a.dat + trow + 8 * k) =
-          *reinterpret_cast<const uint4*>(&T2[d * kPrepTS + 32 * half + 8 * k]);
+          *reinterpret_cast<const uint4*>(&T2[prep_off(d, 32 * half + 8 * k)]);
   }
 }
 
