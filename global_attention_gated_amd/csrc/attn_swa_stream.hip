@@ -149,14 +149,20 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     kraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
     vraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
   };
-  auto store_kv = [&](int tile) {
-    const int slot = tile % kRing;
-    float wk[8], f[8];
-    unpack8(*reinterpret_cast<const uint4*>(Wn + kHeadDim + 8 * lc), wk);
-    unpack8(kraw, f);
-    norm_rope8_g16_w(f, wk, lc, (int64_t)tile * kTK + lr, a.eps, a.rot_pairs, Fr);
-    // the KV-cache value of k_hat (bf16, nearest-even), held exactly as fp16 for the MFMA
-    *reinterpret_cast<uint4*>(Ks + k_off(slot, lr, lc)) = bf16x8_to_f16x8(pack8(f));
+  // store_kv(tile, cached): cached tiles hold k_hat already (the cache ring's bf16 values), the chunk's own tiles
+  // raw k, whose k_hat is computed here at the key's absolute position
+  auto store_kv = [&](int tile, bool cached) {
+    const int slot = (tile % kRing + kRing) % kRing;
+    if (cached) {
+      *reinterpret_cast<uint4*>(Ks + k_off(slot, lr, lc)) = bf16x8_to_f16x8(kraw);
+    } else {
+      float wk[8], f[8];
+      unpack8(*reinterpret_cast<const uint4*>(Wn + kHeadDim + 8 * lc), wk);
+      unpack8(kraw, f);
+      norm_rope8_g16_w(f, wk, lc, (int64_t)a.pos0 + (int64_t)tile * kTK + lr, a.eps, a.rot_pairs, Fr);
+      // the KV-cache value of k_hat (bf16, nearest-even), held exactly as fp16 for the MFMA
+      *reinterpret_cast<uint4*>(Ks + k_off(slot, lr, lc)) = bf16x8_to_f16x8(pack8(f));
+    }
     // v: dim 8lc+e of key lr -> V^T row 8lc+e, stored column vt_col(lr)
     const uint4 v8 = bf16x8_to_f16x8(vraw);
     const uint32_t vw[4] = {v8.x, v8.y, v8.z, v8.w};
@@ -201,14 +207,27 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   if (tid < kMaxRotPairs) Fr[tid] = a.inv_freq_rev[tid];
   lds_barrier();
 
-  // ---- prologue: the first step's window tiles, then its q rows
+  // ---- prologue: the first step's window tiles, then its q rows.  Tiles before the chunk (tile < 0) hold the
+  // positions before pos0: from the cache's ring when there is one (slot p mod W of the sequence's KV head; positions
+  // below 0 stay zero), otherwise zero (and masked).
   {
     const int T0 = p_start / kTK;
     for (int j = jmax; j >= 0; j--) {
       const int tile = T0 - j;
-      if (tile < 0) continue;
+      if (tile < 0) {
+        if (!a.ck) continue;
+        const int64_t p = (int64_t)a.pos0 + (int64_t)tile * kTK + lr;
+        kraw = vraw = make_uint4(0u, 0u, 0u, 0u);
+        if (p >= 0) {
+          const int64_t row = (((int64_t)b * a.Hkv + kvh) * a.window + p % a.window) * kHeadDim + 8 * lc;
+          kraw = *reinterpret_cast<const uint4*>(a.ck + row);
+          vraw = *reinterpret_cast<const uint4*>(a.cv + row);
+        }
+        store_kv(tile, true);
+        continue;
+      }
       load_kv(tile);
-      store_kv(tile);
+      store_kv(tile, false);
     }
   }
   load_rows(qb, QS, p_start, true);
@@ -228,7 +247,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
       const int pi = 4 * (4 * t + g) + m;
       rc[t][m] = 1.0f; rs[t][m] = 0.0f; dc[t][m] = 1.0f; dsn[t][m] = 0.0f;
       if (pi < a.rot_pairs) {
-        rope_cs((int64_t)p_start + 16 * half + l16, Fr[pi], rc[t][m], rs[t][m]);
+        rope_cs((int64_t)a.pos0 + p_start + 16 * half + l16, Fr[pi], rc[t][m], rs[t][m]);
         rope_cs(kStep, Fr[pi], dc[t][m], dsn[t][m]);
       }
     }
@@ -254,7 +273,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
 #pragma unroll
         for (int m = 0; m < 4; m++) {
           const int pi = 4 * (4 * t + g) + m;
-          if (pi < a.rot_pairs) rope_cs((int64_t)i, Fr[pi], rc[t][m], rs[t][m]);
+          if (pi < a.rot_pairs) rope_cs((int64_t)a.pos0 + i, Fr[pi], rc[t][m], rs[t][m]);
         }
     }
 
@@ -290,7 +309,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
             rc[t][m] = c1;
           }
         } else {
-          rope8(f[t], 8 * (4 * t + g), min(i, a.S - 1), a.rot_pairs, Fr);
+          rope8(f[t], 8 * (4 * t + g), (int64_t)a.pos0 + min(i, a.S - 1), a.rot_pairs, Fr);
         }
 #pragma unroll
         for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)f[t][e];
@@ -333,14 +352,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
       sacc[f % kBlocks] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[f / kBlocks], sacc[f % kBlocks], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // mask: key visible iff 0 <= i - key < min(W, i + 1) (one unsigned compare); blocks wholly inside every
+    // mask: key visible iff 0 <= i - key < min(W, pos0 + i + 1) (one unsigned compare; positions are chunk-local,
+    // the bound keeps keys at absolute positions >= 0); blocks wholly inside every
     // window of the wave's 16 queries skip it.  C layout: lane (l16, g) holds keys 4g .. 4g+3 of the block.
     {
-      const unsigned lim = (unsigned)min(a.window, i + 1);
+      const unsigned lim = (unsigned)min((int64_t)a.window, (int64_t)a.pos0 + i + 1);   // keys at positions >= 0
 #pragma unroll
       for (int kb = 0; kb < kBlocks; kb++) {
         const int kt = (T - (kRing - 1)) * kTK + 16 * kb;
-        if (!(kt >= 0 && kt + 15 <= qlo && kt >= qlo + 16 - a.window)) {
+        if (!(kt >= -a.pos0 && kt + 15 <= qlo && kt >= qlo + 16 - a.window)) {
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             const int key = kt + 4 * g + e;
@@ -391,7 +411,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     lds_barrier();                   // ... and every wave's; all waves are past the ring reads
     if (more) {
       ZG_WAIT_VM(4);                 // the next key/value tile (the next step's q rows may stay in flight)
-      store_kv(T + 1);               // into the slot of tile T-4, which no later step reads
+      store_kv(T + 1, false);        // into the slot of tile T-4, which no later step reads
     }
 #pragma unroll
     for (int db = 0; db < 8; db++) {

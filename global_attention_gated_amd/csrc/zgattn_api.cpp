@@ -305,6 +305,23 @@ namespace {
 
 // validate_only: check every argument (the tensor pointers need only be non-null) and return without
 // enqueueing anything (used by the layer entry points before they launch the projections).
+// After a gated chunk with a cache has attended (stream order): its last min(S, W) keys (k_hat, recomputed at their
+// absolute positions) and values into the layer's ring, slot position mod W.
+int ring_write(const void* k, const void* v, const void* kw, const LayerDesc* ld, int32_t B, int32_t S, int32_t Hkv,
+               int32_t window, int64_t pos0, int rot_pairs, float eps, const double* inv_freq_rev, hipStream_t st) {
+  RingWriteArgs ra{};
+  ra.k = static_cast<const uint16_t*>(k);
+  ra.v = static_cast<const uint16_t*>(v);
+  ra.kw = static_cast<const uint16_t*>(kw);
+  ra.kring = ld->k; ra.vring = ld->v;
+  ra.B = B; ra.S = S; ra.Hkv = Hkv; ra.W = window; ra.n = S < window ? S : window; ra.pos0 = pos0;
+  ra.rot_pairs = rot_pairs; ra.eps = eps;
+  std::memcpy(ra.inv_freq_rev, inv_freq_rev, sizeof ra.inv_freq_rev);
+  hipError_t e = launch_ring_write(ra, st);
+  if (e != hipSuccess) return hip_fail(e, "ring write launch");
+  return ZG_OK;
+}
+
 int prefill_common(bool gated, const void* q, const void* k, const void* v, const void* gate, const void* qw,
                    const void* kw, void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
                    int32_t window, int32_t R, double base, float eps, int64_t pos0, zg_kv_cache* cache,
@@ -363,8 +380,10 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rot_pairs = R / 2;
   if (lse && cache) return fail(ZG_EINVAL, "%s: the training forward takes no cache", fn);
-  if (gated && !cache && G == 4 && window <= 128) {
-    // streaming SWA kernel: k_hat computed in its tile loader, no workspace pass
+  if (gated && G == 4 && window <= 128) {
+    // streaming SWA kernel: k_hat computed in its tile loader, no workspace pass; with a cache, the window's keys
+    // before the chunk come from the layer's ring, and the chunk's last keys go to the ring afterwards
+    const LayerDesc* ld = cache ? &cache->layers[layer - 1] : nullptr;
     SwaStreamArgs sa{};
     sa.q = static_cast<const uint16_t*>(q);
     sa.k = static_cast<const uint16_t*>(k);
@@ -381,10 +400,19 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
     sa.n_units = B * Hkv;
     sa.run = swa_stream_run_length(S, sa.n_units);
     sa.lse = lse;
+    sa.pos0 = (int32_t)(cache ? pos0 : 0);
+    if (cache && pos0 > 0) { sa.ck = ld->k; sa.cv = ld->v; }
     fill_inv_freq(sa.inv_freq_rev, rot_pairs, R, base);
-    ScopedTimer tm("attn_swa", st);
-    hipError_t e = launch_swa_stream(sa, st);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    {
+      ScopedTimer tm("attn_swa", st);
+      hipError_t e = launch_swa_stream(sa, st);
+      if (e != hipSuccess) return hip_fail(e, "attention launch");
+    }
+    if (cache) {
+      const int rc = ring_write(k, v, kw, ld, B, S, Hkv, window, pos0, rot_pairs, eps, sa.inv_freq_rev, st);
+      if (rc) return rc;
+      for (int b = 0; b < B; b++) cache->length[(size_t)(layer - 1) * B + b] = pos0 + S;
+    }
     return ZG_OK;
   }
   // tile path: stage the keys the chunk sees (its own, and with a cache the earlier positions from the cache) as
@@ -440,16 +468,8 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   // a gated layer with a cache: the chunk's last min(S, W) positions go to the ring (the staging has read the
   // ring's earlier contents)
   if (gated && cache) {
-    RingWriteArgs ra{};
-    ra.k = k16;
-    ra.v = v16;
-    ra.kw = static_cast<const uint16_t*>(kw);
-    ra.kring = ld->k; ra.vring = ld->v;
-    ra.B = B; ra.S = S; ra.Hkv = Hkv; ra.W = window; ra.n = S < window ? S : window; ra.pos0 = pos0;
-    ra.rot_pairs = rot_pairs; ra.eps = eps;
-    std::memcpy(ra.inv_freq_rev, sa.inv_freq_rev, sizeof ra.inv_freq_rev);
-    hipError_t e = launch_ring_write(ra, st);
-    if (e != hipSuccess) return hip_fail(e, "ring write launch");
+    const int rc = ring_write(k, v, kw, ld, B, S, Hkv, window, pos0, rot_pairs, eps, sa.inv_freq_rev, st);
+    if (rc) return rc;
   }
   if (cache)
     for (int b = 0; b < B; b++) cache->length[(size_t)(layer - 1) * B + b] = pos0 + S;

@@ -156,16 +156,41 @@ def test_gate_plus_infinity_with_a_cache_is_the_global_layer_bit_for_bit(zg):
     cache.close()
 
 
-def test_cached_first_chunk_is_the_cacheless_layer_bit_for_bit(zg):
-    """A chunk at position 0 against an empty cache runs the same staging and tile kernel as a call without a cache,
-    so the outputs agree bit for bit (global layer, and a gated layer the tile kernel takes: window above 128)."""
+@pytest.mark.parametrize("W", [200, 128])
+def test_cached_first_chunk_is_the_cacheless_layer_bit_for_bit(zg, W):
+    """A chunk at position 0 against an empty cache runs the same kernels as a call without a cache, so the outputs
+    agree bit for bit: the global layer, and the gated layer on the tile kernel (window 200) or on the streaming
+    kernel (window 128, GQA group 4, whose ring prefix is then empty)."""
     B, Hq, Hkv, S, R = 1, 16, 2, 333, 42
-    cache = zg.KVCache(n_layers=2, global_layers=[2], batch=B, n_kv_heads=Hkv, window=200, max_tokens=512)
+    if W <= 128:
+        Hq = 4 * Hkv
+    cache = zg.KVCache(n_layers=2, global_layers=[2], batch=B, n_kv_heads=Hkv, window=W, max_tokens=512)
     for layer, gated in ((1, True), (2, False)):
         L = Layer(12, layer, B, S, Hq, Hkv, gated=gated)
-        a = gpu_prefill(zg, L, gated, 200, R, 1e4, 1e-6)
-        c = gpu_prefill(zg, L, gated, 200, R, 1e4, 1e-6, pos0=0, cache=cache, layer=layer)
+        a = gpu_prefill(zg, L, gated, W, R, 1e4, 1e-6)
+        c = gpu_prefill(zg, L, gated, W, R, 1e4, 1e-6, pos0=0, cache=cache, layer=layer)
         np.testing.assert_array_equal(to_host_bits(a), to_host_bits(c))
+    cache.close()
+
+
+@pytest.mark.parametrize("W", [128, 33])
+def test_chunked_swa_stream_small_chunks_match_oracle(zg, W):
+    """Gated chunks on the streaming kernel against a cache ring (GQA group 4, W <= 128): chunks of 1, 33, 1, 97
+    and 160 positions, so the ring prefix is partly empty (pos0 < W), a chunk is shorter than a 32-position step or
+    than the window, and chunk starts fall off the 32-key tile grid; every chunk against the oracle, then the ring."""
+    B, Hq, Hkv, R, base, eps = 2, 8, 2, 42, 1e7, 1e-6
+    S_total = 292
+    cache = zg.KVCache(n_layers=2, global_layers=[2], batch=B, n_kv_heads=Hkv, window=W, max_tokens=512)
+    ocache = oracle.OracleCache(2, [2], B, Hkv, 128, W)
+    pos0 = 0
+    for S in (1, 33, 1, 97, 160):
+        L = Layer(57, 1, B, S, Hq, Hkv, gated=True, pos0=pos0, S_total=S_total)
+        got = to_host_f64(gpu_prefill(zg, L, True, W, R, base, eps, pos0=pos0, cache=cache, layer=1))
+        ref = oracle_prefill(L, True, W, R, base, eps, pos0=pos0, cache=ocache, layer=1)
+        compare(got, ref, f"W {W} chunk of {S} at {pos0}")
+        pos0 += S
+    assert cache.length(1, 0) == S_total
+    assert _cache_check(zg, cache, ocache, 1, False) < 0.01
     cache.close()
 
 
