@@ -20,6 +20,8 @@
 //     behind the compute and no registers hold data in flight beyond one key/value row per thread;
 //   - k_hat = RoPE(RMSNorm(k) w_k) is computed in the tile loader (16 lanes per key row), rounded to bf16
 //     as in the KV cache and stored as fp16, so the layer needs no separate key pass;
+//   - a chunk that continues a cached sequence (pos0 > 0) works in absolute positions (RoPE, mask), and the run's
+//     first window takes the keys before the chunk from the layer's ring (k_hat already, bf16);
 //   - the epilogue applies sigmoid(gate) in the MFMA output layout from the LDS gate rows, writes the bf16
 //     result back in place, and 16 lanes store each 256-byte output row.
 // The LDS tiles use XOR-swizzled 16-byte chunks instead of padding: reads of one chunk by 16 lanes of 16

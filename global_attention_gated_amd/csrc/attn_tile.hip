@@ -1,6 +1,6 @@
 // Tile-path prefill of the ZGCM-1 attention core for gfx950 (CDNA4, wave64, MFMA): every prefill that the streaming
-// gated-SWA kernel does not take -- global layers (one-shot, chunked against the KV cache, the training forward),
-// gated-SWA chunks that continue a cached sequence, and gated layers of other GQA groups or windows above 128.
+// gated-SWA kernel does not take -- global layers (one-shot, chunked against the KV cache, the training forward) and
+// gated layers of other GQA groups or windows above 128 (with or without a cache).
 //
 //   kv_stage_kernel    writes the keys and values a call attends to, once, as fp16 tiles in the layout that the
 //                      attention kernel copies into LDS unchanged: k_hat = RoPE(RMSNorm(k) w_k) of the chunk's own
