@@ -100,6 +100,8 @@ __device__ __forceinline__ void lds_barrier() {
 // 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8)
 #define ZG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((n) | (7 << 4) | (15 << 8))
 
+// CACHED: a chunk at pos0 > 0 whose window starts in the layer's ring; the cache-less kernel compiles without any of it.
+template <bool CACHED>
 __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char Ks[kRing * kKTile];
   __shared__ __attribute__((aligned(16))) unsigned char Vt[kRing * kVTile];
@@ -151,17 +153,18 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     kraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
     vraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
   };
-  // store_kv(tile, cached): cached tiles hold k_hat already (the cache ring's bf16 values), the chunk's own tiles
-  // raw k, whose k_hat is computed here at the key's absolute position
+  // store_kv(tile, cached): cached tiles (tile -4 .. -1, before the chunk) hold k_hat already (the cache ring's bf16
+  // values), the chunk's own tiles raw k, whose k_hat is computed here at the key's absolute position
+  const int64_t pos0 = CACHED ? (int64_t)a.pos0 : 0;
   auto store_kv = [&](int tile, bool cached) {
-    const int slot = (tile % kRing + kRing) % kRing;
+    const int slot = cached ? tile + kRing : tile % kRing;
     if (cached) {
       *reinterpret_cast<uint4*>(Ks + k_off(slot, lr, lc)) = bf16x8_to_f16x8(kraw);
     } else {
       float wk[8], f[8];
       unpack8(*reinterpret_cast<const uint4*>(Wn + kHeadDim + 8 * lc), wk);
       unpack8(kraw, f);
-      norm_rope8_g16_w(f, wk, lc, (int64_t)a.pos0 + (int64_t)tile * kTK + lr, a.eps, a.rot_pairs, Fr);
+      norm_rope8_g16_w(f, wk, lc, pos0 + (int64_t)tile * kTK + lr, a.eps, a.rot_pairs, Fr);
       // the KV-cache value of k_hat (bf16, nearest-even), held exactly as fp16 for the MFMA
       *reinterpret_cast<uint4*>(Ks + k_off(slot, lr, lc)) = bf16x8_to_f16x8(pack8(f));
     }
@@ -217,15 +220,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     for (int j = jmax; j >= 0; j--) {
       const int tile = T0 - j;
       if (tile < 0) {
-        if (!a.ck) continue;
-        const int64_t p = (int64_t)a.pos0 + (int64_t)tile * kTK + lr;
-        kraw = vraw = make_uint4(0u, 0u, 0u, 0u);
-        if (p >= 0) {
-          const int64_t row = (((int64_t)b * a.Hkv + kvh) * a.window + p % a.window) * kHeadDim + 8 * lc;
-          kraw = *reinterpret_cast<const uint4*>(a.ck + row);
-          vraw = *reinterpret_cast<const uint4*>(a.cv + row);
+        if constexpr (CACHED) {
+          const int64_t p = pos0 + (int64_t)tile * kTK + lr;
+          kraw = vraw = make_uint4(0u, 0u, 0u, 0u);
+          if (p >= 0) {
+            const int64_t row = (((int64_t)b * a.Hkv + kvh) * a.window + p % a.window) * kHeadDim + 8 * lc;
+            kraw = *reinterpret_cast<const uint4*>(a.ck + row);
+            vraw = *reinterpret_cast<const uint4*>(a.cv + row);
+          }
+          store_kv(tile, true);
         }
-        store_kv(tile, true);
         continue;
       }
       load_kv(tile);
@@ -249,7 +253,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
       const int pi = 4 * (4 * t + g) + m;
       rc[t][m] = 1.0f; rs[t][m] = 0.0f; dc[t][m] = 1.0f; dsn[t][m] = 0.0f;
       if (pi < a.rot_pairs) {
-        rope_cs((int64_t)a.pos0 + p_start + 16 * half + l16, Fr[pi], rc[t][m], rs[t][m]);
+        rope_cs(pos0 + p_start + 16 * half + l16, Fr[pi], rc[t][m], rs[t][m]);
         rope_cs(kStep, Fr[pi], dc[t][m], dsn[t][m]);
       }
     }
@@ -275,7 +279,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
 #pragma unroll
         for (int m = 0; m < 4; m++) {
           const int pi = 4 * (4 * t + g) + m;
-          if (pi < a.rot_pairs) rope_cs((int64_t)a.pos0 + i, Fr[pi], rc[t][m], rs[t][m]);
+          if (pi < a.rot_pairs) rope_cs(pos0 + i, Fr[pi], rc[t][m], rs[t][m]);
         }
     }
 
@@ -311,7 +315,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
             rc[t][m] = c1;
           }
         } else {
-          rope8(f[t], 8 * (4 * t + g), (int64_t)a.pos0 + min(i, a.S - 1), a.rot_pairs, Fr);
+          rope8(f[t], 8 * (4 * t + g), pos0 + min(i, a.S - 1), a.rot_pairs, Fr);
         }
 #pragma unroll
         for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)f[t][e];
@@ -358,11 +362,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     // the bound keeps keys at absolute positions >= 0); blocks wholly inside every
     // window of the wave's 16 queries skip it.  C layout: lane (l16, g) holds keys 4g .. 4g+3 of the block.
     {
-      const unsigned lim = (unsigned)min((int64_t)a.window, (int64_t)a.pos0 + i + 1);   // keys at positions >= 0
+      const unsigned lim = CACHED ? (unsigned)min((int64_t)a.window, pos0 + i + 1) : (unsigned)min(a.window, i + 1);
 #pragma unroll
       for (int kb = 0; kb < kBlocks; kb++) {
         const int kt = (T - (kRing - 1)) * kTK + 16 * kb;
-        if (!(kt >= -a.pos0 && kt + 15 <= qlo && kt >= qlo + 16 - a.window)) {
+        if (!(kt >= (CACHED ? -(int)pos0 : 0) && kt + 15 <= qlo && kt >= qlo + 16 - a.window)) {
 #pragma unroll
           for (int e = 0; e < 4; e++) {
             const int key = kt + 4 * g + e;
@@ -459,7 +463,8 @@ int swa_stream_run_length(int S, int n_units) {
 hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st) {
   if (a.G != kGroup || a.window < 1 || a.window > kTK * (kRing - 1) || a.run % kStep) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)a.n_units * ((a.S + a.run - 1) / a.run);
-  hipLaunchKernelGGL(attn_swa_stream_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  if (a.ck) hipLaunchKernelGGL(attn_swa_stream_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(attn_swa_stream_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -91,12 +91,12 @@ struct SwaStreamArgs {
   int32_t n_units;       // B * Hkv
   int32_t run;           // positions per work-group
   float* lse;            // [B][Hq][S] natural log of each softmax denominator (training), or null
+  double inv_freq_rev[64];
   // a chunk that continues a cached sequence: its positions are pos0 .. pos0+S-1, and the window's earlier keys come
   // from the layer's ring (k_hat and v, bf16, [B][Hkv][window][D], position p in slot p mod window); ck = null: none
-  int32_t pos0;
   const uint16_t* ck;
   const uint16_t* cv;
-  double inv_freq_rev[64];
+  int32_t pos0;
 };
 
 // Device state of FP8 operands under delayed scaling: n tensors (a projection: 0 = the input x, 1 = the weight
