@@ -9,21 +9,29 @@
 // several dependent HBM round trips per work-group for a few tiles of work; this kernel instead streams:
 //   - one work-group of 8 waves owns a run of consecutive positions of one (sequence, KV head) and walks it
 //     in steps of 32 positions; the 128 rows of a step are the 4 query heads of the group (GQA group 4) x 32
-//     positions, 16 rows per wave (wave w: head w/2, positions 16(w%2) .. +15), one query per lane column
-//     (S^T = K Q^T, O^T = V^T P^T on v_mfma_f32_16x16x32_f16).  Two waves per SIMD overlap one another's
-//     softmax, memory waits and MFMAs; the LDS (ring, gate and q tiles: 144 KiB) allows one work-group per CU;
-//   - the keys of the window live in a 5-slot LDS ring of 32-key tiles (a 32-position step with W <= 128
-//     sees at most 5 tiles); each step adds one tile.  The whole window of a step is scored at once (ten
-//     independent 16-key score chains per wave) and normalised with one exact max per query;
-//   - while a step computes, the next step's q rows and the step's gate rows (straight into LDS with buffer
-//     loads, each wave its own 16 rows) and the next key/value tile are in flight, so HBM latency hides
-//     behind the compute and no registers hold data in flight beyond one key/value row per thread;
-//   - k_hat = RoPE(RMSNorm(k) w_k) is computed in the tile loader (16 lanes per key row), rounded to bf16
+//     positions, 16 rows per wave (wave w: head w%4, positions 16(w/4) .. +15), one query per lane column
+//     (S^T = K Q^T, O^T = V^T P^T on v_mfma_f32_16x16x32_f16); the LDS (ring, gate and q rows: 160 KiB) allows
+//     one work-group per CU;
+//   - the two wave groups (waves 0-3 and 4-7; waves w and w+4 share a SIMD) run half a step apart: a step of a
+//     group is a compute phase (q_hat, the window's scores, softmax, PV) and an output phase (gate, output rows,
+//     half of the next ring tile), and one group's compute phase runs beside the other's output phase, one
+//     work-group barrier between phases;
+//   - the keys of the window live in a 6-slot LDS ring of 32-key tiles: a 32-position step with W <= 128 reads
+//     5 tiles, and the next tile is written (one half by each group) while they are read.  The whole window of
+//     a step is scored at once (ten independent 16-key score chains per wave) and normalised with one exact max
+//     per query;
+//   - each wave's q rows and gate rows go straight from HBM into its own LDS rows with buffer loads whose
+//     destination is LDS, one step ahead, and the raw key/value rows of the next ring half into registers one
+//     step ahead; no wave reads another wave's rows, so only the ring needs the barriers;
+//   - k_hat = RoPE(RMSNorm(k) w_k) is computed in the ring loader (16 lanes per key row), rounded to bf16
 //     as in the KV cache and stored as fp16, so the layer needs no separate key pass;
+//   - the queries' RoPE (pairs of the first 64 dims; more rotary dims take the tile kernel) is carried along the
+//     steps as a fixed rotation per step; a run has at most 256 steps, so the carried value is at most 256 fp32
+//     rotations from the exact angle (relative error ~3e-5, against 2^-12 for q_hat's fp16 rounding);
 //   - a chunk that continues a cached sequence (pos0 > 0) works in absolute positions (RoPE, mask), and the run's
 //     first window takes the keys before the chunk from the layer's ring (k_hat already, bf16);
 //   - the epilogue applies sigmoid(gate) in the MFMA output layout from the LDS gate rows, writes the bf16
-//     result back in place, and 16 lanes store each 256-byte output row.
+//     result back in place, and 16 lanes store each 256-byte output row of the wave.
 // The LDS tiles use XOR-swizzled 16-byte chunks instead of padding: reads of one chunk by 16 lanes of 16
 // different rows hit 16 different bank groups.
 //
@@ -36,11 +44,13 @@ namespace zg {
 namespace {
 
 constexpr int kTK = 32;        // keys per ring tile
-constexpr int kRing = 5;       // ring slots
+constexpr int kWinTiles = 5;   // ring tiles a 32-position step with W <= 128 reads (T-4 .. T)
+constexpr int kRing = 6;       // ring slots: the window's 5 tiles and the next tile, written while they are read
 constexpr int kStep = 32;      // positions per step
 constexpr int kGroup = 4;      // query heads per KV head handled here
 constexpr int kThreads = 512;  // 8 waves
-constexpr int kBlocks = 2 * kRing;   // 16-key score blocks of a step's window
+constexpr int kBlocks = 2 * kWinTiles;   // 16-key score blocks of a step's window
+constexpr int kMaxRunSteps = 256;        // steps per work-group at most (bounds the carried RoPE rotation)
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -107,15 +117,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   __shared__ __attribute__((aligned(16))) unsigned char Vt[kRing * kVTile];
   __shared__ __attribute__((aligned(16))) unsigned char GO[kGO];
   __shared__ __attribute__((aligned(16))) unsigned char QS[kQS];
-  __shared__ __attribute__((aligned(16))) uint16_t Wn[2 * kHeadDim];   // w_q, w_k
-  __shared__ double Fr[kMaxRotPairs];                                   // RoPE inv_freq_rev
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: descriptors, LDS bases
+  const int grp = wave >> 2;      // wave group: 0 takes positions 0..15 of every step, 1 positions 16..31
+  const int head = wave & 3;      // this wave's query head within the KV head's group
+  const int half = grp;
   const int l16 = lane & 15, g = lane >> 4;
-  const int head = wave >> 1, half = wave & 1;   // this wave's head and half step
-  const int qrow = 16 * wave + l16;              // this lane's query row in QS / GO: 32 head + position
+  const int qrow = 16 * wave + l16;              // this lane's query row in QS / GO (16 rows per wave)
 
   // consecutive work-groups walk the (sequence, KV head) units first: with B*Hkv a multiple of 8, all runs
   // of one unit land on one XCD, whose L2 then serves the tiles two neighbouring runs share
@@ -126,8 +136,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   if (p_start >= a.S) return;
   const int p_end = min(p_start + a.run, a.S);
   const int n_steps = (p_end - p_start + kStep - 1) / kStep;
-  const int n_tiles = (a.S + kTK - 1) / kTK;
-  const int jmax = min(kRing - 1, (a.window + kTK - 2) / kTK);   // oldest ring tile a step can need
+  const int jmax = min(kWinTiles - 1, (a.window + kTK - 2) / kTK);   // oldest window tile a step can need
 
   const int64_t rowHq = (int64_t)a.Hq * kHeadDim;      // elements per token of q / gate / out
   const int64_t rowHkv = (int64_t)a.Hkv * kHeadDim;    // elements per token of k / v
@@ -137,34 +146,45 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   const uint16_t* kb = a.k + (int64_t)b * a.S * rowHkv + (int64_t)kvh * kHeadDim;
   const uint16_t* vb = a.v + (int64_t)b * a.S * rowHkv + (int64_t)kvh * kHeadDim;
 
-  // ---- key / value tile loader: thread = (key row lr, 16-byte chunk lc).  The 16 lanes of one key row are one
-  // DPP row, which the k_hat prologue reduces over.  Tiles at or past the sequence end (and the tile after a
-  // run's last step) read as zero through an empty descriptor, so every step issues the same loads.
-  const int lr = tid >> 4, lc = tid & 15;
+  // ---- constants held in registers (the LDS is taken whole by the ring and the row buffers): this thread's w_k
+  // chunk and the RoPE frequencies of its key pairs 4lc .. 4lc+3 (the key loader: chunk lc = tid % 16 of a key row),
+  // and this lane's w_q chunks 4t + g
+  const int lc = tid & 15;
+  const uint4 wk_raw = *reinterpret_cast<const uint4*>(a.kw + 8 * lc);
+  double frk[4];
+#pragma unroll
+  for (int m = 0; m < 4; m++) frk[m] = 4 * lc + m < a.rot_pairs ? a.inv_freq_rev[4 * lc + m] : 0.0;
+  float wq[4][8];
+#pragma unroll
+  for (int t = 0; t < 4; t++) unpack8(*reinterpret_cast<const uint4*>(a.qw + 8 * (4 * t + g)), wq[t]);
+
+  // ---- key / value rows: thread (key row lr, 16-byte chunk lc); the 16 lanes of one key row are one DPP row,
+  // which the k_hat prologue reduces over.  Rows at or past the sequence end read as zero through the descriptor.
   uint4 kraw, vraw;
-  auto load_kv = [&](int tile) {
+  auto load_kv = [&](int tile, int lr) {
     const int t0 = tile * kTK;
     const int rows = max(0, min(kTK, a.S - t0));
     const int nbytes = rows > 0 ? (int)(((rows - 1) * rowHkv + kHeadDim) * 2) : 0;
-    const int64_t base = (int64_t)min(t0, a.S - 1) * rowHkv;
+    const int64_t base = (int64_t)min(max(t0, 0), a.S - 1) * rowHkv;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kb + base), (short)0, nbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vb + base), (short)0, nbytes, 0x00020000);
     const int off = (int)((lr * rowHkv + 8 * lc) * 2);
     kraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
     vraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
   };
-  // store_kv(tile, cached): cached tiles (tile -4 .. -1, before the chunk) hold k_hat already (the cache ring's bf16
-  // values), the chunk's own tiles raw k, whose k_hat is computed here at the key's absolute position
+  // store_kv(tile, lr, cached): row lr of a tile into its ring slot.  Cached tiles (before the chunk) hold k_hat
+  // already (the cache ring's bf16 values), the chunk's own tiles raw k, whose k_hat is computed here at the key's
+  // absolute position (the same arithmetic as every other k_hat of the library)
   const int64_t pos0 = CACHED ? (int64_t)a.pos0 : 0;
-  auto store_kv = [&](int tile, bool cached) {
-    const int slot = cached ? tile + kRing : tile % kRing;
+  auto store_kv = [&](int tile, int lr, bool cached) {
+    const int slot = (tile + kRing) % kRing;   // tile >= -4
     if (cached) {
       *reinterpret_cast<uint4*>(Ks + k_off(slot, lr, lc)) = bf16x8_to_f16x8(kraw);
     } else {
       float wk[8], f[8];
-      unpack8(*reinterpret_cast<const uint4*>(Wn + kHeadDim + 8 * lc), wk);
+      unpack8(wk_raw, wk);
       unpack8(kraw, f);
-      norm_rope8_g16_w(f, wk, lc, pos0 + (int64_t)tile * kTK + lr, a.eps, a.rot_pairs, Fr);
+      norm_rope8_g16_f(f, wk, lc, pos0 + (int64_t)tile * kTK + lr, a.eps, a.rot_pairs, [&](int i) { return frk[i & 3]; });
       // the KV-cache value of k_hat (bf16, nearest-even), held exactly as fp16 for the MFMA
       *reinterpret_cast<uint4*>(Ks + k_off(slot, lr, lc)) = bf16x8_to_f16x8(pack8(f));
     }
@@ -180,10 +200,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
 
   // ---- q rows and gate rows of a step -> QS / GO, straight from HBM (buffer loads with LDS as the destination,
   // 64 lanes x 16 B per instruction).  Wave w loads its own 16 rows: lane l of instruction k fills row
-  // 16w + 4k + l/16 (position 16(w%2) + 4k + l/16 of the step, head w/2), chunk position l%16, which holds the
-  // row's chunk (l%16) ^ (row%16).  The descriptor covers the wave's 16 positions and ends with the sequence
-  // (rows past it read as zero; their outputs are computed but not stored), so the per-lane byte offsets hold
-  // for every step: 4 registers for the whole kernel.
+  // 16w + 4k + l/16 (position 16 half + 4k + l/16 of the step), chunk position l%16, which holds the row's chunk
+  // (l%16) ^ (row%16).  The descriptor covers the wave's 16 positions and ends with the sequence (rows past it read
+  // as zero; their outputs are computed but not stored), so the per-lane byte offsets hold for every step.
   uint32_t qg_off[4];
 #pragma unroll
   for (int k = 0; k < 4; k++) {
@@ -203,20 +222,17 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
                                                16, (int)qg_off[k], 0, 0, 0);
   };
 
-  // ---- the norm weights and RoPE frequencies, once, into LDS (global loads issued later would wait behind
-  // the streaming loads: the vector-memory counter retires in order); the ring starts as zeros: the slots of
-  // tiles before position 0 are read (and masked) by the first steps
+  // ---- the ring starts as zeros: the slots of tiles before position 0 are read (and masked) by the first steps
   for (int x = tid; x < kRing * kKTile / 16; x += kThreads) reinterpret_cast<uint4*>(Ks)[x] = make_uint4(0u, 0u, 0u, 0u);
   for (int x = tid; x < kRing * kVTile / 16; x += kThreads) reinterpret_cast<uint4*>(Vt)[x] = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < 32) reinterpret_cast<uint4*>(Wn)[tid] = *reinterpret_cast<const uint4*>((tid < 16 ? a.qw : a.kw) + 8 * (tid & 15));
-  if (tid < kMaxRotPairs) Fr[tid] = a.inv_freq_rev[tid];
   lds_barrier();
 
-  // ---- prologue: the first step's window tiles, then its q rows.  Tiles before the chunk (tile < 0) hold the
-  // positions before pos0: from the cache's ring when there is one (slot p mod W of the sequence's KV head; positions
-  // below 0 stay zero), otherwise zero (and masked).
+  // ---- prologue: the first step's window tiles (all threads, one row chunk each).  Tiles before the chunk
+  // (tile < 0) hold the positions before pos0: from the cache's ring when there is one (slot p mod W of the
+  // sequence's KV head; positions below 0 stay zero), otherwise zero (and masked).
+  const int T0 = p_start / kTK;
   {
-    const int T0 = p_start / kTK;
+    const int lr = tid >> 4;
     for (int j = jmax; j >= 0; j--) {
       const int tile = T0 - j;
       if (tile < 0) {
@@ -228,23 +244,26 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
             kraw = *reinterpret_cast<const uint4*>(a.ck + row);
             vraw = *reinterpret_cast<const uint4*>(a.cv + row);
           }
-          store_kv(tile, true);
+          store_kv(tile, lr, true);
         }
         continue;
       }
-      load_kv(tile);
-      store_kv(tile, false);
+      load_kv(tile, lr);
+      store_kv(tile, lr, false);
     }
   }
+  // the ring tile a group writes in its next output phase, and its key rows: group 0 rows 16..31 of tile T + 1,
+  // group 1 rows 0..15 of tile T + 2 (T = the step's tile; see the schedule below)
+  const int hr = 16 * (1 - grp) + ((tid & 255) >> 4);
   load_rows(qb, QS, p_start, true);
-  // w_q for this lane's 32 dims (chunks 4t + g), once
-  float wq[4][8];
-#pragma unroll
-  for (int t = 0; t < 4; t++) unpack8(*reinterpret_cast<const uint4*>(Wn + 8 * (4 * t + g)), wq[t]);
-  // RoPE of the lane's query rows in chunks 4t + g, t = 0, 1 (pairs 4(4t + g) + m: every pair below 32), carried
-  // along the steps: the lane's position advances by one step's 32 positions, so each pair's (cos, sin) advances
-  // by a fixed rotation (re-seeded from the exact angle every 16 steps).  Pairs at or past rot_pairs stay at (1, 0).
-  // Rows past the sequence end follow the same progression; their outputs are not stored.
+  load_rows(gb, GO, p_start, true);
+  load_kv(T0 + 1, hr);
+
+  // RoPE of the lane's query rows in chunks 4t + g, t = 0, 1 (pairs 4(4t + g) + m: every pair below 32; the kernel
+  // takes rot_pairs <= 32), carried along the steps: the lane's position advances by one step's 32 positions, so
+  // each pair's (cos, sin) advances by a fixed rotation.  A run has at most kMaxRunSteps steps, so the carried value
+  // is at most that many fp32 rotations away from the exact angle.  Pairs at or past rot_pairs stay at (1, 0).  Rows
+  // past the sequence end follow the same progression; their outputs are not stored.
   float rc[2][4], rs[2][4], dc[2][4], dsn[2][4];
 #pragma unroll
   for (int t = 0; t < 2; t++)
@@ -253,42 +272,46 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
       const int pi = 4 * (4 * t + g) + m;
       rc[t][m] = 1.0f; rs[t][m] = 0.0f; dc[t][m] = 1.0f; dsn[t][m] = 0.0f;
       if (pi < a.rot_pairs) {
-        rope_cs(pos0 + p_start + 16 * half + l16, Fr[pi], rc[t][m], rs[t][m]);
-        rope_cs(kStep, Fr[pi], dc[t][m], dsn[t][m]);
+        const double fr = a.inv_freq_rev[pi];
+        rope_cs(pos0 + p_start + 16 * half + l16, fr, rc[t][m], rs[t][m]);
+        rope_cs(kStep, fr, dc[t][m], dsn[t][m]);
       }
     }
+  ZG_WAIT_VM(0);
+  lds_barrier();
 
-  // MFMA operand offsets within a tile (bytes): K row 16kh + l16, chunk 4t + g (t = 0..3); V^T row 16db + l16,
-  // chunk g (stored keys 8g..8g+7)
-  const half2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // ---- the two wave groups run half a step apart.  Each step of a group is a compute phase M (q_hat, the window's
+  // scores, softmax, PV: LDS-bound MFMA work) and an output phase V (gate, output rows, half a ring tile: VALU work);
+  // group 1 starts with an output phase of its own (the first ring half), so one group's M runs beside the other's V
+  // on every SIMD (wave w and w + 4 share one), one work-group barrier between phases:
+  //   interval 2c:     group 0: M(c)                         group 1: V(c-1), ring rows 0..15 of tile T(c)+1
+  //   interval 2c + 1: group 0: V(c), ring rows 16..31 of T(c)+1   group 1: M(c)
+  // M(c) reads tiles T(c)-4 .. T(c); tile T(c)+1 goes to the slot of T(c)-5, which no phase in flight reads (6 slots);
+  // both halves of it are written before either group's M(c+1).
+  // Per wave and step, the vector-memory operations in issue order: M: q rows of the next step (4 loads into LDS);
+  // V: output rows (4 stores), gate rows of the next step (4 loads into LDS), the next ring half (2 loads).  Rows and
+  // tiles past a run's end use empty descriptors, so every step issues the same operations and the waits below are
+  // fixed counts (the vm counter retires loads and stores in order).
+  floatx4 acc_o[8];
+  float l_run = 0.f;
+  if (grp == 1) {
+    if (n_steps > 1) store_kv(T0 + 1, hr, false);
+    load_kv(T0 + 2, hr);
+    lds_barrier();
+  }
   for (int c = 0; c < n_steps; c++) {
     const int i0 = p_start + c * kStep;
     const int T = i0 / kTK;
     const int i = i0 + 16 * half + l16;           // this lane's query position
     const int qlo = i0 + 16 * half;               // the wave's positions qlo .. qlo+15
-    // this wave's q rows have landed; the previous step's 4 output stores, issued after them, may still be in
-    // flight (the vm counter counts stores too, in order)
-    if (c == 0) ZG_WAIT_VM(0);
-    else ZG_WAIT_VM(4);
-    lds_barrier();                 // the previous step's ring store is visible and its GO reads are done
-    // the carried RoPE rotation is re-seeded from the exact angle every 16 steps, so its rounding cannot build up
-    // over a long run (a run of 8192 positions has 256 steps)
-    if (c > 0 && (c & 15) == 0) {
-#pragma unroll
-      for (int t = 0; t < 2; t++)
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-          const int pi = 4 * (4 * t + g) + m;
-          if (pi < a.rot_pairs) rope_cs(pos0 + i, Fr[pi], rc[t][m], rs[t][m]);
-        }
-    }
-
-    // ---- q_hat of this step: RMSNorm * w_q, partial RoPE, scale by log2(e)/sqrt(D), round to fp16
-    // (MFMA B operand of k-step t: lane holds q_hat[query l16][8(4t + g) .. +8])
+    const bool more = c + 1 < n_steps;
+    // ================= M(c) =================
+    // this wave's q rows have landed (issued in the previous M; since then: 4 stores, 4 + 2 loads)
+    if (c > 0) ZG_WAIT_VM(10);
+    // ---- q_hat of this step (MFMA B operand of k-step t: lane holds q_hat[query l16][8(4t + g) .. +8]), from the
+    // lane's raw chunks 4t + g: RMSNorm * w_q, rope(f, t) on chunks t = 0, 1, scale by log2(e)/sqrt(D), round to fp16
     half8 qf[4];
-    {
-      uint4 qr[4];
-      read_row4(QS, qrow, g, qr);
+    auto q_hat = [&](const uint4 (&qr)[4], auto rope) {
       float f[4][8];
       float ss = 0.f;
 #pragma unroll
@@ -304,37 +327,36 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
       for (int t = 0; t < 4; t++) {
 #pragma unroll
         for (int e = 0; e < 8; e++) f[t][e] = f[t][e] * inv * wq[t][e];
+        rope(f[t], t);
+#pragma unroll
+        for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)f[t][e];
+      }
+    };
+    {
+      uint4 qr[4];
+      read_row4(QS, qrow, g, qr);
+      load_rows(qb, QS, i0 + kStep, more);     // the next step's q rows (this wave has read its own)
+      q_hat(qr, [&](float* f, int t) {   // the carried rotation, advanced to the next step's positions
         if (t < 2) {
 #pragma unroll
           for (int m = 0; m < 4; m++) {
-            const float x0 = f[t][2 * m], x1 = f[t][2 * m + 1];
-            f[t][2 * m] = x0 * rc[t][m] - x1 * rs[t][m];
-            f[t][2 * m + 1] = x0 * rs[t][m] + x1 * rc[t][m];
+            const float x0 = f[2 * m], x1 = f[2 * m + 1];
+            f[2 * m] = x0 * rc[t][m] - x1 * rs[t][m];
+            f[2 * m + 1] = x0 * rs[t][m] + x1 * rc[t][m];
             const float c1 = rc[t][m] * dc[t][m] - rs[t][m] * dsn[t][m];
             rs[t][m] = rs[t][m] * dc[t][m] + rc[t][m] * dsn[t][m];
             rc[t][m] = c1;
           }
-        } else {
-          rope8(f[t], 8 * (4 * t + g), pos0 + min(i, a.S - 1), a.rot_pairs, Fr);
         }
-#pragma unroll
-        for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)f[t][e];
-      }
+      });
     }
-    // this step's gate rows, the next key/value tile and the next step's q rows (into QS: this wave has consumed
-    // its rows above), in that order, all in flight during this step's compute; past the run's last step the
-    // loads are empty, so the counts stay the same
-    const bool more = c + 1 < n_steps;
-    load_rows(gb, GO, i0, true);
-    load_kv(more ? T + 1 : n_tiles);
-    load_rows(qb, QS, i0 + kStep, more);
 
     // ---- the whole window of the step: score blocks of 16 keys, block kb = 2j + kh covering keys
     // 32(T - 4 + j) + 16kh .. +15 (tiles before position 0 sit in zero-filled slots and are masked)
-    int slot_k[kRing], slot_v[kRing];
+    int slot_k[kWinTiles], slot_v[kWinTiles];
 #pragma unroll
-    for (int j = 0; j < kRing; j++) {
-      const int sl = (T - (kRing - 1) + j + kRing) % kRing;   // ring slot of tile T-4+j (T-4 >= -4)
+    for (int j = 0; j < kWinTiles; j++) {
+      const int sl = (T - (kWinTiles - 1) + j + kRing) % kRing;   // ring slot of tile T-4+j (T-4 >= -4)
       slot_k[j] = sl * kKTile;
       slot_v[j] = sl * kVTile;
     }
@@ -365,7 +387,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
       const unsigned lim = CACHED ? (unsigned)min((int64_t)a.window, pos0 + i + 1) : (unsigned)min(a.window, i + 1);
 #pragma unroll
       for (int kb = 0; kb < kBlocks; kb++) {
-        const int kt = (T - (kRing - 1)) * kTK + 16 * kb;
+        const int kt = (T - (kWinTiles - 1)) * kTK + 16 * kb;
         if (!(kt >= (CACHED ? -(int)pos0 : 0) && kt + 15 <= qlo && kt >= qlo + 16 - a.window)) {
 #pragma unroll
           for (int e = 0; e < 4; e++) {
@@ -382,12 +404,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     mx = fmaxf(mx, __shfl_xor(mx, 32));   // finite: every query sees its own key
     // P = exp2(s - m) rounded to fp16; the row sum adds the same rounded values.  O^T = V^T P^T, one k-step per
     // tile: lane (l16, g) supplies P for keys 4g..4g+3 and 16+4g..16+4g+3 of the tile (= stored keys 8g..8g+7)
-    floatx4 acc_o[8];
+    const half2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int db = 0; db < 8; db++) acc_o[db] = (floatx4){0.f, 0.f, 0.f, 0.f};
-    float l_run = 0.f;
+    l_run = 0.f;
 #pragma unroll
-    for (int j = 0; j < kRing; j++) {
+    for (int j = 0; j < kWinTiles; j++) {
       uint32_t wp[4];
 #pragma unroll
       for (int e = 0; e < 2; e++) {
@@ -409,16 +431,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     // training: the log-sum-exp of the query's scores (natural log; scores in log2 units are s log2(e))
     if (a.lse && g == 0 && i < p_end)
       a.lse[((int64_t)b * a.Hq + kvh * kGroup + head) * a.S + i] = (mx + __log2f(l_run)) * 0.6931471805599453f;
+    lds_barrier();
 
+    // ================= V(c) =================
+    // this group's half of the next ring tile, from raw rows loaded in the previous V, and this wave's gate rows,
+    // loaded before them (since then: 4 loads in M)
+    ZG_WAIT_VM(4);
+    if (c + 1 + grp < n_steps) store_kv(T + 1 + grp, hr, false);
     // ---- epilogue.  acc_o[db][e] is dim d = 16db + 4g + e of this lane's query row.
-    // This wave's gate rows have landed in GO: they were issued before the next key/value tile (2 loads) and
-    // the next step's q rows (4 loads), which may stay in flight.
-    ZG_WAIT_VM(6);
-    lds_barrier();                   // ... and every wave's; all waves are past the ring reads
-    if (more) {
-      ZG_WAIT_VM(4);                 // the next key/value tile (the next step's q rows may stay in flight)
-      store_kv(T + 1, false);        // into the slot of tile T-4, which no later step reads
-    }
 #pragma unroll
     for (int db = 0; db < 8; db++) {
       const int d = 16 * db + 4 * g;
@@ -431,37 +451,52 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
         o[e] = acc_o[db][e] * __builtin_amdgcn_rcpf(__builtin_fmaf(l_run, __expf(-gv[e]), l_run));
       *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]));
     }
-    lds_barrier();
-    // coalesced store, 16 lanes per 256-byte row, through a descriptor over this step's valid positions:
-    // rows past the run's end fall outside it and are dropped, so every step issues exactly 4 stores
+    // coalesced store of the wave's own 16 rows, 16 lanes per 256-byte row, through a descriptor over its valid
+    // positions: rows past the run's end fall outside it and are dropped, so every step issues exactly 4 stores
     {
-      const int nvalid = min(kStep, p_end - i0);
+      const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(16, p_end - qlo)));
+      const int prow = __builtin_amdgcn_readfirstlane(min(qlo, a.S - 1));
       const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(ob + (int64_t)i0 * rowHq), (short)0, (int)(nvalid * rowHq * 2), 0x00020000);
+          (void*)(ob + (int64_t)prow * rowHq), (short)0, (int)(nvalid * rowHq * 2), 0x00020000);
+      uint4 orow[4];
 #pragma unroll
       for (int k = 0; k < 4; k++) {
-        const int cc = tid + kThreads * k;
-        const int row = cc >> 4, ch = cc & 15;
-        const int off = (int)(((row & 31) * rowHq + (row >> 5) * kHeadDim + 8 * ch) * 2);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(4 * sizeof(int)))) int,
-                                                                  *reinterpret_cast<const uint4*>(GO + go_off(row, ch))),
+        const int r = 4 * k + (lane >> 4), ch = lane & 15;
+        orow[k] = *reinterpret_cast<const uint4*>(GO + go_off(16 * wave + r, ch));
+      }
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const int r = 4 * k + (lane >> 4), ch = lane & 15;
+        const int off = (int)((r * rowHq + head * kHeadDim + 8 * ch) * 2);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(4 * sizeof(int)))) int, orow[k]),
                                                ro, off, 0, 0);
       }
     }
+    // the next step's gate rows into the same LDS rows, once this wave's reads of them are done, and the raw rows
+    // of this group's next ring half
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the LDS reads are complete (vmcnt 63, expcnt 7: not waited)
+    load_rows(gb, GO, i0 + kStep, more);
+    load_kv(T + 2 + grp, hr);
+    lds_barrier();
   }
+  if (grp == 0) lds_barrier();
 }
 
 }  // namespace
 
 int swa_stream_run_length(int S, int n_units) {
-  // about one work-group per CU (256 CUs; the LDS ring, gate and q tiles of 8 waves take one CU each)
+  // about one work-group per CU (256 CUs; the LDS ring, gate and q tiles of 8 waves take one CU each), at most
+  // kMaxRunSteps steps each
   const int64_t per = ((int64_t)S * n_units + 255) / 256;
-  int run = (int)((per + kStep - 1) / kStep) * kStep;
-  return run < kStep ? kStep : run;
+  int64_t run = (per + kStep - 1) / kStep * kStep;
+  run = run < kStep ? kStep : run;
+  return (int)(run > (int64_t)kStep * kMaxRunSteps ? (int64_t)kStep * kMaxRunSteps : run);
 }
 
 hipError_t launch_swa_stream(const SwaStreamArgs& a, hipStream_t st) {
-  if (a.G != kGroup || a.window < 1 || a.window > kTK * (kRing - 1) || a.run % kStep) return hipErrorInvalidValue;
+  if (a.G != kGroup || a.window < 1 || a.window > kTK * (kWinTiles - 1) || a.rot_pairs > 32 || a.run % kStep ||
+      a.run > kStep * kMaxRunSteps)
+    return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)a.n_units * ((a.S + a.run - 1) / a.run);
   if (a.ck) hipLaunchKernelGGL(attn_swa_stream_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL(attn_swa_stream_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);

@@ -109,27 +109,33 @@ __device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq_rev, float&
 }
 
 // Rotate the pairs of 8 consecutive dims d0..d0+7 (d0 even) of a row at position pos; pairs at or
-// beyond rot_pairs are left alone.  Whole chunks past the rotary dims skip the work.
-__device__ __forceinline__ void rope8(float* f, int d0, int64_t pos, int rot_pairs, const double* inv_freq_rev) {
+// beyond rot_pairs are left alone.  Whole chunks past the rotary dims skip the work.  freq(i) gives
+// inv_freq_rev of pair i (from an array, or from registers a kernel holds them in).
+template <class Freq>
+__device__ __forceinline__ void rope8_f(float* f, int d0, int64_t pos, int rot_pairs, Freq freq) {
   if (d0 >= 2 * rot_pairs) return;
 #pragma unroll
   for (int m = 0; m < 4; m++) {
     const int i = d0 / 2 + m;
     float c, s;
-    rope_cs(pos, inv_freq_rev[i], c, s);
+    rope_cs(pos, freq(i), c, s);
     if (i >= rot_pairs) { c = 1.0f; s = 0.0f; }
     const float x0 = f[2 * m], x1 = f[2 * m + 1];
     f[2 * m] = x0 * c - x1 * s;
     f[2 * m + 1] = x0 * s + x1 * c;
   }
 }
+__device__ __forceinline__ void rope8(float* f, int d0, int64_t pos, int rot_pairs, const double* inv_freq_rev) {
+  rope8_f(f, d0, pos, rot_pairs, [&](int i) { return inv_freq_rev[i]; });
+}
 
 // RMSNorm * w then partial RoPE at position pos, for the 8 dims 8c..8c+7 of a 128-dim row held by a
 // group of 16 consecutive lanes (c = lane within the group; every lane of the group must be active), with
 // the lane's 8 weights wf already unpacked.  Used for every k_hat (and the decode q_hat), so all kernels
 // produce the same bits for the same row.
-__device__ __forceinline__ void norm_rope8_g16_w(float* f, const float* wf, int c, int64_t pos, float eps,
-                                                 int rot_pairs, const double* inv_freq_rev) {
+template <class Freq>
+__device__ __forceinline__ void norm_rope8_g16_f(float* f, const float* wf, int c, int64_t pos, float eps,
+                                                 int rot_pairs, Freq freq) {
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; e++) ss += f[e] * f[e];
@@ -140,7 +146,11 @@ __device__ __forceinline__ void norm_rope8_g16_w(float* f, const float* wf, int 
   const float inv = rsqrtf(ss * (1.0f / kHeadDim) + eps);
 #pragma unroll
   for (int e = 0; e < 8; e++) f[e] = f[e] * inv * wf[e];
-  rope8(f, 8 * c, pos, rot_pairs, inv_freq_rev);
+  rope8_f(f, 8 * c, pos, rot_pairs, freq);
+}
+__device__ __forceinline__ void norm_rope8_g16_w(float* f, const float* wf, int c, int64_t pos, float eps,
+                                                 int rot_pairs, const double* inv_freq_rev) {
+  norm_rope8_g16_f(f, wf, c, pos, eps, rot_pairs, [&](int i) { return inv_freq_rev[i]; });
 }
 __device__ __forceinline__ void norm_rope8_g16(float* f, const uint16_t* w, int c, int64_t pos, float eps,
                                                int rot_pairs, const double* inv_freq_rev) {

@@ -380,9 +380,10 @@ int prefill_common(bool gated, const void* q, const void* k, const void* v, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rot_pairs = R / 2;
   if (lse && cache) return fail(ZG_EINVAL, "%s: the training forward takes no cache", fn);
-  if (gated && G == 4 && window <= 128) {
+  if (gated && G == 4 && window <= 128 && rot_pairs <= 32) {
     // streaming SWA kernel: k_hat computed in its tile loader, no workspace pass; with a cache, the window's keys
-    // before the chunk come from the layer's ring, and the chunk's last keys go to the ring afterwards
+    // before the chunk come from the layer's ring, and the chunk's last keys go to the ring afterwards (it carries
+    // the queries' RoPE for the pairs of the first 64 dims; more rotary dims take the tile path)
     const LayerDesc* ld = cache ? &cache->layers[layer - 1] : nullptr;
     SwaStreamArgs sa{};
     sa.q = static_cast<const uint16_t*>(q);
