@@ -280,8 +280,54 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   ZG_WAIT_VM(0);
   lds_barrier();
 
-  // ---- the two wave groups run half a step apart.  Each step of a group is a compute phase M (q_hat, the window's
-  // scores, softmax, PV: LDS-bound MFMA work) and an output phase V (gate, output rows, half a ring tile: VALU work);
+  // ---- q_hat of a step (MFMA B operand of k-step t: lane holds q_hat[query l16][8(4t + g) .. +8]), from the
+  // lane's raw chunks 4t + g: RMSNorm * w_q, rope(f, t) on chunks t = 0, 1, scale by log2(e)/sqrt(D), round to fp16.
+  // It is computed in the output phase before the step's compute phase, which then starts with its MFMAs.
+  half8 qf[4];
+  auto q_hat = [&](const uint4 (&qr)[4], auto rope) {
+    float f[4][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      unpack8(qr[t], f[t]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) ss += f[t][e] * f[t][e];
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps) * a.q_scale;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) f[t][e] = f[t][e] * inv * wq[t][e];
+      rope(f[t], t);
+#pragma unroll
+      for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)f[t][e];
+    }
+  };
+  // the next step's q_hat from this wave's q rows in LDS, with the carried rotation (then advanced by a step)
+  auto next_q = [&]() {
+    uint4 qr[4];
+    read_row4(QS, qrow, g, qr);
+    q_hat(qr, [&](float* f, int t) {
+      if (t < 2) {
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+          const float x0 = f[2 * m], x1 = f[2 * m + 1];
+          f[2 * m] = x0 * rc[t][m] - x1 * rs[t][m];
+          f[2 * m + 1] = x0 * rs[t][m] + x1 * rc[t][m];
+          const float c1 = rc[t][m] * dc[t][m] - rs[t][m] * dsn[t][m];
+          rs[t][m] = rs[t][m] * dc[t][m] + rc[t][m] * dsn[t][m];
+          rc[t][m] = c1;
+        }
+      }
+    });
+  };
+  next_q();   // step 0 (its q rows landed with the prologue's loads)
+
+  // ---- the two wave groups run half a step apart.  Each step of a group is a compute phase M (the window's scores,
+  // softmax, PV: MFMA work and its dependent VALU) and an output phase V (half a ring tile, gate, output rows, and
+  // the next step's q_hat: VALU work);
   // group 1 starts with an output phase of its own (the first ring half), so one group's M runs beside the other's V
   // on every SIMD (wave w and w + 4 share one), one work-group barrier between phases:
   //   interval 2c:     group 0: M(c)                         group 1: V(c-1), ring rows 0..15 of tile T(c)+1
@@ -289,7 +335,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   // M(c) reads tiles T(c)-4 .. T(c); tile T(c)+1 goes to the slot of T(c)-5, which no phase in flight reads (6 slots);
   // both halves of it are written before either group's M(c+1).
   // Per wave and step, the vector-memory operations in issue order: M: q rows of the next step (4 loads into LDS);
-  // V: output rows (4 stores), gate rows of the next step (4 loads into LDS), the next ring half (2 loads).  Rows and
+  // V: output rows (4 stores), gate rows of the next step (4 loads into LDS), the next ring half (2 loads), then the
+  // wait for the q rows.  Rows and
   // tiles past a run's end use empty descriptors, so every step issues the same operations and the waits below are
   // fixed counts (the vm counter retires loads and stores in order).
   floatx4 acc_o[8];
@@ -306,51 +353,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     const int qlo = i0 + 16 * half;               // the wave's positions qlo .. qlo+15
     const bool more = c + 1 < n_steps;
     // ================= M(c) =================
-    // this wave's q rows have landed (issued in the previous M; since then: 4 stores, 4 + 2 loads)
-    if (c > 0) ZG_WAIT_VM(10);
-    // ---- q_hat of this step (MFMA B operand of k-step t: lane holds q_hat[query l16][8(4t + g) .. +8]), from the
-    // lane's raw chunks 4t + g: RMSNorm * w_q, rope(f, t) on chunks t = 0, 1, scale by log2(e)/sqrt(D), round to fp16
-    half8 qf[4];
-    auto q_hat = [&](const uint4 (&qr)[4], auto rope) {
-      float f[4][8];
-      float ss = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; t++) {
-        unpack8(qr[t], f[t]);
-#pragma unroll
-        for (int e = 0; e < 8; e++) ss += f[t][e] * f[t][e];
-      }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      const float inv = rsqrtf(ss * (1.0f / kHeadDim) + a.eps) * a.q_scale;
-#pragma unroll
-      for (int t = 0; t < 4; t++) {
-#pragma unroll
-        for (int e = 0; e < 8; e++) f[t][e] = f[t][e] * inv * wq[t][e];
-        rope(f[t], t);
-#pragma unroll
-        for (int e = 0; e < 8; e++) qf[t][e] = (_Float16)f[t][e];
-      }
-    };
-    {
-      uint4 qr[4];
-      read_row4(QS, qrow, g, qr);
-      load_rows(qb, QS, i0 + kStep, more);     // the next step's q rows (this wave has read its own)
-      q_hat(qr, [&](float* f, int t) {   // the carried rotation, advanced to the next step's positions
-        if (t < 2) {
-#pragma unroll
-          for (int m = 0; m < 4; m++) {
-            const float x0 = f[2 * m], x1 = f[2 * m + 1];
-            f[2 * m] = x0 * rc[t][m] - x1 * rs[t][m];
-            f[2 * m + 1] = x0 * rs[t][m] + x1 * rc[t][m];
-            const float c1 = rc[t][m] * dc[t][m] - rs[t][m] * dsn[t][m];
-            rs[t][m] = rs[t][m] * dc[t][m] + rc[t][m] * dsn[t][m];
-            rc[t][m] = c1;
-          }
-        }
-      });
-    }
-
+    // q_hat of this step is in qf (computed at the end of the previous output phase, or in the prologue); this
+    // wave's q rows in LDS have been read, so the next step's go there
+    load_rows(qb, QS, i0 + kStep, more);
     // ---- the whole window of the step: score blocks of 16 keys, block kb = 2j + kh covering keys
     // 32(T - 4 + j) + 16kh .. +15 (tiles before position 0 sit in zero-filled slots and are masked)
     int slot_k[kWinTiles], slot_v[kWinTiles];
@@ -477,6 +482,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the LDS reads are complete (vmcnt 63, expcnt 7: not waited)
     load_rows(gb, GO, i0 + kStep, more);
     load_kv(T + 2 + grp, hr);
+    // ---- the next step's q_hat: its q rows were loaded at the start of M (since then: 4 stores, 4 + 2 loads)
+    if (more) {
+      ZG_WAIT_VM(10);
+      next_q();
+    }
     lds_barrier();
   }
   if (grp == 0) lds_barrier();
