@@ -13,9 +13,9 @@
 //     (S^T = K Q^T, O^T = V^T P^T on v_mfma_f32_16x16x32_f16); the LDS (ring, gate and q rows: 160 KiB) allows
 //     one work-group per CU;
 //   - the two wave groups (waves 0-3 and 4-7; waves w and w+4 share a SIMD) run half a step apart: a step of a
-//     group is a compute phase (q_hat, the window's scores, softmax, PV) and an output phase (gate, output rows,
-//     half of the next ring tile), and one group's compute phase runs beside the other's output phase, one
-//     work-group barrier between phases;
+//     group is a compute phase (the window's scores, softmax, PV) and an output phase (half of the next ring tile,
+//     gate, output rows, and the next step's q_hat), and one group's compute phase runs beside the other's output
+//     phase, one work-group barrier between phases;
 //   - the keys of the window live in a 6-slot LDS ring of 32-key tiles: a 32-position step with W <= 128 reads
 //     5 tiles, and the next tile is written (one half by each group) while they are read.  The whole window of
 //     a step is scored at once (ten independent 16-key score chains per wave) and normalised with one exact max
@@ -161,9 +161,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   // ---- key / value rows: thread (key row lr, 16-byte chunk lc); the 16 lanes of one key row are one DPP row,
   // which the k_hat prologue reduces over.  Rows at or past the sequence end read as zero through the descriptor.
   uint4 kraw, vraw;
-  auto load_kv = [&](int tile, int lr) {
+  auto load_kv = [&](int tile, int lr, bool live = true) {   // live = false: an empty load (keeps the counts)
     const int t0 = tile * kTK;
-    const int rows = max(0, min(kTK, a.S - t0));
+    const int rows = live ? max(0, min(kTK, a.S - t0)) : 0;
     const int nbytes = rows > 0 ? (int)(((rows - 1) * rowHkv + kHeadDim) * 2) : 0;
     const int64_t base = (int64_t)min(max(t0, 0), a.S - 1) * rowHkv;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kb + base), (short)0, nbytes, 0x00020000);
@@ -257,7 +257,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   const int hr = 16 * (1 - grp) + ((tid & 255) >> 4);
   load_rows(qb, QS, p_start, true);
   load_rows(gb, GO, p_start, true);
-  load_kv(T0 + 1, hr);
+  load_kv(T0 + 1, hr, n_steps > 1);
 
   // RoPE of the lane's query rows in chunks 4t + g, t = 0, 1 (pairs 4(4t + g) + m: every pair below 32; the kernel
   // takes rot_pairs <= 32), carried along the steps: the lane's position advances by one step's 32 positions, so
@@ -343,7 +343,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
   float l_run = 0.f;
   if (grp == 1) {
     if (n_steps > 1) store_kv(T0 + 1, hr, false);
-    load_kv(T0 + 2, hr);
+    load_kv(T0 + 2, hr, n_steps > 2);
     lds_barrier();
   }
   for (int c = 0; c < n_steps; c++) {
@@ -481,7 +481,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     // of this group's next ring half
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the LDS reads are complete (vmcnt 63, expcnt 7: not waited)
     load_rows(gb, GO, i0 + kStep, more);
-    load_kv(T + 2 + grp, hr);
+    load_kv(T + 2 + grp, hr, c + 2 + grp < n_steps);   // stored in the next V if a step still needs it
     // ---- the next step's q_hat: its q rows were loaded at the start of M (since then: 4 stores, 4 + 2 loads)
     if (more) {
       ZG_WAIT_VM(10);
