@@ -15,6 +15,8 @@ typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 constexpr int kHeadDim = 128;
 constexpr int kMaxRotPairs = kHeadDim / 2;
 constexpr float kLog2e = 1.4426950408889634f;
+// Cache-policy operand of the buffer-load builtins on gfx950: the non-temporal (nt) bit, for data read once.
+constexpr int kCpolNT = 2;
 
 // bf16 bit pattern <-> fp32 (bf16 is the top half of an fp32).
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
