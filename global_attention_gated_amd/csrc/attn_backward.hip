@@ -170,11 +170,11 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdArgs a) {
     xin[pass] = din[pass] = oin[pass] = gin[pass] = z;
     if (s < a.S) {
       const int64_t irow = (((int64_t)b * a.S + s) * H + h) * kHeadDim + 8 * c;   // [B][S][H][D] input row
-      xin[pass] = *reinterpret_cast<const uint4*>((qmode ? a.q : a.k) + irow);
+      xin[pass] = load_nt16((qmode ? a.q : a.k) + irow);
       if (qmode) {
-        din[pass] = *reinterpret_cast<const uint4*>(a.dout + irow);
-        oin[pass] = *reinterpret_cast<const uint4*>(a.out + irow);
-        if (gated) gin[pass] = *reinterpret_cast<const uint4*>(a.gate + irow);
+        din[pass] = load_nt16(a.dout + irow);
+        oin[pass] = load_nt16(a.out + irow);
+        if (gated) gin[pass] = load_nt16(a.gate + irow);
       }
     }
   }

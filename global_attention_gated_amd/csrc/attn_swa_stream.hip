@@ -169,8 +169,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kb + base), (short)0, nbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vb + base), (short)0, nbytes, 0x00020000);
     const int off = (int)((lr * rowHkv + 8 * lc) * 2);
-    kraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-    vraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    kraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, kCpolNT));
+    vraw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kCpolNT));
   };
   // store_kv(tile, lr, cached): row lr of a tile into its ring slot.  Cached tiles (before the chunk) hold k_hat
   // already (the cache ring's bf16 values), the chunk's own tiles raw k, whose k_hat is computed here at the key's
@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
 #pragma unroll
     for (int k = 0; k < 4; k++)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + (16 * wave + 4 * k) * 256),
-                                               16, (int)qg_off[k], 0, 0, 0);
+                                               16, (int)qg_off[k], 0, 0, kCpolNT);
   };
 
   // ---- the ring starts as zeros: the slots of tiles before position 0 are read (and masked) by the first steps

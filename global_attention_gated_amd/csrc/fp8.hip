@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(256) fp8_quantize_kernel(const uint16_t* __res
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint2* qv = reinterpret_cast<uint2*>(q);
   for (; u + stride < n8; u += 2 * stride) {
-    const uint4 a = xv[u], b = xv[u + stride];
+    const uint4 a = load_nt16(xv + u), b = load_nt16(xv + u + stride);
     qv[u] = e4m3x8(a, s, m);
     qv[u + stride] = e4m3x8(b, s, m);
   }
