@@ -76,6 +76,8 @@ SHAPES = [
     (True, 1, 700, 4, 1, 64, 128),
     (True, 1, 65, 4, 1, 127, 42),
     (True, 1, 31, 4, 1, 128, 42),
+    (True, 1, 600, 4, 1, 128, 64),   # the most rotary dims the streaming kernel carries (32 pairs)
+    (True, 1, 300, 4, 1, 128, 66),   # one pair more: the tile kernel
     (False, 2, 300, 8, 2, None, 42),
     (False, 1, 700, 4, 1, None, 42),
     (False, 1, 257, 16, 2, None, 42),
