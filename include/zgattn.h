@@ -122,8 +122,8 @@ uint64_t prefill_workspace_bytes(int32_t B, int32_t S, int32_t Hkv, int32_t D);
  *     ring, whose length must equal pos0, and the chunk's last min(S, W) positions are written into
  *     the ring (length becomes pos0+S).  Without a cache pos0 must be 0.
  *   workspace: device buffer of at least prefill_workspace_bytes_at(B, S, Hkv, D, pos0 (0 without a cache), window)
- *     bytes, 16-byte aligned (the streaming kernel of the common case, GQA group 4 and W <= 128, with or without a
- *     cache, does not touch it).
+ *     bytes, 16-byte aligned (the streaming kernel of the common case, GQA group 4, W <= 128 and rotary_dims <= 64,
+ *     with or without a cache, does not touch it).
  * S == 0 or B == 0 is a no-op.  Errors: EINVAL, EUNSUPPORTED, ERANGE, EHIP. */
 int swa_prefill(const void* q, const void* k, const void* v, const void* gate, const void* q_norm_w,
                 const void* k_norm_w, void* out, int32_t B, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
