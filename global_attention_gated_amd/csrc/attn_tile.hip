@@ -64,13 +64,13 @@ __global__ void __launch_bounds__(256) kv_stage_kernel(StageArgs a) {
       const int r = g + 16 * rr, p = p0 + r;
       const int sc = min(max(p - a.pos0, 0), a.S - 1);
       float f[8];
-      unpack8(*reinterpret_cast<const uint4*>(a.k + ((row_b + sc) * a.Hkv + h) * kHeadDim + 8 * c), f);
+      unpack8(load_nt16(a.k + ((row_b + sc) * a.Hkv + h) * kHeadDim + 8 * c), f);
       norm_rope8_g16(f, a.kw, c, a.pos0 + sc, a.eps, a.rot_pairs, a.inv_freq_rev);
       uint4 kb = pack8(f);   // the KV-cache value of k_hat (bf16, nearest-even)
       if (p >= a.pos0 && p < pend) {
         if (a.dk) *reinterpret_cast<uint4*>(a.dk + cache_row(p) + 8 * c) = kb;
       } else if (p < a.pos0) {
-        kb = *reinterpret_cast<const uint4*>(a.ck + cache_row(p) + 8 * c);
+        kb = load_nt16(a.ck + cache_row(p) + 8 * c);
       } else {
         kb = make_uint4(0u, 0u, 0u, 0u);
       }
@@ -87,10 +87,10 @@ __global__ void __launch_bounds__(256) kv_stage_kernel(StageArgs a) {
       const int p = p0 + 4 * vq + rr;
       uint4 x = make_uint4(0u, 0u, 0u, 0u);
       if (p >= a.pos0 && p < pend) {
-        x = *reinterpret_cast<const uint4*>(a.v + ((row_b + (p - a.pos0)) * a.Hkv + h) * kHeadDim + 8 * vd);
+        x = load_nt16(a.v + ((row_b + (p - a.pos0)) * a.Hkv + h) * kHeadDim + 8 * vd);
         if (a.dv) *reinterpret_cast<uint4*>(a.dv + cache_row(p) + 8 * vd) = x;
       } else if (p < a.pos0) {
-        x = *reinterpret_cast<const uint4*>(a.cv + cache_row(p) + 8 * vd);
+        x = load_nt16(a.cv + cache_row(p) + 8 * vd);
       }
       x = bf16x8_to_f16x8(x);
       w[rr][0] = x.x; w[rr][1] = x.y; w[rr][2] = x.z; w[rr][3] = x.w;
