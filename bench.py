@@ -622,6 +622,32 @@ def cpu_baseline(S=16384, n_rows=8192, seed=1003):
 
 
 # ------------------------------------------------------------------------------------------ main
+def run_gemm_ceiling(shapes=((8192, 8192, 8192), (16384, 16384, 8192), (16384, 8192, 16384)), calls=20, warmup=5):
+    """What a vendor library's dense fp16 GEMM (torch.matmul on hipBLASLt) reaches on this GPU: the practical
+    ceiling that power sets for MFMA-dense work, the context of the attention kernel's MFMA fraction."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    out = []
+    for M, N, K in shapes:
+        a = torch.randn(M, K, device="cuda", dtype=torch.float16, generator=gen)
+        b = torch.randn(K, N, device="cuda", dtype=torch.float16, generator=gen)
+        for _ in range(warmup):
+            c = a @ b
+        sync()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(calls):
+            c = a @ b
+        e1.record()
+        sync()
+        ms = e0.elapsed_time(e1) / calls
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        log(f"gemm: fp16 {M}x{N}x{K} {ms:.3f} ms, {tf:.0f} TFLOP/s = {tf / MFMA_PEAK_TFLOPS:.3f} of the peak")
+        out.append({"M": M, "N": N, "K": K, "ms": ms, "tflops": tf, "frac": tf / MFMA_PEAK_TFLOPS})
+        del a, b, c
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -642,6 +668,9 @@ def main():
     ap.add_argument("--chunked", action="store_true",
                     help="instead of the benchmark: prefill one 262,144-token sequence in 16,384-token chunks through "
                          "the 32-layer schedule against the KV cache (one JSON line)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="instead of the benchmark: time torch's fp16 matmul (hipBLASLt) on three large square-ish "
+                         "GEMMs, the practical MFMA ceiling of this GPU (one JSON line)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="also copy a GIB-sized device tensor 3 times (a plain copy kernel of known traffic, for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -663,6 +692,14 @@ def main():
         log(f"copy calibration: 3 elementwise copies of {n * 4} bytes (read {n * 4} B + write {n * 4} B each)")
         del src, dst
         torch.cuda.empty_cache()
+    if args.gemm_ceiling:
+        print(json.dumps({
+            "metric": "dense fp16 GEMM TFLOP/s (vendor library), context for the MFMA roofline",
+            "unit": "TFLOP/s", "n_gpus": 1, "data": "synthetic", "higher_is_better": True, "dtype": "fp16",
+            "config": {"workload": "torch.matmul fp16, 20 timed calls per shape"}, "peak": MFMA_PEAK_TFLOPS,
+            "gemms": run_gemm_ceiling(),
+        }), flush=True)
+        return
     if args.chunked:
         res = run_chunked(zg)
         log(f"chunked: {res['ms_total']:.1f} ms, {res['tokens_per_s']:.0f} tokens/s, global tile kernel "
