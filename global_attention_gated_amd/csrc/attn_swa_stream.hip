@@ -353,6 +353,9 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     const int qlo = i0 + 16 * half;               // the wave's positions qlo .. qlo+15
     const bool more = c + 1 < n_steps;
     // ================= M(c) =================
+    // the compute phase is the critical one: on a SIMD this wave's instructions issue ahead of the other group's
+    // output-phase wave while it is in M
+    __builtin_amdgcn_s_setprio(1);
     // q_hat of this step is in qf (computed at the end of the previous output phase, or in the prologue); this
     // wave's q rows in LDS have been read, so the next step's go there
     load_rows(qb, QS, i0 + kStep, more);
@@ -436,6 +439,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_swa_stream_kernel(SwaStreamA
     // training: the log-sum-exp of the query's scores (natural log; scores in log2 units are s log2(e))
     if (a.lse && g == 0 && i < p_end)
       a.lse[((int64_t)b * a.Hq + kvh * kGroup + head) * a.S + i] = (mx + __log2f(l_run)) * 0.6931471805599453f;
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
 
     // ================= V(c) =================
