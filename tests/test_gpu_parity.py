@@ -1,7 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the same seeded inputs.
 
 Bar: |gpu_bf16 - oracle_fp64| <= 1e-2 per element and <= 1e-3 on average; KV-cache layout and indexing
-bit-exact (V bytes equal; K within one bf16 ulp of the oracle's rounding of k_hat).
+bit-exact (V bytes equal; K within one bf16 ulp of the oracle's rounding of k_hat, or 4e-6 absolute where the
+rotation cancels to a value near zero).
 """
 import numpy as np
 import pytest
@@ -223,7 +224,14 @@ def _cache_check(zg, cache, ocache, layer, glob):
         V = np.where(valid[:, None, :, None], V, 0)
     np.testing.assert_array_equal(V, OV)
     kd = np.abs(K.astype(np.int32) - OK.astype(np.int32))     # same sign: bit distance = ulp distance
-    assert kd.max() <= 1, f"layer {layer}: k_hat differs by {kd.max()} ulp"
+    # k_hat is computed in fp32 (the rotary angle reduced to one revolution in fp64, then rounded to 24 bits for the
+    # hardware sine and cosine: ~1e-6 absolute on the O(1) terms of x cos - y sin).  Rounded to bf16 that is one ulp
+    # at most, except where the rotation cancels to a value near zero: there the same absolute error spans a few
+    # ulps (or a sign), so elements beyond one ulp are held to it in absolute terms.
+    far = kd > 1
+    if far.any():
+        ad = np.abs(synth.bf16_bits_to_f64(K[far]) - synth.bf16_bits_to_f64(OK[far]))
+        assert ad.max() <= 4e-6, f"layer {layer}: k_hat differs by {kd[far].max()} ulp, {ad.max():.2e} absolute"
     return float(np.mean(kd != 0))
 
 
