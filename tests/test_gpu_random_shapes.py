@@ -8,7 +8,7 @@ so both SWA kernels and the global kernel see lengths that end mid-tile and mid-
 import numpy as np
 import pytest
 
-from _inputs import Layer, compare, to_host_f64
+from _inputs import Layer, compare, to_dev, to_host_f64
 from test_gpu_parity import gpu_prefill, oracle_prefill, zg  # noqa: F401  (zg is a fixture)
 
 pytestmark = pytest.mark.gpu
@@ -102,5 +102,66 @@ def test_chunked_prefill_random_splits(zg, case):
             assert all(cache.length(layer, b) == S_total for b in range(B))
             mism.append(_cache_check(zg, cache, ocache, layer, not gated))
         assert max(mism) < 0.01
+    finally:
+        cache.close()
+
+
+# ------------------------------------------------------------------------------------------ decode
+N_DECODE_CASES = 6
+
+
+def draw_decode_case(idx):
+    rng = np.random.default_rng(7500 + idx)
+    Lh = int(rng.integers(2, 5))
+    glob = sorted(int(x) + 1 for x in rng.choice(Lh, size=int(rng.integers(1, Lh)), replace=False))
+    B = int(rng.integers(1, 5))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    W = int(rng.integers(1, 65))
+    R = 2 * int(rng.integers(0, 65))
+    S0 = int(rng.integers(1, 600))
+    base = float(rng.choice([1e4, 1e7]))
+    return Lh, glob, B, G * Hkv, Hkv, W, R, S0, base
+
+
+DECODE_CASES = [draw_decode_case(i) for i in range(N_DECODE_CASES)]
+
+
+def _decode_id(c):
+    Lh, glob, B, Hq, Hkv, W, R, S0, base = c
+    return f"L{Lh}-global{'_'.join(map(str, glob))}-B{B}-{Hq}q{Hkv}kv-W{W}-R{R}-S0_{S0}-base{base:g}"
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[_decode_id(c) for c in DECODE_CASES])
+def test_decode_random_shape(zg, case):
+    """Prefill S0 tokens into a cache of Lh layers (the drawn ones global), then decode until every ring has wrapped
+    (at least 6 steps); each step against the oracle's decode, then every layer's cache image."""
+    import oracle
+    import synth
+    from test_gpu_parity import _cache_check, _decode_inputs
+    Lh, glob, B, Hq, Hkv, W, R, S0, base = case
+    eps = 1e-6
+    steps = 6 if S0 >= W else W - S0 + 6     # past the ring's first wrap in every case
+    cache = zg.KVCache(n_layers=Lh, global_layers=glob, batch=B, n_kv_heads=Hkv, window=W, max_tokens=S0 + steps + 8)
+    ocache = oracle.OracleCache(Lh, glob, B, Hkv, 128, W)
+    try:
+        wq = np.stack([synth.norm_weight_bf16(13, li, synth.TENSOR_WQ, 128) for li in range(Lh)])
+        wk = np.stack([synth.norm_weight_bf16(13, li, synth.TENSOR_WK, 128) for li in range(Lh)])
+        for li in range(Lh):
+            gated = (li + 1) not in glob
+            L = Layer(13 + S0, li, B, S0, Hq, Hkv, gated=gated)
+            L.wq, L.wk, L.dwq, L.dwk = wq[li], wk[li], to_dev(wq[li]), to_dev(wk[li])
+            gpu_prefill(zg, L, gated, W, R, base, eps, cache=cache, layer=li + 1)
+            oracle_prefill(L, gated, W, R, base, eps, cache=ocache, layer=li + 1)
+        dwq, dwk = to_dev(wq), to_dev(wk)
+        for step in range(steps):
+            p = S0 + step
+            q, k, v, g = _decode_inputs(13 + S0, Lh, B, Hq, Hkv, step)
+            got = to_host_f64(zg.hybrid_decode_step(to_dev(q), to_dev(k), to_dev(v), to_dev(g), dwq, dwk, [p] * B,
+                                                    cache, rotary_dims=R, rope_base=base, eps=eps))
+            ref = oracle.decode_step(q, k, v, g, wq, wk, [p] * B, ocache, rotary_dims=R, base=base, eps=eps)
+            compare(got, ref, f"{_decode_id(case)} step at {p}")
+        for li in range(Lh):
+            _cache_check(zg, cache, ocache, li + 1, (li + 1) in glob)
     finally:
         cache.close()
