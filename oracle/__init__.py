@@ -312,7 +312,7 @@ def _rmsnorm_backward(x, w, dy, eps: float):
 
 
 def prefill_layer_backward(q, k, v, gate, wq, wk, dout, *, window: int | None, rotary_dims: int, base: float,
-                           eps: float, delta_from_bf16_out: bool = False) -> dict:
+                           eps: float, delta_from_bf16_out: bool = False, dA_bf16: bool = False) -> dict:
     """Gradients of one attention layer's output (prefill_layer without a cache, positions 0..S-1) with respect
     to its inputs, given dout = dL/d(out) [B,S,Hq,D].  Returns float64 arrays: dq [B,S,Hq,D], dk, dv [B,S,Hkv,D],
     dgate [B,S,Hq,D] (None for a global layer), dwq, dwk [D]; and the forward's out and lse [B,S,Hq] (natural log
@@ -328,7 +328,9 @@ def prefill_layer_backward(q, k, v, gate, wq, wk, dout, *, window: int | None, r
 
     rowsum(p (.) dp) equals dout . out; delta_from_bf16_out=True forms it from the layer's bf16 output instead, as
     a backward that is handed the bf16 output must (the exact result is the default; the variant measures what
-    that rounding alone costs)."""
+    that rounding alone costs).  dA_bf16=True rounds dA to bf16 before it enters dp and dv, as a backward whose
+    gradient products take bf16 operands does (at a query that sees one key, p = 1 and the exact ds is zero; with
+    the rounded dA and the bf16 output's Delta it is not)."""
     q = np.asarray(q)
     B, S, Hq, D = q.shape
     Hkv = np.asarray(k).shape[2]
@@ -368,6 +370,8 @@ def prefill_layer_backward(q, k, v, gate, wq, wk, dout, *, window: int | None, r
                 out[b, :, h] = A * sg
                 dA = do[b, :, h] * sg
                 dg[b, :, h] = do[b, :, h] * A * sg * (1.0 - sg)
+            if dA_bf16:
+                dA = bf16_to_f64(round_bf16(dA))
             dp = dA @ vf[b, :, kh].T
             if delta_from_bf16_out:
                 delta = np.sum(do[b, :, h] * bf16_to_f64(round_bf16(out[b, :, h])), axis=1, keepdims=True)

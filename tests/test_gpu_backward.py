@@ -6,7 +6,12 @@ Bar of the backward, per gradient X against the exact X_ref (elementwise, then t
     |err| <= 2 |D_X| + 2^-7 |X_ref| + R_X / 16,        mean |err| <= 2 mean |D_X| + 0.005 R_X
 with R_X = rms(X_ref) (dv's rms where X_ref is identically zero: one visible key), and D_X the change in the
 exact gradient when Delta_i = dout_i . out_i is formed from the bf16 output, as this backward (the standard
-flash-attention form) must: out is handed over in bf16, 2^-9 relative per element.  The other terms: the bf16
+flash-attention form) must: out is handed over in bf16, 2^-9 relative per element; and when dA = dout (.)
+sigmoid(g) enters dp and dv as the bf16 operand the gradient products take.  At the first positions of a sequence,
+where a query sees one to three keys (p near 1), ds = p (dp - Delta) is the difference of two values of size
+|dA| |v| whose exact difference is zero or small, and these two roundings are most of the error there; R_X, the
+rms over the whole gradient, shrinks as windows widen and sequences grow, so the R_X / 16 term alone does not cover
+them (a seeded random case with 32 query heads, W 200-300, S 1045: 1.04 x that bound at positions 0-2 only).  The other terms: the bf16
 rounding of every result (2^-9 |X|, 2^-7 leaves margin), and the bf16 operands of the gradient products (dA, P,
 dS, q_hat: 2^-9 each, fp32 accumulation), whose errors scale with the summed terms rather than with the result:
 ds_ij = p_ij (dp_ij - Delta_i) subtracts two values of size ~sqrt(D) |dout| |v| to get a much smaller one.
@@ -38,7 +43,8 @@ def _problem(seed, gated, B, S, Hq, Hkv, W):
     dout = synth.normal_bf16(seed, 1, synth.TENSOR_DOUT, (B, S, Hq, 128))
     kw = dict(window=W if gated else None, rotary_dims=42, base=1e4, eps=1e-6)
     ref = oracle.prefill_layer_backward(L.q, L.k, L.v, L.gate, L.wq, L.wk, dout, **kw)
-    ref16 = oracle.prefill_layer_backward(L.q, L.k, L.v, L.gate, L.wq, L.wk, dout, delta_from_bf16_out=True, **kw)
+    ref16 = oracle.prefill_layer_backward(L.q, L.k, L.v, L.gate, L.wq, L.wk, dout, delta_from_bf16_out=True,
+                                          dA_bf16=True, **kw)
     return L, dout, ref, ref16
 
 

@@ -165,3 +165,53 @@ def test_decode_random_shape(zg, case):
             _cache_check(zg, cache, ocache, li + 1, (li + 1) in glob)
     finally:
         cache.close()
+
+
+# ------------------------------------------------------------------------------------------ backward
+N_BACKWARD_CASES = 6
+
+
+def draw_backward_case(idx):
+    rng = np.random.default_rng(7700 + idx)
+    gated = idx % 3 != 2
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = 4                                       # the backward's one GQA group (others are EUNSUPPORTED)
+    W = int(rng.integers(1, 300)) if gated else 0
+    R = 2 * int(rng.integers(0, 65))
+    S = int(rng.integers(1, (1500 if gated else 1000) // B + 1))
+    base = float(rng.choice([1e4, 1e7]))
+    eps = float(rng.choice([1e-6, 1e-5]))
+    return gated, B, S, G * Hkv, Hkv, W, R, base, eps
+
+
+BACKWARD_CASES = [draw_backward_case(i) for i in range(N_BACKWARD_CASES)]
+
+
+def _backward_id(c):
+    gated, B, S, Hq, Hkv, W, R, base, eps = c
+    return f"{'swa' if gated else 'global'}-B{B}-S{S}-{Hq}q{Hkv}kv-W{W}-R{R}-base{base:g}-eps{eps:g}"
+
+
+@pytest.mark.parametrize("case", BACKWARD_CASES, ids=[_backward_id(c) for c in BACKWARD_CASES])
+def test_training_backward_random_shape(zg, case):
+    """The training forward's out and lse feed the backward; forward against the oracle at the forward bar, every
+    gradient against the oracle's exact gradients at the backward bar of the fixed-shape backward tests."""
+    import oracle
+    import synth
+    from test_gpu_backward import _check
+    gated, B, S, Hq, Hkv, W, R, base, eps = case
+    L = Layer(8100 + S, 1, B, S, Hq, Hkv, gated=gated)
+    dout = synth.normal_bf16(8100 + S, 1, synth.TENSOR_DOUT, (B, S, Hq, 128))
+    kw = dict(window=W if gated else None, rotary_dims=R, base=base, eps=eps)
+    ref = oracle.prefill_layer_backward(L.q, L.k, L.v, L.gate, L.wq, L.wk, dout, **kw)
+    ref16 = oracle.prefill_layer_backward(L.q, L.k, L.v, L.gate, L.wq, L.wk, dout, delta_from_bf16_out=True,
+                                          dA_bf16=True, **kw)
+    out, lse = zg.prefill_train(L.dq, L.dk, L.dv, L.dgate, L.dwq, L.dwk, window=W, rotary_dims=R, rope_base=base,
+                                eps=eps)
+    compare(to_host_f64(out), ref["out"], f"{_backward_id(case)} training forward out")
+    compare(lse.detach().cpu().numpy().transpose(0, 2, 1).astype(np.float64), ref["lse"],
+            f"{_backward_id(case)} training forward lse")
+    g = zg.prefill_backward(L.dq, L.dk, L.dv, L.dgate, L.dwq, L.dwk, out, lse, to_dev(dout), window=W,
+                            rotary_dims=R, rope_base=base, eps=eps)
+    _check(g, ref, ref16, gated, _backward_id(case))

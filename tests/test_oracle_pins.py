@@ -615,6 +615,24 @@ def test_backward_window_one_and_closed_gate():
         assert not np.any(z[n]), n
 
 
+def test_backward_bf16_dA_variant():
+    """dA_bf16 rounds dA = dout (.) sigmoid(g) to bf16 before dp and dv.  W = 1 (p = 1): dv is then exactly the sum
+    over the group's heads of the rounded dA; with the exact Delta (the row sum of p dp, same dp) ds is still zero,
+    so dq = dk = 0; the gate's gradient does not go through dA and is unchanged."""
+    B, S, Hq, Hkv = 1, 9, 2, 1
+    q, k, v, g, wq, wk, do = _bwd_problem(5, B, S, Hq, Hkv)
+    kw = dict(window=1, rotary_dims=42, base=1e4, eps=1e-6)
+    r = oracle.prefill_layer_backward(q, k, v, g, wq, wk, do, dA_bf16=True, **kw)
+    exact = oracle.prefill_layer_backward(q, k, v, g, wq, wk, do, **kw)
+    sg = 1.0 / (1.0 + np.exp(-oracle.bf16_to_f64(g)))
+    dA16 = oracle.bf16_to_f64(oracle.round_bf16(do * sg))
+    np.testing.assert_allclose(r["dv"][:, :, 0], dA16.sum(axis=2), rtol=1e-12, atol=1e-13)
+    assert np.abs(r["dv"] - exact["dv"]).max() > 0          # the rounding is applied
+    for n in ("dq", "dk", "dwq", "dwk"):
+        assert np.abs(r[n]).max() < 1e-13, n
+    np.testing.assert_array_equal(r["dgate"], exact["dgate"])
+
+
 @pytest.mark.parametrize("window", [7, None])
 def test_backward_rows_equals_full_backward(window):
     """The row-sampled backward (row blocks, one KV head) against the whole-layer backward at a small size, for
